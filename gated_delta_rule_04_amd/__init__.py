@@ -1,0 +1,169 @@
+"""Python binding of libgdn.so, the MI355X gated delta-rule library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C-ABI declared in ``include/gdn.h``.  PyTorch supplies
+device memory and the current HIP stream.  There is no CPU fallback: if the
+library is missing or does not load, every call raises.
+
+    o, S_final = chunk_fwd(q, k, v, alpha, beta, S0)      # prefill
+    o = decode_step(q, k, v, alpha, beta, S)               # one token, S in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["chunk_fwd", "decode_step", "load", "lib_path", "GDNError",
+           "DECAY_NONE", "DECAY_SCALAR", "DECAY_CHANNEL", "EXPORTED_SYMBOLS"]
+
+DECAY_NONE, DECAY_SCALAR, DECAY_CHANNEL = 0, 1, 2
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step",
+                    "gdn_status_string", "gdn_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GDNError(RuntimeError):
+    """A non-zero gdn_status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgdn.so (once).  Raises if it is missing: there is no fallback."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libgdn.so is not built (%s); run "
+                               "`python -m gated_delta_rule_04_amd.build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        lib.gdn_chunk_fwd_workspace_bytes.argtypes = [i] * 8
+        lib.gdn_chunk_fwd_workspace_bytes.restype = sz
+        lib.gdn_chunk_fwd.argtypes = [vp] * 8 + [vp, sz] + [i] * 8 + [vp]
+        lib.gdn_chunk_fwd.restype = i
+        lib.gdn_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
+        lib.gdn_decode_step.restype = i
+        lib.gdn_status_string.argtypes = [i]
+        lib.gdn_status_string.restype = ctypes.c_char_p
+        lib.gdn_version.argtypes = []
+        lib.gdn_version.restype = i
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().gdn_status_string(status).decode()
+        raise GDNError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _infer_mode(alpha, q_dim):
+    if alpha is None:
+        return DECAY_NONE
+    return DECAY_SCALAR if alpha.dim() == q_dim - 1 else DECAY_CHANNEL
+
+
+def _require(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16, mode=DECAY_SCALAR, chunk=64) -> int:
+    return int(load().gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, _DTYPES[dtype], mode))
+
+
+def chunk_fwd(q, k, v, alpha, beta, S0=None, *, mode=None, chunk=64, o=None, S_final=None,
+              need_final=True, stream=None):
+    """Chunked prefill through ``gdn_chunk_fwd``.
+
+    q, k [B, T, H, dk]; v [B, T, H, dv] (fp32 or bf16, one dtype);
+    alpha fp32 [B, T, H] (scalar decay), ``dtype`` [B, T, H, dk] (per-channel
+    decay) or None (no decay); beta fp32 [B, T, H]; S0 fp32 [B, H, dv, dk] or None.
+    Returns (o, S_final); S_final is None when ``need_final`` is False."""
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, dtype)
+    _require(beta, "beta", torch.float32)
+    _require(S0, "S0", torch.float32)
+    if mode == DECAY_SCALAR:
+        _require(alpha, "alpha", torch.float32)
+    elif mode == DECAY_CHANNEL:
+        _require(alpha, "alpha", dtype)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dtype, device=q.device)
+    if S_final is None and need_final:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _require(o, "o", dtype)
+    _require(S_final, "S_final", torch.float32)
+    ws_bytes = int(lib.gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, _DTYPES[dtype], mode))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None), _ptr(beta),
+                           _ptr(S0), _ptr(o), _ptr(S_final), _ptr(ws), ws_bytes,
+                           B, T, H, dk, dv, chunk, _DTYPES[dtype], mode, _stream(stream))
+    _check(st)
+    return o, S_final
+
+
+def decode_step(q, k, v, alpha, beta, S, *, mode=None, o=None, stream=None):
+    """One decode step through ``gdn_decode_step``; S is updated in place.
+
+    q, k [B, H, dk]; v [B, H, dv]; alpha fp32 [B, H], ``dtype`` [B, H, dk] or
+    None; beta fp32 [B, H]; S fp32 [B, H, dv, dk].  Returns o [B, H, dv]."""
+    lib = load()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, dtype)
+    _require(beta, "beta", torch.float32)
+    _require(S, "S", torch.float32)
+    if mode == DECAY_SCALAR:
+        _require(alpha, "alpha", torch.float32)
+    elif mode == DECAY_CHANNEL:
+        _require(alpha, "alpha", dtype)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dtype, device=q.device)
+    _require(o, "o", dtype)
+    st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None), _ptr(beta),
+                             _ptr(S), _ptr(o), B, H, dk, dv, _DTYPES[dtype], mode, _stream(stream))
+    _check(st)
+    return o

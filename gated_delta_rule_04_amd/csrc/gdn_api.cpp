@@ -1,0 +1,159 @@
+// C-ABI of libgdn.so: argument validation, then the launches.
+// The declarations, layouts and error semantics are in include/gdn.h.
+#include "gdn.h"
+
+#include <stdint.h>
+
+#include "gdn_internal.h"
+
+namespace {
+
+constexpr int kChunk = 64;
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+
+size_t elem_size(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+// Byte range [lo, hi) of a buffer; an empty range never overlaps.
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, size_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, p ? lo + bytes : lo};
+}
+
+bool overlaps(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// n = a * b * c * d with an overflow check against 2^62 elements.
+bool count4(long long a, long long b, long long c, long long d, long long* n) {
+  const long long lim = 1LL << 62;
+  long long x = 1;
+  for (long long f : {a, b, c, d}) {
+    if (f < 0) return false;
+    if (f != 0 && x > lim / f) return false;
+    x *= f;
+  }
+  *n = x;
+  return true;
+}
+
+gdn_status check_common(int B, int H, int dk, int dv, gdn_dtype dtype, gdn_decay mode) {
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (mode != GDN_DECAY_NONE && mode != GDN_DECAY_SCALAR && mode != GDN_DECAY_CHANNEL)
+    return GDN_ERR_DTYPE;
+  if (B < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_SHAPE;
+  if (!supported_dim(dk) || !supported_dim(dv)) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return 100; }
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: invalid or overflowing size";
+    case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unknown dtype or decay mode";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: d_k, d_v or chunk not supported";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace too small";
+    case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: the HIP runtime refused the launch";
+    case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: forbidden aliasing between arguments";
+  }
+  return "unknown gdn_status";
+}
+
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                     gdn_dtype dtype, gdn_decay mode) {
+  // The fused chunk kernel keeps every intermediate on chip.
+  (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)chunk; (void)dtype; (void)mode;
+  return 0;
+}
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                         const float* beta, const float* S0, void* o, float* S_final,
+                         void* workspace, size_t workspace_bytes, int B, int T, int H, int dk,
+                         int dv, int chunk, gdn_dtype dtype, gdn_decay mode,
+                         hipStream_t stream) {
+  gdn_status st = check_common(B, H, dk, dv, dtype, mode);
+  if (st != GDN_OK) return st;
+  if (T < 0) return GDN_ERR_SHAPE;
+  if (chunk != kChunk) return GDN_ERR_UNSUPPORTED;
+  long long nqk, nv, ntok, nS;
+  if (!count4(B, T, H, dk, &nqk) || !count4(B, T, H, dv, &nv) || !count4(B, T, H, 1, &ntok) ||
+      !count4(B, H, dv, dk, &nS))
+    return GDN_ERR_SHAPE;
+  if ((long long)B * H * (dv / 32) > 0x7fffffffLL) return GDN_ERR_SHAPE;
+  if (workspace_bytes < gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, mode))
+    return GDN_ERR_WORKSPACE;
+  (void)workspace;
+  if (B == 0 || H == 0) return GDN_OK;
+  const bool has_tokens = T > 0;
+  if (has_tokens) {
+    if (!q || !k || !v || !beta || !o) return GDN_ERR_NULL;
+    if (mode != GDN_DECAY_NONE && !alpha) return GDN_ERR_NULL;
+  }
+  if (!has_tokens && !S_final) return GDN_OK;  // nothing to write
+
+  const size_t es = elem_size(dtype);
+  const size_t a_bytes = mode == GDN_DECAY_SCALAR ? (size_t)ntok * 4
+                         : mode == GDN_DECAY_CHANNEL ? (size_t)nqk * es : 0;
+  Range rq = range_of(has_tokens ? q : nullptr, (size_t)nqk * es);
+  Range rk = range_of(has_tokens ? k : nullptr, (size_t)nqk * es);
+  Range rv = range_of(has_tokens ? v : nullptr, (size_t)nv * es);
+  Range ra = range_of(has_tokens && mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes);
+  Range rb = range_of(has_tokens ? beta : nullptr, (size_t)ntok * 4);
+  Range rs0 = range_of(S0, (size_t)nS * 4);
+  Range ro = range_of(has_tokens ? o : nullptr, (size_t)nv * es);
+  Range rsf = range_of(S_final, (size_t)nS * 4);
+  for (Range in : {rq, rk, rv, ra, rb, rs0})
+    if (overlaps(ro, in)) return GDN_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, ra, rb, ro})
+    if (overlaps(rsf, in)) return GDN_ERR_ALIAS;
+  if (overlaps(rsf, rs0) && (const void*)S_final != (const void*)S0) return GDN_ERR_ALIAS;
+
+  gdn::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_final, B, T, H, dk, dv, (int)dtype,
+                     (int)mode};
+  return gdn::launch_prefill(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                           const float* beta, float* S, void* o, int B, int H, int dk, int dv,
+                           gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
+  gdn_status st = check_common(B, H, dk, dv, dtype, mode);
+  if (st != GDN_OK) return st;
+  long long nqk, nv, nh, nS;
+  if (!count4(B, H, dk, 1, &nqk) || !count4(B, H, dv, 1, &nv) || !count4(B, H, 1, 1, &nh) ||
+      !count4(B, H, dv, dk, &nS))
+    return GDN_ERR_SHAPE;
+  if ((long long)B * H > 0x7fffffffLL) return GDN_ERR_SHAPE;
+  if (B == 0 || H == 0) return GDN_OK;
+  if (!q || !k || !v || !beta || !S || !o) return GDN_ERR_NULL;
+  if (mode != GDN_DECAY_NONE && !alpha) return GDN_ERR_NULL;
+
+  const size_t es = elem_size(dtype);
+  const size_t a_bytes = mode == GDN_DECAY_SCALAR ? (size_t)nh * 4
+                         : mode == GDN_DECAY_CHANNEL ? (size_t)nqk * es : 0;
+  Range rq = range_of(q, (size_t)nqk * es), rk = range_of(k, (size_t)nqk * es);
+  Range rv = range_of(v, (size_t)nv * es);
+  Range ra = range_of(mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes);
+  Range rb = range_of(beta, (size_t)nh * 4);
+  Range rs = range_of(S, (size_t)nS * 4), ro = range_of(o, (size_t)nv * es);
+  for (Range in : {rq, rk, rv, ra, rb, rs})
+    if (overlaps(ro, in)) return GDN_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, ra, rb})
+    if (overlaps(rs, in)) return GDN_ERR_ALIAS;
+
+  gdn::DecodeArgs a{q, k, v, alpha, beta, S, o, B, H, dk, dv, (int)dtype, (int)mode};
+  return gdn::launch_decode(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // extern "C"

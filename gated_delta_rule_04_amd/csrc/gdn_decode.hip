@@ -1,0 +1,164 @@
+// Decode step of the gated delta rule: one token, state updated in place.
+//
+// Per state row i (a value channel) the step is the recurrence body:
+//   s_k = S_i D k,  s_q = S_i D q,  u_i = beta (v_i - s_k),
+//   o_i = s_q + u_i (k . q),        S_i <- S_i D + u_i k^T
+// which is the predict/correct reading of the Gated DeltaNet output ("Enhancing
+// Linear Attention with Residual Learning" notes, section 1.2, Table 1) and needs
+// the row only once for both dot products.  Rows are independent linear systems
+// that share the key-side transition ("On State Reduction in Linear Attention"
+// notes, section 2.5), so every row is handled by its own group of lanes with
+// no cross-row communication.
+//
+// Layout of the work: one 256-thread workgroup per (b, h) head.  Eight lanes
+// share a row; lane l of the group owns the float4 columns {4l + 32j}, so each
+// 64-lane wave touches eight rows as eight contiguous 128-byte segments per
+// load instruction (coalesced 128-bit accesses).  The fp32 row is held in
+// registers between the read and the write, and the two row dot products are
+// finished with three xor-shuffles over the eight lanes.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLanesPerRow = 8;
+
+__device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ inline float4 load4(const __bf16* p) {
+  uint2 raw = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16_to_f32(raw.x & 0xffff), bf16_to_f32(raw.x >> 16),
+                     bf16_to_f32(raw.y & 0xffff), bf16_to_f32(raw.y >> 16));
+}
+
+__device__ inline float load1(const float* p) { return *p; }
+__device__ inline float load1(const __bf16* p) {
+  return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+}
+
+__device__ inline void store1(float* p, float x) { *p = x; }
+__device__ inline void store1(__bf16* p, float x) { *p = (__bf16)x; }
+
+__device__ inline float group8_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  return x;
+}
+
+template <typename E, int DK, int DV, int MODE>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  constexpr int NQ = DK / (4 * kLanesPerRow);            // float4 per lane per row
+  constexpr int NR = DV * kLanesPerRow / kThreads;       // rows per thread
+  static_assert(NQ >= 1 && NR >= 1, "unsupported head size");
+
+  const size_t bh = blockIdx.x;
+  const int l8 = threadIdx.x % kLanesPerRow;
+  const int g = threadIdx.x / kLanesPerRow;              // row group 0..31
+
+  const E* q = static_cast<const E*>(a.q) + bh * DK;
+  const E* k = static_cast<const E*>(a.k) + bh * DK;
+  const E* v = static_cast<const E*>(a.v) + bh * DV;
+  float* S = a.S + bh * (size_t)DV * DK;
+  E* o = static_cast<E*>(a.o) + bh * DV;
+
+  // State rows first: these are the bytes that matter, issue them early.
+  float4 s[NR][NQ];
+#pragma unroll
+  for (int m = 0; m < NR; ++m)
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) s[m][j] = load4(S + (size_t)(g + 32 * m) * DK + 4 * l8 + 32 * j);
+
+  float4 kf[NQ], qf[NQ], af[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    kf[j] = load4(k + 4 * l8 + 32 * j);
+    qf[j] = load4(q + 4 * l8 + 32 * j);
+    if (MODE == 2) af[j] = load4(static_cast<const E*>(a.alpha) + bh * DK + 4 * l8 + 32 * j);
+  }
+  const float beta = a.beta[bh];
+  float alpha = 1.f;
+  if (MODE == 1) alpha = static_cast<const float*>(a.alpha)[bh];
+  float vr[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) vr[m] = load1(v + g + 32 * m);
+
+  // k . q over the head (every group computes it; it is tiny)
+  float kq = 0.f;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
+    kq += kf[j].x * qf[j].x + kf[j].y * qf[j].y + kf[j].z * qf[j].z + kf[j].w * qf[j].w;
+  kq = group8_sum(kq);
+
+  // D k and D q for the per-channel decay (the scalar decay is applied to the sums)
+  float4 kd[NQ], qd[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    if (MODE == 2) {
+      kd[j] = make_float4(kf[j].x * af[j].x, kf[j].y * af[j].y, kf[j].z * af[j].z, kf[j].w * af[j].w);
+      qd[j] = make_float4(qf[j].x * af[j].x, qf[j].y * af[j].y, qf[j].z * af[j].z, qf[j].w * af[j].w);
+    } else {
+      kd[j] = kf[j];
+      qd[j] = qf[j];
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    float pk = 0.f, pq = 0.f;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      pk += s[m][j].x * kd[j].x + s[m][j].y * kd[j].y + s[m][j].z * kd[j].z + s[m][j].w * kd[j].w;
+      pq += s[m][j].x * qd[j].x + s[m][j].y * qd[j].y + s[m][j].z * qd[j].z + s[m][j].w * qd[j].w;
+    }
+    pk = group8_sum(pk);
+    pq = group8_sum(pq);
+    if (MODE == 1) {
+      pk *= alpha;
+      pq *= alpha;
+    }
+    const float u = beta * (vr[m] - pk);
+    const float out = pq + u * kq;
+    if (l8 == 0) store1(o + g + 32 * m, out);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      float4 d = MODE == 2 ? af[j] : make_float4(alpha, alpha, alpha, alpha);
+      float4 r;
+      r.x = s[m][j].x * d.x + u * kf[j].x;
+      r.y = s[m][j].y * d.y + u * kf[j].y;
+      r.z = s[m][j].z * d.z + u * kf[j].z;
+      r.w = s[m][j].w * d.w + u * kf[j].w;
+      *reinterpret_cast<float4*>(S + (size_t)(g + 32 * m) * DK + 4 * l8 + 32 * j) = r;
+    }
+  }
+}
+
+template <typename E, int DK, int DV>
+hipError_t launch_mode(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)(a.B * a.H)), block(kThreads);
+  switch (a.mode) {
+    case 0: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 0>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 1>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 2>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_dtype(const DecodeArgs& a, hipStream_t stream) {
+  if (a.dk == 128 && a.dv == 128) return launch_mode<E, 128, 128>(a, stream);
+  if (a.dk == 64 && a.dv == 128) return launch_mode<E, 64, 128>(a, stream);
+  if (a.dk == 128 && a.dv == 64) return launch_mode<E, 128, 64>(a, stream);
+  return launch_mode<E, 64, 64>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  return a.dtype == 1 ? launch_dtype<__bf16>(a, stream) : launch_dtype<float>(a, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,48 @@
+// Internal declarations shared by the translation units of libgdn.so.
+// Not part of the C-ABI; include/gdn.h is.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Arguments of one prefill launch.  Pointers are device pointers; layouts are
+// the C-ABI's: q, k [B, T, H, dk]; v, o [B, T, H, dv]; alpha [B, T, H] or
+// [B, T, H, dk]; beta [B, T, H]; S0, S_final [B, H, dv, dk].
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* alpha;
+  const float* beta;
+  const float* S0;   // may be null (zeros)
+  void* o;
+  float* S_final;    // may be null
+  int B, T, H, dk, dv;
+  int dtype;         // 0 fp32, 1 bf16
+  int mode;          // 0 none, 1 scalar, 2 channel
+};
+
+// Arguments of one decode launch: q, k [B, H, dk]; v, o [B, H, dv];
+// alpha [B, H] or [B, H, dk]; beta [B, H]; S [B, H, dv, dk] in/out.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* alpha;
+  const float* beta;
+  float* S;
+  void* o;
+  int B, H, dk, dv;
+  int dtype;
+  int mode;
+};
+
+// Enqueue the prefill kernels; returns the launch status.
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Enqueue one decode step; returns the launch status.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace gdn

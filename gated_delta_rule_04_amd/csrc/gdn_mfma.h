@@ -1,0 +1,113 @@
+// MFMA tile helpers for gfx950 (CDNA4), wave64.
+//
+// All products in the chunk kernels are "NT" products with both operands stored
+// in LDS with the contraction index contiguous:
+//     C[m][n] += sum_k A[m][k] * B[n][k]
+// One call computes one 32x32 fp32 tile.  Operand fragments: lane l reads the
+// eight consecutive k values A[l % 32][k0 + 8 (l / 32) + 0..7] (one 16-byte LDS
+// read for bf16, two for fp32) and the same for B.
+//   bf16: one v_mfma_f32_32x32x16_bf16 per 16 k values.
+//   fp32: eight v_mfma_f32_32x32x2f32 per 16 k values; MFMA m consumes k value
+//         8 (l / 32) + m of each lane, which is a permutation of the k order of
+//         the sum and leaves the result a full-fp32 dot product.
+// Accumulator element v of lane l holds C[row][col] with
+//     row = 8 (v / 4) + 4 (l / 32) + (v % 4),   col = l % 32.
+// (Layouts checked on the device against a host product.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename E>
+struct Frag;
+
+template <>
+struct Frag<__bf16> {
+  bf16x8 v;
+};
+
+template <>
+struct Frag<float> {
+  float4 lo, hi;
+};
+
+__device__ inline Frag<__bf16> frag_load(const __bf16* p) {
+  Frag<__bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+
+__device__ inline Frag<float> frag_load(const float* p) {
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const float4*>(p);
+  f.hi = *reinterpret_cast<const float4*>(p + 4);
+  return f;
+}
+
+__device__ inline void mma16(f32x16& acc, const Frag<__bf16>& a, const Frag<__bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+__device__ inline void mma16(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+}
+
+// acc += A[0:32, 0:16 nk] * B[0:32, 0:16 nk]^T, A and B in LDS with leading
+// dimensions lda and ldb (elements), k contiguous.
+template <typename E>
+__device__ inline void tile_nt(f32x16& acc, const E* A, int lda, const E* B, int ldb, int nk,
+                               int lane) {
+  const E* pa = A + (lane & 31) * lda + (lane >> 5) * 8;
+  const E* pb = B + (lane & 31) * ldb + (lane >> 5) * 8;
+#pragma unroll 4
+  for (int s = 0; s < nk; ++s) mma16(acc, frag_load(pa + 16 * s), frag_load(pb + 16 * s));
+}
+
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Row of accumulator element (4 g + e) for this lane: 8 g + 4 (lane / 32) + e.
+__device__ inline int acc_row(int g, int e, int lane) { return 8 * g + 4 * (lane >> 5) + e; }
+
+__device__ inline float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <typename E>
+__device__ inline E to_elem(float x);
+template <>
+__device__ inline float to_elem<float>(float x) { return x; }
+template <>
+__device__ inline __bf16 to_elem<__bf16>(float x) { return (__bf16)x; }
+
+// Store four consecutive elements (8 or 16 bytes).
+__device__ inline void store4(__bf16* p, float a, float b, float c, float d) {
+  bf16x4 t;
+  t[0] = (__bf16)a; t[1] = (__bf16)b; t[2] = (__bf16)c; t[3] = (__bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = t;
+}
+__device__ inline void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+__device__ inline float load_elem(const float* p) { return *p; }
+__device__ inline float load_elem(const __bf16* p) {
+  return bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(p));
+}
+
+}  // namespace gdn

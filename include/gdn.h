@@ -1,0 +1,151 @@
+/*
+ * gdn.h — C-ABI of the MI355X (gfx950) gated delta-rule library (libgdn.so).
+ *
+ * The library computes the gated delta-rule linear-attention recurrence, per
+ * batch entry b and head h, with a state S of shape d_v x d_k:
+ *
+ *     S_t = S_{t-1} D_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+ *
+ * where D_t is
+ *   GDN_DECAY_NONE     I                   (DeltaNet: "Linear Attention
+ *                                           Architectures" notes, section 2.3,
+ *                                           Eqs. 9-10 and 14; "On State Reduction
+ *                                           in Linear Attention" notes, section
+ *                                           2.1, Eq. 2)
+ *   GDN_DECAY_SCALAR   alpha_t I           (Gated DeltaNet: linear-attention
+ *                                           notes, section 2.4, Eqs. 15-17)
+ *   GDN_DECAY_CHANNEL  Diag(alpha_t)       (Kimi Delta Attention: same notes,
+ *                                           section 2.5, Eqs. 18-20; the diagonal
+ *                                           acts on the key channels, from the right)
+ *
+ * The decay is applied before the write error is formed, and the output reads
+ * the updated state (linear-attention notes, section 2.1, Eq. 8).  No scale
+ * is applied to q (NextTransformer "method sources" page, backend section:
+ * scale = 1); q and k are used as given (a layer normalises them beforehand).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major tensors in
+ *    the layouts stated per argument.  The caller owns every buffer; the library
+ *    allocates nothing, keeps no global state and is re-entrant.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *    returns without synchronising.
+ *  - Arguments are validated before anything is enqueued.  On any error the
+ *    call returns a negative gdn_status, writes nothing and enqueues nothing.
+ *    A failed kernel launch returns GDN_ERR_LAUNCH.  No exception crosses the ABI.
+ *  - Gates may take their boundary values: beta in [0, 1], alpha in [0, 1].
+ *  - Supported sizes: d_k in {64, 128}, d_v in {64, 128}, chunk = 64.
+ *    Other sizes return GDN_ERR_UNSUPPORTED.
+ *  - Per-channel decay numerics: inside a chunk the kernels form decay ratios
+ *    relative to anchors at most 16 tokens away, so results are exact up to
+ *    rounding as long as, for every channel, the product of alpha over any 16
+ *    consecutive tokens is at least 1e-36.  Stronger decay can overflow fp32
+ *    inside a chunk and yield non-finite outputs.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = -1,         /* a required pointer is NULL                      */
+  GDN_ERR_SHAPE = -2,        /* a size is negative, zero where it must not be,  */
+                             /* or the element count overflows                  */
+  GDN_ERR_DTYPE = -3,        /* unknown gdn_dtype or gdn_decay value            */
+  GDN_ERR_UNSUPPORTED = -4,  /* d_k, d_v or chunk outside the supported set     */
+  GDN_ERR_WORKSPACE = -5,    /* workspace smaller than the size queried         */
+  GDN_ERR_LAUNCH = -6,       /* the HIP runtime refused a launch or a copy      */
+  GDN_ERR_ALIAS = -7         /* forbidden aliasing between inputs and outputs   */
+} gdn_status;
+
+/* Element type of q, k, v and o (and of a per-channel alpha). */
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Decay family; see the header comment. */
+typedef enum gdn_decay {
+  GDN_DECAY_NONE = 0,     /* alpha unused, may be NULL                          */
+  GDN_DECAY_SCALAR = 1,   /* alpha fp32, one value per (b, t, h)                */
+  GDN_DECAY_CHANNEL = 2   /* alpha in `dtype`, one value per (b, t, h, key chan)*/
+} gdn_decay;
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 means the
+ * workspace pointer may be NULL).  Returns 0 for arguments gdn_chunk_fwd would
+ * reject.
+ */
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                     gdn_dtype dtype, gdn_decay mode);
+
+/*
+ * Chunked prefill over T tokens (any T >= 0; the last chunk may be partial).
+ *
+ *   q, k      [B, T, H, dk]   `dtype`
+ *   v         [B, T, H, dv]   `dtype`
+ *   alpha     mode SCALAR: fp32 [B, T, H]; mode CHANNEL: `dtype` [B, T, H, dk];
+ *             mode NONE: ignored (may be NULL)
+ *   beta      fp32 [B, T, H]
+ *   S0        fp32 [B, H, dv, dk], the state before token 0; NULL means zeros
+ *             ("On State Reduction" notes, section 2.1: S_0 = 0)
+ *   o         [B, T, H, dv]   `dtype`, written: o_t = S_t q_t, rounded to
+ *             nearest-even from fp32 when `dtype` is bf16
+ *   S_final   fp32 [B, H, dv, dk], written: the state after the last token; may
+ *             be NULL when the caller does not need it.  S_final == S0 (in-place
+ *             hand-off) is allowed; no other output may alias an input.
+ *   workspace device memory of at least gdn_chunk_fwd_workspace_bytes(...)
+ *             bytes (may be NULL when that is 0); its contents on entry do not
+ *             matter and on return are unspecified.
+ *
+ * The chunkwise form (decay-weighted beta K K^T, a unit-lower-triangular
+ * solve, then a sequential pass over chunks carrying the fp32 state) is an
+ * exact rewrite of the token recurrence; the NextTransformer page's numerics
+ * section describes the same precision split used here: fp32 carried state
+ * and accumulation, bf16 operands when the inputs are bf16.
+ * T = 0 copies S0 (or zeros) to S_final and writes no o.
+ */
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                         const void* alpha, const float* beta, const float* S0,
+                         void* o, float* S_final,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int T, int H, int dk, int dv, int chunk,
+                         gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
+
+/*
+ * One decode step (the recurrence body for a single token), S updated in place.
+ *
+ *   q, k      [B, H, dk]   `dtype`
+ *   v         [B, H, dv]   `dtype`
+ *   alpha     mode SCALAR: fp32 [B, H]; mode CHANNEL: `dtype` [B, H, dk];
+ *             mode NONE: ignored (may be NULL)
+ *   beta      fp32 [B, H]
+ *   S         fp32 [B, H, dv, dk], read and overwritten with the new state
+ *   o         [B, H, dv]   `dtype`, written
+ *
+ * Per state row i the step needs S_i D k and S_i D q (one pass over the row),
+ * then u_i = beta (v_i - S_i D k), o_i = S_i D q + u_i (k . q) and
+ * S_i <- S_i D + u_i k^T — the predict/correct reading of the Gated DeltaNet
+ * output ("Enhancing Linear Attention with Residual Learning" notes, section
+ * 1.2, Table 1) — so the fp32 state is read once and written once.
+ * o must not alias S, q, k or v.
+ */
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
+                           const void* alpha, const float* beta, float* S, void* o,
+                           int B, int H, int dk, int dv,
+                           gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* gdn_status_string(gdn_status s);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,130 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/gdn.h
+declares, and its host-side validation rejects bad arguments before any launch.
+
+Only calls that validation must reject are made here (no compute call runs
+without a GPU).  The pointers are fake addresses: validation never dereferences
+them, and every call below fails validation before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "gated_delta_rule_04_amd", "libgdn.so")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_WS, E_LAUNCH, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libgdn.so is not built; run python -m gated_delta_rule_04_amd.build")
+    lib = ctypes.CDLL(LIB)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.gdn_chunk_fwd.argtypes = [vp] * 8 + [vp, sz] + [i] * 8 + [vp]
+    lib.gdn_chunk_fwd.restype = i
+    lib.gdn_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
+    lib.gdn_decode_step.restype = i
+    lib.gdn_status_string.argtypes = [i]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_chunk_fwd_workspace_bytes.argtypes = [i] * 8
+    lib.gdn_chunk_fwd_workspace_bytes.restype = sz
+    return lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"gdn_chunk_fwd", "gdn_decode_step", "gdn_chunk_fwd_workspace_bytes",
+            "gdn_status_string", "gdn_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    import gated_delta_rule_04_amd as gdn
+    assert set(gdn.EXPORTED_SYMBOLS) == set(names)
+
+
+def test_status_strings(lib):
+    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_WS, E_LAUNCH, E_ALIAS):
+        s = lib.gdn_status_string(st)
+        assert s and s.startswith(b"GDN_")
+    assert lib.gdn_status_string(12345) == b"unknown gdn_status"
+    assert lib.gdn_version() == 100
+
+
+# fake, disjoint device addresses (never dereferenced: every call fails validation)
+def _bufs(base=1 << 40, span=1 << 36):
+    return [base + i * span for i in range(8)]
+
+
+def _fwd(lib, B=2, T=100, H=3, dk=128, dv=128, chunk=64, dtype=1, mode=1, ptrs=None, ws=0,
+         ws_bytes=0):
+    q, k, v, a, b, s0, o, sf = ptrs if ptrs is not None else _bufs()
+    return lib.gdn_chunk_fwd(q, k, v, a, b, s0, o, sf, ws, ws_bytes, B, T, H, dk, dv, chunk,
+                             dtype, mode, None)
+
+
+def test_chunk_fwd_rejects_bad_sizes(lib):
+    assert _fwd(lib, dk=96) == E_UNSUP
+    assert _fwd(lib, dv=256) == E_UNSUP
+    assert _fwd(lib, chunk=32) == E_UNSUP
+    assert _fwd(lib, T=-1) == E_SHAPE
+    assert _fwd(lib, B=-1) == E_SHAPE
+    assert _fwd(lib, dk=0) == E_SHAPE
+    assert _fwd(lib, dtype=7) == E_DTYPE
+    assert _fwd(lib, mode=3) == E_DTYPE
+    assert _fwd(lib, B=1 << 30, T=1 << 30, H=1 << 20) == E_SHAPE   # element count overflow
+
+
+def test_chunk_fwd_rejects_null_and_alias(lib):
+    q, k, v, a, b, s0, o, sf = _bufs()
+    assert _fwd(lib, ptrs=[0, k, v, a, b, s0, o, sf]) == E_NULL
+    assert _fwd(lib, ptrs=[q, k, v, a, 0, s0, o, sf]) == E_NULL
+    assert _fwd(lib, ptrs=[q, k, v, a, b, s0, 0, sf]) == E_NULL
+    assert _fwd(lib, ptrs=[q, k, v, 0, b, s0, o, sf], mode=1) == E_NULL
+    assert _fwd(lib, ptrs=[q, k, v, 0, b, s0, o, sf], mode=2) == E_NULL
+    assert _fwd(lib, ptrs=[q, k, v, a, b, s0, q + 64, sf]) == E_ALIAS      # o inside q
+    assert _fwd(lib, ptrs=[q, k, v, a, b, s0, o, o + 2]) == E_ALIAS        # S_final inside o
+    assert _fwd(lib, ptrs=[q, k, v, a, b, s0, o, s0 + 16]) == E_ALIAS      # partial overlap S0
+    assert _fwd(lib, ptrs=[q, k, v, a, b, s0, o, v]) == E_ALIAS
+
+
+def test_chunk_fwd_empty_batch_is_a_no_op(lib):
+    # nothing to compute: returns OK without touching the (fake) pointers
+    assert _fwd(lib, B=0) == OK
+    assert _fwd(lib, H=0) == OK
+    assert _fwd(lib, T=0, ptrs=[0, 0, 0, 0, 0, 0, 0, 0]) == OK   # no S_final requested
+
+
+def test_workspace_query(lib):
+    assert lib.gdn_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 64, 1, 1) == 0
+
+
+def test_decode_rejects_bad_arguments(lib):
+    q, k, v, a, b, S, o, _ = _bufs()
+
+    def dec(ptrs=(q, k, v, a, b, S, o), B=4, H=2, dk=128, dv=64, dtype=1, mode=1):
+        return lib.gdn_decode_step(*ptrs, B, H, dk, dv, dtype, mode, None)
+
+    assert dec(dk=32) == E_UNSUP
+    assert dec(dtype=2) == E_DTYPE
+    assert dec(B=-2) == E_SHAPE
+    assert dec(ptrs=(q, k, v, a, b, 0, o)) == E_NULL
+    assert dec(ptrs=(q, k, v, 0, b, S, o), mode=2) == E_NULL
+    assert dec(ptrs=(q, k, v, a, b, S, S + 8)) == E_ALIAS
+    assert dec(ptrs=(q, k, v, a, b, q, o)) == E_ALIAS
+    assert dec(B=0) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import gated_delta_rule_04_amd as gdn
+    monkeypatch.setattr(gdn, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gdn, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        gdn.load()
