@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta-rule path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+the chunked prefill of the Gated DeltaNet bf16 workload (B=8, H=16, T=4096,
+d_k=d_v=128, chunk 64, random fp32 S0) followed by the first decode token on
+the state it returns.  ``value`` is prefill throughput in tokens/s (B*T per
+step).  The decode step's own throughput (GB/s against HBM peak) is measured
+on the batch-64 x 16-head decode workload, 1024 steps captured in a HIP graph,
+both in place on one state (as the recurrence runs) and rotated over 16 state
+buffers so the 67 MB state cannot stay in the 256 MB Infinity Cache.
+
+Printed: one JSON line (the contract below), preceded by progress lines on
+stderr.  Peaks are MI355X's published figures: HBM 8 TB/s, dense bf16 MFMA
+2.5 PFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gated_delta_rule_04_amd as gdn  # noqa: E402
+import workloads as W  # noqa: E402
+
+METRIC = "prefill tokens/s + % bf16 MFMA peak; decode step GB/s + % HBM peak (1 GPU)"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+CHUNK = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_gdn_bf16_b8_h16_t4096_d128_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc", f)
+                  for f in ("gdn_chunk.hip", "gdn_mfma.h", "gdn_internal.h")]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------
+# algorithmic work (per launch), independent of how the kernels do it
+# ------------------------------------------------------------------------------
+
+def prefill_bytes(w: W.Prefill) -> int:
+    """Every input read once and every output written once."""
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    tok = w.B * w.T * w.H
+    b = tok * (2 * w.dk + 2 * w.dv) * es          # q, k, v, o
+    b += tok * 4                                   # beta
+    if w.mode == W.MODE_SCALAR:
+        b += tok * 4
+    elif w.mode == W.MODE_CHANNEL:
+        b += tok * w.dk * es
+    state = w.B * w.H * w.dv * w.dk * 4
+    b += state * (2 if w.s0_std > 0 else 1)        # S0 (if given) + S_final
+    return b
+
+
+def prefill_flops(w: W.Prefill, dense: bool) -> float:
+    """Per token-head: the five C x C-sized products (A, W-or-X side, U, Q K^T,
+    P U) at half size (causal) or full tile size (dense), the three state
+    contractions and the triangular solve, FLOP = 2 MAC."""
+    C, dk, dv = CHUNK, w.dk, w.dv
+    tri = 1.0 if dense else 0.5
+    per = 2.0 * (tri * C * (3 * dk + 2 * dv) + 3 * dk * dv + C * C / 6.0)
+    return per * w.B * w.T * w.H
+
+
+def decode_bytes(w: W.Decode) -> int:
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    heads = w.B * w.H
+    b = 2 * heads * w.dv * w.dk * 4                   # state read + write
+    b += heads * (2 * w.dk + 2 * w.dv) * es           # q, k, v, o
+    b += heads * 4 * (2 if w.mode == W.MODE_SCALAR else 1)
+    if w.mode == W.MODE_CHANNEL:
+        b += heads * w.dk * es
+    return b
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed rocprofv3 counter summary,
+    or None when it is absent or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------------------
+# GPU measurements
+# ------------------------------------------------------------------------------
+
+def bench_step(w: W.Prefill, steps: int, warmup: int):
+    """Time exactly ``steps`` steps (prefill + first decode token).  The prefill
+    kernel's own duration is taken with HIP events on the stream it runs on."""
+    log("generating %s" % w.name)
+    host = W.make_prefill(w)
+    dev = {k: (None if v is None else v.cuda()) for k, v in host.items()}
+    tok = W.make_decode(W.Decode("next_token", w.B, w.H, w.dk, w.dv, 1, w.dtype, w.gate, 0.0,
+                                 seed=w.seed + 100))
+    tdev = {k: (None if v is None else v.cuda()) for k, v in tok.items()}
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=w.dtype, device="cuda")
+    S = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+    o1 = torch.empty((w.B, w.H, w.dv), dtype=w.dtype, device="cuda")
+    a1 = None if tdev["alpha"] is None else tdev["alpha"][0]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        gdn.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["S0"],
+                      mode=w.mode, o=o, S_final=S)
+        if ev is not None:
+            ev[1].record()
+        gdn.decode_step(tdev["q"][0], tdev["k"][0], tdev["v"][0], a1, tdev["beta"][0], S, o=o1,
+                        mode=w.mode)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    # outputs of the last step, for the parity spot check against the oracle
+    gdn.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["S0"],
+                  mode=w.mode, o=o, S_final=S)
+    torch.cuda.synchronize()
+    return dict(wall_s=wall, kernel_ms=kern_ms, host=host, o=o, S=S)
+
+
+def bench_decode(w: W.Decode, reps: int = 3, rotate: int = 1):
+    """``w.steps`` decode steps captured in one HIP graph; per-step time from
+    the median replay.  ``rotate`` > 1 cycles the steps over that many state
+    buffers (HBM-resident working set)."""
+    inp = W.make_decode(w)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items() if k != "S"}
+    states = [inp["S"].cuda() for _ in range(rotate)]
+    o = torch.empty((w.steps, w.B, w.H, w.dv), dtype=w.dtype, device="cuda")
+
+    def run_all():
+        for t in range(w.steps):
+            a = None if d["alpha"] is None else d["alpha"][t]
+            gdn.decode_step(d["q"][t], d["k"][t], d["v"][t], a, d["beta"][t], states[t % rotate],
+                            o=o[t], mode=w.mode)
+
+    run_all()                                  # eager warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        run_all()
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / w.steps)
+    del g
+    ms = sorted(times)[len(times) // 2]
+    gb = decode_bytes(w) / (ms * 1e-3) / 1e9
+    return dict(us_per_step=ms * 1e3, gbps=gb, hbm_frac=gb / HBM_PEAK_GBPS)
+
+
+def device_copy_gbps(nbytes=1 << 30):
+    """Plain device-to-device copy (read + write) as the achievable-bandwidth reference."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the same workload
+# ------------------------------------------------------------------------------
+
+def cpu_baseline(w: W.Prefill, host, o_gpu, S_gpu, budget_s: float = 12.0):
+    import numpy as np
+    import oracle  # test infrastructure: used only for this baseline leg
+    threads = oracle.num_threads()
+
+    def rows(n):
+        return {k: (None if v is None else v[:n]) for k, v in host.items()}
+
+    t0 = time.perf_counter()
+    ro, rS = oracle.gdn_fwd(**{k: v for k, v in rows(1).items()}, mode=w.mode)
+    t1 = time.perf_counter() - t0
+    n = 1
+    extra = int(max(0, min(w.B - 1, budget_s / max(t1, 1e-3) - 1)))
+    if extra > 0:
+        sub = {k: (None if v is None else v[1:1 + extra]) for k, v in host.items()}
+        t0 = time.perf_counter()
+        ro2, rS2 = oracle.gdn_fwd(**sub, mode=w.mode)
+        t2 = time.perf_counter() - t0
+        ro, rS = np.concatenate([ro, ro2]), np.concatenate([rS, rS2])
+        n, secs = 1 + extra, t1 + t2
+    else:
+        secs = t1
+    toks = n * w.T
+    og = o_gpu[:n].float().cpu().numpy()
+    Sg = S_gpu[:n].cpu().numpy()
+    parity = dict(rel_err_o=W.per_head_rel_err(og, ro, (0, 2)),
+                  rel_err_S=W.per_head_rel_err(Sg, rS, (0, 1)), rows_checked=n)
+    base = dict(value=toks / secs, unit="tokens/s", cores=threads, kind="oracle",
+                sample="fp64 token loop over batch rows 0..%d (%d of %d rows, all %d heads, "
+                       "T=%d): %.1f s on %d threads" % (n - 1, n, w.B, w.H, w.T, secs, threads))
+    return base, parity
+
+
+# ------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.GDN_BF16_PREFILL.name,
+                    choices=[w.name for w in W.PREFILL_WORKLOADS])
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the path on a single MI355X "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    gdn.load()
+    w = next(x for x in W.PREFILL_WORKLOADS if x.name == args.workload)
+
+    r = bench_step(w, args.steps, args.warmup)
+    ms_step = r["wall_s"] * 1e3 / args.steps
+    kern_ms = r["kernel_ms"][len(r["kernel_ms"]) // 2]
+    kern_mean_ms = sum(r["kernel_ms"]) / len(r["kernel_ms"])
+    tokens = w.B * w.T
+    nbytes, f_c, f_d = prefill_bytes(w), prefill_flops(w, False), prefill_flops(w, True)
+    log("prefill kernel %.1f us (median of %d), step %.3f ms" % (kern_ms * 1e3, args.steps, ms_step))
+
+    prefill = dict(kernel_us_median=kern_ms * 1e3, kernel_us_mean=kern_mean_ms * 1e3,
+                   tokens_per_s_kernel=tokens / (kern_ms * 1e-3),
+                   tflops_causal=f_c / (kern_ms * 1e-3) / 1e12,
+                   mfma_frac_causal=f_c / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                   tflops_dense=f_d / (kern_ms * 1e-3) / 1e12,
+                   mfma_frac_dense=f_d / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                   hbm_gbps=nbytes / (kern_ms * 1e-3) / 1e9,
+                   hbm_frac=nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                   algorithmic_bytes=nbytes, flops_causal=f_c, flops_dense=f_d)
+    traffic = measured_traffic()
+    roofline = dict(bound="hbm", achieved=nbytes / (kern_mean_ms * 1e-3) / 1e9,
+                    peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=nbytes / (kern_mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    traffic=traffic, kernel="chunk_kernel (fused chunked prefill)",
+                    launch_us=kern_mean_ms * 1e3)
+
+    decode = None
+    if not args.no_decode:
+        decode = {}
+        for dw in W.DECODE_WORKLOADS:
+            lit = bench_decode(dw, rotate=1)
+            rot = bench_decode(dw, rotate=16)
+            decode[dw.name] = dict(bytes_per_step=decode_bytes(dw),
+                                   in_place=lit, rotated_16_states=rot)
+            log("decode %s: in place %.2f us/step %.0f GB/s; rotated %.2f us/step %.0f GB/s" % (
+                dw.name, lit["us_per_step"], lit["gbps"], rot["us_per_step"], rot["gbps"]))
+        decode["device_copy_gbps"] = device_copy_gbps()
+
+    base, parity = None, None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        base, parity = cpu_baseline(w, r["host"], r["o"], r["S"])
+        prefill.update(parity)
+        log("oracle %.0f tokens/s; parity o %.2e S %.2e" % (base["value"], parity["rel_err_o"],
+                                                          parity["rel_err_S"]))
+
+    out = dict(metric=METRIC, value=tokens / (ms_step * 1e-3), unit="tokens/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True,
+               scaling="weak", vs_baseline=None,
+               dtype="bf16" if w.dtype == torch.bfloat16 else "f32", data="synthetic",
+               config=dict(workload=w.name, B=w.B, H=w.H, T=w.T, dk=w.dk, dv=w.dv, chunk=CHUNK,
+                           decay={0: "none", 1: "scalar", 2: "channel"}[w.mode],
+                           step="chunked prefill + first decode token",
+                           state="fp32", parallelism="single GPU"),
+               roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,86 +25,120 @@
 // Reduction" notes, section 2.5), so slices of d_v never talk to each other.
 // The fp32 state slice lives in MFMA accumulator registers for the whole
 // sequence; a copy in the operand dtype is kept in LDS for the next chunk's
-// K S^T and Q S^T.  Every product is a 32x32 MFMA tile fed from LDS; all
-// intermediates (A, T, X, U, P) stay in LDS, so HBM sees q, k, v and beta/alpha
-// once, o once, and S0 / S_final once per head.
+// K S^T and Q S^T.  Every product is an MFMA tile fed from LDS and all
+// intermediates (A, T, X, U, P) stay in LDS, so HBM sees q, k, v and the gates
+// once, o once, and S0 / S_final once per head.  The next chunk's q, k, v and
+// gates are loaded into registers while the current chunk computes.
+//
+// Per chunk step:
+//   commit   prefetched registers -> LDS (K rows, K^T, Q rows, V^T, gates)
+//   phase 1  A and P tiles (bf16/fp32 MFMA), X and diag(gamma) Q S^T tiles
+//   solve    T = (I + A)^-1 diag(beta): 16x16 diagonal inverses by forward
+//            substitution, then two levels of fp32 MFMA block products
+//   phase 4  U = T X
+//   phase 5  O = diag(gamma) Q S^T + P U  -> HBM
+//   phase 6  S^T <- gamma_C S^T + K^T (diag(exp(G_C - G)) U)
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
 namespace gdn {
 namespace {
 
-constexpr int C = 64;            // chunk length
-constexpr int kThreads = 256;    // four waves
+constexpr int C = 64;                // chunk length
+constexpr int kThreads = 256;        // four waves
 constexpr float kLogFloor = -100.f;  // gates below e^-100 act as e^-100 (= 0 in fp32 products)
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // LDS plan (byte offsets).  Lifetimes inside one chunk step:
-//   Kr    K rows [64][LDK]              load .. phase 3b
-//   Qr    Q rows [64][LDK]              load .. phase 3     } same region
-//   Kt    K^T    [DK][LDT]              phase 3b .. 6       }
-//   Sb    state copy S[i][c] [DVS][LDS] phase 6 .. next phase 3
-//   Vt    V^T slice [DVS][LDT]          load .. phase 3
-//   Pm    P [64][LDT]                   phase 1 .. 5
-//   Tm    T [64][LDT]                   phase 2 .. 4 (fp32 mode: also the solve's L^-1)
-//   Am    A fp32 [64][LDA]              phase 1 .. 2        } same region
-//   Li    L^-1 fp32 [64][LDA] (bf16)    phase 2             }
-//   Mt    3 x 16 x 16 fp32              phase 2             }
-//   Xt, Ut, Uw  [DVS][LDT] each         phase 3 .. 6        }
-//   G, Bt 64 fp32 each                  load .. 6
-template <typename E, int DK, int DVS>
+//   Kr    K rows [64][LDK]               commit .. phase 1
+//   Qr    Q rows [64][LDK]               commit .. phase 1
+//   Kt    K^T    [DK][LDT]               commit (or after phase 1) .. phase 6
+//         (fp32 with d_k = 128: shares Q's region to fit in 160 KiB)
+//   Sb    state copy S[i][c] [DVS][LDSB] phase 6 .. next phase 1
+//   Vt    V^T slice [DVS][LDT]           commit .. phase 1
+//   Xt    X^T slice [DVS][LDT]           phase 1 .. phase 4
+//   Pm    P [64][LDT]                    phase 1 .. phase 5
+//   Tm    T [64][LDT]                    solve .. phase 4 (fp32: also the solve's L^-1)
+//   Am    A fp32 [64][LDA]               phase 1 .. solve       } one region
+//   Li    L^-1 fp32 [64][LDA] (bf16)     solve                  }
+//   Mt    fp32 [32][LDM]                 solve                  }
+//   Ut, Uw  [DVS][LDT] each              phase 4 .. phase 6     }
+//   G, Bt, Eg, Ec  64 fp32 each          commit .. phase 6
+template <typename E, int DK, int DVS, bool SEPKT>
 struct Plan {
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = DK + PAD;
   static constexpr int LDT = C + PAD;
   static constexpr int LDSB = DK + PAD;
   static constexpr int LDA = C + 4;
+  static constexpr int LDM = 32 + 4;
   static constexpr bool kF32 = sizeof(E) == 4;
+  static constexpr size_t es = sizeof(E);
   static constexpr size_t kr = 0;
-  static constexpr size_t qr = kr + (size_t)C * LDK * sizeof(E);
-  static constexpr size_t sb = qr + cmax((size_t)C * LDK, (size_t)DK * LDT) * sizeof(E);
-  static constexpr size_t vt = sb + (size_t)DVS * LDSB * sizeof(E);
-  static constexpr size_t pm = vt + (size_t)DVS * LDT * sizeof(E);
-  static constexpr size_t tm = pm + (size_t)C * LDT * sizeof(E);
-  static constexpr size_t region = tm + (size_t)C * LDT * sizeof(E);
+  static constexpr size_t qr = kr + (size_t)C * LDK * es;
+  static constexpr size_t kt = SEPKT ? qr + (size_t)C * LDK * es : qr;
+  static constexpr size_t sb = SEPKT ? kt + (size_t)DK * LDT * es
+                                     : qr + cmax((size_t)C * LDK, (size_t)DK * LDT) * es;
+  static constexpr size_t vt = sb + (size_t)DVS * LDSB * es;
+  static constexpr size_t xt = vt + (size_t)DVS * LDT * es;
+  static constexpr size_t pm = xt + (size_t)DVS * LDT * es;
+  static constexpr size_t tm = pm + (size_t)C * LDT * es;
+  static constexpr size_t region = tm + (size_t)C * LDT * es;
   static constexpr size_t am = region;
   static constexpr size_t li = am + (size_t)C * LDA * 4;
   static constexpr size_t mt = kF32 ? li : li + (size_t)C * LDA * 4;
-  static constexpr size_t solve_end = mt + 3 * 256 * 4;
-  static constexpr size_t xu_end = region + 3 * (size_t)DVS * LDT * sizeof(E);
-  static constexpr size_t g = cmax(solve_end, xu_end);
-  static constexpr size_t total = g + 2 * C * 4;
+  static constexpr size_t solve_end = mt + (size_t)32 * LDM * 4;
+  static constexpr size_t ut = region;
+  static constexpr size_t uw = ut + (size_t)DVS * LDT * es;
+  static constexpr size_t u_end = uw + (size_t)DVS * LDT * es;
+  static constexpr size_t g = cmax(solve_end, u_end);
+  static constexpr size_t total = g + 4 * C * 4;
   static_assert(!kF32 || LDT == LDA, "fp32 mode keeps L^-1 in the T buffer");
-  static_assert(total <= 160 * 1024, "LDS plan exceeds 160 KiB");
 };
+
+template <typename E, int DK, int DVS>
+constexpr bool sep_kt_fits() {
+  return Plan<E, DK, DVS, true>::total <= 160 * 1024;
+}
 
 template <typename E, int DK, int DVS, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
-  using L = Plan<E, DK, DVS>;
+  constexpr bool SEPKT = sep_kt_fits<E, DK, DVS>();
+  using L = Plan<E, DK, DVS, SEPKT>;
+  static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
   constexpr int NI = DVS / 32;       // 32-wide value blocks in the slice
   constexpr int NC = DK / 32;        // 32-wide key blocks
   constexpr int NT = NC * NI;        // state tiles
   constexpr int NST = (NT + 3) / 4;  // state tiles per wave
   constexpr int EPC = 16 / (int)sizeof(E);  // elements per 16-byte chunk
-  constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB, LDA = L::LDA;
+  constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB, LDA = L::LDA, LDM = L::LDM;
+  // prefetch geometry: blocks of 4 rows x one 16-byte chunk, row group fastest
+  constexpr int CPR = DK / EPC;              // chunks per q/k row
+  constexpr int NKB = 16 * CPR;              // 4-row blocks per q/k tile
+  constexpr int KBT = (NKB + kThreads - 1) / kThreads;
+  constexpr int CPV = DVS / EPC;             // chunks per v row (slice)
+  constexpr int NVB = 16 * CPV;
+  constexpr int VBT = (NVB + kThreads - 1) / kThreads;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
   E* Kr = reinterpret_cast<E*>(smem + L::kr);
   E* Qr = reinterpret_cast<E*>(smem + L::qr);
-  E* Kt = Qr;
+  E* Kt = reinterpret_cast<E*>(smem + L::kt);
   E* Sb = reinterpret_cast<E*>(smem + L::sb);
   E* Vt = reinterpret_cast<E*>(smem + L::vt);
+  E* Xt = reinterpret_cast<E*>(smem + L::xt);
   E* Pm = reinterpret_cast<E*>(smem + L::pm);
   E* Tm = reinterpret_cast<E*>(smem + L::tm);
   float* Am = reinterpret_cast<float*>(smem + L::am);
   float* Li = L::kF32 ? reinterpret_cast<float*>(smem + L::tm) : reinterpret_cast<float*>(smem + L::li);
   float* Mt = reinterpret_cast<float*>(smem + L::mt);
-  E* Xt = reinterpret_cast<E*>(smem + L::region);
-  E* Ut = Xt + DVS * LDT;
-  E* Uw = Ut + DVS * LDT;
+  E* Ut = reinterpret_cast<E*>(smem + L::ut);
+  E* Uw = reinterpret_cast<E*>(smem + L::uw);
   float* G = reinterpret_cast<float*>(smem + L::g);
   float* Bt = G + C;
+  float* Eg = G + 2 * C;   // exp(G_r)
+  float* Ec = G + 3 * C;   // exp(G_C - G_r)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31;
@@ -125,16 +159,20 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
   E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
   const size_t sbase = ((size_t)b * H + h) * dv + i0;  // first state row of the slice
 
-  // Tile ownership for phases 3-5: (row block rb, value block ib) of X, U, O.
-  int own_rb = -1, own_ib = 0, x_rb = -1;
+  // Tile ownership.  X, O_inter (phase 1), U (phase 4) and O (phase 5) tiles of
+  // row block own_rb and value block own_ib belong to one wave; the three A/P
+  // tile pairs (j block, r block) in {(0,0), (0,1), (1,1)} go to the waves with
+  // the least other work.
+  int own_rb = -1, own_ib = 0, ap = -1;
   if (NI == 2) {
     own_rb = wave >> 1;
     own_ib = wave & 1;
-    x_rb = own_rb;
+    ap = wave < 3 ? wave : -1;
   } else {
-    if (wave >= 2) own_rb = wave - 2;
-    else x_rb = wave;
+    if (wave < 2) own_rb = wave;
+    ap = wave == 0 ? 2 : (wave >= 2 ? wave - 2 : -1);
   }
+  const int ap_jb = ap == 2 ? 1 : 0, ap_rb = ap == 0 ? 0 : 1;
 
   // Initial state: S0 or zeros, into registers and the operand copy.
   f32x16 Sacc[NST];
@@ -158,217 +196,284 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
     }
   }
 
-  const int nchunks = (T + C - 1) / C;
-  for (int n = 0; n < nchunks; ++n) {
+  // ---- prefetch registers ----
+  // Loads are unconditional (rows past the sequence end re-read its last row and
+  // are zeroed at commit) so the compiler keeps them in flight across the chunk.
+  uint4 pk[KBT][4], pq[KBT][4], pv[VBT][4];
+  float p_beta = 0.f, p_alpha = 1.f;
+  int p_cn = 0;
+
+  auto prefetch = [&](int n) __attribute__((always_inline)) {
     const int t0 = n * C;
     const int cn = min(C, T - t0);
-    __syncthreads();
+    p_cn = cn;
+#pragma unroll
+    for (int m = 0; m < KBT; ++m) {
+      const int blk = tid + kThreads * m;
+      const int bq = blk < NKB ? blk : 0;
+      const int rg = bq % 16, cc = bq / 16;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = min(4 * rg + rr, cn - 1);
+        pk[m][rr] = *reinterpret_cast<const uint4*>(kg + (size_t)(t0 + r) * qk_tok + cc * EPC);
+        pq[m][rr] = *reinterpret_cast<const uint4*>(qg + (size_t)(t0 + r) * qk_tok + cc * EPC);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < VBT; ++m) {
+      const int blk = tid + kThreads * m;
+      const int bq = blk < NVB ? blk : 0;
+      const int rg = bq % 16, cc = bq / 16;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = min(4 * rg + rr, cn - 1);
+        pv[m][rr] = *reinterpret_cast<const uint4*>(vg + (size_t)(t0 + r) * v_tok + cc * EPC);
+      }
+    }
+    const size_t tok = ((size_t)b * T + t0 + min(lane, cn - 1)) * H + h;
+    p_beta = a.beta[tok];
+    if (MODE == 1) p_alpha = static_cast<const float*>(a.alpha)[tok];
+  };
 
-    // ---- phase 0: gates (log-decay prefix G, beta) and the K, Q, V tiles ----
+  auto commit = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < KBT; ++m) {
+      const int blk = tid + kThreads * m;
+      if (blk < NKB) {
+        const int rg = blk % 16, cc = blk / 16;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const bool ok = 4 * rg + rr < p_cn;
+          pk[m][rr] = keep_or_zero(pk[m][rr], ok);
+          *reinterpret_cast<uint4*>(Kr + (4 * rg + rr) * LDK + cc * EPC) = pk[m][rr];
+          *reinterpret_cast<uint4*>(Qr + (4 * rg + rr) * LDK + cc * EPC) = keep_or_zero(pq[m][rr], ok);
+        }
+        if (SEPKT) {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            store_col4(Kt + (cc * EPC + e) * LDT + 4 * rg, pk[m][0], pk[m][1], pk[m][2], pk[m][3], e);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < VBT; ++m) {
+      const int blk = tid + kThreads * m;
+      if (blk < NVB) {
+        const int rg = blk % 16, cc = blk / 16;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) pv[m][rr] = keep_or_zero(pv[m][rr], 4 * rg + rr < p_cn);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          store_col4(Vt + (cc * EPC + e) * LDT + 4 * rg, pv[m][0], pv[m][1], pv[m][2], pv[m][3], e);
+      }
+    }
     if (wave == 0) {
-      const int r = lane;
-      const bool ok = r < cn;
-      const size_t tok = ((size_t)b * T + t0 + r) * H + h;
-      const float bt = ok ? a.beta[tok] : 0.f;
-      float la = 0.f;
-      if (MODE == 1 && ok) la = fmaxf(logf(static_cast<const float*>(a.alpha)[tok]), kLogFloor);
+      const bool ok = lane < p_cn;
+      float la = (MODE == 1 && ok) ? fmaxf(logf(p_alpha), kLogFloor) : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(la, off);
         if (lane >= off) la += y;
       }
-      G[r] = la;
-      Bt[r] = bt;
+      const float GC = __shfl(la, 63);
+      G[lane] = la;
+      Bt[lane] = ok ? p_beta : 0.f;
+      Eg[lane] = __expf(la);
+      Ec[lane] = __expf(GC - la);
     }
+  };
+
+  const int nchunks = (T + C - 1) / C;
+  if (nchunks > 0) prefetch(0);
+  for (int n = 0; n < nchunks; ++n) {
+    const int t0 = n * C;
+    const int cn = min(C, T - t0);
+    __syncthreads();   // every reader of the previous chunk's buffers is done
+    commit();
+    if (n + 1 < nchunks) prefetch(n + 1);
+    __syncthreads();
+
+    // ---- phase 1: A, P tiles; X and O_inter tiles ----
+    // A/P tile pair (jb, rb) holds rows j of the j-block and columns r of the
+    // r-block (shared K_j operand), so each lane writes four consecutive j of one
+    // row r.  The X and O_inter tiles of (own_rb, own_ib) share the S operand.
+    f32x16 xacc = zero16(), oacc = zero16(), aacc = zero16(), pacc = zero16();
     {
-      constexpr int CPR = DK / EPC;  // 16-byte chunks per row
+      const E* Ax = Kr + (own_rb < 0 ? 0 : own_rb) * 32 * LDK;
+      const E* Ao = Qr + (own_rb < 0 ? 0 : own_rb) * 32 * LDK;
+      const E* Bs = Sb + own_ib * 32 * LDSB;
+      const E* Aj = Kr + ap_jb * 32 * LDK;
+      const E* C0 = Kr + ap_rb * 32 * LDK;
+      const E* C1 = Qr + ap_rb * 32 * LDK;
+      if (own_rb >= 0 && ap >= 0)
+        tile_nt4<DK / 16>(xacc, oacc, aacc, pacc, Ax, Ao, Bs, Aj, C0, C1, LDK, LDSB, lane);
+      else if (own_rb >= 0)
+        tile_nt2_shared_b<DK / 16>(xacc, oacc, Ax, Ao, LDK, Bs, LDSB, lane);
+      else if (ap >= 0)
+        tile_nt2_shared_a<DK / 16>(aacc, pacc, Aj, LDK, C0, C1, LDK, lane);
+    }
+    if (ap >= 0) {
+      const int r = ap_rb * 32 + col;
+      const float Gr = G[r];
+      const float br = Bt[r];
 #pragma unroll
-      for (int m = 0; m < C * CPR / kThreads; ++m) {
-        const int qi = tid + kThreads * m, r = qi / CPR, cc = qi % CPR;
-        uint4 kx = make_uint4(0, 0, 0, 0), qx = make_uint4(0, 0, 0, 0);
-        if (r < cn) {
-          kx = *reinterpret_cast<const uint4*>(kg + (size_t)(t0 + r) * qk_tok + cc * EPC);
-          qx = *reinterpret_cast<const uint4*>(qg + (size_t)(t0 + r) * qk_tok + cc * EPC);
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = ap_jb * 32 + acc_row(g, 0, lane);
+        const float4 gj = *reinterpret_cast<const float4*>(G + j0);
+        const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+        float xa[4], xp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d = __expf(Gr - gjv[e]);
+          xa[e] = (j0 + e < r) ? br * d * aacc[4 * g + e] : 0.f;
+          xp[e] = (j0 + e <= r) ? d * pacc[4 * g + e] : 0.f;
         }
-        *reinterpret_cast<uint4*>(Kr + r * LDK + cc * EPC) = kx;
-        *reinterpret_cast<uint4*>(Qr + r * LDK + cc * EPC) = qx;
+        store4(Am + r * LDA + j0, xa[0], xa[1], xa[2], xa[3]);
+        store4(Pm + r * LDT + j0, xp[0], xp[1], xp[2], xp[3]);
       }
-      constexpr int CPV = DVS / EPC;
-      for (int qi = tid; qi < C * CPV; qi += kThreads) {
-        const int r = qi / CPV, cc = qi % CPV;
-        union { uint4 raw; E e[EPC]; } tmp;
-        tmp.raw = make_uint4(0, 0, 0, 0);
-        if (r < cn) tmp.raw = *reinterpret_cast<const uint4*>(vg + (size_t)(t0 + r) * v_tok + cc * EPC);
+    }
+    if (own_rb >= 0) {
+      const int i = own_ib * 32 + col;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) Vt[(cc * EPC + e) * LDT + r] = tmp.e[e];
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = own_rb * 32 + acc_row(g, 0, lane);
+        const float4 eg = *reinterpret_cast<const float4*>(Eg + r0);
+        store4(Xt + i * LDT + r0,
+               load_elem(Vt + i * LDT + r0 + 0) - eg.x * xacc[4 * g + 0],
+               load_elem(Vt + i * LDT + r0 + 1) - eg.y * xacc[4 * g + 1],
+               load_elem(Vt + i * LDT + r0 + 2) - eg.z * xacc[4 * g + 2],
+               load_elem(Vt + i * LDT + r0 + 3) - eg.w * xacc[4 * g + 3]);
+        oacc[4 * g + 0] *= eg.x;
+        oacc[4 * g + 1] *= eg.y;
+        oacc[4 * g + 2] *= eg.z;
+        oacc[4 * g + 3] *= eg.w;
       }
     }
     __syncthreads();
 
-    // ---- phase 1: A (fp32) and P from K K^T and K Q^T tiles ----
-    // Tile (jb, rb) holds rows j of the j-block and columns r of the r-block, so
-    // each lane writes four consecutive j of one row r.
+    // ---- K^T for phase 6 when it shares Q's region (fp32, d_k = 128) ----
+    if (!SEPKT) {
+      for (int blk = tid; blk < NKB; blk += kThreads) {
+        const int rg = blk % 16, cc = blk / 16;
+        uint4 v[4];
 #pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int tt = wave + 4 * rep;
-      if (tt < 6) {
-        const bool isA = tt < 3;
-        const int idx = tt % 3;
-        const int jb = idx == 2 ? 1 : 0, rb = idx == 0 ? 0 : 1;
-        f32x16 acc = zero16();
-        tile_nt(acc, Kr + jb * 32 * LDK, LDK, (isA ? Kr : Qr) + rb * 32 * LDK, LDK, DK / 16, lane);
-        const int r = rb * 32 + col;
-        const float Gr = G[r];
-        if (isA) {
-          const float br = Bt[r];
+        for (int rr = 0; rr < 4; ++rr)
+          v[rr] = *reinterpret_cast<const uint4*>(Kr + (4 * rg + rr) * LDK + cc * EPC);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int j0 = jb * 32 + acc_row(g, 0, lane);
-            float x[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              x[e] = (j0 + e < r) ? br * __expf(Gr - G[j0 + e]) * acc[4 * g + e] : 0.f;
-            store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int j0 = jb * 32 + acc_row(g, 0, lane);
-            float x[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              x[e] = (j0 + e <= r) ? __expf(Gr - G[j0 + e]) * acc[4 * g + e] : 0.f;
-            store4(Pm + r * LDT + j0, x[0], x[1], x[2], x[3]);
-          }
-        }
+        for (int e = 0; e < EPC; ++e)
+          store_col4(Kt + (cc * EPC + e) * LDT + 4 * rg, v[0], v[1], v[2], v[3], e);
       }
     }
-    __syncthreads();
 
-    // ---- phase 2: T = (I + A)^-1 diag(beta), blocked by 16 ----
-    // (a) inverse of each unit-lower 16x16 diagonal block, one column per thread
-    if (tid < 64) {
-      const int I = tid >> 4, c = tid & 15;
+    // ---- solve (a): inverses of the four unit-lower 16x16 diagonal blocks ----
+    // Wave w owns block w; lane c (< 16) computes column c by forward substitution.
+    {
+      const int I = wave, c = lane & 15;
       const float* base = Am + (16 * I) * LDA + 16 * I;
       float y[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < i; ++j) s += base[i * LDA + j] * y[j];
+        for (int jq = 0; jq < (i + 3) / 4; ++jq) {
+          const float4 a4 = *reinterpret_cast<const float4*>(base + i * LDA + 4 * jq);
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * jq + e < i) s += av[e] * y[4 * jq + e];
+        }
         y[i] = i < c ? 0.f : (i == c ? 1.f : -s);
       }
+      if (lane < 16) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Li[(16 * I + i) * LDA + 16 * I + c] = y[i];
-    }
-    __syncthreads();
-    // (b) off-diagonal blocks by distance d: L^-1_IJ = -L^-1_II sum_{K=J}^{I-1} A_IK L^-1_KJ
-    {
-      const int i = tid >> 4, j = tid & 15;
-      for (int d = 1; d < 4; ++d) {
-        for (int bk = 0; bk < 4 - d; ++bk) {
-          const int I = bk + d, J = bk;
-          float s = 0.f;
-          for (int K = J; K < I; ++K) {
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk)
-              s += Am[(16 * I + i) * LDA + 16 * K + kk] * Li[(16 * K + kk) * LDA + 16 * J + j];
-          }
-          Mt[bk * 256 + i * 16 + j] = s;
-        }
-        __syncthreads();
-        for (int bk = 0; bk < 4 - d; ++bk) {
-          const int I = bk + d, J = bk;
-          float s = 0.f;
-#pragma unroll
-          for (int m = 0; m < 16; ++m) s += Li[(16 * I + i) * LDA + 16 * I + m] * Mt[bk * 256 + m * 16 + j];
-          Li[(16 * I + i) * LDA + 16 * J + j] = -s;
-        }
-        __syncthreads();
+        for (int i = 0; i < 16; ++i) Li[(16 * I + i) * LDA + 16 * I + c] = y[i];
       }
     }
-    // (c) T[r][j] = L^-1[r][j] beta_j on and below the diagonal, 0 above
+    __syncthreads();
+    // ---- solve (b): L^-1_{b+1,b} = -L^-1_{b+1,b+1} (A_{b+1,b} L^-1_{b,b}), b = 0, 2 ----
+    // fp32 MFMA 16x16x4; lane l uses k index 4 (l / 16) + s in step s, so the
+    // first product's accumulator is directly the second product's B operand.
+    if (wave < 2) {
+      const int bb = 2 * wave, m = lane & 15, hq = lane >> 4;
+      f32x4 mprod = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int k = 4 * hq + s;
+        mprod = mma_f32_16x16(Am[(16 * (bb + 1) + m) * LDA + 16 * bb + k],
+                              Li[(16 * bb + k) * LDA + 16 * bb + m], mprod);
+      }
+      f32x4 r = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        r = mma_f32_16x16(Li[(16 * (bb + 1) + m) * LDA + 16 * (bb + 1) + 4 * hq + s], mprod[s], r);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Li[(16 * (bb + 1) + 4 * hq + v) * LDA + 16 * bb + m] = -r[v];
+    }
+    __syncthreads();
+    // ---- solve (c): the 32x32 block L^-1_{1,0} = -L^-1_{11} (A_{10} L^-1_{00}) ----
+    {
+      const int mi = wave >> 1, ni = wave & 1, m = lane & 15, hq = lane >> 4;
+      f32x4 acc = zero4();
+      // L^-1_{00} is lower triangular: its rows 0..15 vanish in columns 16..31
+      for (int s = ni ? 4 : 0; s < 8; ++s) {
+        const int k = 4 * s + hq;
+        acc = mma_f32_16x16(Am[(32 + 16 * mi + m) * LDA + k], Li[k * LDA + 16 * ni + m], acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Mt[(16 * mi + 4 * hq + v) * LDM + 16 * ni + m] = acc[v];
+    }
+    __syncthreads();
+    {
+      const int mi = wave >> 1, ni = wave & 1, m = lane & 15, hq = lane >> 4;
+      f32x4 acc = zero4();
+      // L^-1_{11} is lower triangular: its rows 0..15 vanish in columns 16..31
+      for (int s = 0; s < (mi ? 8 : 4); ++s) {
+        const int k = 4 * s + hq;
+        acc = mma_f32_16x16(Li[(32 + 16 * mi + m) * LDA + 32 + k], Mt[k * LDM + 16 * ni + m], acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) Li[(32 + 16 * mi + 4 * hq + v) * LDA + 16 * ni + m] = -acc[v];
+    }
+    __syncthreads();
+    // ---- solve (d): T[r][j] = L^-1[r][j] beta_j on and below the diagonal, 0 above ----
     {
       const int r = tid >> 2, jc = (tid & 3) * 16;
+      float x[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = jc + e;
-        const float x = j <= r ? Li[r * LDA + j] * Bt[j] : 0.f;
-        Tm[r * LDT + j] = to_elem<E>(x);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(Li + r * LDA + jc + 4 * q4);
+        const float4 b4 = *reinterpret_cast<const float4*>(Bt + jc + 4 * q4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q4 + e] = (jc + 4 * q4 + e <= r) ? lv[e] * bv[e] : 0.f;
       }
-    }
-    // phase 3 writes Xt over the solve's scratch region
-    __syncthreads();
-
-    // ---- phase 3: X = V - diag(gamma) K S^T  and  O_inter = diag(gamma) Q S^T ----
-    f32x16 oacc = zero16();
-    if (x_rb >= 0) {
-      const int ib = NI == 2 ? own_ib : 0;
-      f32x16 xacc = zero16();
-      tile_nt(xacc, Kr + x_rb * 32 * LDK, LDK, Sb + ib * 32 * LDSB, LDSB, DK / 16, lane);
-      const int i = ib * 32 + col;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = x_rb * 32 + acc_row(g, 0, lane);
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          x[e] = load_elem(Vt + i * LDT + r0 + e) - __expf(G[r0 + e]) * xacc[4 * g + e];
-        store4(Xt + i * LDT + r0, x[0], x[1], x[2], x[3]);
-      }
-    }
-    if (own_rb >= 0) {
-      tile_nt(oacc, Qr + own_rb * 32 * LDK, LDK, Sb + own_ib * 32 * LDSB, LDSB, DK / 16, lane);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = own_rb * 32 + acc_row(g, 0, lane);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[4 * g + e] *= __expf(G[r0 + e]);
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        store4(Tm + r * LDT + jc + 4 * q4, x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
     }
     __syncthreads();
-
-    // ---- phase 3b: K^T into the Q region (4 rows x one 16-byte chunk per step) ----
-    {
-      constexpr int CPR = DK / EPC;
-      for (int blk = tid; blk < (C / 4) * CPR; blk += kThreads) {
-        const int rg = blk / CPR, cc = blk % CPR;
-        union Row { uint4 raw; E e[EPC]; } v[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          v[m].raw = *reinterpret_cast<const uint4*>(Kr + (4 * rg + m) * LDK + cc * EPC);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          E* dst = Kt + (cc * EPC + e) * LDT + 4 * rg;
-          dst[0] = v[0].e[e];
-          dst[1] = v[1].e[e];
-          dst[2] = v[2].e[e];
-          dst[3] = v[3].e[e];
-        }
-      }
-    }
 
     // ---- phase 4: U = T X; store U^T and the decay-weighted copy for the state ----
     if (own_rb >= 0) {
       f32x16 uacc = zero16();
-      tile_nt(uacc, Tm + own_rb * 32 * LDT, LDT, Xt + own_ib * 32 * LDT, LDT, (own_rb + 1) * 2, lane);
+      if (own_rb == 0) tile_nt_k<2>(uacc, Tm, LDT, Xt + own_ib * 32 * LDT, LDT, lane);
+      else tile_nt_k<4>(uacc, Tm + 32 * LDT, LDT, Xt + own_ib * 32 * LDT, LDT, lane);
       const int i = own_ib * 32 + col;
-      const float GC = G[C - 1];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = own_rb * 32 + acc_row(g, 0, lane);
+        const float4 ec = *reinterpret_cast<const float4*>(Ec + r0);
         store4(Ut + i * LDT + r0, uacc[4 * g], uacc[4 * g + 1], uacc[4 * g + 2], uacc[4 * g + 3]);
-        float w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = uacc[4 * g + e] * __expf(GC - G[r0 + e]);
-        store4(Uw + i * LDT + r0, w[0], w[1], w[2], w[3]);
+        store4(Uw + i * LDT + r0, uacc[4 * g] * ec.x, uacc[4 * g + 1] * ec.y,
+               uacc[4 * g + 2] * ec.z, uacc[4 * g + 3] * ec.w);
       }
     }
     __syncthreads();
 
     // ---- phase 5: O = O_inter + P U, written to HBM ----
     if (own_rb >= 0) {
-      tile_nt(oacc, Pm + own_rb * 32 * LDT, LDT, Ut + own_ib * 32 * LDT, LDT, (own_rb + 1) * 2, lane);
+      if (own_rb == 0) tile_nt_k<2>(oacc, Pm, LDT, Ut + own_ib * 32 * LDT, LDT, lane);
+      else tile_nt_k<4>(oacc, Pm + 32 * LDT, LDT, Ut + own_ib * 32 * LDT, LDT, lane);
       const int i = own_ib * 32 + col;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -382,16 +487,30 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
 
     // ---- phase 6: S^T <- gamma_C S^T + K^T Uw  (fp32 accumulators), refresh Sb ----
     {
-      const float gC = __expf(G[C - 1]);
+      const float gC = Eg[C - 1];
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
+      if (NST == 2 && wave + 4 < NT) {
+        // tiles wave and wave + 4 share the value block: one Uw fragment, two MFMAs
+        tile_nt2_shared_b<C / 16>(Sacc[0], Sacc[NST - 1], Kt + (wave / NI) * 32 * LDT,
+                                  Kt + ((wave + 4) / NI) * 32 * LDT, LDT,
+                                  Uw + (wave % NI) * 32 * LDT, LDT, lane);
+      } else {
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const int t = wave + 4 * st;
+          if (t < NT)
+            tile_nt_k<C / 16>(Sacc[st], Kt + (t / NI) * 32 * LDT, LDT, Uw + (t % NI) * 32 * LDT,
+                              LDT, lane);
+        }
+      }
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const int t = wave + 4 * st;
         if (t < NT) {
-          const int cb = t / NI, ib = t % NI;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
-          tile_nt(Sacc[st], Kt + cb * 32 * LDT, LDT, Uw + ib * 32 * LDT, LDT, C / 16, lane);
-          const int i = ib * 32 + col;
+          const int cb = t / NI, ib = t % NI, i = ib * 32 + col;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int c0 = cb * 32 + acc_row(g, 0, lane);
@@ -431,12 +550,13 @@ hipError_t launch_slices(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Slice width: 64 value rows per workgroup when that still gives at least one
-// workgroup per compute unit (256), else 32.
+// Slice width: 64 value rows per workgroup (bf16) when that still gives at least
+// one workgroup per compute unit (256), else 32.  fp32 tiles take twice the LDS,
+// so fp32 always uses 32-row slices.
 template <typename E, int DK>
 hipError_t launch_dk(const PrefillArgs& a, hipStream_t stream) {
-  if constexpr (sizeof(E) == 4 && DK == 128) {
-    return launch_slices<E, DK, 32>(a, stream);  // a 64-row fp32 slice does not fit in LDS
+  if constexpr (sizeof(E) == 4) {
+    return launch_slices<E, DK, 32>(a, stream);
   } else {
     const long long wg64 = (long long)a.B * a.H * (a.dv / 64);
     if (wg64 >= 256) return launch_slices<E, DK, 64>(a, stream);
