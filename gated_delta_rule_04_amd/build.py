@@ -32,6 +32,8 @@ def hipcc() -> str:
 def compile_flags():
     return ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep register arrays (prefetch buffers) in registers, never in spare LDS
+            "-mllvm", "-disable-promote-alloca-to-lds",
             "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -73,9 +73,10 @@ const char* gdn_status_string(gdn_status s) {
 
 size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
                                      gdn_dtype dtype, gdn_decay mode) {
-  // The fused chunk kernel keeps every intermediate on chip.
-  (void)B; (void)T; (void)H; (void)dk; (void)dv; (void)chunk; (void)dtype; (void)mode;
-  return 0;
+  if (check_common(B, H, dk, dv, dtype, mode) != GDN_OK || T < 0 || chunk != kChunk) return 0;
+  long long n;
+  if (!count4(B, T, H, 1, &n)) return 0;
+  return gdn::prefill_workspace_bytes(B, T, H, (int)dtype);
 }
 
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
@@ -92,10 +93,10 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void
       !count4(B, H, dv, dk, &nS))
     return GDN_ERR_SHAPE;
   if ((long long)B * H * (dv / 32) > 0x7fffffffLL) return GDN_ERR_SHAPE;
-  if (workspace_bytes < gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, mode))
-    return GDN_ERR_WORKSPACE;
-  (void)workspace;
+  const size_t ws_need = gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, mode);
+  if (workspace_bytes < ws_need) return GDN_ERR_WORKSPACE;
   if (B == 0 || H == 0) return GDN_OK;
+  if (ws_need > 0 && !workspace) return GDN_ERR_NULL;
   const bool has_tokens = T > 0;
   if (has_tokens) {
     if (!q || !k || !v || !beta || !o) return GDN_ERR_NULL;
@@ -119,10 +120,13 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void
   for (Range in : {rq, rk, rv, ra, rb, ro})
     if (overlaps(rsf, in)) return GDN_ERR_ALIAS;
   if (overlaps(rsf, rs0) && (const void*)S_final != (const void*)S0) return GDN_ERR_ALIAS;
+  Range rw = range_of(ws_need > 0 ? workspace : nullptr, ws_need);
+  for (Range in : {rq, rk, rv, ra, rb, rs0, ro, rsf})
+    if (overlaps(rw, in)) return GDN_ERR_ALIAS;
 
   gdn::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_final, B, T, H, dk, dv, (int)dtype,
                      (int)mode};
-  return gdn::launch_prefill(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+  return gdn::launch_prefill(a, workspace, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const void* alpha,

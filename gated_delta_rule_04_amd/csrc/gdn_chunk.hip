@@ -20,24 +20,29 @@
 // state-reduction notes' (section 2.2); the NextTransformer page names the
 // triangular inverse of its chunked kernel in its numerics section.)
 //
-// One workgroup of 256 threads (four waves) owns one (b, h, d_v slice) and walks
-// the chunks of its head in order; value rows are independent ("On State
-// Reduction" notes, section 2.5), so slices of d_v never talk to each other.
-// The fp32 state slice lives in MFMA accumulator registers for the whole
-// sequence; a copy in the operand dtype is kept in LDS for the next chunk's
-// K S^T and Q S^T.  Every product is an MFMA tile fed from LDS and all
-// intermediates (A, T, X, U, P) stay in LDS, so HBM sees q, k, v and the gates
-// once, o once, and S0 / S_final once per head.  The next chunk's q, k, v and
-// gates are loaded into registers while the current chunk computes.
+// A and T depend only on the chunk's keys and gates, never on the state, so
+// they are computed by a first, fully parallel kernel (one workgroup per chunk
+// of every head, several workgroups per compute unit) and handed to the
+// sequential kernel through a workspace: T in the operand dtype, 64 x 64 per
+// chunk.  The sequential kernel then only carries the state chain
+// X -> U -> (O, S) per chunk.
 //
-// Per chunk step:
-//   commit   prefetched registers -> LDS (K rows, K^T, Q rows, V^T, gates)
-//   phase 1  A and P tiles (bf16/fp32 MFMA), X and diag(gamma) Q S^T tiles
-//   solve    T = (I + A)^-1 diag(beta): 16x16 diagonal inverses by forward
-//            substitution, then two levels of fp32 MFMA block products
-//   phase 4  U = T X
-//   phase 5  O = diag(gamma) Q S^T + P U  -> HBM
-//   phase 6  S^T <- gamma_C S^T + K^T (diag(exp(G_C - G)) U)
+// chunk_prep_kernel  (grid B * H * N_chunks)
+//   K tile and gates -> A (MFMA) -> 16x16 diagonal inverses (quad-DPP forward
+//   substitution) -> two levels of fp32 MFMA block products -> T -> workspace.
+// chunk_state_kernel (grid B * H * d_v / DVS, chunks in order)
+//   One workgroup of four waves owns one (b, h, d_v slice); value rows are
+//   independent ("On State Reduction" notes, section 2.5).  The fp32 state slice
+//   lives in MFMA accumulator registers for the whole sequence, with a copy in
+//   the operand dtype in LDS for the next chunk's K S^T and Q S^T.  The next
+//   chunk's q, k, v, T and gates are loaded into registers while the current
+//   chunk computes.  Per chunk:
+//     commit   prefetched registers -> LDS (K rows, K^T, Q rows, V^T, T, gates),
+//              previous chunk's staged O -> HBM
+//     phase 1  P tiles, X and diag(gamma) Q S^T tiles
+//     phase 4  U = T X
+//     phase 5  O = diag(gamma) Q S^T + P U, staged in LDS
+//     phase 6  S^T <- gamma_C S^T + K^T (diag(exp(G_C - G)) U)
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
@@ -50,30 +55,269 @@ constexpr float kLogFloor = -100.f;  // gates below e^-100 act as e^-100 (= 0 in
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
-// LDS plan (byte offsets).  Lifetimes inside one chunk step:
+// Tiles are moved between HBM, registers and LDS in blocks of 4 rows x one
+// 16-byte chunk.  Block blk of a tile with cpr chunks per row covers rows
+// 4 blk_row .. 4 blk_row + 3 and chunk blk_col.  Four consecutive blocks take
+// four row groups of one chunk, the next four the next chunk: a wave's global
+// loads cover whole rows, its row-major 16-byte LDS writes hit distinct banks,
+// and its transposed 8-byte writes collide at most two-way.
+__device__ inline int blk_row(int blk, int cpr) { return (blk & 3) + 4 * (blk / (4 * cpr)); }
+__device__ inline int blk_col(int blk, int cpr) { return (blk >> 2) % cpr; }
+
+// Workspace layout, per chunk of every head (chunk index = head * N_chunks + n):
+//   T      C x C elements of the operand dtype, row-major
+//   gates  3 x C fp32: G_r, exp(G_r), exp(G_C - G_r)
+// T blocks come first (all chunks), then the gate blocks.
+constexpr size_t kGateFloats = 3 * C;
+
+template <typename E>
+__device__ inline float* gate_block(E* tws, size_t nchunks_total, size_t chunk) {
+  return reinterpret_cast<float*>(tws + nchunks_total * C * C) + chunk * kGateFloats;
+}
+template <typename E>
+__device__ inline const float* gate_block(const E* tws, size_t nchunks_total, size_t chunk) {
+  return reinterpret_cast<const float*>(tws + nchunks_total * C * C) + chunk * kGateFloats;
+}
+
+// Sum over the four lanes of a quad (lanes 4c .. 4c + 3), result in all four.
+__device__ inline float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+  return x;
+}
+
+// Gates of one chunk, lane r of the wave holding token r: inclusive prefix G of
+// log alpha (0 past the sequence end).
+template <int MODE>
+__device__ inline float chunk_log_decay(float alpha, bool ok) {
+  float la = (MODE == 1 && ok) ? fmaxf(logf(alpha), kLogFloor) : 0.f;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(la, off);
+    if (lane >= off) la += y;
+  }
+  return la;
+}
+
+// ---------------------------------------------------------------------------
+// chunk_prep_kernel: T = (I + A)^-1 diag(beta) for one chunk of one head.
+// ---------------------------------------------------------------------------
+// LDS: K rows [64][LDK] (then L^-1 fp32 [64][LDA] in the same bytes), A fp32
+// [64][LDA] (then T [64][LDT]), Mt fp32 [32][LDM], G and beta.
+template <typename E, int DK>
+struct PrepPlan {
+  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDA = C + 4;
+  static constexpr int LDT = C + PAD;
+  static constexpr int LDM = 32 + 4;
+  static constexpr size_t kr = 0;  // also L^-1
+  static constexpr size_t am = cmax((size_t)C * LDK * sizeof(E), (size_t)C * LDA * 4);
+  static constexpr size_t mt = am + cmax((size_t)C * LDA * 4, (size_t)C * LDT * sizeof(E));
+  static constexpr size_t g = mt + (size_t)32 * LDM * 4;
+  static constexpr size_t total = g + 2 * C * 4;
+};
+
+template <typename E, int DK, int MODE>
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* __restrict__ tws,
+                                                              int nchunks) {
+  const size_t nchunks_total = (size_t)a.B * a.H * nchunks;
+  using L = PrepPlan<E, DK>;
+  constexpr int EPC = 16 / (int)sizeof(E);
+  constexpr int CPR = DK / EPC;
+  constexpr int NKB = 16 * CPR;
+  constexpr int LDK = L::LDK, LDA = L::LDA, LDT = L::LDT, LDM = L::LDM;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
+  E* Kr = reinterpret_cast<E*>(smem + L::kr);
+  float* Li = reinterpret_cast<float*>(smem + L::kr);
+  float* Am = reinterpret_cast<float*>(smem + L::am);
+  E* Tm = reinterpret_cast<E*>(smem + L::am);
+  float* Mt = reinterpret_cast<float*>(smem + L::mt);
+  float* G = reinterpret_cast<float*>(smem + L::g);
+  float* Bt = G + C;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
+  const int H = a.H, T = a.T;
+  const int n = blockIdx.x % nchunks;
+  const int bh = blockIdx.x / nchunks;
+  const int h = bh % H, b = bh / H;
+  const int t0 = n * C, cn = min(C, T - t0);
+  const size_t tok0 = (size_t)b * T + t0;   // first token of the chunk in [B, T]
+
+  // K rows (rows past the sequence end repeat its last row: beta = 0 there, so
+  // they never reach A or T)
+  {
+    const E* kg = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
+    const size_t ktok = (size_t)H * DK;
+    for (int blk = tid; blk < NKB; blk += kThreads) {
+      const int rg = blk_row(blk, CPR), cc = blk_col(blk, CPR);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 4 * rg + rr;
+        *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) =
+            *reinterpret_cast<const u32x4*>(kg + (size_t)min(r, cn - 1) * ktok + cc * EPC);
+      }
+    }
+  }
+  if (wave == 0) {
+    const bool ok = lane < cn;
+    const size_t tok = (tok0 + min(lane, cn - 1)) * H + h;
+    const float al = MODE == 1 ? static_cast<const float*>(a.alpha)[tok] : 1.f;
+    const float bt = a.beta[tok];
+    const float g = chunk_log_decay<MODE>(al, ok);
+    const float gC = __shfl(g, C - 1);
+    G[lane] = g;
+    Bt[lane] = ok ? bt : 0.f;
+    float* gw = gate_block(tws, nchunks_total, blockIdx.x);
+    gw[lane] = g;
+    gw[C + lane] = __expf(g);
+    gw[2 * C + lane] = __expf(gC - g);
+  }
+  __syncthreads();
+
+  // A tiles (j block, r block) in {(0,0), (0,1), (1,1)}: rows j, columns r.
+  if (wave < 3) {
+    const int jb = wave == 2 ? 1 : 0, rb = wave == 0 ? 0 : 1;
+    f32x16 acc = zero16();
+    tile_nt_k<DK / 16>(acc, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
+    const int r = rb * 32 + col;
+    const float Gr = G[r], br = Bt[r];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j0 = jb * 32 + acc_row(g, 0, lane);
+      const float4 gj = *reinterpret_cast<const float4*>(G + j0);
+      const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (j0 + e < r) ? br * __expf(Gr - gjv[e]) * acc[4 * g + e] : 0.f;
+      store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
+    }
+  }
+  __syncthreads();
+
+  // (a) inverse of each unit-lower 16x16 diagonal block: wave w owns block w;
+  // lane 4c + p computes column c, rows 4p .. 4p + 3, summing its part of each
+  // row's dot product and finishing it across the quad.
+  {
+    const int I = wave, c = lane >> 2, p = lane & 3;
+    const float* arow = Am + (16 * I) * LDA + 16 * I + 4 * p;
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 a4 = *reinterpret_cast<const float4*>(arow + i * LDA);
+      float part = a4.x * y[0] + a4.y * y[1] + a4.z * y[2] + a4.w * y[3];
+      part = quad_sum(part);
+      const float yi = i < c ? 0.f : (i == c ? 1.f : -part);
+      if (p == (i >> 2)) y[i & 3] = yi;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Li[(16 * I + 4 * p + e) * LDA + 16 * I + c] = y[e];
+  }
+  __syncthreads();
+  // (b) L^-1_{b+1,b} = -L^-1_{b+1,b+1} (A_{b+1,b} L^-1_{b,b}), b = 0, 2, fp32 MFMA
+  // 16x16x4; lane l uses k index 4 (l / 16) + s in step s, so the first
+  // product's accumulator is directly the second product's B operand.
+  if (wave < 2) {
+    const int bb = 2 * wave, m = lane & 15, hq = lane >> 4;
+    f32x4 mprod = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k = 4 * hq + s;
+      mprod = mma_f32_16x16(Am[(16 * (bb + 1) + m) * LDA + 16 * bb + k],
+                            Li[(16 * bb + k) * LDA + 16 * bb + m], mprod);
+    }
+    f32x4 r = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      r = mma_f32_16x16(Li[(16 * (bb + 1) + m) * LDA + 16 * (bb + 1) + 4 * hq + s], mprod[s], r);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Li[(16 * (bb + 1) + 4 * hq + v) * LDA + 16 * bb + m] = -r[v];
+  }
+  __syncthreads();
+  // (c) the 32x32 block L^-1_{1,0} = -L^-1_{11} (A_{10} L^-1_{00}).  L^-1_{00} and
+  // L^-1_{11} are lower triangular: their rows 0..15 vanish in columns 16..31,
+  // so those k steps take zero operands (selected, never read as data).
+  const int mi = wave >> 1, ni = wave & 1, m16 = lane & 15, hq = lane >> 4;
+  {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int k = 4 * s + hq;
+      const bool live = ni == 0 || s >= 4;
+      const float av = Am[(32 + 16 * mi + m16) * LDA + k];
+      const float bv = Li[k * LDA + 16 * ni + m16];
+      acc = mma_f32_16x16(live ? av : 0.f, live ? bv : 0.f, acc);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Mt[(16 * mi + 4 * hq + v) * LDM + 16 * ni + m16] = acc[v];
+  }
+  __syncthreads();   // A is dead from here: T takes its bytes
+  {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int k = 4 * s + hq;
+      const bool live = mi == 1 || s < 4;
+      const float av = Li[(32 + 16 * mi + m16) * LDA + 32 + k];
+      const float bv = Mt[k * LDM + 16 * ni + m16];
+      acc = mma_f32_16x16(live ? av : 0.f, live ? bv : 0.f, acc);
+    }
+    const float bj = Bt[16 * ni + m16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      Tm[(32 + 16 * mi + 4 * hq + v) * LDT + 16 * ni + m16] = to_elem<E>(-acc[v] * bj);
+    // T on the two diagonal 32x32 blocks, zeros above them: 8 columns per thread
+    const int q = tid >> 7, r = 32 * q + ((tid & 127) >> 2), jc = 32 * q + (tid & 3) * 8;
+    float x[8];
+#pragma unroll
+    for (int q4 = 0; q4 < 2; ++q4) {
+      const float4 l4 = *reinterpret_cast<const float4*>(Li + r * LDA + jc + 4 * q4);
+      const float4 b4 = *reinterpret_cast<const float4*>(Bt + jc + 4 * q4);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * q4 + e] = (jc + 4 * q4 + e <= r) ? lv[e] * bv[e] : 0.f;
+    }
+    store4(Tm + r * LDT + jc, x[0], x[1], x[2], x[3]);
+    store4(Tm + r * LDT + jc + 4, x[4], x[5], x[6], x[7]);
+    if (q == 0) {
+      store4(Tm + r * LDT + 32 + (tid & 3) * 8, 0.f, 0.f, 0.f, 0.f);
+      store4(Tm + r * LDT + 36 + (tid & 3) * 8, 0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __syncthreads();
+  // T -> workspace, 64 x 64 contiguous, 16-byte stores
+  {
+    E* dst = tws + (size_t)blockIdx.x * C * C;
+    constexpr int CPT = C / EPC;
+    for (int q = tid; q < C * CPT; q += kThreads) {
+      const int r = q / CPT, cc = q % CPT;
+      *reinterpret_cast<u32x4*>(dst + r * C + cc * EPC) = *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk_state_kernel: the sequential pass over the chunks of one (b, h, slice).
+// ---------------------------------------------------------------------------
+// LDS plan.  Lifetimes inside one chunk step:
 //   Kr    K rows [64][LDK]               commit .. phase 1
 //   Qr    Q rows [64][LDK]               commit .. phase 1
 //   Kt    K^T    [DK][LDT]               commit (or after phase 1) .. phase 6
 //         (fp32 with d_k = 128: shares Q's region to fit in 160 KiB)
 //   Sb    state copy S[i][c] [DVS][LDSB] phase 6 .. next phase 1
 //   Vt    V^T slice [DVS][LDT]           commit .. phase 1
-//   Xt    X^T slice [DVS][LDT]           phase 1 .. phase 4
+//   Xt    X^T slice [DVS][LDT]           phase 1 .. phase 4; then O staging
 //   Pm    P [64][LDT]                    phase 1 .. phase 5
-//   Tm    T [64][LDT]                    solve .. phase 4 (fp32: also the solve's L^-1)
-//   Am    A fp32 [64][LDA]               phase 1 .. solve       } one region
-//   Li    L^-1 fp32 [64][LDA] (bf16)     solve                  }
-//   Mt    fp32 [32][LDM]                 solve                  }
-//   Ut, Uw  [DVS][LDT] each              phase 4 .. phase 6     }
-//   G, Bt, Eg, Ec  64 fp32 each          commit .. phase 6
+//   Tm    T [64][LDT]                    commit .. phase 4
+//   Ut, Uw  [DVS][LDT] each              phase 4 .. phase 6
+//   G, Eg, Ec  64 fp32 each              commit .. phase 6
 template <typename E, int DK, int DVS, bool SEPKT>
-struct Plan {
+struct StatePlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = DK + PAD;
   static constexpr int LDT = C + PAD;
   static constexpr int LDSB = DK + PAD;
-  static constexpr int LDA = C + 4;
-  static constexpr int LDM = 32 + 4;
-  static constexpr bool kF32 = sizeof(E) == 4;
   static constexpr size_t es = sizeof(E);
   static constexpr size_t kr = 0;
   static constexpr size_t qr = kr + (size_t)C * LDK * es;
@@ -84,42 +328,52 @@ struct Plan {
   static constexpr size_t xt = vt + (size_t)DVS * LDT * es;
   static constexpr size_t pm = xt + (size_t)DVS * LDT * es;
   static constexpr size_t tm = pm + (size_t)C * LDT * es;
-  static constexpr size_t region = tm + (size_t)C * LDT * es;
-  static constexpr size_t am = region;
-  static constexpr size_t li = am + (size_t)C * LDA * 4;
-  static constexpr size_t mt = kF32 ? li : li + (size_t)C * LDA * 4;
-  static constexpr size_t solve_end = mt + (size_t)32 * LDM * 4;
-  static constexpr size_t ut = region;
+  static constexpr size_t ut = tm + (size_t)C * LDT * es;
   static constexpr size_t uw = ut + (size_t)DVS * LDT * es;
-  static constexpr size_t u_end = uw + (size_t)DVS * LDT * es;
-  static constexpr size_t g = cmax(solve_end, u_end);
-  static constexpr size_t total = g + 4 * C * 4;
-  static_assert(!kF32 || LDT == LDA, "fp32 mode keeps L^-1 in the T buffer");
+  static constexpr size_t g = uw + (size_t)DVS * LDT * es;
+  static constexpr size_t total = g + 3 * C * 4;
 };
 
 template <typename E, int DK, int DVS>
 constexpr bool sep_kt_fits() {
-  return Plan<E, DK, DVS, true>::total <= 160 * 1024;
+  return StatePlan<E, DK, DVS, true>::total <= 160 * 1024;
+}
+
+// Element e of four 16-byte chunks (four consecutive rows), stored as four
+// consecutive elements: the transpose used to build K^T and V^T.
+__device__ inline void store_col4(__bf16* dst, const u32x4& r0, const u32x4& r1, const u32x4& r2,
+                                  const u32x4& r3, int e) {
+  const int w = e >> 1;
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  const uint32_t lo = __builtin_amdgcn_perm(word_of(r1, w), word_of(r0, w), sel);
+  const uint32_t hi = __builtin_amdgcn_perm(word_of(r3, w), word_of(r2, w), sel);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+}
+__device__ inline void store_col4(float* dst, const u32x4& r0, const u32x4& r1, const u32x4& r2,
+                                  const u32x4& r3, int e) {
+  *reinterpret_cast<u32x4*>(dst) = u32x4{word_of(r0, e), word_of(r1, e), word_of(r2, e), word_of(r3, e)};
 }
 
 template <typename E, int DK, int DVS, int MODE>
-__global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, const E* __restrict__ tws) {
   constexpr bool SEPKT = sep_kt_fits<E, DK, DVS>();
-  using L = Plan<E, DK, DVS, SEPKT>;
+  using L = StatePlan<E, DK, DVS, SEPKT>;
   static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
   constexpr int NI = DVS / 32;       // 32-wide value blocks in the slice
   constexpr int NC = DK / 32;        // 32-wide key blocks
   constexpr int NT = NC * NI;        // state tiles
   constexpr int NST = (NT + 3) / 4;  // state tiles per wave
   constexpr int EPC = 16 / (int)sizeof(E);  // elements per 16-byte chunk
-  constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB, LDA = L::LDA, LDM = L::LDM;
-  // prefetch geometry: blocks of 4 rows x one 16-byte chunk, row group fastest
+  constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB;
+  // prefetch geometry: blocks of 4 rows x one 16-byte chunk (blk_row / blk_col)
   constexpr int CPR = DK / EPC;              // chunks per q/k row
   constexpr int NKB = 16 * CPR;              // 4-row blocks per q/k tile
   constexpr int KBT = (NKB + kThreads - 1) / kThreads;
   constexpr int CPV = DVS / EPC;             // chunks per v row (slice)
   constexpr int NVB = 16 * CPV;
   constexpr int VBT = (NVB + kThreads - 1) / kThreads;
+  constexpr int CPT = C / EPC;               // chunks per T row
+  constexpr int TBT = C * CPT / kThreads;    // T chunks per thread
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
   E* Kr = reinterpret_cast<E*>(smem + L::kr);
@@ -130,49 +384,59 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
   E* Xt = reinterpret_cast<E*>(smem + L::xt);
   E* Pm = reinterpret_cast<E*>(smem + L::pm);
   E* Tm = reinterpret_cast<E*>(smem + L::tm);
-  float* Am = reinterpret_cast<float*>(smem + L::am);
-  float* Li = L::kF32 ? reinterpret_cast<float*>(smem + L::tm) : reinterpret_cast<float*>(smem + L::li);
-  float* Mt = reinterpret_cast<float*>(smem + L::mt);
   E* Ut = reinterpret_cast<E*>(smem + L::ut);
   E* Uw = reinterpret_cast<E*>(smem + L::uw);
-  float* G = reinterpret_cast<float*>(smem + L::g);
-  float* Bt = G + C;
-  float* Eg = G + 2 * C;   // exp(G_r)
-  float* Ec = G + 3 * C;   // exp(G_C - G_r)
+  float* G = reinterpret_cast<float*>(smem + L::g);   // gate block, as in the workspace
+  float* Eg = G + C;       // exp(G_r)
+  float* Ec = G + 2 * C;   // exp(G_C - G_r)
+  // O staging (rows r, OST elements apart) reuses X^T's region, free after phase 4
+  constexpr int OST = (sizeof(E) == 2 && DVS == 64) ? 72 : DVS;
+  static_assert(C * OST <= DVS * LDT, "O staging does not fit in the X^T region");
+  E* Os = Xt;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31;
   const int H = a.H, T = a.T, dv = a.dv;
   const int nsl = dv / DVS;
-  int bid = blockIdx.x;
-  const int sl = bid % nsl;
-  bid /= nsl;
-  const int h = bid % H;
-  const int b = bid / H;
+  const int nheads = a.B * H;
+  // Workgroups are dispatched round-robin over the eight XCDs: give the slices
+  // of one head the same XCD (same L2) when the head count allows it.
+  int head, sl;
+  if ((nheads & 7) == 0) {
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    head = xcd + 8 * (j / nsl);
+    sl = j % nsl;
+  } else {
+    head = blockIdx.x / nsl;
+    sl = blockIdx.x % nsl;
+  }
+  const int h = head % H, b = head / H;
   const int i0 = sl * DVS;
+  const int nchunks = (T + C - 1) / C;
 
   const size_t qk_tok = (size_t)H * DK;   // stride between tokens in q, k
   const size_t v_tok = (size_t)H * dv;    // stride between tokens in v, o
   const E* qg = static_cast<const E*>(a.q) + ((size_t)b * T * H + h) * DK;
   const E* kg = static_cast<const E*>(a.k) + ((size_t)b * T * H + h) * DK;
   const E* vg = static_cast<const E*>(a.v) + ((size_t)b * T * H + h) * dv + i0;
+  const E* tg = tws + (size_t)head * nchunks * C * C;
   E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
   const size_t sbase = ((size_t)b * H + h) * dv + i0;  // first state row of the slice
 
   // Tile ownership.  X, O_inter (phase 1), U (phase 4) and O (phase 5) tiles of
-  // row block own_rb and value block own_ib belong to one wave; the three A/P
-  // tile pairs (j block, r block) in {(0,0), (0,1), (1,1)} go to the waves with
-  // the least other work.
-  int own_rb = -1, own_ib = 0, ap = -1;
+  // row block own_rb and value block own_ib belong to one wave; the three P
+  // tiles (j block, r block) in {(0,0), (0,1), (1,1)} go to the waves with the
+  // least other work.
+  int own_rb = -1, own_ib = 0, pt0 = -1, pt1 = -1;
   if (NI == 2) {
     own_rb = wave >> 1;
     own_ib = wave & 1;
-    ap = wave < 3 ? wave : -1;
+    pt0 = wave < 3 ? wave : -1;
   } else {
     if (wave < 2) own_rb = wave;
-    ap = wave == 0 ? 2 : (wave >= 2 ? wave - 2 : -1);
+    if (wave == 2) { pt0 = 0; pt1 = 2; }
+    if (wave == 3) pt0 = 1;
   }
-  const int ap_jb = ap == 2 ? 1 : 0, ap_rb = ap == 0 ? 0 : 1;
 
   // Initial state: S0 or zeros, into registers and the operand copy.
   f32x16 Sacc[NST];
@@ -197,42 +461,48 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
   }
 
   // ---- prefetch registers ----
-  // Loads are unconditional (rows past the sequence end re-read its last row and
-  // are zeroed at commit) so the compiler keeps them in flight across the chunk.
-  uint4 pk[KBT][4], pq[KBT][4], pv[VBT][4];
-  float p_beta = 0.f, p_alpha = 1.f;
-  int p_cn = 0;
+  // Loads are unconditional, so the compiler keeps them in flight across the
+  // chunk.  Rows past the sequence end re-read its last row: T's rows and
+  // columns of those tokens are zero (their beta is zero), so they never reach
+  // U, O or S, and their O rows are not written.
+  u32x4 pk[KBT][4], pq[KBT][4], pv[VBT][4], pt[TBT];
+  u32x4 pg = u32x4{0u, 0u, 0u, 0u};   // gate block: 48 chunks, threads 0..47
+  const size_t nchunks_total = (size_t)a.B * H * nchunks;
 
   auto prefetch = [&](int n) __attribute__((always_inline)) {
     const int t0 = n * C;
-    const int cn = min(C, T - t0);
-    p_cn = cn;
+    const int rmax = min(C, T - t0) - 1;
+    const E* kq = kg + (size_t)t0 * qk_tok;
+    const E* qq = qg + (size_t)t0 * qk_tok;
+    const E* vq = vg + (size_t)t0 * v_tok;
 #pragma unroll
     for (int m = 0; m < KBT; ++m) {
       const int blk = tid + kThreads * m;
       const int bq = blk < NKB ? blk : 0;
-      const int rg = bq % 16, cc = bq / 16;
+      const int rg = blk_row(bq, CPR), cc = blk_col(bq, CPR);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int r = min(4 * rg + rr, cn - 1);
-        pk[m][rr] = *reinterpret_cast<const uint4*>(kg + (size_t)(t0 + r) * qk_tok + cc * EPC);
-        pq[m][rr] = *reinterpret_cast<const uint4*>(qg + (size_t)(t0 + r) * qk_tok + cc * EPC);
+        const uint32_t off = (uint32_t)min(4 * rg + rr, rmax) * (uint32_t)qk_tok + cc * EPC;
+        pk[m][rr] = *reinterpret_cast<const u32x4*>(kq + off);
+        pq[m][rr] = *reinterpret_cast<const u32x4*>(qq + off);
       }
     }
 #pragma unroll
     for (int m = 0; m < VBT; ++m) {
       const int blk = tid + kThreads * m;
       const int bq = blk < NVB ? blk : 0;
-      const int rg = bq % 16, cc = bq / 16;
+      const int rg = blk_row(bq, CPV), cc = blk_col(bq, CPV);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int r = min(4 * rg + rr, cn - 1);
-        pv[m][rr] = *reinterpret_cast<const uint4*>(vg + (size_t)(t0 + r) * v_tok + cc * EPC);
+        const uint32_t off = (uint32_t)min(4 * rg + rr, rmax) * (uint32_t)v_tok + cc * EPC;
+        pv[m][rr] = *reinterpret_cast<const u32x4*>(vq + off);
       }
     }
-    const size_t tok = ((size_t)b * T + t0 + min(lane, cn - 1)) * H + h;
-    p_beta = a.beta[tok];
-    if (MODE == 1) p_alpha = static_cast<const float*>(a.alpha)[tok];
+    const E* tq = tg + (size_t)n * C * C;
+#pragma unroll
+    for (int m = 0; m < TBT; ++m) pt[m] = *reinterpret_cast<const u32x4*>(tq + (tid + kThreads * m) * EPC);
+    const float* gq = gate_block(tws, nchunks_total, (size_t)head * nchunks + n);
+    pg = *reinterpret_cast<const u32x4*>(gq + 4 * min(tid, (int)kGateFloats / 4 - 1));
   };
 
   auto commit = [&]() __attribute__((always_inline)) {
@@ -240,13 +510,11 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
     for (int m = 0; m < KBT; ++m) {
       const int blk = tid + kThreads * m;
       if (blk < NKB) {
-        const int rg = blk % 16, cc = blk / 16;
+        const int rg = blk_row(blk, CPR), cc = blk_col(blk, CPR);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const bool ok = 4 * rg + rr < p_cn;
-          pk[m][rr] = keep_or_zero(pk[m][rr], ok);
-          *reinterpret_cast<uint4*>(Kr + (4 * rg + rr) * LDK + cc * EPC) = pk[m][rr];
-          *reinterpret_cast<uint4*>(Qr + (4 * rg + rr) * LDK + cc * EPC) = keep_or_zero(pq[m][rr], ok);
+          *reinterpret_cast<u32x4*>(Kr + (4 * rg + rr) * LDK + cc * EPC) = pk[m][rr];
+          *reinterpret_cast<u32x4*>(Qr + (4 * rg + rr) * LDK + cc * EPC) = pq[m][rr];
         }
         if (SEPKT) {
 #pragma unroll
@@ -259,90 +527,95 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
     for (int m = 0; m < VBT; ++m) {
       const int blk = tid + kThreads * m;
       if (blk < NVB) {
-        const int rg = blk % 16, cc = blk / 16;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) pv[m][rr] = keep_or_zero(pv[m][rr], 4 * rg + rr < p_cn);
+        const int rg = blk_row(blk, CPV), cc = blk_col(blk, CPV);
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
           store_col4(Vt + (cc * EPC + e) * LDT + 4 * rg, pv[m][0], pv[m][1], pv[m][2], pv[m][3], e);
       }
     }
-    if (wave == 0) {
-      const bool ok = lane < p_cn;
-      float la = (MODE == 1 && ok) ? fmaxf(logf(p_alpha), kLogFloor) : 0.f;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(la, off);
-        if (lane >= off) la += y;
-      }
-      const float GC = __shfl(la, 63);
-      G[lane] = la;
-      Bt[lane] = ok ? p_beta : 0.f;
-      Eg[lane] = __expf(la);
-      Ec[lane] = __expf(GC - la);
+    for (int m = 0; m < TBT; ++m) {
+      const int q = tid + kThreads * m, r = q / CPT, cc = q % CPT;
+      *reinterpret_cast<u32x4*>(Tm + r * LDT + cc * EPC) = pt[m];
+    }
+    if (tid < (int)kGateFloats / 4) *reinterpret_cast<u32x4*>(G + 4 * tid) = pg;
+  };
+
+  // Staged O rows of a chunk -> HBM, 16-byte stores along each row.
+  auto flush_o = [&](int t0f, int cnf) __attribute__((always_inline)) {
+    constexpr int CPO = DVS / EPC;
+    E* oq = og + (size_t)t0f * v_tok;
+    for (int q = tid; q < C * CPO; q += kThreads) {
+      const int r = q / CPO, cc = q % CPO;
+      if (r < cnf)
+        *reinterpret_cast<u32x4*>(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC) =
+            *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC);
     }
   };
 
-  const int nchunks = (T + C - 1) / C;
-  if (nchunks > 0) prefetch(0);
-  for (int n = 0; n < nchunks; ++n) {
-    const int t0 = n * C;
-    const int cn = min(C, T - t0);
-    __syncthreads();   // every reader of the previous chunk's buffers is done
-    commit();
-    if (n + 1 < nchunks) prefetch(n + 1);
-    __syncthreads();
+  // P tile (jb, rb) from its accumulator: decay weights and the causal mask.
+  auto p_epilogue = [&](const f32x16& pacc, int ptile) __attribute__((always_inline)) {
+    const int jb = ptile == 2 ? 1 : 0, rb = ptile == 0 ? 0 : 1;
+    const int r = rb * 32 + col;
+    const float Gr = G[r];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j0 = jb * 32 + acc_row(g, 0, lane);
+      const float4 gj = *reinterpret_cast<const float4*>(G + j0);
+      const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (j0 + e <= r) ? __expf(Gr - gjv[e]) * pacc[4 * g + e] : 0.f;
+      store4(Pm + r * LDT + j0, x[0], x[1], x[2], x[3]);
+    }
+  };
 
-    // ---- phase 1: A, P tiles; X and O_inter tiles ----
-    // A/P tile pair (jb, rb) holds rows j of the j-block and columns r of the
-    // r-block (shared K_j operand), so each lane writes four consecutive j of one
-    // row r.  The X and O_inter tiles of (own_rb, own_ib) share the S operand.
-    f32x16 xacc = zero16(), oacc = zero16(), aacc = zero16(), pacc = zero16();
-    {
-      const E* Ax = Kr + (own_rb < 0 ? 0 : own_rb) * 32 * LDK;
-      const E* Ao = Qr + (own_rb < 0 ? 0 : own_rb) * 32 * LDK;
+  // Iteration -1 only issues the first prefetch (one call site per helper keeps
+  // the prefetch registers in registers).  Later prefetches are issued at the
+  // start of phase 1, where the memory pipe works under the MFMA chains.
+  for (int n = -1; n < nchunks; ++n) {
+    if (n >= 0) {
+      __syncthreads();   // every reader of the previous chunk's buffers is done
+      if (n > 0) flush_o((n - 1) * C, C);
+      commit();
+      __syncthreads();
+    }
+    if (n + 1 < nchunks) prefetch(n + 1);
+    if (n < 0) continue;
+
+    // ---- phase 1: P tiles; X and O_inter tiles ----
+    // P tile (jb, rb) holds rows j of the j-block and columns r of the r-block,
+    // so each lane writes four consecutive j of one row r.  The X and O_inter
+    // tiles of (own_rb, own_ib) share the S operand.
+    f32x16 xacc = zero16(), oacc = zero16(), pacc0 = zero16(), pacc1 = zero16();
+    const int pjb0 = pt0 == 2 ? 1 : 0, prb0 = pt0 == 0 ? 0 : 1;
+    if (own_rb >= 0) {
+      const E* Ax = Kr + own_rb * 32 * LDK;
+      const E* Ao = Qr + own_rb * 32 * LDK;
       const E* Bs = Sb + own_ib * 32 * LDSB;
-      const E* Aj = Kr + ap_jb * 32 * LDK;
-      const E* C0 = Kr + ap_rb * 32 * LDK;
-      const E* C1 = Qr + ap_rb * 32 * LDK;
-      if (own_rb >= 0 && ap >= 0)
-        tile_nt4<DK / 16>(xacc, oacc, aacc, pacc, Ax, Ao, Bs, Aj, C0, C1, LDK, LDSB, lane);
-      else if (own_rb >= 0)
+      if (pt0 >= 0)
+        tile_nt3<DK / 16>(xacc, oacc, pacc0, Ax, Ao, Bs, Kr + pjb0 * 32 * LDK, Qr + prb0 * 32 * LDK,
+                          LDK, LDSB, lane);
+      else
         tile_nt2_shared_b<DK / 16>(xacc, oacc, Ax, Ao, LDK, Bs, LDSB, lane);
-      else if (ap >= 0)
-        tile_nt2_shared_a<DK / 16>(aacc, pacc, Aj, LDK, C0, C1, LDK, lane);
+    } else if (pt0 >= 0) {
+      if (pt1 >= 0)
+        tile_nt2_pairs<DK / 16>(pacc0, pacc1, Kr + pjb0 * 32 * LDK, Qr + prb0 * 32 * LDK,
+                                Kr + 32 * LDK, Qr + 32 * LDK, LDK, lane);
+      else
+        tile_nt_k<DK / 16>(pacc0, Kr + pjb0 * 32 * LDK, LDK, Qr + prb0 * 32 * LDK, LDK, lane);
     }
-    if (ap >= 0) {
-      const int r = ap_rb * 32 + col;
-      const float Gr = G[r];
-      const float br = Bt[r];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j0 = ap_jb * 32 + acc_row(g, 0, lane);
-        const float4 gj = *reinterpret_cast<const float4*>(G + j0);
-        const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
-        float xa[4], xp[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float d = __expf(Gr - gjv[e]);
-          xa[e] = (j0 + e < r) ? br * d * aacc[4 * g + e] : 0.f;
-          xp[e] = (j0 + e <= r) ? d * pacc[4 * g + e] : 0.f;
-        }
-        store4(Am + r * LDA + j0, xa[0], xa[1], xa[2], xa[3]);
-        store4(Pm + r * LDT + j0, xp[0], xp[1], xp[2], xp[3]);
-      }
-    }
+    if (pt0 >= 0) p_epilogue(pacc0, pt0);
+    if (pt1 >= 0) p_epilogue(pacc1, pt1);
     if (own_rb >= 0) {
       const int i = own_ib * 32 + col;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = own_rb * 32 + acc_row(g, 0, lane);
         const float4 eg = *reinterpret_cast<const float4*>(Eg + r0);
-        store4(Xt + i * LDT + r0,
-               load_elem(Vt + i * LDT + r0 + 0) - eg.x * xacc[4 * g + 0],
-               load_elem(Vt + i * LDT + r0 + 1) - eg.y * xacc[4 * g + 1],
-               load_elem(Vt + i * LDT + r0 + 2) - eg.z * xacc[4 * g + 2],
-               load_elem(Vt + i * LDT + r0 + 3) - eg.w * xacc[4 * g + 3]);
+        const float4 v4 = load4_elem(Vt + i * LDT + r0);
+        store4(Xt + i * LDT + r0, v4.x - eg.x * xacc[4 * g + 0], v4.y - eg.y * xacc[4 * g + 1],
+               v4.z - eg.z * xacc[4 * g + 2], v4.w - eg.w * xacc[4 * g + 3]);
         oacc[4 * g + 0] *= eg.x;
         oacc[4 * g + 1] *= eg.y;
         oacc[4 * g + 2] *= eg.z;
@@ -354,104 +627,16 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
     // ---- K^T for phase 6 when it shares Q's region (fp32, d_k = 128) ----
     if (!SEPKT) {
       for (int blk = tid; blk < NKB; blk += kThreads) {
-        const int rg = blk % 16, cc = blk / 16;
-        uint4 v[4];
+        const int rg = blk_row(blk, CPR), cc = blk_col(blk, CPR);
+        u32x4 v[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          v[rr] = *reinterpret_cast<const uint4*>(Kr + (4 * rg + rr) * LDK + cc * EPC);
+          v[rr] = *reinterpret_cast<const u32x4*>(Kr + (4 * rg + rr) * LDK + cc * EPC);
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
           store_col4(Kt + (cc * EPC + e) * LDT + 4 * rg, v[0], v[1], v[2], v[3], e);
       }
     }
-
-    // ---- solve (a): inverses of the four unit-lower 16x16 diagonal blocks ----
-    // Wave w owns block w; lane c (< 16) computes column c by forward substitution.
-    {
-      const int I = wave, c = lane & 15;
-      const float* base = Am + (16 * I) * LDA + 16 * I;
-      float y[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = 0.f;
-#pragma unroll
-        for (int jq = 0; jq < (i + 3) / 4; ++jq) {
-          const float4 a4 = *reinterpret_cast<const float4*>(base + i * LDA + 4 * jq);
-          const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * jq + e < i) s += av[e] * y[4 * jq + e];
-        }
-        y[i] = i < c ? 0.f : (i == c ? 1.f : -s);
-      }
-      if (lane < 16) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Li[(16 * I + i) * LDA + 16 * I + c] = y[i];
-      }
-    }
-    __syncthreads();
-    // ---- solve (b): L^-1_{b+1,b} = -L^-1_{b+1,b+1} (A_{b+1,b} L^-1_{b,b}), b = 0, 2 ----
-    // fp32 MFMA 16x16x4; lane l uses k index 4 (l / 16) + s in step s, so the
-    // first product's accumulator is directly the second product's B operand.
-    if (wave < 2) {
-      const int bb = 2 * wave, m = lane & 15, hq = lane >> 4;
-      f32x4 mprod = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int k = 4 * hq + s;
-        mprod = mma_f32_16x16(Am[(16 * (bb + 1) + m) * LDA + 16 * bb + k],
-                              Li[(16 * bb + k) * LDA + 16 * bb + m], mprod);
-      }
-      f32x4 r = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        r = mma_f32_16x16(Li[(16 * (bb + 1) + m) * LDA + 16 * (bb + 1) + 4 * hq + s], mprod[s], r);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) Li[(16 * (bb + 1) + 4 * hq + v) * LDA + 16 * bb + m] = -r[v];
-    }
-    __syncthreads();
-    // ---- solve (c): the 32x32 block L^-1_{1,0} = -L^-1_{11} (A_{10} L^-1_{00}) ----
-    {
-      const int mi = wave >> 1, ni = wave & 1, m = lane & 15, hq = lane >> 4;
-      f32x4 acc = zero4();
-      // L^-1_{00} is lower triangular: its rows 0..15 vanish in columns 16..31
-      for (int s = ni ? 4 : 0; s < 8; ++s) {
-        const int k = 4 * s + hq;
-        acc = mma_f32_16x16(Am[(32 + 16 * mi + m) * LDA + k], Li[k * LDA + 16 * ni + m], acc);
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) Mt[(16 * mi + 4 * hq + v) * LDM + 16 * ni + m] = acc[v];
-    }
-    __syncthreads();
-    {
-      const int mi = wave >> 1, ni = wave & 1, m = lane & 15, hq = lane >> 4;
-      f32x4 acc = zero4();
-      // L^-1_{11} is lower triangular: its rows 0..15 vanish in columns 16..31
-      for (int s = 0; s < (mi ? 8 : 4); ++s) {
-        const int k = 4 * s + hq;
-        acc = mma_f32_16x16(Li[(32 + 16 * mi + m) * LDA + 32 + k], Mt[k * LDM + 16 * ni + m], acc);
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) Li[(32 + 16 * mi + 4 * hq + v) * LDA + 16 * ni + m] = -acc[v];
-    }
-    __syncthreads();
-    // ---- solve (d): T[r][j] = L^-1[r][j] beta_j on and below the diagonal, 0 above ----
-    {
-      const int r = tid >> 2, jc = (tid & 3) * 16;
-      float x[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 l4 = *reinterpret_cast<const float4*>(Li + r * LDA + jc + 4 * q4);
-        const float4 b4 = *reinterpret_cast<const float4*>(Bt + jc + 4 * q4);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * q4 + e] = (jc + 4 * q4 + e <= r) ? lv[e] * bv[e] : 0.f;
-      }
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        store4(Tm + r * LDT + jc + 4 * q4, x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
-    }
-    __syncthreads();
 
     // ---- phase 4: U = T X; store U^T and the decay-weighted copy for the state ----
     if (own_rb >= 0) {
@@ -470,19 +655,16 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
-    // ---- phase 5: O = O_inter + P U, written to HBM ----
+    // ---- phase 5: O = O_inter + P U, staged in LDS (rows r, OST apart) ----
     if (own_rb >= 0) {
       if (own_rb == 0) tile_nt_k<2>(oacc, Pm, LDT, Ut + own_ib * 32 * LDT, LDT, lane);
       else tile_nt_k<4>(oacc, Pm + 32 * LDT, LDT, Ut + own_ib * 32 * LDT, LDT, lane);
       const int i = own_ib * 32 + col;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = own_rb * 32 + acc_row(g, e, lane);
-          if (r < cn) og[(size_t)(t0 + r) * v_tok + i] = to_elem<E>(oacc[4 * g + e]);
-        }
-      }
+        for (int e = 0; e < 4; ++e)
+          Os[(own_rb * 32 + acc_row(g, e, lane)) * OST + i] = to_elem<E>(oacc[4 * g + e]);
     }
 
     // ---- phase 6: S^T <- gamma_C S^T + K^T Uw  (fp32 accumulators), refresh Sb ----
@@ -521,6 +703,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
       }
     }
   }
+  if (nchunks > 0) {
+    __syncthreads();
+    flush_o((nchunks - 1) * C, T - (nchunks - 1) * C);
+  }
 
   // Final state of the slice.
   if (a.S_final) {
@@ -541,12 +727,12 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PrefillArgs a) {
 }
 
 template <typename E, int DK, int DVS>
-hipError_t launch_slices(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) {
   dim3 grid((unsigned)((size_t)a.B * a.H * (a.dv / DVS))), block(kThreads);
   if (a.mode == 0)
-    hipLaunchKernelGGL((chunk_kernel<E, DK, DVS, 0>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 0>), grid, block, 0, stream, a, tws);
   else
-    hipLaunchKernelGGL((chunk_kernel<E, DK, DVS, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 1>), grid, block, 0, stream, a, tws);
   return hipGetLastError();
 }
 
@@ -554,22 +740,39 @@ hipError_t launch_slices(const PrefillArgs& a, hipStream_t stream) {
 // one workgroup per compute unit (256), else 32.  fp32 tiles take twice the LDS,
 // so fp32 always uses 32-row slices.
 template <typename E, int DK>
-hipError_t launch_dk(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) {
+  E* tws = static_cast<E*>(workspace);
+  const int nchunks = (a.T + C - 1) / C;
+  if (nchunks > 0) {
+    dim3 grid((unsigned)((size_t)a.B * a.H * nchunks)), block(kThreads);
+    if (a.mode == 0)
+      hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 0>), grid, block, 0, stream, a, tws, nchunks);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 1>), grid, block, 0, stream, a, tws, nchunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if constexpr (sizeof(E) == 4) {
-    return launch_slices<E, DK, 32>(a, stream);
+    return launch_state<E, DK, 32>(a, tws, stream);
   } else {
     const long long wg64 = (long long)a.B * a.H * (a.dv / 64);
-    if (wg64 >= 256) return launch_slices<E, DK, 64>(a, stream);
-    return launch_slices<E, DK, 32>(a, stream);
+    if (wg64 >= 256) return launch_state<E, DK, 64>(a, tws, stream);
+    return launch_state<E, DK, 32>(a, tws, stream);
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+size_t prefill_workspace_bytes(int B, int T, int H, int dtype) {
+  const size_t chunks = (size_t)B * H * (((size_t)T + C - 1) / C);
+  return chunks * (C * C * (dtype == 1 ? 2 : 4) + kGateFloats * 4);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream) {
   if (a.mode == 2) return hipErrorNotSupported;
-  if (a.dtype == 1) return a.dk == 128 ? launch_dk<__bf16, 128>(a, stream) : launch_dk<__bf16, 64>(a, stream);
-  return a.dk == 128 ? launch_dk<float, 128>(a, stream) : launch_dk<float, 64>(a, stream);
+  if (a.dtype == 1)
+    return a.dk == 128 ? launch_dk<__bf16, 128>(a, workspace, stream) : launch_dk<__bf16, 64>(a, workspace, stream);
+  return a.dk == 128 ? launch_dk<float, 128>(a, workspace, stream) : launch_dk<float, 64>(a, workspace, stream);
 }
 
 }  // namespace gdn

@@ -24,6 +24,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 bytes moved as one value (a native vector, so copies stay in registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename E>
 struct Frag;
@@ -100,37 +102,32 @@ __device__ inline void tile_nt2_shared_b(f32x16& acc0, f32x16& acc1, const E* A0
   }
 }
 
-// Two tiles that share the A operand: acc0 += A B0^T, acc1 += A B1^T.
+// Two independent tiles, interleaved: acc0 += A0 B0^T, acc1 += A1 B1^T.
 template <int NK, typename E>
-__device__ inline void tile_nt2_shared_a(f32x16& acc0, f32x16& acc1, const E* A, int lda,
-                                         const E* B0, const E* B1, int ldb, int lane) {
-  const E* pa = A + (lane & 31) * lda + (lane >> 5) * 8;
-  const int rb = (lane & 31) * ldb + (lane >> 5) * 8;
+__device__ inline void tile_nt2_pairs(f32x16& acc0, f32x16& acc1, const E* A0, const E* B0,
+                                      const E* A1, const E* B1, int ld, int lane) {
+  const int ro = (lane & 31) * ld + (lane >> 5) * 8;
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
-    const Frag<E> fa = frag_load(pa + 16 * s);
-    mma16(acc0, fa, frag_load(B0 + rb + 16 * s));
-    mma16(acc1, fa, frag_load(B1 + rb + 16 * s));
+    mma16(acc0, frag_load(A0 + ro + 16 * s), frag_load(B0 + ro + 16 * s));
+    mma16(acc1, frag_load(A1 + ro + 16 * s), frag_load(B1 + ro + 16 * s));
   }
 }
 
-// Both pairs at once (four independent accumulation chains):
-//   x += Ax B^T, o += Ao B^T   (shared B, leading dimensions lda / ldb)
-//   a += Aj C0^T, p += Aj C1^T (shared Aj, all leading dimension lda)
+// Three tiles at once (independent accumulation chains):
+//   x += Ax B^T, o += Ao B^T   (shared B; A leading dimension lda, B ldb)
+//   p += Pa Pb^T               (both leading dimension lda)
 template <int NK, typename E>
-__device__ inline void tile_nt4(f32x16& x, f32x16& o, f32x16& a, f32x16& p, const E* Ax,
-                                const E* Ao, const E* B, const E* Aj, const E* C0, const E* C1,
-                                int lda, int ldb, int lane) {
+__device__ inline void tile_nt3(f32x16& x, f32x16& o, f32x16& p, const E* Ax, const E* Ao,
+                                const E* B, const E* Pa, const E* Pb, int lda, int ldb, int lane) {
   const int ra = (lane & 31) * lda + (lane >> 5) * 8;
   const int rb = (lane & 31) * ldb + (lane >> 5) * 8;
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
     const Frag<E> fb = frag_load(B + rb + 16 * s);
-    const Frag<E> fj = frag_load(Aj + ra + 16 * s);
     mma16(x, frag_load(Ax + ra + 16 * s), fb);
-    mma16(a, fj, frag_load(C0 + ra + 16 * s));
+    mma16(p, frag_load(Pa + ra + 16 * s), frag_load(Pb + ra + 16 * s));
     mma16(o, frag_load(Ao + ra + 16 * s), fb);
-    mma16(p, fj, frag_load(C1 + ra + 16 * s));
   }
 }
 
@@ -147,39 +144,8 @@ __device__ inline f32x4 zero4() {
   return z;
 }
 
-// Store four elements that are already in the element type.
-__device__ inline void store4_raw(__bf16* p, __bf16 a, __bf16 b, __bf16 c, __bf16 d) {
-  bf16x4 t;
-  t[0] = a; t[1] = b; t[2] = c; t[3] = d;
-  *reinterpret_cast<bf16x4*>(p) = t;
-}
-__device__ inline void store4_raw(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-}
-
 // 32-bit word i (compile-time after unrolling) of a 16-byte chunk.
-__device__ inline uint32_t word_of(const uint4& u, int i) {
-  return i == 0 ? u.x : (i == 1 ? u.y : (i == 2 ? u.z : u.w));
-}
-
-// u if keep, else zeros (component-wise, so the chunk stays in registers).
-__device__ inline uint4 keep_or_zero(const uint4& u, bool keep) {
-  return make_uint4(keep ? u.x : 0u, keep ? u.y : 0u, keep ? u.z : 0u, keep ? u.w : 0u);
-}
-
-// Element e of four 16-byte chunks (four consecutive rows of a tile), stored as
-// four consecutive elements: the column-to-row transpose used to build K^T and V^T.
-__device__ inline void store_col4(__bf16* dst, const uint4& r0, const uint4& r1, const uint4& r2,
-                                  const uint4& r3, int e) {
-  const int w = e >> 1, sh = 16 * (e & 1);
-  const uint32_t x0 = (word_of(r0, w) >> sh) & 0xffffu, x1 = (word_of(r1, w) >> sh) & 0xffffu;
-  const uint32_t x2 = (word_of(r2, w) >> sh) & 0xffffu, x3 = (word_of(r3, w) >> sh) & 0xffffu;
-  *reinterpret_cast<uint2*>(dst) = make_uint2(x0 | (x1 << 16), x2 | (x3 << 16));
-}
-__device__ inline void store_col4(float* dst, const uint4& r0, const uint4& r1, const uint4& r2,
-                                  const uint4& r3, int e) {
-  *reinterpret_cast<uint4*>(dst) = make_uint4(word_of(r0, e), word_of(r1, e), word_of(r2, e), word_of(r3, e));
-}
+__device__ inline uint32_t word_of(const u32x4& u, int i) { return u[i]; }
 
 __device__ inline f32x16 zero16() {
   f32x16 z;
@@ -210,9 +176,12 @@ __device__ inline void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
-__device__ inline float load_elem(const float* p) { return *p; }
-__device__ inline float load_elem(const __bf16* p) {
-  return bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(p));
+// Four consecutive elements as fp32 (one 8- or 16-byte LDS read).
+__device__ inline float4 load4_elem(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ inline float4 load4_elem(const __bf16* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
 }
 
 }  // namespace gdn
