@@ -63,8 +63,9 @@ def _bufs(base=1 << 40, span=1 << 36):
     return [base + i * span for i in range(8)]
 
 
-def _fwd(lib, B=2, T=100, H=3, dk=128, dv=128, chunk=64, dtype=1, mode=1, ptrs=None, ws=0,
-         ws_bytes=0):
+def _fwd(lib, B=2, T=100, H=3, dk=128, dv=128, chunk=64, dtype=1, mode=1, ptrs=None,
+         ws=(1 << 40) + 9 * (1 << 36),
+         ws_bytes=1 << 30):
     q, k, v, a, b, s0, o, sf = ptrs if ptrs is not None else _bufs()
     return lib.gdn_chunk_fwd(q, k, v, a, b, s0, o, sf, ws, ws_bytes, B, T, H, dk, dv, chunk,
                              dtype, mode, None)
@@ -102,8 +103,26 @@ def test_chunk_fwd_empty_batch_is_a_no_op(lib):
     assert _fwd(lib, T=0, ptrs=[0, 0, 0, 0, 0, 0, 0, 0]) == OK   # no S_final requested
 
 
+def _ws_bytes(B, T, H, es):
+    chunks = B * H * ((T + 63) // 64)
+    return chunks * (64 * 64 * es + 3 * 64 * 4)     # T per chunk + three fp32 gate rows
+
+
 def test_workspace_query(lib):
-    assert lib.gdn_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 64, 1, 1) == 0
+    assert lib.gdn_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 64, 1, 1) == _ws_bytes(8, 4096, 16, 2)
+    assert lib.gdn_chunk_fwd_workspace_bytes(1, 256, 2, 64, 64, 64, 0, 1) == _ws_bytes(1, 256, 2, 4)
+    assert lib.gdn_chunk_fwd_workspace_bytes(2, 65, 3, 128, 64, 64, 1, 0) == _ws_bytes(2, 65, 3, 2)
+    assert lib.gdn_chunk_fwd_workspace_bytes(2, 0, 3, 128, 64, 64, 1, 1) == 0
+    assert lib.gdn_chunk_fwd_workspace_bytes(2, 10, 3, 96, 64, 64, 1, 1) == 0      # unsupported
+
+
+def test_chunk_fwd_checks_workspace(lib):
+    q, k, v, a, b, s0, o, sf = _bufs()
+    need = _ws_bytes(2, 100, 3, 2)
+    ws = (1 << 40) + 9 * (1 << 36)
+    assert _fwd(lib, ws=ws, ws_bytes=need - 1) == E_WS
+    assert _fwd(lib, ws=0, ws_bytes=need) == E_NULL
+    assert _fwd(lib, ws=q + 128, ws_bytes=need) == E_ALIAS     # workspace over q
 
 
 def test_decode_rejects_bad_arguments(lib):
