@@ -192,7 +192,9 @@ def bench_decode(w: W.Decode, reps: int = 3, rotate: int = 1):
 
 
 def device_copy_gbps(nbytes=1 << 30):
-    """Plain device-to-device copy (read + write) as the achievable-bandwidth reference."""
+    """Plain device-to-device copy of 1 GiB (read + write), five launches: the
+    achievable-bandwidth reference, and the known-size kernel that scales the
+    HBM byte counters (FETCH_SIZE / WRITE_SIZE) of a counter run."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -245,6 +247,62 @@ def cpu_baseline(w: W.Prefill, host, o_gpu, S_gpu, budget_s: float = 12.0):
 
 
 # ------------------------------------------------------------------------------
+# rocprofv3 output -> committed summaries (runs on any host, reads CSV files)
+# ------------------------------------------------------------------------------
+
+def _csv_rows(path):
+    import csv
+    import glob
+    out = []
+    for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            out += list(csv.DictReader(fh))
+    return out
+
+
+def _per_dispatch(rows, counter):
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] == counter:
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def summarize_pmc(fetch_dir, write_dir, out_json):
+    """HBM bytes per prefill launch from a FETCH_SIZE run and a WRITE_SIZE run of
+    this script (KiB per dispatch), each scaled by what the counter reads for the
+    1 GiB device copy that the same run performs."""
+    fetch = _per_dispatch(_csv_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch(_csv_rows(write_dir), "WRITE_SIZE")
+    copy_kib = (1 << 30) / 1024.0
+
+    def copy_scale(per):
+        vals = [v for (d, k), v in per.items() if "copyBuffer" in k and v > 0.25 * copy_kib]
+        return copy_kib / (sum(vals) / len(vals))
+
+    def kernel_kib(per, name):
+        vals = [v for (d, k), v in per.items() if name in k]
+        return sum(vals) / len(vals), len(vals)
+
+    fs, ws = copy_scale(fetch), copy_scale(write)
+    rec = dict(kernel_source_sha256=kernel_source_hash(), fetch_scale=fs, write_scale=ws,
+               note="FETCH_SIZE / WRITE_SIZE KiB per dispatch, scaled so the 1 GiB device "
+                    "copy reads 1 GiB and writes 1 GiB")
+    total = 0.0
+    for name in ("chunk_prep_kernel", "chunk_state_kernel"):
+        fk, nf = kernel_kib(fetch, name)
+        wk, nw = kernel_kib(write, name)
+        rec[name] = dict(fetch_kib=fk, write_kib=wk, dispatches=[nf, nw],
+                         hbm_read_bytes=fk * 1024 * fs, hbm_write_bytes=wk * 1024 * ws)
+        total += fk * 1024 * fs + wk * 1024 * ws
+    rec["hbm_bytes_per_launch"] = total
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+# ------------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -255,7 +313,12 @@ def main():
                     choices=[w.name for w in W.PREFILL_WORKLOADS])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], TRAFFIC_FILE)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs the path on a single MI355X "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -287,7 +350,8 @@ def main():
     roofline = dict(bound="hbm", achieved=nbytes / (kern_mean_ms * 1e-3) / 1e9,
                     peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=nbytes / (kern_mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                    traffic=traffic, kernel="chunk_kernel (fused chunked prefill)",
+                    traffic=traffic,
+                    kernel="gdn_chunk_fwd launch: chunk_prep_kernel + chunk_state_kernel",
                     launch_us=kern_mean_ms * 1e3)
 
     decode = None
@@ -300,7 +364,9 @@ def main():
                                    in_place=lit, rotated_16_states=rot)
             log("decode %s: in place %.2f us/step %.0f GB/s; rotated %.2f us/step %.0f GB/s" % (
                 dw.name, lit["us_per_step"], lit["gbps"], rot["us_per_step"], rot["gbps"]))
-        decode["device_copy_gbps"] = device_copy_gbps()
+
+    copy_gbps = device_copy_gbps()   # also the known-size reference for HBM byte counters
+    log("device copy %.0f GB/s" % copy_gbps)
 
     base, parity = None, None
     if not args.no_cpu_baseline:
@@ -318,7 +384,8 @@ def main():
                            decay={0: "none", 1: "scalar", 2: "channel"}[w.mode],
                            step="chunked prefill + first decode token",
                            state="fp32", parallelism="single GPU"),
-               roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode)
+               roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode,
+               device_copy_gbps=copy_gbps)
     print(json.dumps(out), flush=True)
 
 
