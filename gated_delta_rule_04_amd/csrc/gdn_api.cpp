@@ -76,7 +76,7 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
   if (check_common(B, H, dk, dv, dtype, mode) != GDN_OK || T < 0 || chunk != kChunk) return 0;
   long long n;
   if (!count4(B, T, H, 1, &n)) return 0;
-  return gdn::prefill_workspace_bytes(B, T, H, (int)dtype);
+  return gdn::prefill_workspace_bytes(B, T, H, dk, (int)dtype, (int)mode);
 }
 
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,

@@ -100,102 +100,26 @@ __device__ inline float chunk_log_decay(float alpha, bool ok) {
   return la;
 }
 
-// ---------------------------------------------------------------------------
-// chunk_prep_kernel: T = (I + A)^-1 diag(beta) for one chunk of one head.
-// ---------------------------------------------------------------------------
-// LDS: K rows [64][LDK] (then L^-1 fp32 [64][LDA] in the same bytes), A fp32
-// [64][LDA] (then T [64][LDT]), Mt fp32 [32][LDM], G and beta.
-template <typename E, int DK>
-struct PrepPlan {
-  static constexpr int PAD = 16 / (int)sizeof(E);
-  static constexpr int LDK = DK + PAD;
+// T = (I + A)^-1 diag(beta) for one chunk, in LDS.
+//   Am  A, fp32 [C][LDA]: read below the diagonal; inside the 16x16 diagonal
+//       blocks the entries on and above the diagonal must be zero
+//   Bt  beta [C] (zero for rows past the sequence end)
+//   Li  scratch for L^-1 = (I + A)^-1, fp32 [C][LDA]
+//   Mt  scratch, fp32 [32][LDM]
+//   Tm  T in the operand dtype [C][LDT]; may share Am's bytes
+// All threads of the workgroup take part; it ends with a barrier.
+template <typename E>
+struct SolveLd {
   static constexpr int LDA = C + 4;
-  static constexpr int LDT = C + PAD;
+  static constexpr int LDT = C + 16 / (int)sizeof(E);
   static constexpr int LDM = 32 + 4;
-  static constexpr size_t kr = 0;  // also L^-1
-  static constexpr size_t am = cmax((size_t)C * LDK * sizeof(E), (size_t)C * LDA * 4);
-  static constexpr size_t mt = am + cmax((size_t)C * LDA * 4, (size_t)C * LDT * sizeof(E));
-  static constexpr size_t g = mt + (size_t)32 * LDM * 4;
-  static constexpr size_t total = g + 2 * C * 4;
 };
 
-template <typename E, int DK, int MODE>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* __restrict__ tws,
-                                                              int nchunks) {
-  const size_t nchunks_total = (size_t)a.B * a.H * nchunks;
-  using L = PrepPlan<E, DK>;
-  constexpr int EPC = 16 / (int)sizeof(E);
-  constexpr int CPR = DK / EPC;
-  constexpr int NKB = 16 * CPR;
-  constexpr int LDK = L::LDK, LDA = L::LDA, LDT = L::LDT, LDM = L::LDM;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
-  E* Kr = reinterpret_cast<E*>(smem + L::kr);
-  float* Li = reinterpret_cast<float*>(smem + L::kr);
-  float* Am = reinterpret_cast<float*>(smem + L::am);
-  E* Tm = reinterpret_cast<E*>(smem + L::am);
-  float* Mt = reinterpret_cast<float*>(smem + L::mt);
-  float* G = reinterpret_cast<float*>(smem + L::g);
-  float* Bt = G + C;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
-  const int H = a.H, T = a.T;
-  const int n = blockIdx.x % nchunks;
-  const int bh = blockIdx.x / nchunks;
-  const int h = bh % H, b = bh / H;
-  const int t0 = n * C, cn = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;   // first token of the chunk in [B, T]
-
-  // K rows (rows past the sequence end repeat its last row: beta = 0 there, so
-  // they never reach A or T)
-  {
-    const E* kg = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
-    const size_t ktok = (size_t)H * DK;
-    for (int blk = tid; blk < NKB; blk += kThreads) {
-      const int rg = blk_row(blk, CPR), cc = blk_col(blk, CPR);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = 4 * rg + rr;
-        *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) =
-            *reinterpret_cast<const u32x4*>(kg + (size_t)min(r, cn - 1) * ktok + cc * EPC);
-      }
-    }
-  }
-  if (wave == 0) {
-    const bool ok = lane < cn;
-    const size_t tok = (tok0 + min(lane, cn - 1)) * H + h;
-    const float al = MODE == 1 ? static_cast<const float*>(a.alpha)[tok] : 1.f;
-    const float bt = a.beta[tok];
-    const float g = chunk_log_decay<MODE>(al, ok);
-    const float gC = __shfl(g, C - 1);
-    G[lane] = g;
-    Bt[lane] = ok ? bt : 0.f;
-    float* gw = gate_block(tws, nchunks_total, blockIdx.x);
-    gw[lane] = g;
-    gw[C + lane] = __expf(g);
-    gw[2 * C + lane] = __expf(gC - g);
-  }
-  __syncthreads();
-
-  // A tiles (j block, r block) in {(0,0), (0,1), (1,1)}: rows j, columns r.
-  if (wave < 3) {
-    const int jb = wave == 2 ? 1 : 0, rb = wave == 0 ? 0 : 1;
-    f32x16 acc = zero16();
-    tile_nt_k<DK / 16>(acc, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
-    const int r = rb * 32 + col;
-    const float Gr = G[r], br = Bt[r];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int j0 = jb * 32 + acc_row(g, 0, lane);
-      const float4 gj = *reinterpret_cast<const float4*>(G + j0);
-      const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
-      float x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (j0 + e < r) ? br * __expf(Gr - gjv[e]) * acc[4 * g + e] : 0.f;
-      store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
-    }
-  }
-  __syncthreads();
-
+template <typename E>
+__device__ inline void tri_solve(const float* Am, float* Li, float* Mt, const float* Bt, E* Tm,
+                                 int tid) {
+  constexpr int LDA = SolveLd<E>::LDA, LDT = SolveLd<E>::LDT, LDM = SolveLd<E>::LDM;
+  const int lane = tid & 63, wave = tid >> 6;
   // (a) inverse of each unit-lower 16x16 diagonal block: wave w owns block w;
   // lane 4c + p computes column c, rows 4p .. 4p + 3, summing its part of each
   // row's dot product and finishing it across the quad.
@@ -286,6 +210,105 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     }
   }
   __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// chunk_prep_kernel: T = (I + A)^-1 diag(beta) for one chunk of one head.
+// ---------------------------------------------------------------------------
+// LDS: K rows [64][LDK] (then L^-1 fp32 [64][LDA] in the same bytes), A fp32
+// [64][LDA] (then T [64][LDT]), Mt fp32 [32][LDM], G and beta.
+template <typename E, int DK>
+struct PrepPlan {
+  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDA = SolveLd<E>::LDA;
+  static constexpr int LDT = SolveLd<E>::LDT;
+  static constexpr int LDM = SolveLd<E>::LDM;
+  static constexpr size_t kr = 0;  // also L^-1
+  static constexpr size_t am = cmax((size_t)C * LDK * sizeof(E), (size_t)C * LDA * 4);
+  static constexpr size_t mt = am + cmax((size_t)C * LDA * 4, (size_t)C * LDT * sizeof(E));
+  static constexpr size_t g = mt + (size_t)32 * LDM * 4;
+  static constexpr size_t total = g + 2 * C * 4;
+};
+
+template <typename E, int DK, int MODE>
+__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* __restrict__ tws,
+                                                              int nchunks) {
+  const size_t nchunks_total = (size_t)a.B * a.H * nchunks;
+  using L = PrepPlan<E, DK>;
+  constexpr int EPC = 16 / (int)sizeof(E);
+  constexpr int CPR = DK / EPC;
+  constexpr int NKB = 16 * CPR;
+  constexpr int LDK = L::LDK, LDA = L::LDA, LDT = L::LDT;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
+  E* Kr = reinterpret_cast<E*>(smem + L::kr);
+  float* Li = reinterpret_cast<float*>(smem + L::kr);
+  float* Am = reinterpret_cast<float*>(smem + L::am);
+  E* Tm = reinterpret_cast<E*>(smem + L::am);
+  float* Mt = reinterpret_cast<float*>(smem + L::mt);
+  float* G = reinterpret_cast<float*>(smem + L::g);
+  float* Bt = G + C;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
+  const int H = a.H, T = a.T;
+  const int n = blockIdx.x % nchunks;
+  const int bh = blockIdx.x / nchunks;
+  const int h = bh % H, b = bh / H;
+  const int t0 = n * C, cn = min(C, T - t0);
+  const size_t tok0 = (size_t)b * T + t0;   // first token of the chunk in [B, T]
+
+  // K rows (rows past the sequence end repeat its last row: beta = 0 there, so
+  // they never reach A or T)
+  {
+    const E* kg = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
+    const size_t ktok = (size_t)H * DK;
+    for (int blk = tid; blk < NKB; blk += kThreads) {
+      const int rg = blk_row(blk, CPR), cc = blk_col(blk, CPR);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 4 * rg + rr;
+        *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) =
+            *reinterpret_cast<const u32x4*>(kg + (size_t)min(r, cn - 1) * ktok + cc * EPC);
+      }
+    }
+  }
+  if (wave == 0) {
+    const bool ok = lane < cn;
+    const size_t tok = (tok0 + min(lane, cn - 1)) * H + h;
+    const float al = MODE == 1 ? static_cast<const float*>(a.alpha)[tok] : 1.f;
+    const float bt = a.beta[tok];
+    const float g = chunk_log_decay<MODE>(al, ok);
+    const float gC = __shfl(g, C - 1);
+    G[lane] = g;
+    Bt[lane] = ok ? bt : 0.f;
+    float* gw = gate_block(tws, nchunks_total, blockIdx.x);
+    gw[lane] = g;
+    gw[C + lane] = __expf(g);
+    gw[2 * C + lane] = __expf(gC - g);
+  }
+  __syncthreads();
+
+  // A tiles (j block, r block) in {(0,0), (0,1), (1,1)}: rows j, columns r.
+  if (wave < 3) {
+    const int jb = wave == 2 ? 1 : 0, rb = wave == 0 ? 0 : 1;
+    f32x16 acc = zero16();
+    tile_nt_k<DK / 16>(acc, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
+    const int r = rb * 32 + col;
+    const float Gr = G[r], br = Bt[r];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j0 = jb * 32 + acc_row(g, 0, lane);
+      const float4 gj = *reinterpret_cast<const float4*>(G + j0);
+      const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (j0 + e < r) ? br * __expf(Gr - gjv[e]) * acc[4 * g + e] : 0.f;
+      store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
+    }
+  }
+  __syncthreads();
+
+  tri_solve<E>(Am, Li, Mt, Bt, Tm, tid);
   // T -> workspace, 64 x 64 contiguous, 16-byte stores
   {
     E* dst = tws + (size_t)blockIdx.x * C * C;
@@ -293,6 +316,274 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     for (int q = tid; q < C * CPT; q += kThreads) {
       const int r = q / CPT, cc = q % CPT;
       *reinterpret_cast<u32x4*>(dst + r * C + cc * EPC) = *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk_prep_kda: per-channel decay (Kimi Delta Attention), one chunk of one head.
+// ---------------------------------------------------------------------------
+// With G_r[c] the running sum of log alpha_t[c] inside the chunk,
+//   A[r][j] = beta_r sum_c k_r[c] k_j[c] exp(G_r[c] - G_j[c])      j < r
+//   P[r][j] =        sum_c q_r[c] k_j[c] exp(G_r[c] - G_j[c])      j <= r
+// The weight depends on the channel, so it cannot be applied after the
+// contraction.  It is split at an anchor token m: exp(G_r - G_m) scales the
+// r-side operand and exp(G_m - G_j) the j-side one, and each 32x32 tile is one
+// MFMA product of two scaled operand tiles:
+//   rows 32..63 x columns 0..31   m = 31: both factors are at most 1
+//   diagonal blocks               m = 15 and 47: each factor spans at most 16
+//                                 tokens of decay
+// Masked entries (j > r) of the diagonal blocks may overflow; the epilogues
+// replace them by zero with a select, never with arithmetic.
+// Instead of gates, the state kernel gets decay-scaled operands (the chunk form
+// with Diag(exp(G_r)) in place of gamma_r):
+//   Kg = K . exp(G)          X = V - Kg S^T
+//   Qg = Q . exp(G)          O_inter = Qg S^T
+//   Kc = K . exp(G_C - G)    S_{n+1} = S Diag(gC) + U^T Kc
+//   gC = exp(G_C)
+
+// Per-chunk workspace record of the per-channel path (chunk index = head *
+// N_chunks + n), offsets in elements of the operand dtype:
+//   T [C][C], P [C][C], Kg [C][DK], Qg [C][DK], Kc [C][DK], then gC: DK fp32.
+template <typename E, int DK>
+struct KdaRec {
+  static constexpr size_t t = 0;
+  static constexpr size_t p = (size_t)C * C;
+  static constexpr size_t kg = 2 * (size_t)C * C;
+  static constexpr size_t qg = kg + (size_t)C * DK;
+  static constexpr size_t kc = qg + (size_t)C * DK;
+  static constexpr size_t gc = kc + (size_t)C * DK;
+  static constexpr size_t elems = gc + (size_t)DK * 4 / sizeof(E);
+};
+
+// A 16-byte chunk of the operand dtype as fp32 values, and back (round to
+// nearest even).
+template <typename E>
+__device__ inline void unpack16(const u32x4& u, float* f);
+template <>
+__device__ inline void unpack16<__bf16>(const u32x4& u, float* f) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[2 * w] = __uint_as_float(u[w] << 16);
+    f[2 * w + 1] = __uint_as_float(u[w] & 0xffff0000u);
+  }
+}
+template <>
+__device__ inline void unpack16<float>(const u32x4& u, float* f) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) f[w] = __uint_as_float(u[w]);
+}
+template <typename E>
+__device__ inline u32x4 pack16(const float* f);
+template <>
+__device__ inline u32x4 pack16<__bf16>(const float* f) {
+  bf16x8 t;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = (__bf16)f[i];
+  return __builtin_bit_cast(u32x4, t);
+}
+template <>
+__device__ inline u32x4 pack16<float>(const float* f) {
+  return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+}
+
+// LDS: region 1 holds G (fp32 [C][LDG]) while the operands are built, then A
+// (fp32 [C][LDA], later T) and P [C][LDT]; region 2 holds three 32-row operand
+// tiles, then L^-1 and Mt of the solve; then prefix segment totals and beta.
+template <typename E, int DK>
+struct KdaPrepPlan {
+  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDG = DK + 4;
+  static constexpr int LDA = SolveLd<E>::LDA;
+  static constexpr int LDT = SolveLd<E>::LDT;
+  static constexpr int LDM = SolveLd<E>::LDM;
+  static constexpr int NSEG = kThreads / DK;   // prefix segments per channel
+  static constexpr size_t g = 0;
+  static constexpr size_t am = 0;
+  static constexpr size_t pm = (size_t)C * LDA * 4;
+  static constexpr size_t r1 = cmax((size_t)C * LDG * 4, pm + (size_t)C * LDT * sizeof(E));
+  static constexpr size_t ops = r1;
+  static constexpr size_t li = ops;
+  static constexpr size_t mt = li + (size_t)C * LDA * 4;
+  static constexpr size_t r2 = cmax((size_t)3 * 32 * LDK * sizeof(E), (size_t)C * LDA * 4 + 32 * LDM * 4);
+  static constexpr size_t tot = ops + r2;
+  static constexpr size_t bt = tot + (size_t)NSEG * DK * 4;
+  static constexpr size_t total = bt + C * 4;
+};
+
+template <typename E, int DK>
+__global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __restrict__ tws,
+                                                           int nchunks) {
+  using L = KdaPrepPlan<E, DK>;
+  using R = KdaRec<E, DK>;
+  constexpr int EPC = 16 / (int)sizeof(E);
+  constexpr int CPR = DK / EPC;
+  constexpr int LDK = L::LDK, LDG = L::LDG, LDA = L::LDA, LDT = L::LDT;
+  constexpr int NSEG = L::NSEG, RPS = C / NSEG;   // rows per prefix segment
+  constexpr int IPT = 32 * CPR / kThreads;         // (row, chunk) items per thread per 32 rows
+  static_assert(32 * CPR % kThreads == 0 && kThreads % CPR == 0, "item split");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
+  float* Gl = reinterpret_cast<float*>(smem + L::g);
+  float* Am = reinterpret_cast<float*>(smem + L::am);
+  E* Tm = reinterpret_cast<E*>(smem + L::am);
+  E* Pm = reinterpret_cast<E*>(smem + L::pm);
+  E* Rop = reinterpret_cast<E*>(smem + L::ops);   // r-side K operand
+  E* Qop = Rop + 32 * LDK;                         // r-side Q operand
+  E* Cop = Rop + 64 * LDK;                         // j-side K operand
+  float* Li = reinterpret_cast<float*>(smem + L::li);
+  float* Mt = reinterpret_cast<float*>(smem + L::mt);
+  float* Tot = reinterpret_cast<float*>(smem + L::tot);
+  float* Bt = reinterpret_cast<float*>(smem + L::bt);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
+  const int H = a.H, T = a.T;
+  const int n = blockIdx.x % nchunks;
+  const int bh = blockIdx.x / nchunks;
+  const int h = bh % H, b = bh / H;
+  const int t0 = n * C, cn = min(C, T - t0);
+  const size_t tok0 = (size_t)b * T + t0;
+  const size_t qk_tok = (size_t)H * DK;
+  const E* kgl = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
+  const E* qgl = static_cast<const E*>(a.q) + (tok0 * H + h) * DK;
+  E* rec = tws + (size_t)blockIdx.x * R::elems;
+
+  // G, per channel: thread (segment s, channel c) scans RPS rows, then adds the
+  // totals of the segments before it.  Rows past the sequence end add nothing.
+  {
+    const int c = tid % DK, s = tid / DK;
+    const E* ag = static_cast<const E*>(a.alpha) + (tok0 * H + h) * DK + c;
+    float g[RPS];
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) {
+      const int r = s * RPS + i;
+      const float al = (float)ag[(size_t)min(r, cn - 1) * qk_tok];
+      g[i] = r < cn ? fmaxf(logf(al), kLogFloor) : 0.f;
+    }
+#pragma unroll
+    for (int i = 1; i < RPS; ++i) g[i] += g[i - 1];
+    Tot[s * DK + c] = g[RPS - 1];
+    if (tid < C) Bt[tid] = tid < cn ? a.beta[(tok0 + tid) * H + h] : 0.f;
+    __syncthreads();
+    float off = 0.f;
+    for (int s2 = 0; s2 < s; ++s2) off += Tot[s2 * DK + c];
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) Gl[(s * RPS + i) * LDG + c] = g[i] + off;
+  }
+  __syncthreads();
+  if (tid < DK) reinterpret_cast<float*>(rec + R::gc)[tid] = __expf(Gl[(C - 1) * LDG + tid]);
+
+  // Three passes build operand tiles; after each, two waves take MFMA tiles:
+  //   pass 0  rows 0..31, anchor 15    wave 0: A(0,0)   wave 1: P(0,0)
+  //   pass 1  rows 32..63, anchor 47   wave 2: A(1,1)   wave 3: P(1,1)
+  //   pass 2  anchor 31: j side rows 0..31, r side rows 32..63
+  //                                    wave 0: A(1,0)   wave 1: P(1,0)
+  // (tile (R, J): rows r of block R, columns j of block J).  Passes 0 and 1 also
+  // write Kg, Qg and Kc.  Accumulators stay in registers until G is dead.
+  f32x16 acc0 = zero16(), acc1 = zero16();
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    if (pass > 0) __syncthreads();   // the previous pass's tiles are consumed
+#pragma unroll
+    for (int m = 0; m < (pass < 2 ? IPT : 2 * IPT); ++m) {
+      const int it = tid + kThreads * m, rl = it / CPR, c0 = (it % CPR) * EPC;
+      const int r = pass == 1 ? 32 + rl : rl;
+      const uint32_t off = (uint32_t)min(r, cn - 1) * (uint32_t)qk_tok + c0;
+      float kf[EPC], qf[EPC], gr[EPC], ga[EPC], x[EPC], y[EPC], z[EPC];
+      unpack16<E>(*reinterpret_cast<const u32x4*>(kgl + off), kf);
+      unpack16<E>(*reinterpret_cast<const u32x4*>(qgl + off), qf);
+      const int anchor = pass == 2 ? 31 : (pass == 0 ? 15 : 47);
+#pragma unroll
+      for (int e = 0; e < EPC; e += 4) {
+        const float4 g4 = *reinterpret_cast<const float4*>(Gl + r * LDG + c0 + e);
+        const float4 a4 = *reinterpret_cast<const float4*>(Gl + anchor * LDG + c0 + e);
+        gr[e] = g4.x; gr[e + 1] = g4.y; gr[e + 2] = g4.z; gr[e + 3] = g4.w;
+        ga[e] = a4.x; ga[e + 1] = a4.y; ga[e + 2] = a4.z; ga[e + 3] = a4.w;
+      }
+      if (pass < 2) {
+        float gl[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(Gl + (C - 1) * LDG + c0 + e);
+          gl[e] = l4.x; gl[e + 1] = l4.y; gl[e + 2] = l4.z; gl[e + 3] = l4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const float w = __expf(gr[e]);
+          x[e] = kf[e] * w;
+          y[e] = qf[e] * w;
+          z[e] = kf[e] * __expf(gl[e] - gr[e]);
+        }
+        const size_t ro = (size_t)r * DK + c0;
+        *reinterpret_cast<u32x4*>(rec + R::kg + ro) = pack16<E>(x);
+        *reinterpret_cast<u32x4*>(rec + R::qg + ro) = pack16<E>(y);
+        *reinterpret_cast<u32x4*>(rec + R::kc + ro) = pack16<E>(z);
+      }
+      const int lr = r & 31;
+      if (pass < 2 || r >= 32) {   // r side: exp(G_r - G_m)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const float w = __expf(gr[e] - ga[e]);
+          x[e] = kf[e] * w;
+          y[e] = qf[e] * w;
+        }
+        *reinterpret_cast<u32x4*>(Rop + lr * LDK + c0) = pack16<E>(x);
+        *reinterpret_cast<u32x4*>(Qop + lr * LDK + c0) = pack16<E>(y);
+      }
+      if (pass < 2 || r < 32) {    // j side: exp(G_m - G_j)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) z[e] = kf[e] * __expf(ga[e] - gr[e]);
+        *reinterpret_cast<u32x4*>(Cop + lr * LDK + c0) = pack16<E>(z);
+      }
+    }
+    __syncthreads();
+    // tile (R, J) accumulates rows j (Cop) x columns r (Rop or Qop)
+    const bool mine = pass == 2 ? wave < 2 : (wave >> 1) == pass;
+    if (mine) tile_nt_k<DK / 16>(pass == 2 ? acc1 : acc0, Cop, LDK, (wave & 1) ? Qop : Rop, LDK, lane);
+  }
+  __syncthreads();   // G is dead: A and P take region 1
+
+  // Epilogues.  A[r][j] = beta_r acc for j < r; P[r][j] = acc for j <= r.
+  {
+    const bool isP = wave & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t == 1 && wave >= 2) break;
+      const int Rb = t == 1 ? 1 : (wave >> 1), Jb = t == 1 ? 0 : (wave >> 1);
+      const f32x16& acc = t == 1 ? acc1 : acc0;
+      const int r = Rb * 32 + col;
+      const float br = Bt[r];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = Jb * 32 + acc_row(g, 0, lane);
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[4 * g + e];
+          x[e] = isP ? (j0 + e <= r ? v : 0.f) : (j0 + e < r ? br * v : 0.f);
+        }
+        if (isP) store4(Pm + r * LDT + j0, x[0], x[1], x[2], x[3]);
+        else store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
+      }
+    }
+    if (wave >= 2) {   // P rows 0..31, columns 32..63 are zero
+      const int q = tid - 128, r = q >> 2, j0 = 32 + 8 * (q & 3);
+      store4(Pm + r * LDT + j0, 0.f, 0.f, 0.f, 0.f);
+      store4(Pm + r * LDT + j0 + 4, 0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __syncthreads();
+
+  tri_solve<E>(Am, Li, Mt, Bt, Tm, tid);
+  // T and P -> the record, 64 x 64 contiguous each, 16-byte stores
+  {
+    constexpr int CPT = C / EPC;
+    for (int q = tid; q < C * CPT; q += kThreads) {
+      const int r = q / CPT, cc = q % CPT;
+      *reinterpret_cast<u32x4*>(rec + R::t + r * C + cc * EPC) =
+          *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC);
+      *reinterpret_cast<u32x4*>(rec + R::p + r * C + cc * EPC) =
+          *reinterpret_cast<const u32x4*>(Pm + r * LDT + cc * EPC);
     }
   }
 }
@@ -357,7 +648,9 @@ __device__ inline void store_col4(float* dst, const u32x4& r0, const u32x4& r1, 
 template <typename E, int DK, int DVS, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, const E* __restrict__ tws) {
   constexpr bool SEPKT = sep_kt_fits<E, DK, DVS>();
+  constexpr bool KDA = MODE == 2;   // per-channel decay: operands come pre-scaled
   using L = StatePlan<E, DK, DVS, SEPKT>;
+  using R = KdaRec<E, DK>;
   static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
   constexpr int NI = DVS / 32;       // 32-wide value blocks in the slice
   constexpr int NC = DK / 32;        // 32-wide key blocks
@@ -389,6 +682,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   float* G = reinterpret_cast<float*>(smem + L::g);   // gate block, as in the workspace
   float* Eg = G + C;       // exp(G_r)
   float* Ec = G + 2 * C;   // exp(G_C - G_r)
+  float* Gc = G;           // per-channel decay: exp(G_C[c]), DK values
   // O staging (rows r, OST elements apart) reuses X^T's region, free after phase 4
   constexpr int OST = (sizeof(E) == 2 && DVS == 64) ? 72 : DVS;
   static_assert(C * OST <= DVS * LDT, "O staging does not fit in the X^T region");
@@ -419,7 +713,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   const E* qg = static_cast<const E*>(a.q) + ((size_t)b * T * H + h) * DK;
   const E* kg = static_cast<const E*>(a.k) + ((size_t)b * T * H + h) * DK;
   const E* vg = static_cast<const E*>(a.v) + ((size_t)b * T * H + h) * dv + i0;
-  const E* tg = tws + (size_t)head * nchunks * C * C;
+  const E* tg = tws + (size_t)head * nchunks * C * C;      // T blocks (scalar gates)
+  const E* recs = tws + (size_t)head * nchunks * R::elems;   // records (per-channel decay)
   E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
   const size_t sbase = ((size_t)b * H + h) * dv + i0;  // first state row of the slice
 
@@ -437,6 +732,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     if (wave == 2) { pt0 = 0; pt1 = 2; }
     if (wave == 3) pt0 = 1;
   }
+  if (KDA) pt0 = pt1 = -1;   // P arrives with the chunk
 
   // Initial state: S0 or zeros, into registers and the operand copy.
   f32x16 Sacc[NST];
@@ -466,25 +762,44 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   // columns of those tokens are zero (their beta is zero), so they never reach
   // U, O or S, and their O rows are not written.
   u32x4 pk[KBT][4], pq[KBT][4], pv[VBT][4], pt[TBT];
-  u32x4 pg = u32x4{0u, 0u, 0u, 0u};   // gate block: 48 chunks, threads 0..47
+  u32x4 pg = u32x4{0u, 0u, 0u, 0u};   // gate block: 48 chunks, threads 0..47 (gC: DK / 4)
+  u32x4 pkc[KDA && SEPKT ? KBT : 1][4], pp[KDA ? TBT : 1];   // Kc rows and P
   const size_t nchunks_total = (size_t)a.B * H * nchunks;
 
   auto prefetch = [&](int n) __attribute__((always_inline)) {
     const int t0 = n * C;
     const int rmax = min(C, T - t0) - 1;
-    const E* kq = kg + (size_t)t0 * qk_tok;
-    const E* qq = qg + (size_t)t0 * qk_tok;
     const E* vq = vg + (size_t)t0 * v_tok;
+    if constexpr (KDA) {
+      // every row of a record is written (rows past the end are finite copies)
+      const E* rq = recs + (size_t)n * R::elems;
 #pragma unroll
-    for (int m = 0; m < KBT; ++m) {
-      const int blk = tid + kThreads * m;
-      const int bq = blk < NKB ? blk : 0;
-      const int rg = blk_row(bq, CPR), cc = blk_col(bq, CPR);
+      for (int m = 0; m < KBT; ++m) {
+        const int blk = tid + kThreads * m;
+        const int bq = blk < NKB ? blk : 0;
+        const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const uint32_t off = (uint32_t)min(4 * rg + rr, rmax) * (uint32_t)qk_tok + cc * EPC;
-        pk[m][rr] = *reinterpret_cast<const u32x4*>(kq + off);
-        pq[m][rr] = *reinterpret_cast<const u32x4*>(qq + off);
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t off = (uint32_t)(4 * rb4 + rr) * DK + cc * EPC;
+          pk[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::kg + off);
+          pq[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::qg + off);
+          if constexpr (SEPKT) pkc[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::kc + off);
+        }
+      }
+    } else {
+      const E* kq = kg + (size_t)t0 * qk_tok;
+      const E* qq = qg + (size_t)t0 * qk_tok;
+#pragma unroll
+      for (int m = 0; m < KBT; ++m) {
+        const int blk = tid + kThreads * m;
+        const int bq = blk < NKB ? blk : 0;
+        const int rg = blk_row(bq, CPR), cc = blk_col(bq, CPR);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t off = (uint32_t)min(4 * rg + rr, rmax) * (uint32_t)qk_tok + cc * EPC;
+          pk[m][rr] = *reinterpret_cast<const u32x4*>(kq + off);
+          pq[m][rr] = *reinterpret_cast<const u32x4*>(qq + off);
+        }
       }
     }
 #pragma unroll
@@ -498,11 +813,22 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
         pv[m][rr] = *reinterpret_cast<const u32x4*>(vq + off);
       }
     }
-    const E* tq = tg + (size_t)n * C * C;
+    if constexpr (KDA) {
+      const E* rq = recs + (size_t)n * R::elems;
 #pragma unroll
-    for (int m = 0; m < TBT; ++m) pt[m] = *reinterpret_cast<const u32x4*>(tq + (tid + kThreads * m) * EPC);
-    const float* gq = gate_block(tws, nchunks_total, (size_t)head * nchunks + n);
-    pg = *reinterpret_cast<const u32x4*>(gq + 4 * min(tid, (int)kGateFloats / 4 - 1));
+      for (int m = 0; m < TBT; ++m) {
+        pt[m] = *reinterpret_cast<const u32x4*>(rq + R::t + (tid + kThreads * m) * EPC);
+        pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (tid + kThreads * m) * EPC);
+      }
+      pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::gc) +
+                                           4 * min(tid, DK / 4 - 1));
+    } else {
+      const E* tq = tg + (size_t)n * C * C;
+#pragma unroll
+      for (int m = 0; m < TBT; ++m) pt[m] = *reinterpret_cast<const u32x4*>(tq + (tid + kThreads * m) * EPC);
+      const float* gq = gate_block(tws, nchunks_total, (size_t)head * nchunks + n);
+      pg = *reinterpret_cast<const u32x4*>(gq + 4 * min(tid, (int)kGateFloats / 4 - 1));
+    }
   };
 
   auto commit = [&]() __attribute__((always_inline)) {
@@ -516,10 +842,11 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
           *reinterpret_cast<u32x4*>(Kr + (4 * rg + rr) * LDK + cc * EPC) = pk[m][rr];
           *reinterpret_cast<u32x4*>(Qr + (4 * rg + rr) * LDK + cc * EPC) = pq[m][rr];
         }
-        if (SEPKT) {
+        if constexpr (SEPKT) {
+          const auto& src = KDA ? pkc[m] : pk[m];
 #pragma unroll
           for (int e = 0; e < EPC; ++e)
-            store_col4(Kt + (cc * EPC + e) * LDT + 4 * rg, pk[m][0], pk[m][1], pk[m][2], pk[m][3], e);
+            store_col4(Kt + (cc * EPC + e) * LDT + 4 * rg, src[0], src[1], src[2], src[3], e);
         }
       }
     }
@@ -537,8 +864,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     for (int m = 0; m < TBT; ++m) {
       const int q = tid + kThreads * m, r = q / CPT, cc = q % CPT;
       *reinterpret_cast<u32x4*>(Tm + r * LDT + cc * EPC) = pt[m];
+      if constexpr (KDA) *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
     }
-    if (tid < (int)kGateFloats / 4) *reinterpret_cast<u32x4*>(G + 4 * tid) = pg;
+    if (tid < (KDA ? DK / 4 : (int)kGateFloats / 4)) *reinterpret_cast<u32x4*>(G + 4 * tid) = pg;
   };
 
   // Staged O rows of a chunk -> HBM, 16-byte stores along each row.
@@ -612,7 +940,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = own_rb * 32 + acc_row(g, 0, lane);
-        const float4 eg = *reinterpret_cast<const float4*>(Eg + r0);
+        const float4 eg = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
         const float4 v4 = load4_elem(Vt + i * LDT + r0);
         store4(Xt + i * LDT + r0, v4.x - eg.x * xacc[4 * g + 0], v4.y - eg.y * xacc[4 * g + 1],
                v4.z - eg.z * xacc[4 * g + 2], v4.w - eg.w * xacc[4 * g + 3]);
@@ -626,15 +954,17 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 
     // ---- K^T for phase 6 when it shares Q's region (fp32, d_k = 128) ----
     if (!SEPKT) {
+      const E* kcq = recs + (size_t)n * R::elems + R::kc;   // per-channel decay: Kc rows
       for (int blk = tid; blk < NKB; blk += kThreads) {
-        const int rg = blk_row(blk, CPR), cc = blk_col(blk, CPR);
+        const int rg4 = blk_row(blk, CPR), cc = blk_col(blk, CPR);
         u32x4 v[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          v[rr] = *reinterpret_cast<const u32x4*>(Kr + (4 * rg + rr) * LDK + cc * EPC);
+          v[rr] = KDA ? *reinterpret_cast<const u32x4*>(kcq + (4 * rg4 + rr) * DK + cc * EPC)
+                      : *reinterpret_cast<const u32x4*>(Kr + (4 * rg4 + rr) * LDK + cc * EPC);
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
-          store_col4(Kt + (cc * EPC + e) * LDT + 4 * rg, v[0], v[1], v[2], v[3], e);
+          store_col4(Kt + (cc * EPC + e) * LDT + 4 * rg4, v[0], v[1], v[2], v[3], e);
       }
     }
 
@@ -647,10 +977,12 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = own_rb * 32 + acc_row(g, 0, lane);
-        const float4 ec = *reinterpret_cast<const float4*>(Ec + r0);
         store4(Ut + i * LDT + r0, uacc[4 * g], uacc[4 * g + 1], uacc[4 * g + 2], uacc[4 * g + 3]);
-        store4(Uw + i * LDT + r0, uacc[4 * g] * ec.x, uacc[4 * g + 1] * ec.y,
-               uacc[4 * g + 2] * ec.z, uacc[4 * g + 3] * ec.w);
+        if constexpr (!KDA) {
+          const float4 ec = *reinterpret_cast<const float4*>(Ec + r0);
+          store4(Uw + i * LDT + r0, uacc[4 * g] * ec.x, uacc[4 * g + 1] * ec.y,
+                 uacc[4 * g + 2] * ec.z, uacc[4 * g + 3] * ec.w);
+        }
       }
     }
     __syncthreads();
@@ -668,23 +1000,42 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     }
 
     // ---- phase 6: S^T <- gamma_C S^T + K^T Uw  (fp32 accumulators), refresh Sb ----
+    // (per-channel decay: S^T <- Diag(gC) S^T + Kc^T U)
     {
-      const float gC = Eg[C - 1];
+      if constexpr (KDA) {
 #pragma unroll
-      for (int st = 0; st < NST; ++st)
+        for (int st = 0; st < NST; ++st) {
+          const int cb = (wave + 4 * st) / NI;
+          if (cb < NC) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
+            for (int g = 0; g < 4; ++g) {
+              const float4 d = *reinterpret_cast<const float4*>(Gc + cb * 32 + acc_row(g, 0, lane));
+              Sacc[st][4 * g + 0] *= d.x;
+              Sacc[st][4 * g + 1] *= d.y;
+              Sacc[st][4 * g + 2] *= d.z;
+              Sacc[st][4 * g + 3] *= d.w;
+            }
+          }
+        }
+      } else {
+        const float gC = Eg[C - 1];
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
+      }
+      const E* Ub = KDA ? Ut : Uw;
       if (NST == 2 && wave + 4 < NT) {
         // tiles wave and wave + 4 share the value block: one Uw fragment, two MFMAs
         tile_nt2_shared_b<C / 16>(Sacc[0], Sacc[NST - 1], Kt + (wave / NI) * 32 * LDT,
                                   Kt + ((wave + 4) / NI) * 32 * LDT, LDT,
-                                  Uw + (wave % NI) * 32 * LDT, LDT, lane);
+                                  Ub + (wave % NI) * 32 * LDT, LDT, lane);
       } else {
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
           const int t = wave + 4 * st;
           if (t < NT)
-            tile_nt_k<C / 16>(Sacc[st], Kt + (t / NI) * 32 * LDT, LDT, Uw + (t % NI) * 32 * LDT,
+            tile_nt_k<C / 16>(Sacc[st], Kt + (t / NI) * 32 * LDT, LDT, Ub + (t % NI) * 32 * LDT,
                               LDT, lane);
         }
       }
@@ -731,8 +1082,10 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
   dim3 grid((unsigned)((size_t)a.B * a.H * (a.dv / DVS))), block(kThreads);
   if (a.mode == 0)
     hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 0>), grid, block, 0, stream, a, tws);
-  else
+  else if (a.mode == 1)
     hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 1>), grid, block, 0, stream, a, tws);
+  else
+    hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 2>), grid, block, 0, stream, a, tws);
   return hipGetLastError();
 }
 
@@ -747,8 +1100,10 @@ hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) 
     dim3 grid((unsigned)((size_t)a.B * a.H * nchunks)), block(kThreads);
     if (a.mode == 0)
       hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 0>), grid, block, 0, stream, a, tws, nchunks);
-    else
+    else if (a.mode == 1)
       hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 1>), grid, block, 0, stream, a, tws, nchunks);
+    else
+      hipLaunchKernelGGL((chunk_prep_kda<E, DK>), grid, block, 0, stream, a, tws, nchunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -763,13 +1118,14 @@ hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) 
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int B, int T, int H, int dtype) {
+size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dtype, int mode) {
   const size_t chunks = (size_t)B * H * (((size_t)T + C - 1) / C);
-  return chunks * (C * C * (dtype == 1 ? 2 : 4) + kGateFloats * 4);
+  const size_t es = dtype == 1 ? 2 : 4;
+  if (mode == 2) return chunks * ((2 * (size_t)C * C + 3 * (size_t)C * dk) * es + 4 * (size_t)dk);
+  return chunks * (C * C * es + kGateFloats * 4);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream) {
-  if (a.mode == 2) return hipErrorNotSupported;
   if (a.dtype == 1)
     return a.dk == 128 ? launch_dk<__bf16, 128>(a, workspace, stream) : launch_dk<__bf16, 64>(a, workspace, stream);
   return a.dk == 128 ? launch_dk<float, 128>(a, workspace, stream) : launch_dk<float, 64>(a, workspace, stream);

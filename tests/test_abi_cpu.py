@@ -103,8 +103,10 @@ def test_chunk_fwd_empty_batch_is_a_no_op(lib):
     assert _fwd(lib, T=0, ptrs=[0, 0, 0, 0, 0, 0, 0, 0]) == OK   # no S_final requested
 
 
-def _ws_bytes(B, T, H, es):
+def _ws_bytes(B, T, H, es, dk=128, mode=1):
     chunks = B * H * ((T + 63) // 64)
+    if mode == 2:   # T, P, three scaled copies of K / Q, per-channel decay
+        return chunks * ((2 * 64 * 64 + 3 * 64 * dk) * es + 4 * dk)
     return chunks * (64 * 64 * es + 3 * 64 * 4)     # T per chunk + three fp32 gate rows
 
 
@@ -112,6 +114,8 @@ def test_workspace_query(lib):
     assert lib.gdn_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 64, 1, 1) == _ws_bytes(8, 4096, 16, 2)
     assert lib.gdn_chunk_fwd_workspace_bytes(1, 256, 2, 64, 64, 64, 0, 1) == _ws_bytes(1, 256, 2, 4)
     assert lib.gdn_chunk_fwd_workspace_bytes(2, 65, 3, 128, 64, 64, 1, 0) == _ws_bytes(2, 65, 3, 2)
+    assert lib.gdn_chunk_fwd_workspace_bytes(4, 8192, 16, 128, 128, 64, 1, 2) == _ws_bytes(4, 8192, 16, 2, 128, 2)
+    assert lib.gdn_chunk_fwd_workspace_bytes(1, 100, 2, 64, 128, 64, 0, 2) == _ws_bytes(1, 100, 2, 4, 64, 2)
     assert lib.gdn_chunk_fwd_workspace_bytes(2, 0, 3, 128, 64, 64, 1, 1) == 0
     assert lib.gdn_chunk_fwd_workspace_bytes(2, 10, 3, 96, 64, 64, 1, 1) == 0      # unsupported
 
@@ -123,6 +127,8 @@ def test_chunk_fwd_checks_workspace(lib):
     assert _fwd(lib, ws=ws, ws_bytes=need - 1) == E_WS
     assert _fwd(lib, ws=0, ws_bytes=need) == E_NULL
     assert _fwd(lib, ws=q + 128, ws_bytes=need) == E_ALIAS     # workspace over q
+    need2 = _ws_bytes(2, 100, 3, 2, 128, 2)
+    assert _fwd(lib, mode=2, ws=ws, ws_bytes=need2 - 1) == E_WS
 
 
 def test_decode_rejects_bad_arguments(lib):

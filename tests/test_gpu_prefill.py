@@ -1,4 +1,5 @@
-"""Chunked prefill on the GPU against the fp64 oracle (DeltaNet and Gated DeltaNet)."""
+"""Chunked prefill on the GPU against the fp64 oracle (DeltaNet, Gated DeltaNet and
+per-channel decay)."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ from gdn_testlib import TOL, check_prefill, gpu_prefill, oracle_prefill, rel_o, 
 
 pytestmark = pytest.mark.gpu
 
-GATE_OF_MODE = {0: "none", 1: "exp01"}
+GATE_OF_MODE = {0: "none", 1: "exp01", 2: "kda_clamped"}
 
 
 def _small(T, dk, dv, dtype, mode, s0, B=1, H=2, seed=5):
@@ -17,7 +18,7 @@ def _small(T, dk, dv, dtype, mode, s0, B=1, H=2, seed=5):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 200])
 def test_prefill_small(gpu, dtype, mode, dk, dv, T):
@@ -27,10 +28,55 @@ def test_prefill_small(gpu, dtype, mode, dk, dv, T):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("dk", [64, 128])
-def test_prefill_wide_slices(gpu, dtype, dk):
+@pytest.mark.parametrize("mode", [1, 2])
+def test_prefill_wide_slices(gpu, dtype, dk, mode):
     """Enough heads for 64-row value slices per workgroup."""
-    w = _small(130, dk, 64, dtype, 1, s0=True, B=4, H=64, seed=9)
-    check_prefill(gpu, W.make_prefill(w), 1, dtype)
+    w = _small(130, dk, 64, dtype, mode, s0=True, B=4, H=64, seed=9)
+    check_prefill(gpu, W.make_prefill(w), mode, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("gate", ["exp01_channel", "kda_literal"])
+@pytest.mark.parametrize("dk,T", [(64, 200), (128, 130), (128, 256)])
+def test_prefill_channel_gates(gpu, dtype, gate, dk, T):
+    """Per-channel decay with mild gates and with the strong literal gate (typical
+    alpha about 0.05: decay ratios span many orders of magnitude inside a chunk)."""
+    w = W.Prefill("kda", 2, 3, T, dk, 128, dtype, gate, 0.1, seed=T + dk + 7)
+    check_prefill(gpu, W.make_prefill(w), 2, dtype)
+
+
+def test_prefill_channel_decay_equal_channels_is_scalar_decay(gpu):
+    """A per-channel gate equal across channels is the scalar gate: the GPU's
+    per-channel path against the oracle run in scalar mode."""
+    w = _small(200, 128, 128, torch.float32, 2, s0=True, B=2, H=3, seed=31)
+    inp = W.make_prefill(w)
+    a1 = inp["alpha"][..., 0].contiguous()
+    inp["alpha"] = a1[..., None].expand_as(inp["alpha"]).contiguous()
+    o, S = gpu_prefill(gpu, inp, 2)
+    ro, rS = oracle_prefill(dict(inp, alpha=a1), 1)
+    assert rel_o(o, ro) <= 1e-4 and rel_S(S, rS) <= 1e-4
+
+
+def test_prefill_channel_gates_at_boundary_values(gpu):
+    """Per-channel alpha in {0.25, 1} mixed across channels and tokens, then alpha = 1."""
+    w = _small(150, 128, 128, torch.float32, 2, s0=True, B=1, H=2, seed=32)
+    inp = W.make_prefill(w)
+    g = torch.Generator().manual_seed(33)
+    inp["alpha"] = torch.where(torch.rand(inp["alpha"].shape, generator=g) < 0.7, 1.0, 0.25)
+    check_prefill(gpu, inp, 2, torch.float32)
+    inp["alpha"] = torch.ones_like(inp["alpha"])
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    _, S = gpu_prefill(gpu, inp, 2)
+    assert rel_S(S, inp["S0"].numpy()) <= 1e-6
+
+
+def test_prefill_kda_workload_sampled(gpu):
+    """B=4, H=16, T=8192, d=128, bf16, per-channel decay: all heads on the GPU,
+    four checked."""
+    w = W.KDA_BF16_PREFILL
+    heads = [(0, 0), (1, 9), (2, 4), (3, 15)]
+    eo, eS = check_prefill(gpu, W.make_prefill(w), w.mode, w.dtype, heads=heads)
+    print("kda bf16 b4 h16 t8192: rel err o %.2e, S %.2e" % (eo, eS))
 
 
 def test_prefill_gdn_fp32_workload(gpu):
@@ -100,9 +146,10 @@ def test_prefill_in_place_state_and_no_final(gpu):
     assert torch.equal(S1, S_io) and torch.equal(o1, o2) and torch.equal(o1, o3)
 
 
-def test_prefill_split_equals_whole(gpu):
+@pytest.mark.parametrize("mode", [1, 2])
+def test_prefill_split_equals_whole(gpu, mode):
     """prefill(T1) then prefill(T2, S0 = S_final) against the oracle over T1 + T2."""
-    w = _small(257, 128, 128, torch.bfloat16, 1, s0=True, B=1, H=4)
+    w = _small(257, 128, 128, torch.bfloat16, mode, s0=True, B=1, H=4)
     inp = W.make_prefill(w)
     dev = to_dev(inp)
     t1 = 100
@@ -114,7 +161,7 @@ def test_prefill_split_equals_whole(gpu):
                            part(dev["v"], slice(t1, None)), part(dev["alpha"], slice(t1, None)),
                            part(dev["beta"], slice(t1, None)), Sa)
     torch.cuda.synchronize()
-    ro, rS = oracle_prefill(inp, 1)
+    ro, rS = oracle_prefill(inp, mode)
     o = torch.cat([oa, ob], 1).float().cpu().numpy()
     assert rel_o(o, ro) <= 2e-2 and rel_S(Sb.cpu().numpy(), rS) <= 2e-2
 
@@ -129,11 +176,12 @@ def test_prefill_is_deterministic(gpu):
         assert torch.equal(o, runs[0][0]) and torch.equal(S, runs[0][1])
 
 
-def test_prefill_matches_decode_steps(gpu):
+@pytest.mark.parametrize("mode", [1, 2])
+def test_prefill_matches_decode_steps(gpu, mode):
     """T decode steps and one prefill over the same T tokens agree."""
-    w = _small(70, 64, 128, torch.float32, 1, s0=True, B=2, H=3)
+    w = _small(70, 64, 128, torch.float32, mode, s0=True, B=2, H=3)
     inp = W.make_prefill(w)
-    o_p, S_p = gpu_prefill(gpu, inp, 1)
+    o_p, S_p = gpu_prefill(gpu, inp, mode)
     dev = to_dev(inp)
     S = dev["S0"].clone()
     outs = []
