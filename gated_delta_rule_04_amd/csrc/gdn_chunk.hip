@@ -333,6 +333,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
 //   rows 32..63 x columns 0..31   m = 31: both factors are at most 1
 //   diagonal blocks               m = 15 and 47: each factor spans at most 16
 //                                 tokens of decay
+// In a diagonal block, a channel whose decay on either side of the anchor
+// exceeds exp(kSplitLimit) could overflow or underflow its factors; it is left
+// out of the MFMA (zero operands) and its exact contribution, with the weight
+// exp(G_r - G_j) <= 1 taken directly, is added by the wave that owns the tile.
 // Masked entries (j > r) of the diagonal blocks may overflow; the epilogues
 // replace them by zero with a select, never with arithmetic.
 // Instead of gates, the state kernel gets decay-scaled operands (the chunk form
@@ -387,9 +391,13 @@ __device__ inline u32x4 pack16<float>(const float* f) {
   return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
 }
 
+constexpr float kSplitLimit = 64.f;
+
 // LDS: region 1 holds G (fp32 [C][LDG]) while the operands are built, then A
 // (fp32 [C][LDA], later T) and P [C][LDT]; region 2 holds three 32-row operand
-// tiles, then L^-1 and Mt of the solve; then prefix segment totals and beta.
+// tiles, then L^-1 and Mt of the solve; then the unscaled K and Q rows of the
+// current diagonal block, prefix segment totals, beta and the bit masks of
+// the channels left out of each diagonal block's MFMA.
 template <typename E, int DK>
 struct KdaPrepPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
@@ -407,9 +415,11 @@ struct KdaPrepPlan {
   static constexpr size_t li = ops;
   static constexpr size_t mt = li + (size_t)C * LDA * 4;
   static constexpr size_t r2 = cmax((size_t)3 * 32 * LDK * sizeof(E), (size_t)C * LDA * 4 + 32 * LDM * 4);
-  static constexpr size_t tot = ops + r2;
+  static constexpr size_t raw = ops + r2;
+  static constexpr size_t tot = raw + (size_t)2 * 32 * LDK * sizeof(E);
   static constexpr size_t bt = tot + (size_t)NSEG * DK * 4;
-  static constexpr size_t total = bt + C * 4;
+  static constexpr size_t msk = bt + C * 4;
+  static constexpr size_t total = msk + (size_t)2 * (DK / 32) * 4;
 };
 
 template <typename E, int DK>
@@ -433,8 +443,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   E* Cop = Rop + 64 * LDK;                         // j-side K operand
   float* Li = reinterpret_cast<float*>(smem + L::li);
   float* Mt = reinterpret_cast<float*>(smem + L::mt);
+  E* Kraw = reinterpret_cast<E*>(smem + L::raw);   // unscaled rows of the current block
+  E* Qraw = Kraw + 32 * LDK;
   float* Tot = reinterpret_cast<float*>(smem + L::tot);
   float* Bt = reinterpret_cast<float*>(smem + L::bt);
+  uint32_t* Msk = reinterpret_cast<uint32_t*>(smem + L::msk);   // [2][DK / 32]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
   const int H = a.H, T = a.T;
@@ -448,17 +461,32 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   const E* qgl = static_cast<const E*>(a.q) + (tok0 * H + h) * DK;
   E* rec = tws + (size_t)blockIdx.x * R::elems;
 
+  // This thread's (row, 16-byte chunk) items of K and Q, loaded once for all
+  // passes: item m is row (tid + kThreads m) / CPR (rows 0..31 for m < IPT,
+  // 32..63 above), channels c0 = ((tid + kThreads m) % CPR) EPC.  Rows past the
+  // sequence end repeat its last row.
+  u32x4 kreg[2 * IPT], qreg[2 * IPT];
   // G, per channel: thread (segment s, channel c) scans RPS rows, then adds the
   // totals of the segments before it.  Rows past the sequence end add nothing.
   {
     const int c = tid % DK, s = tid / DK;
     const E* ag = static_cast<const E*>(a.alpha) + (tok0 * H + h) * DK + c;
+    // all loads first and unconditional (a load under the row test would be
+    // waited for one at a time), then log and select
     float g[RPS];
 #pragma unroll
+    for (int i = 0; i < RPS; ++i) g[i] = (float)ag[(size_t)min(s * RPS + i, cn - 1) * qk_tok];
+#pragma unroll
+    for (int m = 0; m < 2 * IPT; ++m) {
+      const int it = tid + kThreads * m;
+      const uint32_t off = (uint32_t)min(it / CPR, cn - 1) * (uint32_t)qk_tok + (it % CPR) * EPC;
+      kreg[m] = *reinterpret_cast<const u32x4*>(kgl + off);
+      qreg[m] = *reinterpret_cast<const u32x4*>(qgl + off);
+    }
+#pragma unroll
     for (int i = 0; i < RPS; ++i) {
-      const int r = s * RPS + i;
-      const float al = (float)ag[(size_t)min(r, cn - 1) * qk_tok];
-      g[i] = r < cn ? fmaxf(logf(al), kLogFloor) : 0.f;
+      const float la = fmaxf(__logf(g[i]), kLogFloor);
+      g[i] = s * RPS + i < cn ? la : 0.f;
     }
 #pragma unroll
     for (int i = 1; i < RPS; ++i) g[i] += g[i - 1];
@@ -472,6 +500,20 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   }
   __syncthreads();
   if (tid < DK) reinterpret_cast<float*>(rec + R::gc)[tid] = __expf(Gl[(C - 1) * LDG + tid]);
+  // channels too strongly decayed inside a diagonal block for the anchor split:
+  // thread (D, c) for D < 2; a wave covers 64 channels of one block
+  if (tid < 2 * DK) {
+    const int D = tid / DK, c = tid % DK, m = 32 * D + 15;
+    const float gm = Gl[m * LDG + c];
+    const bool out = Gl[32 * D * LDG + c] - gm > kSplitLimit || gm - Gl[(32 * D + 31) * LDG + c] > kSplitLimit;
+    const unsigned long long bits = __ballot(out);
+    if (lane == 0) {
+      const int w0 = D * (DK / 32) + (c >> 5);
+      Msk[w0] = (uint32_t)bits;
+      Msk[w0 + 1] = (uint32_t)(bits >> 32);
+    }
+  }
+  __syncthreads();
 
   // Three passes build operand tiles; after each, two waves take MFMA tiles:
   //   pass 0  rows 0..31, anchor 15    wave 0: A(0,0)   wave 1: P(0,0)
@@ -485,13 +527,13 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   for (int pass = 0; pass < 3; ++pass) {
     if (pass > 0) __syncthreads();   // the previous pass's tiles are consumed
 #pragma unroll
-    for (int m = 0; m < (pass < 2 ? IPT : 2 * IPT); ++m) {
-      const int it = tid + kThreads * m, rl = it / CPR, c0 = (it % CPR) * EPC;
-      const int r = pass == 1 ? 32 + rl : rl;
-      const uint32_t off = (uint32_t)min(r, cn - 1) * (uint32_t)qk_tok + c0;
+    for (int m = (pass == 1 ? IPT : 0); m < (pass == 0 ? IPT : 2 * IPT); ++m) {
+      const int it = tid + kThreads * m, r = it / CPR, c0 = (it % CPR) * EPC;
       float kf[EPC], qf[EPC], gr[EPC], ga[EPC], x[EPC], y[EPC], z[EPC];
-      unpack16<E>(*reinterpret_cast<const u32x4*>(kgl + off), kf);
-      unpack16<E>(*reinterpret_cast<const u32x4*>(qgl + off), qf);
+      const u32x4 kraw = kreg[m];
+      const u32x4 qraw = qreg[m];
+      unpack16<E>(kraw, kf);
+      unpack16<E>(qraw, qf);
       const int anchor = pass == 2 ? 31 : (pass == 0 ? 15 : 47);
 #pragma unroll
       for (int e = 0; e < EPC; e += 4) {
@@ -520,19 +562,27 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
         *reinterpret_cast<u32x4*>(rec + R::kc + ro) = pack16<E>(z);
       }
       const int lr = r & 31;
+      // diagonal blocks: channels outside the split take zero operands
+      uint32_t keep = ~0u;
+      if (pass < 2) {
+        *reinterpret_cast<u32x4*>(Kraw + lr * LDK + c0) = kraw;
+        *reinterpret_cast<u32x4*>(Qraw + lr * LDK + c0) = qraw;
+        keep = ~(Msk[pass * (DK / 32) + (c0 >> 5)] >> (c0 & 31));
+      }
       if (pass < 2 || r >= 32) {   // r side: exp(G_r - G_m)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
           const float w = __expf(gr[e] - ga[e]);
-          x[e] = kf[e] * w;
-          y[e] = qf[e] * w;
+          const bool k1 = (keep >> e) & 1u;
+          x[e] = k1 ? kf[e] * w : 0.f;
+          y[e] = k1 ? qf[e] * w : 0.f;
         }
         *reinterpret_cast<u32x4*>(Rop + lr * LDK + c0) = pack16<E>(x);
         *reinterpret_cast<u32x4*>(Qop + lr * LDK + c0) = pack16<E>(y);
       }
       if (pass < 2 || r < 32) {    // j side: exp(G_m - G_j)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) z[e] = kf[e] * __expf(ga[e] - gr[e]);
+        for (int e = 0; e < EPC; ++e) z[e] = ((keep >> e) & 1u) ? kf[e] * __expf(ga[e] - gr[e]) : 0.f;
         *reinterpret_cast<u32x4*>(Cop + lr * LDK + c0) = pack16<E>(z);
       }
     }
@@ -540,6 +590,28 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
     // tile (R, J) accumulates rows j (Cop) x columns r (Rop or Qop)
     const bool mine = pass == 2 ? wave < 2 : (wave >> 1) == pass;
     if (mine) tile_nt_k<DK / 16>(pass == 2 ? acc1 : acc0, Cop, LDK, (wave & 1) ? Qop : Rop, LDK, lane);
+    if (pass < 2 && mine) {
+      // exact contributions of the channels left out of this diagonal block
+      const int r = 32 * pass + col;
+      const E* xr = ((wave & 1) ? Qraw : Kraw) + col * LDK;
+#pragma unroll 1
+      for (int wd = 0; wd < DK / 32; ++wd) {
+        uint32_t bits = __builtin_amdgcn_readfirstlane(Msk[pass * (DK / 32) + wd]);
+        while (bits) {
+          const int c = 32 * wd + __builtin_ctz(bits);
+          bits &= bits - 1;
+          const float gr = Gl[r * LDG + c];
+          const float xv = (float)xr[c];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int jl = acc_row(v >> 2, v & 3, lane), j = 32 * pass + jl;
+            const float w = __expf(fminf(gr - Gl[j * LDG + c], 0.f));
+            const float t = xv * (float)Kraw[jl * LDK + c] * w;
+            acc0[v] += j <= r ? t : 0.f;
+          }
+        }
+      }
+    }
   }
   __syncthreads();   // G is dead: A and P take region 1
 

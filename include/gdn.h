@@ -36,11 +36,12 @@
  *  - Gates may take their boundary values: beta in [0, 1], alpha in [0, 1].
  *  - Supported sizes: d_k in {64, 128}, d_v in {64, 128}, chunk = 64.
  *    Other sizes return GDN_ERR_UNSUPPORTED.
- *  - Per-channel decay numerics: inside a chunk the kernels form decay ratios
- *    relative to anchors at most 16 tokens away, so results are exact up to
- *    rounding as long as, for every channel, the product of alpha over any 16
- *    consecutive tokens is at least 1e-36.  Stronger decay can overflow fp32
- *    inside a chunk and yield non-finite outputs.
+ *  - Decay numerics: log alpha is floored at -100 (alpha below e^-100 acts as
+ *    e^-100, which is 0 in every fp32 product).  Per-channel decay: inside a
+ *    chunk the kernels split decay ratios at anchor tokens at most 16 tokens
+ *    away; a channel whose decay over such a span exceeds e^64 is handled by
+ *    an exact element-wise path instead (slower, same results), so any alpha
+ *    in [0, 1] is accepted, including exact zeros.
  */
 #ifndef GDN_H
 #define GDN_H

@@ -57,13 +57,20 @@ def test_prefill_channel_decay_equal_channels_is_scalar_decay(gpu):
     assert rel_o(o, ro) <= 1e-4 and rel_S(S, rS) <= 1e-4
 
 
-def test_prefill_channel_gates_at_boundary_values(gpu):
-    """Per-channel alpha in {0.25, 1} mixed across channels and tokens, then alpha = 1."""
-    w = _small(150, 128, 128, torch.float32, 2, s0=True, B=1, H=2, seed=32)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_prefill_channel_gates_at_boundary_values(gpu, dtype, dk):
+    """Per-channel alpha in {0, 1} mixed across channels and tokens (hard resets of
+    single channels), alpha = 0 everywhere, tiny alpha, then alpha = 1 with beta = 0."""
+    w = _small(150, dk, 128, dtype, 2, s0=True, B=1, H=2, seed=32)
     inp = W.make_prefill(w)
     g = torch.Generator().manual_seed(33)
-    inp["alpha"] = torch.where(torch.rand(inp["alpha"].shape, generator=g) < 0.7, 1.0, 0.25)
-    check_prefill(gpu, inp, 2, torch.float32)
+    inp["alpha"] = (torch.rand(inp["alpha"].shape, generator=g) < 0.7).to(dtype)
+    check_prefill(gpu, inp, 2, dtype)
+    inp["alpha"] = torch.zeros_like(inp["alpha"])
+    check_prefill(gpu, inp, 2, dtype)
+    inp["alpha"] = torch.where(torch.rand(inp["alpha"].shape, generator=g) < 0.9, 1.0, 1e-30).to(dtype)
+    check_prefill(gpu, inp, 2, dtype)
     inp["alpha"] = torch.ones_like(inp["alpha"])
     inp["beta"] = torch.zeros_like(inp["beta"])
     _, S = gpu_prefill(gpu, inp, 2)
