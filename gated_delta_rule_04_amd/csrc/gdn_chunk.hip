@@ -64,20 +64,20 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 __device__ inline int blk_row(int blk, int cpr) { return (blk & 3) + 4 * (blk / (4 * cpr)); }
 __device__ inline int blk_col(int blk, int cpr) { return (blk >> 2) % cpr; }
 
-// Workspace layout, per chunk of every head (chunk index = head * N_chunks + n):
-//   T      C x C elements of the operand dtype, row-major
-//   gates  3 x C fp32: G_r, exp(G_r), exp(G_C - G_r)
-// T blocks come first (all chunks), then the gate blocks.
+// Workspace: one record per chunk of every head (chunk index = head *
+// N_chunks + n).  Scalar or no decay, offsets in elements of the operand dtype:
+//   T [C][C], P [C][C] (row-major), then the gate rows, 3 x C fp32:
+//   G_r, exp(G_r), exp(G_C - G_r).
+// (The per-channel record is KdaRec below.)
 constexpr size_t kGateFloats = 3 * C;
 
 template <typename E>
-__device__ inline float* gate_block(E* tws, size_t nchunks_total, size_t chunk) {
-  return reinterpret_cast<float*>(tws + nchunks_total * C * C) + chunk * kGateFloats;
-}
-template <typename E>
-__device__ inline const float* gate_block(const E* tws, size_t nchunks_total, size_t chunk) {
-  return reinterpret_cast<const float*>(tws + nchunks_total * C * C) + chunk * kGateFloats;
-}
+struct GateRec {
+  static constexpr size_t t = 0;
+  static constexpr size_t p = (size_t)C * C;
+  static constexpr size_t g = 2 * (size_t)C * C;   // fp32 region
+  static constexpr size_t elems = g + kGateFloats * 4 / sizeof(E);
+};
 
 // Sum over the four lanes of a quad (lanes 4c .. 4c + 3), result in all four.
 __device__ inline float quad_sum(float x) {
@@ -213,10 +213,11 @@ __device__ inline void tri_solve(const float* Am, float* Li, float* Mt, const fl
 }
 
 // ---------------------------------------------------------------------------
-// chunk_prep_kernel: T = (I + A)^-1 diag(beta) for one chunk of one head.
+// chunk_prep_kernel: T = (I + A)^-1 diag(beta) and P for one chunk of one head.
 // ---------------------------------------------------------------------------
-// LDS: K rows [64][LDK] (then L^-1 fp32 [64][LDA] in the same bytes), A fp32
-// [64][LDA] (then T [64][LDT]), Mt fp32 [32][LDM], G and beta.
+// Neither depends on the state, so both leave the sequential kernel.
+// LDS: K rows [64][LDK] (then L^-1 fp32 [64][LDA]), Q rows [64][LDK] (then A
+// fp32 [64][LDA], then T [64][LDT]), P [64][LDT], Mt fp32 [32][LDM], G, beta.
 template <typename E, int DK>
 struct PrepPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
@@ -224,9 +225,11 @@ struct PrepPlan {
   static constexpr int LDA = SolveLd<E>::LDA;
   static constexpr int LDT = SolveLd<E>::LDT;
   static constexpr int LDM = SolveLd<E>::LDM;
-  static constexpr size_t kr = 0;  // also L^-1
-  static constexpr size_t am = cmax((size_t)C * LDK * sizeof(E), (size_t)C * LDA * 4);
-  static constexpr size_t mt = am + cmax((size_t)C * LDA * 4, (size_t)C * LDT * sizeof(E));
+  static constexpr size_t es = sizeof(E);
+  static constexpr size_t kr = 0;   // also L^-1
+  static constexpr size_t am = cmax((size_t)C * LDK * es, (size_t)C * LDA * 4);   // Q, then A, then T
+  static constexpr size_t pm = am + cmax((size_t)C * LDK * es, cmax((size_t)C * LDA * 4, (size_t)C * LDT * es));
+  static constexpr size_t mt = pm + (size_t)C * LDT * es;
   static constexpr size_t g = mt + (size_t)32 * LDM * 4;
   static constexpr size_t total = g + 2 * C * 4;
 };
@@ -234,8 +237,8 @@ struct PrepPlan {
 template <typename E, int DK, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* __restrict__ tws,
                                                               int nchunks) {
-  const size_t nchunks_total = (size_t)a.B * a.H * nchunks;
   using L = PrepPlan<E, DK>;
+  using R = GateRec<E>;
   constexpr int EPC = 16 / (int)sizeof(E);
   constexpr int CPR = DK / EPC;
   constexpr int NKB = 16 * CPR;
@@ -243,8 +246,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
   E* Kr = reinterpret_cast<E*>(smem + L::kr);
   float* Li = reinterpret_cast<float*>(smem + L::kr);
+  E* Qr = reinterpret_cast<E*>(smem + L::am);
   float* Am = reinterpret_cast<float*>(smem + L::am);
   E* Tm = reinterpret_cast<E*>(smem + L::am);
+  E* Pm = reinterpret_cast<E*>(smem + L::pm);
   float* Mt = reinterpret_cast<float*>(smem + L::mt);
   float* G = reinterpret_cast<float*>(smem + L::g);
   float* Bt = G + C;
@@ -256,19 +261,22 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   const int h = bh % H, b = bh / H;
   const int t0 = n * C, cn = min(C, T - t0);
   const size_t tok0 = (size_t)b * T + t0;   // first token of the chunk in [B, T]
+  E* rec = tws + (size_t)blockIdx.x * R::elems;
 
-  // K rows (rows past the sequence end repeat its last row: beta = 0 there, so
-  // they never reach A or T)
+  // K and Q rows (rows past the sequence end repeat its last row: beta = 0
+  // there, so they never reach A or T, and P's rows of them are never used)
   {
     const E* kg = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
+    const E* qg = static_cast<const E*>(a.q) + (tok0 * H + h) * DK;
     const size_t ktok = (size_t)H * DK;
     for (int blk = tid; blk < NKB; blk += kThreads) {
       const int rg = blk_row(blk, CPR), cc = blk_col(blk, CPR);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r = 4 * rg + rr;
-        *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) =
-            *reinterpret_cast<const u32x4*>(kg + (size_t)min(r, cn - 1) * ktok + cc * EPC);
+        const size_t off = (size_t)min(r, cn - 1) * ktok + cc * EPC;
+        *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = *reinterpret_cast<const u32x4*>(kg + off);
+        *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = *reinterpret_cast<const u32x4*>(qg + off);
       }
     }
   }
@@ -281,18 +289,24 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     const float gC = __shfl(g, C - 1);
     G[lane] = g;
     Bt[lane] = ok ? bt : 0.f;
-    float* gw = gate_block(tws, nchunks_total, blockIdx.x);
+    float* gw = reinterpret_cast<float*>(rec + R::g);
     gw[lane] = g;
     gw[C + lane] = __expf(g);
     gw[2 * C + lane] = __expf(gC - g);
   }
   __syncthreads();
 
-  // A tiles (j block, r block) in {(0,0), (0,1), (1,1)}: rows j, columns r.
+  // A and P tiles (j block, r block) in {(0,0), (0,1), (1,1)}, rows j and
+  // columns r; wave w < 3 takes tile w of both.
+  const int jb = wave == 2 ? 1 : 0, rb = wave == 0 ? 0 : 1;
+  f32x16 acca = zero16(), accp = zero16();
+  if (wave < 3)
+    tile_nt2_pairs<DK / 16>(acca, accp, Kr + jb * 32 * LDK, Kr + rb * 32 * LDK, Kr + jb * 32 * LDK,
+                            Qr + rb * 32 * LDK, LDK, lane);
+  __syncthreads();   // Q is dead: A takes its bytes
+  // A[r][j] = beta_r exp(G_r - G_j) k_r.k_j (j < r); P[r][j] = exp(G_r - G_j) q_r.k_j
+  // (j <= r).  Masked entries are selected away (their weight may overflow).
   if (wave < 3) {
-    const int jb = wave == 2 ? 1 : 0, rb = wave == 0 ? 0 : 1;
-    f32x16 acc = zero16();
-    tile_nt_k<DK / 16>(acc, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
     const int r = rb * 32 + col;
     const float Gr = G[r], br = Bt[r];
 #pragma unroll
@@ -300,22 +314,33 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
       const int j0 = jb * 32 + acc_row(g, 0, lane);
       const float4 gj = *reinterpret_cast<const float4*>(G + j0);
       const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
-      float x[4];
+      float x[4], y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (j0 + e < r) ? br * __expf(Gr - gjv[e]) * acc[4 * g + e] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const float w = __expf(Gr - gjv[e]);
+        x[e] = (j0 + e < r) ? br * w * acca[4 * g + e] : 0.f;
+        y[e] = (j0 + e <= r) ? w * accp[4 * g + e] : 0.f;
+      }
       store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
+      store4(Pm + r * LDT + j0, y[0], y[1], y[2], y[3]);
     }
+  } else {   // P rows 0..31, columns 32..63 are zero
+    const int q = tid - 192, r = q >> 1, j0 = 32 + 16 * (q & 1);
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) store4(Pm + r * LDT + j0 + e, 0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
   tri_solve<E>(Am, Li, Mt, Bt, Tm, tid);
-  // T -> workspace, 64 x 64 contiguous, 16-byte stores
+  // T and P -> the record, 64 x 64 contiguous each, 16-byte stores
   {
-    E* dst = tws + (size_t)blockIdx.x * C * C;
     constexpr int CPT = C / EPC;
     for (int q = tid; q < C * CPT; q += kThreads) {
       const int r = q / CPT, cc = q % CPT;
-      *reinterpret_cast<u32x4*>(dst + r * C + cc * EPC) = *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC);
+      *reinterpret_cast<u32x4*>(rec + R::t + r * C + cc * EPC) =
+          *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC);
+      *reinterpret_cast<u32x4*>(rec + R::p + r * C + cc * EPC) =
+          *reinterpret_cast<const u32x4*>(Pm + r * LDT + cc * EPC);
     }
   }
 }
@@ -356,8 +381,18 @@ struct KdaRec {
   static constexpr size_t kg = 2 * (size_t)C * C;
   static constexpr size_t qg = kg + (size_t)C * DK;
   static constexpr size_t kc = qg + (size_t)C * DK;
-  static constexpr size_t gc = kc + (size_t)C * DK;
-  static constexpr size_t elems = gc + (size_t)DK * 4 / sizeof(E);
+  static constexpr size_t g = kc + (size_t)C * DK;   // fp32 region
+  static constexpr size_t elems = g + (size_t)DK * 4 / sizeof(E);
+};
+
+// The workspace record of a decay mode.
+template <typename E, int DK, int MODE>
+struct RecOf {
+  using type = GateRec<E>;
+};
+template <typename E, int DK>
+struct RecOf<E, DK, 2> {
+  using type = KdaRec<E, DK>;
 };
 
 // A 16-byte chunk of the operand dtype as fp32 values, and back (round to
@@ -499,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
     for (int i = 0; i < RPS; ++i) Gl[(s * RPS + i) * LDG + c] = g[i] + off;
   }
   __syncthreads();
-  if (tid < DK) reinterpret_cast<float*>(rec + R::gc)[tid] = __expf(Gl[(C - 1) * LDG + tid]);
+  if (tid < DK) reinterpret_cast<float*>(rec + R::g)[tid] = __expf(Gl[(C - 1) * LDG + tid]);
   // channels too strongly decayed inside a diagonal block for the anchor split:
   // thread (D, c) for D < 2; a wave covers 64 channels of one block
   if (tid < 2 * DK) {
@@ -722,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   constexpr bool SEPKT = sep_kt_fits<E, DK, DVS>();
   constexpr bool KDA = MODE == 2;   // per-channel decay: operands come pre-scaled
   using L = StatePlan<E, DK, DVS, SEPKT>;
-  using R = KdaRec<E, DK>;
+  using R = typename RecOf<E, DK, MODE>::type;
   static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
   constexpr int NI = DVS / 32;       // 32-wide value blocks in the slice
   constexpr int NC = DK / 32;        // 32-wide key blocks
@@ -785,26 +820,19 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   const E* qg = static_cast<const E*>(a.q) + ((size_t)b * T * H + h) * DK;
   const E* kg = static_cast<const E*>(a.k) + ((size_t)b * T * H + h) * DK;
   const E* vg = static_cast<const E*>(a.v) + ((size_t)b * T * H + h) * dv + i0;
-  const E* tg = tws + (size_t)head * nchunks * C * C;      // T blocks (scalar gates)
-  const E* recs = tws + (size_t)head * nchunks * R::elems;   // records (per-channel decay)
+  const E* recs = tws + (size_t)head * nchunks * R::elems;   // per-chunk records
   E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
   const size_t sbase = ((size_t)b * H + h) * dv + i0;  // first state row of the slice
 
-  // Tile ownership.  X, O_inter (phase 1), U (phase 4) and O (phase 5) tiles of
-  // row block own_rb and value block own_ib belong to one wave; the three P
-  // tiles (j block, r block) in {(0,0), (0,1), (1,1)} go to the waves with the
-  // least other work.
-  int own_rb = -1, own_ib = 0, pt0 = -1, pt1 = -1;
+  // Tile ownership: X, O_inter (phase 1), U (phase 4) and O (phase 5) tiles of
+  // row block own_rb and value block own_ib belong to one wave.
+  int own_rb = -1, own_ib = 0;
   if (NI == 2) {
     own_rb = wave >> 1;
     own_ib = wave & 1;
-    pt0 = wave < 3 ? wave : -1;
-  } else {
-    if (wave < 2) own_rb = wave;
-    if (wave == 2) { pt0 = 0; pt1 = 2; }
-    if (wave == 3) pt0 = 1;
+  } else if (wave < 2) {
+    own_rb = wave;
   }
-  if (KDA) pt0 = pt1 = -1;   // P arrives with the chunk
 
   // Initial state: S0 or zeros, into registers and the operand copy.
   f32x16 Sacc[NST];
@@ -835,8 +863,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   // U, O or S, and their O rows are not written.
   u32x4 pk[KBT][4], pq[KBT][4], pv[VBT][4], pt[TBT];
   u32x4 pg = u32x4{0u, 0u, 0u, 0u};   // gate block: 48 chunks, threads 0..47 (gC: DK / 4)
-  u32x4 pkc[KDA && SEPKT ? KBT : 1][4], pp[KDA ? TBT : 1];   // Kc rows and P
-  const size_t nchunks_total = (size_t)a.B * H * nchunks;
+  u32x4 pkc[KDA && SEPKT ? KBT : 1][4], pp[TBT];   // Kc rows (per-channel decay) and P
 
   auto prefetch = [&](int n) __attribute__((always_inline)) {
     const int t0 = n * C;
@@ -885,21 +912,15 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
         pv[m][rr] = *reinterpret_cast<const u32x4*>(vq + off);
       }
     }
-    if constexpr (KDA) {
+    {
       const E* rq = recs + (size_t)n * R::elems;
 #pragma unroll
       for (int m = 0; m < TBT; ++m) {
         pt[m] = *reinterpret_cast<const u32x4*>(rq + R::t + (tid + kThreads * m) * EPC);
         pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (tid + kThreads * m) * EPC);
       }
-      pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::gc) +
-                                           4 * min(tid, DK / 4 - 1));
-    } else {
-      const E* tq = tg + (size_t)n * C * C;
-#pragma unroll
-      for (int m = 0; m < TBT; ++m) pt[m] = *reinterpret_cast<const u32x4*>(tq + (tid + kThreads * m) * EPC);
-      const float* gq = gate_block(tws, nchunks_total, (size_t)head * nchunks + n);
-      pg = *reinterpret_cast<const u32x4*>(gq + 4 * min(tid, (int)kGateFloats / 4 - 1));
+      constexpr int NG4 = (KDA ? DK : (int)kGateFloats) / 4;   // 16-byte chunks of the fp32 rows
+      pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(tid, NG4 - 1));
     }
   };
 
@@ -936,7 +957,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     for (int m = 0; m < TBT; ++m) {
       const int q = tid + kThreads * m, r = q / CPT, cc = q % CPT;
       *reinterpret_cast<u32x4*>(Tm + r * LDT + cc * EPC) = pt[m];
-      if constexpr (KDA) *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
+      *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
     }
     if (tid < (KDA ? DK / 4 : (int)kGateFloats / 4)) *reinterpret_cast<u32x4*>(G + 4 * tid) = pg;
   };
@@ -953,23 +974,6 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     }
   };
 
-  // P tile (jb, rb) from its accumulator: decay weights and the causal mask.
-  auto p_epilogue = [&](const f32x16& pacc, int ptile) __attribute__((always_inline)) {
-    const int jb = ptile == 2 ? 1 : 0, rb = ptile == 0 ? 0 : 1;
-    const int r = rb * 32 + col;
-    const float Gr = G[r];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int j0 = jb * 32 + acc_row(g, 0, lane);
-      const float4 gj = *reinterpret_cast<const float4*>(G + j0);
-      const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
-      float x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (j0 + e <= r) ? __expf(Gr - gjv[e]) * pacc[4 * g + e] : 0.f;
-      store4(Pm + r * LDT + j0, x[0], x[1], x[2], x[3]);
-    }
-  };
-
   // Iteration -1 only issues the first prefetch (one call site per helper keeps
   // the prefetch registers in registers).  Later prefetches are issued at the
   // start of phase 1, where the memory pipe works under the MFMA chains.
@@ -983,30 +987,11 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     if (n + 1 < nchunks) prefetch(n + 1);
     if (n < 0) continue;
 
-    // ---- phase 1: P tiles; X and O_inter tiles ----
-    // P tile (jb, rb) holds rows j of the j-block and columns r of the r-block,
-    // so each lane writes four consecutive j of one row r.  The X and O_inter
-    // tiles of (own_rb, own_ib) share the S operand.
-    f32x16 xacc = zero16(), oacc = zero16(), pacc0 = zero16(), pacc1 = zero16();
-    const int pjb0 = pt0 == 2 ? 1 : 0, prb0 = pt0 == 0 ? 0 : 1;
-    if (own_rb >= 0) {
-      const E* Ax = Kr + own_rb * 32 * LDK;
-      const E* Ao = Qr + own_rb * 32 * LDK;
-      const E* Bs = Sb + own_ib * 32 * LDSB;
-      if (pt0 >= 0)
-        tile_nt3<DK / 16>(xacc, oacc, pacc0, Ax, Ao, Bs, Kr + pjb0 * 32 * LDK, Qr + prb0 * 32 * LDK,
-                          LDK, LDSB, lane);
-      else
-        tile_nt2_shared_b<DK / 16>(xacc, oacc, Ax, Ao, LDK, Bs, LDSB, lane);
-    } else if (pt0 >= 0) {
-      if (pt1 >= 0)
-        tile_nt2_pairs<DK / 16>(pacc0, pacc1, Kr + pjb0 * 32 * LDK, Qr + prb0 * 32 * LDK,
-                                Kr + 32 * LDK, Qr + 32 * LDK, LDK, lane);
-      else
-        tile_nt_k<DK / 16>(pacc0, Kr + pjb0 * 32 * LDK, LDK, Qr + prb0 * 32 * LDK, LDK, lane);
-    }
-    if (pt0 >= 0) p_epilogue(pacc0, pt0);
-    if (pt1 >= 0) p_epilogue(pacc1, pt1);
+    // ---- phase 1: X and O_inter tiles (they share the S operand) ----
+    f32x16 xacc = zero16(), oacc = zero16();
+    if (own_rb >= 0)
+      tile_nt2_shared_b<DK / 16>(xacc, oacc, Kr + own_rb * 32 * LDK, Qr + own_rb * 32 * LDK, LDK,
+                                 Sb + own_ib * 32 * LDSB, LDSB, lane);
     if (own_rb >= 0) {
       const int i = own_ib * 32 + col;
 #pragma unroll
@@ -1025,15 +1010,19 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     __syncthreads();
 
     // ---- K^T for phase 6 when it shares Q's region (fp32, d_k = 128) ----
-    if (!SEPKT) {
-      const E* kcq = recs + (size_t)n * R::elems + R::kc;   // per-channel decay: Kc rows
+    if constexpr (!SEPKT) {
       for (int blk = tid; blk < NKB; blk += kThreads) {
         const int rg4 = blk_row(blk, CPR), cc = blk_col(blk, CPR);
         u32x4 v[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          v[rr] = KDA ? *reinterpret_cast<const u32x4*>(kcq + (4 * rg4 + rr) * DK + cc * EPC)
-                      : *reinterpret_cast<const u32x4*>(Kr + (4 * rg4 + rr) * LDK + cc * EPC);
+        for (int rr = 0; rr < 4; ++rr) {
+          if constexpr (KDA) {   // per-channel decay: the decay-scaled Kc rows
+            const E* kcq = recs + (size_t)n * R::elems + R::kc;
+            v[rr] = *reinterpret_cast<const u32x4*>(kcq + (4 * rg4 + rr) * DK + cc * EPC);
+          } else {
+            v[rr] = *reinterpret_cast<const u32x4*>(Kr + (4 * rg4 + rr) * LDK + cc * EPC);
+          }
+        }
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
           store_col4(Kt + (cc * EPC + e) * LDT + 4 * rg4, v[0], v[1], v[2], v[3], e);
@@ -1149,15 +1138,447 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   }
 }
 
+// ---------------------------------------------------------------------------
+// chunk_state_ws: the sequential pass in bf16 with eight waves.
+// ---------------------------------------------------------------------------
+// Waves 0-3 carry the state chain (phases 1, 4, 5 and 6 of chunk_state_kernel,
+// same tile ownership).  Waves 4-7 move data: while the chain works on chunk
+// n they load later chunks from HBM into registers and write each LDS buffer
+// in an interval in which nobody reads it, and they write the staged O rows
+// out.  Issuing the loads costs the compute unit about 40 bytes per clock;
+// here it runs beside the MFMA chain instead of inside it.  Per chunk there
+// are three barriers.  Between them:
+//   interval  waves 0-3                 waves 4-7
+//   I1        phase 1: X, O_inter       P(n); O(n-1) -> HBM; load T, P, gates of n+1
+//   I4        phase 4: U = T X          K, Q rows, V^T, K^T of n+1
+//   I6        phases 5, 6: O and S      T and gates of n+1; load K, Q, V of n+2
+// K^T and the gate rows are double-buffered (K^T of n+1 is written while
+// phase 6 of n has yet to read K^T of n; the gate rows are read in every
+// interval); O has a staging buffer of its own.  The two roles run separate
+// loops with the same barrier count, so their registers do not add up.
+template <typename E, int DK, int DVS>
+struct WsPlan {
+  static constexpr int PAD = 16 / (int)sizeof(E);
+  static constexpr int LDK = DK + PAD;
+  static constexpr int LDT = C + PAD;
+  static constexpr int LDSB = DK + PAD;
+  static constexpr int OST = DVS + PAD;
+  static constexpr size_t es = sizeof(E);
+  static constexpr size_t kr = 0;
+  static constexpr size_t qr = kr + (size_t)C * LDK * es;
+  static constexpr size_t kt = qr + (size_t)C * LDK * es;         // two buffers
+  static constexpr size_t sb = kt + 2 * (size_t)DK * LDT * es;
+  static constexpr size_t vt = sb + (size_t)DVS * LDSB * es;
+  static constexpr size_t xt = vt + (size_t)DVS * LDT * es;
+  static constexpr size_t os = xt + (size_t)DVS * LDT * es;
+  static constexpr size_t pm = os + (size_t)C * OST * es;
+  static constexpr size_t tm = pm + (size_t)C * LDT * es;
+  static constexpr size_t ut = tm + (size_t)C * LDT * es;
+  static constexpr size_t uw = ut + (size_t)DVS * LDT * es;
+  static constexpr size_t g = uw + (size_t)DVS * LDT * es;       // two buffers
+  static constexpr size_t total = g + 2 * kGateFloats * 4;
+};
+
+constexpr int kWsThreads = 512;
+
+template <typename E, int DK, int DVS, int MODE>
+__global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws) {
+  using L = WsPlan<E, DK, DVS>;
+  static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
+  constexpr bool KDA = MODE == 2;
+  using R = typename RecOf<E, DK, MODE>::type;
+  constexpr int NI = DVS / 32;       // 32-wide value blocks in the slice
+  constexpr int NC = DK / 32;        // 32-wide key blocks
+  constexpr int NT = NC * NI;        // state tiles
+  constexpr int NST = (NT + 3) / 4;  // state tiles per chain wave
+  constexpr int EPC = 16 / (int)sizeof(E);
+  constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB, OST = L::OST;
+  // data-wave geometry (256 threads): blocks of 4 rows x one 16-byte chunk
+  constexpr int PT = 256;
+  constexpr int CPR = DK / EPC;
+  constexpr int NKB = 16 * CPR;
+  constexpr int KBT = (NKB + PT - 1) / PT;
+  constexpr int CPV = DVS / EPC;
+  constexpr int NVB = 16 * CPV;
+  constexpr int VBT = (NVB + PT - 1) / PT;
+  constexpr int CPT = C / EPC;
+  constexpr int TBT = C * CPT / PT;
+  constexpr int NG4 = (KDA ? DK : (int)kGateFloats) / 4;   // 16-byte chunks of the fp32 rows
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
+  E* Kr = reinterpret_cast<E*>(smem + L::kr);
+  E* Qr = reinterpret_cast<E*>(smem + L::qr);
+  E* Ktb = reinterpret_cast<E*>(smem + L::kt);          // two K^T buffers, DK * LDT apart
+  E* Sb = reinterpret_cast<E*>(smem + L::sb);
+  E* Vt = reinterpret_cast<E*>(smem + L::vt);
+  E* Xt = reinterpret_cast<E*>(smem + L::xt);
+  E* Os = reinterpret_cast<E*>(smem + L::os);
+  E* Pm = reinterpret_cast<E*>(smem + L::pm);
+  E* Tm = reinterpret_cast<E*>(smem + L::tm);
+  E* Ut = reinterpret_cast<E*>(smem + L::ut);
+  E* Uw = reinterpret_cast<E*>(smem + L::uw);
+  float* Gbuf = reinterpret_cast<float*>(smem + L::g);  // two gate blocks (or gC rows)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31;
+  const int H = a.H, T = a.T, dv = a.dv;
+  const int nsl = dv / DVS;
+  const int nheads = a.B * H;
+  // Workgroups are dispatched round-robin over the eight XCDs: give the slices
+  // of one head the same XCD (same L2) when the head count allows it.
+  int head, sl;
+  if ((nheads & 7) == 0) {
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    head = xcd + 8 * (j / nsl);
+    sl = j % nsl;
+  } else {
+    head = blockIdx.x / nsl;
+    sl = blockIdx.x % nsl;
+  }
+  const int h = head % H, b = head / H;
+  const int i0 = sl * DVS;
+  const int nchunks = (T + C - 1) / C;
+  const size_t v_tok = (size_t)H * dv;
+  const size_t sbase = ((size_t)b * H + h) * dv + i0;
+
+  if (wave >= 4) {
+    // ======================= data waves =======================
+    const int ptid = tid - 256;
+    const size_t qk_tok = (size_t)H * DK;
+    const E* qg = static_cast<const E*>(a.q) + ((size_t)b * T * H + h) * DK;
+    const E* kg = static_cast<const E*>(a.k) + ((size_t)b * T * H + h) * DK;
+    const E* vg = static_cast<const E*>(a.v) + ((size_t)b * T * H + h) * dv + i0;
+    const E* recs = tws + (size_t)head * nchunks * R::elems;
+    E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
+
+    u32x4 pk[KBT][4], pq[KBT][4], pv[VBT][4], pkc[KDA ? KBT : 1][4];   // rows of a chunk
+    u32x4 pt[TBT], pp[TBT], pg;                                         // T, P, gates of a chunk
+
+    // Loads are unconditional; rows past the sequence end re-read its last
+    // row (T's rows and columns of those tokens are zero).
+    auto load_rows = [&](int n) __attribute__((always_inline)) {
+      const int t0 = n * C;
+      const int rmax = min(C, T - t0) - 1;
+      if constexpr (KDA) {
+        const E* rq = recs + (size_t)n * R::elems;
+#pragma unroll
+        for (int m = 0; m < KBT; ++m) {
+          const int blk = ptid + PT * m;
+          const int bq = blk < NKB ? blk : 0;
+          const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t off = (uint32_t)(4 * rb4 + rr) * DK + cc * EPC;
+            pk[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::kg + off);
+            pq[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::qg + off);
+            pkc[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::kc + off);
+          }
+        }
+      } else {
+        const E* kq = kg + (size_t)t0 * qk_tok;
+        const E* qq = qg + (size_t)t0 * qk_tok;
+#pragma unroll
+        for (int m = 0; m < KBT; ++m) {
+          const int blk = ptid + PT * m;
+          const int bq = blk < NKB ? blk : 0;
+          const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)qk_tok + cc * EPC;
+            pk[m][rr] = *reinterpret_cast<const u32x4*>(kq + off);
+            pq[m][rr] = *reinterpret_cast<const u32x4*>(qq + off);
+          }
+        }
+      }
+      const E* vq = vg + (size_t)t0 * v_tok;
+#pragma unroll
+      for (int m = 0; m < VBT; ++m) {
+        const int blk = ptid + PT * m;
+        const int bq = blk < NVB ? blk : 0;
+        const int rb4 = blk_row(bq, CPV), cc = blk_col(bq, CPV);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)v_tok + cc * EPC;
+          pv[m][rr] = *reinterpret_cast<const u32x4*>(vq + off);
+        }
+      }
+    };
+    auto load_tp = [&](int n) __attribute__((always_inline)) {
+      const E* rq = recs + (size_t)n * R::elems;
+#pragma unroll
+      for (int m = 0; m < TBT; ++m) {
+        pt[m] = *reinterpret_cast<const u32x4*>(rq + R::t + (ptid + PT * m) * EPC);
+        pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (ptid + PT * m) * EPC);
+      }
+      pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(ptid, NG4 - 1));
+    };
+    // K and Q rows, V^T and K^T (buffer kb) of a chunk.
+    auto commit_rows = [&](int kb) __attribute__((always_inline)) {
+      E* Kt = Ktb + kb * DK * LDT;
+#pragma unroll
+      for (int m = 0; m < KBT; ++m) {
+        const int blk = ptid + PT * m;
+        if (blk < NKB) {
+          const int rb4 = blk_row(blk, CPR), cc = blk_col(blk, CPR);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            *reinterpret_cast<u32x4*>(Kr + (4 * rb4 + rr) * LDK + cc * EPC) = pk[m][rr];
+            *reinterpret_cast<u32x4*>(Qr + (4 * rb4 + rr) * LDK + cc * EPC) = pq[m][rr];
+          }
+          const auto& src = KDA ? pkc[m] : pk[m];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            store_col4(Kt + (cc * EPC + e) * LDT + 4 * rb4, src[0], src[1], src[2], src[3], e);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < VBT; ++m) {
+        const int blk = ptid + PT * m;
+        if (blk < NVB) {
+          const int rb4 = blk_row(blk, CPV), cc = blk_col(blk, CPV);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            store_col4(Vt + (cc * EPC + e) * LDT + 4 * rb4, pv[m][0], pv[m][1], pv[m][2], pv[m][3], e);
+        }
+      }
+    };
+    auto commit_p = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < TBT; ++m) {
+        const int q = ptid + PT * m, r = q / CPT, cc = q % CPT;
+        *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
+      }
+    };
+    auto commit_t = [&](int gb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < TBT; ++m) {
+        const int q = ptid + PT * m, r = q / CPT, cc = q % CPT;
+        *reinterpret_cast<u32x4*>(Tm + r * LDT + cc * EPC) = pt[m];
+      }
+      if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * kGateFloats + 4 * ptid) = pg;
+    };
+    // Staged O rows of a chunk -> HBM, 16-byte stores along each row.
+    auto flush_o = [&](int t0f, int cnf) __attribute__((always_inline)) {
+      constexpr int CPO = DVS / EPC;
+      E* oq = og + (size_t)t0f * v_tok;
+      for (int q = ptid; q < C * CPO; q += PT) {
+        const int r = q / CPO, cc = q % CPO;
+        if (r < cnf)
+          *reinterpret_cast<u32x4*>(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC) =
+              *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC);
+      }
+    };
+
+    if (nchunks > 0) {
+      load_rows(0);
+      load_tp(0);
+      commit_rows(0);
+      commit_p();
+      commit_t(0);
+      load_rows(min(1, nchunks - 1));
+    }
+    __syncthreads();
+    for (int n = 0; n < nchunks; ++n) {
+      // I1
+      if (n > 0) {
+        commit_p();                 // P(n), loaded during chunk n - 1
+        flush_o((n - 1) * C, C);
+      }
+      load_tp(min(n + 1, nchunks - 1));
+      __syncthreads();
+      // I4
+      if (n + 1 < nchunks) commit_rows((n + 1) & 1);
+      __syncthreads();
+      // I6
+      if (n + 1 < nchunks) commit_t((n + 1) & 1);
+      load_rows(min(n + 2, nchunks - 1));
+      __syncthreads();
+    }
+    if (nchunks > 0) flush_o((nchunks - 1) * C, T - (nchunks - 1) * C);
+    return;
+  }
+
+  // ======================= chain waves =======================
+  // X, O_inter (phase 1), U (phase 4) and O (phase 5) tiles of row block own_rb
+  // and value block own_ib belong to one wave.
+  int own_rb = -1, own_ib = 0;
+  if (NI == 2) {
+    own_rb = wave >> 1;
+    own_ib = wave & 1;
+  } else if (wave < 2) {
+    own_rb = wave;
+  }
+
+  f32x16 Sacc[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    Sacc[st] = zero16();
+    const int t = wave + 4 * st;
+    if (t < NT) {
+      const int cb = t / NI, ib = t % NI, i = ib * 32 + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = cb * 32 + acc_row(g, 0, lane);
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (a.S0) x = *reinterpret_cast<const float4*>(a.S0 + (sbase + i) * DK + c0);
+        Sacc[st][4 * g + 0] = x.x;
+        Sacc[st][4 * g + 1] = x.y;
+        Sacc[st][4 * g + 2] = x.z;
+        Sacc[st][4 * g + 3] = x.w;
+        store4(Sb + i * LDSB + c0, x.x, x.y, x.z, x.w);
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int n = 0; n < nchunks; ++n) {
+    const float* G = Gbuf + (n & 1) * kGateFloats;
+    const float* Eg = G + C;
+    const float* Ec = G + 2 * C;
+    const E* Kt = Ktb + (n & 1) * DK * LDT;
+
+    // ---- I1, phase 1: X and O_inter tiles (they share the S operand) ----
+    f32x16 xacc = zero16(), oacc = zero16();
+    if (own_rb >= 0) {
+      tile_nt2_shared_b<DK / 16>(xacc, oacc, Kr + own_rb * 32 * LDK, Qr + own_rb * 32 * LDK, LDK,
+                                 Sb + own_ib * 32 * LDSB, LDSB, lane);
+      const int i = own_ib * 32 + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = own_rb * 32 + acc_row(g, 0, lane);
+        const float4 eg = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
+        const float4 v4 = load4_elem(Vt + i * LDT + r0);
+        store4(Xt + i * LDT + r0, v4.x - eg.x * xacc[4 * g + 0], v4.y - eg.y * xacc[4 * g + 1],
+               v4.z - eg.z * xacc[4 * g + 2], v4.w - eg.w * xacc[4 * g + 3]);
+        oacc[4 * g + 0] *= eg.x;
+        oacc[4 * g + 1] *= eg.y;
+        oacc[4 * g + 2] *= eg.z;
+        oacc[4 * g + 3] *= eg.w;
+      }
+    }
+    __syncthreads();
+
+    // ---- I4, phase 4: U = T X; U^T and the decay-weighted copy for the state ----
+    if (own_rb >= 0) {
+      f32x16 uacc = zero16();
+      if (own_rb == 0) tile_nt_k<2>(uacc, Tm, LDT, Xt + own_ib * 32 * LDT, LDT, lane);
+      else tile_nt_k<4>(uacc, Tm + 32 * LDT, LDT, Xt + own_ib * 32 * LDT, LDT, lane);
+      const int i = own_ib * 32 + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = own_rb * 32 + acc_row(g, 0, lane);
+        store4(Ut + i * LDT + r0, uacc[4 * g], uacc[4 * g + 1], uacc[4 * g + 2], uacc[4 * g + 3]);
+        if constexpr (!KDA) {
+          const float4 ec = *reinterpret_cast<const float4*>(Ec + r0);
+          store4(Uw + i * LDT + r0, uacc[4 * g] * ec.x, uacc[4 * g + 1] * ec.y,
+                 uacc[4 * g + 2] * ec.z, uacc[4 * g + 3] * ec.w);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- I6, phase 5: O = O_inter + P U, staged for the data waves ----
+    if (own_rb >= 0) {
+      if (own_rb == 0) tile_nt_k<2>(oacc, Pm, LDT, Ut + own_ib * 32 * LDT, LDT, lane);
+      else tile_nt_k<4>(oacc, Pm + 32 * LDT, LDT, Ut + own_ib * 32 * LDT, LDT, lane);
+      const int i = own_ib * 32 + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Os[(own_rb * 32 + acc_row(g, e, lane)) * OST + i] = to_elem<E>(oacc[4 * g + e]);
+    }
+    // ---- phase 6: S^T <- gamma_C S^T + K^T Uw (per-channel: Diag(gC) S^T + Kc^T U) ----
+    {
+      if constexpr (KDA) {
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const int cb = (wave + 4 * st) / NI;
+          if (cb < NC) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const float4 d = *reinterpret_cast<const float4*>(G + cb * 32 + acc_row(g, 0, lane));
+              Sacc[st][4 * g + 0] *= d.x;
+              Sacc[st][4 * g + 1] *= d.y;
+              Sacc[st][4 * g + 2] *= d.z;
+              Sacc[st][4 * g + 3] *= d.w;
+            }
+          }
+        }
+      } else {
+        const float gC = Eg[C - 1];
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
+      }
+      const E* Ub = KDA ? Ut : Uw;
+      if (NST == 2 && wave + 4 < NT) {
+        tile_nt2_shared_b<C / 16>(Sacc[0], Sacc[NST - 1], Kt + (wave / NI) * 32 * LDT,
+                                  Kt + ((wave + 4) / NI) * 32 * LDT, LDT,
+                                  Ub + (wave % NI) * 32 * LDT, LDT, lane);
+      } else {
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const int t = wave + 4 * st;
+          if (t < NT)
+            tile_nt_k<C / 16>(Sacc[st], Kt + (t / NI) * 32 * LDT, LDT, Ub + (t % NI) * 32 * LDT,
+                              LDT, lane);
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int t = wave + 4 * st;
+        if (t < NT) {
+          const int cb = t / NI, ib = t % NI, i = ib * 32 + col;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c0 = cb * 32 + acc_row(g, 0, lane);
+            store4(Sb + i * LDSB + c0, Sacc[st][4 * g], Sacc[st][4 * g + 1], Sacc[st][4 * g + 2],
+                   Sacc[st][4 * g + 3]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (a.S_final) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int t = wave + 4 * st;
+      if (t < NT) {
+        const int cb = t / NI, ib = t % NI, i = ib * 32 + col;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = cb * 32 + acc_row(g, 0, lane);
+          *reinterpret_cast<float4*>(a.S_final + (sbase + i) * DK + c0) =
+              make_float4(Sacc[st][4 * g], Sacc[st][4 * g + 1], Sacc[st][4 * g + 2], Sacc[st][4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
 template <typename E, int DK, int DVS>
 hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) {
   dim3 grid((unsigned)((size_t)a.B * a.H * (a.dv / DVS))), block(kThreads);
-  if (a.mode == 0)
-    hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 0>), grid, block, 0, stream, a, tws);
-  else if (a.mode == 1)
-    hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 1>), grid, block, 0, stream, a, tws);
-  else
-    hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 2>), grid, block, 0, stream, a, tws);
+  if constexpr (sizeof(E) == 2) {
+    dim3 wblock(kWsThreads);
+    if (a.mode == 0)
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0>), grid, wblock, 0, stream, a, tws);
+    else if (a.mode == 1)
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1>), grid, wblock, 0, stream, a, tws);
+    else
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2>), grid, wblock, 0, stream, a, tws);
+  } else {
+    if (a.mode == 0)
+      hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 0>), grid, block, 0, stream, a, tws);
+    else if (a.mode == 1)
+      hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 1>), grid, block, 0, stream, a, tws);
+    else
+      hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 2>), grid, block, 0, stream, a, tws);
+  }
   return hipGetLastError();
 }
 
@@ -1194,7 +1615,7 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dtype, int mode)
   const size_t chunks = (size_t)B * H * (((size_t)T + C - 1) / C);
   const size_t es = dtype == 1 ? 2 : 4;
   if (mode == 2) return chunks * ((2 * (size_t)C * C + 3 * (size_t)C * dk) * es + 4 * (size_t)dk);
-  return chunks * (C * C * es + kGateFloats * 4);
+  return chunks * (2 * (size_t)C * C * es + kGateFloats * 4);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream) {

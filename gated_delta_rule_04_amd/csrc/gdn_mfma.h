@@ -68,24 +68,36 @@ __device__ inline void mma16(f32x16& acc, const Frag<float>& a, const Frag<float
   acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
 }
 
-// acc += A[0:32, 0:16 nk] * B[0:32, 0:16 nk]^T, A and B in LDS with leading
-// dimensions lda and ldb (elements), k contiguous.
-template <typename E>
-__device__ inline void tile_nt(f32x16& acc, const E* A, int lda, const E* B, int ldb, int nk,
-                               int lane) {
-  const E* pa = A + (lane & 31) * lda + (lane >> 5) * 8;
-  const E* pb = B + (lane & 31) * ldb + (lane >> 5) * 8;
-#pragma unroll 4
-  for (int s = 0; s < nk; ++s) mma16(acc, frag_load(pa + 16 * s), frag_load(pb + 16 * s));
-}
+// The helpers below are fully unrolled over the NK k steps.  The fragments of
+// step s + kAhead are loaded before the MFMAs of step s are issued, and
+// scheduling fences keep that order (left alone, the scheduler moves each
+// load next to its MFMA and the LDS latency of every step is exposed).
+constexpr int kAhead = 2;
 
-// Same with a compile-time k extent, fully unrolled (fragment loads hoisted).
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// acc += A[0:32, 0:16 NK] * B[0:32, 0:16 NK]^T, A and B in LDS with leading
+// dimensions lda and ldb (elements), k contiguous.
 template <int NK, typename E>
 __device__ inline void tile_nt_k(f32x16& acc, const E* A, int lda, const E* B, int ldb, int lane) {
   const E* pa = A + (lane & 31) * lda + (lane >> 5) * 8;
   const E* pb = B + (lane & 31) * ldb + (lane >> 5) * 8;
+  Frag<E> fa[NK], fb[NK];
 #pragma unroll
-  for (int s = 0; s < NK; ++s) mma16(acc, frag_load(pa + 16 * s), frag_load(pb + 16 * s));
+  for (int s = 0; s < kAhead && s < NK; ++s) {
+    fa[s] = frag_load(pa + 16 * s);
+    fb[s] = frag_load(pb + 16 * s);
+  }
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    if (s + kAhead < NK) {
+      fa[s + kAhead] = frag_load(pa + 16 * (s + kAhead));
+      fb[s + kAhead] = frag_load(pb + 16 * (s + kAhead));
+    }
+    sched_fence();
+    mma16(acc, fa[s], fb[s]);
+    sched_fence();
+  }
 }
 
 // Two tiles that share the B operand: acc0 += A0 B^T, acc1 += A1 B^T.
@@ -94,11 +106,25 @@ __device__ inline void tile_nt2_shared_b(f32x16& acc0, f32x16& acc1, const E* A0
                                          int lda, const E* B, int ldb, int lane) {
   const int ra = (lane & 31) * lda + (lane >> 5) * 8;
   const E* pb = B + (lane & 31) * ldb + (lane >> 5) * 8;
+  Frag<E> fb[NK], f0[NK], f1[NK];
+#pragma unroll
+  for (int s = 0; s < kAhead && s < NK; ++s) {
+    fb[s] = frag_load(pb + 16 * s);
+    f0[s] = frag_load(A0 + ra + 16 * s);
+    f1[s] = frag_load(A1 + ra + 16 * s);
+  }
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
-    const Frag<E> fb = frag_load(pb + 16 * s);
-    mma16(acc0, frag_load(A0 + ra + 16 * s), fb);
-    mma16(acc1, frag_load(A1 + ra + 16 * s), fb);
+    if (s + kAhead < NK) {
+      const int t = s + kAhead;
+      fb[t] = frag_load(pb + 16 * t);
+      f0[t] = frag_load(A0 + ra + 16 * t);
+      f1[t] = frag_load(A1 + ra + 16 * t);
+    }
+    sched_fence();
+    mma16(acc0, f0[s], fb[s]);
+    mma16(acc1, f1[s], fb[s]);
+    sched_fence();
   }
 }
 
@@ -107,10 +133,27 @@ template <int NK, typename E>
 __device__ inline void tile_nt2_pairs(f32x16& acc0, f32x16& acc1, const E* A0, const E* B0,
                                       const E* A1, const E* B1, int ld, int lane) {
   const int ro = (lane & 31) * ld + (lane >> 5) * 8;
+  Frag<E> a0[NK], b0[NK], a1[NK], b1[NK];
+#pragma unroll
+  for (int s = 0; s < kAhead && s < NK; ++s) {
+    a0[s] = frag_load(A0 + ro + 16 * s);
+    b0[s] = frag_load(B0 + ro + 16 * s);
+    a1[s] = frag_load(A1 + ro + 16 * s);
+    b1[s] = frag_load(B1 + ro + 16 * s);
+  }
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
-    mma16(acc0, frag_load(A0 + ro + 16 * s), frag_load(B0 + ro + 16 * s));
-    mma16(acc1, frag_load(A1 + ro + 16 * s), frag_load(B1 + ro + 16 * s));
+    if (s + kAhead < NK) {
+      const int o = ro + 16 * (s + kAhead), t = s + kAhead;
+      a0[t] = frag_load(A0 + o);
+      b0[t] = frag_load(B0 + o);
+      a1[t] = frag_load(A1 + o);
+      b1[t] = frag_load(B1 + o);
+    }
+    sched_fence();
+    mma16(acc0, a0[s], b0[s]);
+    mma16(acc1, a1[s], b1[s]);
+    sched_fence();
   }
 }
 
@@ -122,12 +165,30 @@ __device__ inline void tile_nt3(f32x16& x, f32x16& o, f32x16& p, const E* Ax, co
                                 const E* B, const E* Pa, const E* Pb, int lda, int ldb, int lane) {
   const int ra = (lane & 31) * lda + (lane >> 5) * 8;
   const int rb = (lane & 31) * ldb + (lane >> 5) * 8;
+  Frag<E> fb[NK], fx[NK], fo[NK], fpa[NK], fpb[NK];
+#pragma unroll
+  for (int s = 0; s < kAhead && s < NK; ++s) {
+    fb[s] = frag_load(B + rb + 16 * s);
+    fx[s] = frag_load(Ax + ra + 16 * s);
+    fo[s] = frag_load(Ao + ra + 16 * s);
+    fpa[s] = frag_load(Pa + ra + 16 * s);
+    fpb[s] = frag_load(Pb + ra + 16 * s);
+  }
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
-    const Frag<E> fb = frag_load(B + rb + 16 * s);
-    mma16(x, frag_load(Ax + ra + 16 * s), fb);
-    mma16(p, frag_load(Pa + ra + 16 * s), frag_load(Pb + ra + 16 * s));
-    mma16(o, frag_load(Ao + ra + 16 * s), fb);
+    if (s + kAhead < NK) {
+      const int t = s + kAhead, oa = ra + 16 * t;
+      fb[t] = frag_load(B + rb + 16 * t);
+      fx[t] = frag_load(Ax + oa);
+      fo[t] = frag_load(Ao + oa);
+      fpa[t] = frag_load(Pa + oa);
+      fpb[t] = frag_load(Pb + oa);
+    }
+    sched_fence();
+    mma16(x, fx[s], fb[s]);
+    mma16(p, fpa[s], fpb[s]);
+    mma16(o, fo[s], fb[s]);
+    sched_fence();
   }
 }
 
