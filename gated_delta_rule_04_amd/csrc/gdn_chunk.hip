@@ -116,8 +116,8 @@ struct SolveLd {
 };
 
 template <typename E>
-__device__ inline void tri_solve(const float* Am, float* Li, float* Mt, const float* Bt, E* Tm,
-                                 int tid) {
+__device__ __attribute__((always_inline)) inline void tri_solve(const float* Am, float* Li, float* Mt,
+                                                                const float* Bt, E* Tm, int tid) {
   constexpr int LDA = SolveLd<E>::LDA, LDT = SolveLd<E>::LDT, LDM = SolveLd<E>::LDM;
   const int lane = tid & 63, wave = tid >> 6;
   // (a) inverse of each unit-lower 16x16 diagonal block: wave w owns block w;
@@ -217,7 +217,8 @@ __device__ inline void tri_solve(const float* Am, float* Li, float* Mt, const fl
 // ---------------------------------------------------------------------------
 // Neither depends on the state, so both leave the sequential kernel.
 // LDS: K rows [64][LDK] (then L^-1 fp32 [64][LDA]), Q rows [64][LDK] (then A
-// fp32 [64][LDA], then T [64][LDT]), P [64][LDT], Mt fp32 [32][LDM], G, beta.
+// fp32 [64][LDA], then T [64][LDT]), Mt fp32 [32][LDM], G, beta.  P goes to
+// the record straight from the accumulators.
 template <typename E, int DK>
 struct PrepPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
@@ -228,8 +229,7 @@ struct PrepPlan {
   static constexpr size_t es = sizeof(E);
   static constexpr size_t kr = 0;   // also L^-1
   static constexpr size_t am = cmax((size_t)C * LDK * es, (size_t)C * LDA * 4);   // Q, then A, then T
-  static constexpr size_t pm = am + cmax((size_t)C * LDK * es, cmax((size_t)C * LDA * 4, (size_t)C * LDT * es));
-  static constexpr size_t mt = pm + (size_t)C * LDT * es;
+  static constexpr size_t mt = am + cmax((size_t)C * LDK * es, cmax((size_t)C * LDA * 4, (size_t)C * LDT * es));
   static constexpr size_t g = mt + (size_t)32 * LDM * 4;
   static constexpr size_t total = g + 2 * C * 4;
 };
@@ -249,7 +249,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   E* Qr = reinterpret_cast<E*>(smem + L::am);
   float* Am = reinterpret_cast<float*>(smem + L::am);
   E* Tm = reinterpret_cast<E*>(smem + L::am);
-  E* Pm = reinterpret_cast<E*>(smem + L::pm);
   float* Mt = reinterpret_cast<float*>(smem + L::mt);
   float* G = reinterpret_cast<float*>(smem + L::g);
   float* Bt = G + C;
@@ -262,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   const int t0 = n * C, cn = min(C, T - t0);
   const size_t tok0 = (size_t)b * T + t0;   // first token of the chunk in [B, T]
   E* rec = tws + (size_t)blockIdx.x * R::elems;
+  E* Pw = rec + R::p;
 
   // K and Q rows (rows past the sequence end repeat its last row: beta = 0
   // there, so they never reach A or T, and P's rows of them are never used)
@@ -322,25 +322,23 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
         y[e] = (j0 + e <= r) ? w * accp[4 * g + e] : 0.f;
       }
       store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
-      store4(Pm + r * LDT + j0, y[0], y[1], y[2], y[3]);
+      store4(Pw + r * C + j0, y[0], y[1], y[2], y[3]);
     }
   } else {   // P rows 0..31, columns 32..63 are zero
     const int q = tid - 192, r = q >> 1, j0 = 32 + 16 * (q & 1);
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) store4(Pm + r * LDT + j0 + e, 0.f, 0.f, 0.f, 0.f);
+    for (int e = 0; e < 16; e += 4) store4(Pw + r * C + j0 + e, 0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
   tri_solve<E>(Am, Li, Mt, Bt, Tm, tid);
-  // T and P -> the record, 64 x 64 contiguous each, 16-byte stores
+  // T -> the record, 64 x 64 contiguous, 16-byte stores
   {
     constexpr int CPT = C / EPC;
     for (int q = tid; q < C * CPT; q += kThreads) {
       const int r = q / CPT, cc = q % CPT;
       *reinterpret_cast<u32x4*>(rec + R::t + r * C + cc * EPC) =
           *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC);
-      *reinterpret_cast<u32x4*>(rec + R::p + r * C + cc * EPC) =
-          *reinterpret_cast<const u32x4*>(Pm + r * LDT + cc * EPC);
     }
   }
 }
@@ -1252,7 +1250,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
 
     u32x4 pk[KBT][4], pq[KBT][4], pv[VBT][4], pkc[KDA ? KBT : 1][4];   // rows of a chunk
-    u32x4 pt[TBT], pp[TBT], pg;                                         // T, P, gates of a chunk
+    u32x4 pt[TBT], pp[TBT], pg = u32x4{0u, 0u, 0u, 0u};                // T, P, gates of a chunk
 
     // Loads are unconditional; rows past the sequence end re-read its last
     // row (T's rows and columns of those tokens are zero).
@@ -1294,12 +1292,13 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
 #pragma unroll
       for (int m = 0; m < VBT; ++m) {
         const int blk = ptid + PT * m;
-        const int bq = blk < NVB ? blk : 0;
-        const int rb4 = blk_row(bq, CPV), cc = blk_col(bq, CPV);
+        if (blk < NVB) {   // whole waves (NVB is a multiple of 64)
+          const int rb4 = blk_row(blk, CPV), cc = blk_col(blk, CPV);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)v_tok + cc * EPC;
-          pv[m][rr] = *reinterpret_cast<const u32x4*>(vq + off);
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)v_tok + cc * EPC;
+            pv[m][rr] = *reinterpret_cast<const u32x4*>(vq + off);
+          }
         }
       }
     };
@@ -1310,7 +1309,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         pt[m] = *reinterpret_cast<const u32x4*>(rq + R::t + (ptid + PT * m) * EPC);
         pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (ptid + PT * m) * EPC);
       }
-      pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(ptid, NG4 - 1));
+      if (ptid < NG4) pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * ptid);
     };
     // K and Q rows, V^T and K^T (buffer kb) of a chunk.
     auto commit_rows = [&](int kb) __attribute__((always_inline)) {
