@@ -1,10 +1,11 @@
-// Chunked prefill of the gated delta rule (DeltaNet and Gated DeltaNet decay).
+// Chunked prefill of the gated delta rule: DeltaNet, Gated DeltaNet (scalar
+// decay) and Kimi Delta Attention (per-channel decay).
 //
-// The token recurrence ("Linear Attention Architectures" notes, sections 2.3-2.4,
-// Eqs. 9-10 and 15-17; state d_v x d_k as in the "On State Reduction" notes,
-// section 2.1) is rewritten per chunk of C = 64 tokens.  With G_r the running sum
-// of log alpha inside the chunk (gamma_r = exp(G_r)), entry state S_n and the
-// chunk's row-stacked K, Q, V:
+// The token recurrence ("Linear Attention Architectures" notes, sections 2.3-2.5,
+// Eqs. 9-10, 15-17 and 18-20; state d_v x d_k as in the "On State Reduction"
+// notes, section 2.1) is rewritten per chunk of C = 64 tokens.  With G_r the
+// running sum of log alpha inside the chunk (gamma_r = exp(G_r)), entry state
+// S_n and the chunk's row-stacked K, Q, V:
 //
 //   A[r][j] = beta_r exp(G_r - G_j) (k_r . k_j)      j < r     decay-weighted beta K K^T
 //   T       = (I + A)^-1 diag(beta)                            unit-lower-triangular solve
@@ -18,31 +19,29 @@
 // (gamma_r / gamma_j) u_j k_j^T; putting it into u_r = beta_r (v_r - S_{r-1}
 // alpha_r k_r) gives (I + A) U = diag(beta) X.  The pseudo-value name u_t is the
 // state-reduction notes' (section 2.2); the NextTransformer page names the
-// triangular inverse of its chunked kernel in its numerics section.)
+// triangular inverse of its chunked kernel in its numerics section.  With
+// per-channel decay the exponentials are per key channel; see chunk_prep_kda.)
 //
-// A and T depend only on the chunk's keys and gates, never on the state, so
-// they are computed by a first, fully parallel kernel (one workgroup per chunk
-// of every head, several workgroups per compute unit) and handed to the
-// sequential kernel through a workspace: T in the operand dtype, 64 x 64 per
-// chunk.  The sequential kernel then only carries the state chain
-// X -> U -> (O, S) per chunk.
+// A, T and P depend only on the chunk's keys, queries and gates, never on the
+// state, so a first, fully parallel kernel (one workgroup per chunk of every
+// head) computes them and hands them to the sequential kernel through a
+// workspace record per chunk.  The sequential kernel then only carries the
+// state chain X -> U -> (O, S) per chunk.
 //
-// chunk_prep_kernel  (grid B * H * N_chunks)
-//   K tile and gates -> A (MFMA) -> 16x16 diagonal inverses (quad-DPP forward
-//   substitution) -> two levels of fp32 MFMA block products -> T -> workspace.
-// chunk_state_kernel (grid B * H * d_v / DVS, chunks in order)
-//   One workgroup of four waves owns one (b, h, d_v slice); value rows are
-//   independent ("On State Reduction" notes, section 2.5).  The fp32 state slice
-//   lives in MFMA accumulator registers for the whole sequence, with a copy in
-//   the operand dtype in LDS for the next chunk's K S^T and Q S^T.  The next
-//   chunk's q, k, v, T and gates are loaded into registers while the current
-//   chunk computes.  Per chunk:
-//     commit   prefetched registers -> LDS (K rows, K^T, Q rows, V^T, T, gates),
-//              previous chunk's staged O -> HBM
-//     phase 1  P tiles, X and diag(gamma) Q S^T tiles
-//     phase 4  U = T X
-//     phase 5  O = diag(gamma) Q S^T + P U, staged in LDS
-//     phase 6  S^T <- gamma_C S^T + K^T (diag(exp(G_C - G)) U)
+// chunk_prep_kernel  (none / scalar decay; grid B * H * N_chunks)
+//   K, Q tiles and gates -> A and P (MFMA) -> 16x16 diagonal inverses
+//   (quad-DPP forward substitution) -> two levels of fp32 MFMA block products
+//   -> T; T, P and the gate rows -> record.
+// chunk_prep_kda     (per-channel decay; grid B * H * N_chunks)
+//   per-channel prefix of log alpha -> anchor-split decay factors -> A and P
+//   (MFMA) -> T; T, P, the decay-scaled K / Q operands and exp(G_C) -> record.
+// chunk_state_ws     (bf16; grid B * H * d_v / DVS, chunks in order)
+//   Four chain waves carry the fp32 state slice in MFMA accumulators; four
+//   data waves stream the chunks into LDS and the outputs back out.  Value
+//   rows are independent ("On State Reduction" notes, section 2.5), so each
+//   workgroup owns one (b, h, d_v slice).
+// chunk_state_kernel (fp32; the same phases with four waves that also move
+//   the data themselves)
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
