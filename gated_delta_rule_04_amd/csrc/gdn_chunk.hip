@@ -63,6 +63,16 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 __device__ inline int blk_row(int blk, int cpr) { return (blk & 3) + 4 * (blk / (4 * cpr)); }
 __device__ inline int blk_col(int blk, int cpr) { return (blk >> 2) % cpr; }
 
+// 16-byte loads and stores of data touched once per kernel (inputs read once,
+// workspace and outputs written once): non-temporal, so they do not displace
+// the lines other workgroups still reuse.
+__device__ inline u32x4 ld_once(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+__device__ inline void st_once(void* p, const u32x4& v) {
+  __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+}
+
 // Workspace: one record per chunk of every head (chunk index = head *
 // N_chunks + n).  Scalar or no decay, offsets in elements of the operand dtype:
 //   T [C][C], P [C][C] (row-major), then the gate rows, 3 x C fp32:
@@ -274,8 +284,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
       for (int rr = 0; rr < 4; ++rr) {
         const int r = 4 * rg + rr;
         const size_t off = (size_t)min(r, cn - 1) * ktok + cc * EPC;
-        *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = *reinterpret_cast<const u32x4*>(kg + off);
-        *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = *reinterpret_cast<const u32x4*>(qg + off);
+        *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = ld_once(kg + off);
+        *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = ld_once(qg + off);
       }
     }
   }
@@ -336,8 +346,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     constexpr int CPT = C / EPC;
     for (int q = tid; q < C * CPT; q += kThreads) {
       const int r = q / CPT, cc = q % CPT;
-      *reinterpret_cast<u32x4*>(rec + R::t + r * C + cc * EPC) =
-          *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC);
+      st_once(rec + R::t + r * C + cc * EPC, *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC));
     }
   }
 }
@@ -512,8 +521,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
     for (int m = 0; m < 2 * IPT; ++m) {
       const int it = tid + kThreads * m;
       const uint32_t off = (uint32_t)min(it / CPR, cn - 1) * (uint32_t)qk_tok + (it % CPR) * EPC;
-      kreg[m] = *reinterpret_cast<const u32x4*>(kgl + off);
-      qreg[m] = *reinterpret_cast<const u32x4*>(qgl + off);
+      kreg[m] = ld_once(kgl + off);
+      qreg[m] = ld_once(qgl + off);
     }
 #pragma unroll
     for (int i = 0; i < RPS; ++i) {
@@ -589,9 +598,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
           z[e] = kf[e] * __expf(gl[e] - gr[e]);
         }
         const size_t ro = (size_t)r * DK + c0;
-        *reinterpret_cast<u32x4*>(rec + R::kg + ro) = pack16<E>(x);
-        *reinterpret_cast<u32x4*>(rec + R::qg + ro) = pack16<E>(y);
-        *reinterpret_cast<u32x4*>(rec + R::kc + ro) = pack16<E>(z);
+        st_once(rec + R::kg + ro, pack16<E>(x));
+        st_once(rec + R::qg + ro, pack16<E>(y));
+        st_once(rec + R::kc + ro, pack16<E>(z));
       }
       const int lr = r & 31;
       // diagonal blocks: channels outside the split take zero operands
@@ -684,10 +693,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
     constexpr int CPT = C / EPC;
     for (int q = tid; q < C * CPT; q += kThreads) {
       const int r = q / CPT, cc = q % CPT;
-      *reinterpret_cast<u32x4*>(rec + R::t + r * C + cc * EPC) =
-          *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC);
-      *reinterpret_cast<u32x4*>(rec + R::p + r * C + cc * EPC) =
-          *reinterpret_cast<const u32x4*>(Pm + r * LDT + cc * EPC);
+      st_once(rec + R::t + r * C + cc * EPC, *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC));
+      st_once(rec + R::p + r * C + cc * EPC, *reinterpret_cast<const u32x4*>(Pm + r * LDT + cc * EPC));
     }
   }
 }
@@ -906,7 +913,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const uint32_t off = (uint32_t)min(4 * rg + rr, rmax) * (uint32_t)v_tok + cc * EPC;
-        pv[m][rr] = *reinterpret_cast<const u32x4*>(vq + off);
+        pv[m][rr] = ld_once(vq + off);
       }
     }
     {
@@ -966,8 +973,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     for (int q = tid; q < C * CPO; q += kThreads) {
       const int r = q / CPO, cc = q % CPO;
       if (r < cnf)
-        *reinterpret_cast<u32x4*>(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC) =
-            *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC);
+        st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC));
     }
   };
 
@@ -1296,7 +1302,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)v_tok + cc * EPC;
-            pv[m][rr] = *reinterpret_cast<const u32x4*>(vq + off);
+            pv[m][rr] = ld_once(vq + off);
           }
         }
       }
@@ -1362,8 +1368,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       for (int q = ptid; q < C * CPO; q += PT) {
         const int r = q / CPO, cc = q % CPO;
         if (r < cnf)
-          *reinterpret_cast<u32x4*>(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC) =
-              *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC);
+          st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC));
       }
     };
 
