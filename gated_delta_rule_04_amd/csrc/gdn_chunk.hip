@@ -58,8 +58,10 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 // 16-byte chunk.  Block blk of a tile with cpr chunks per row covers rows
 // 4 blk_row .. 4 blk_row + 3 and chunk blk_col.  Four consecutive blocks take
 // four row groups of one chunk, the next four the next chunk: a wave's global
-// loads cover whole rows, its row-major 16-byte LDS writes hit distinct banks,
-// and its transposed 8-byte writes collide at most two-way.
+// loads cover whole rows and its row-major 16-byte LDS writes hit distinct
+// banks.  (Its transposed 8-byte writes of K^T and V^T do collide: rows 8
+// chunks apart share banks.  Measured: remapping a wave to all row groups of
+// four chunks removes that but costs more on the global side.)
 __device__ inline int blk_row(int blk, int cpr) { return (blk & 3) + 4 * (blk / (4 * cpr)); }
 __device__ inline int blk_col(int blk, int cpr) { return (blk >> 2) % cpr; }
 
@@ -1144,21 +1146,29 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 // ---------------------------------------------------------------------------
 // chunk_state_ws: the sequential pass in bf16 with eight waves.
 // ---------------------------------------------------------------------------
-// Waves 0-3 carry the state chain (phases 1, 4, 5 and 6 of chunk_state_kernel,
-// same tile ownership).  Waves 4-7 move data: while the chain works on chunk
-// n they load later chunks from HBM into registers and write each LDS buffer
-// in an interval in which nobody reads it, and they write the staged O rows
-// out.  Issuing the loads costs the compute unit about 40 bytes per clock;
-// here it runs beside the MFMA chain instead of inside it.  Per chunk there
-// are three barriers.  Between them:
-//   interval  waves 0-3                 waves 4-7
-//   I1        phase 1: X, O_inter       P(n); O(n-1) -> HBM; load T, P, gates of n+1
-//   I4        phase 4: U = T X          K, Q rows, V^T, K^T of n+1
-//   I6        phases 5, 6: O and S      T and gates of n+1; load K, Q, V of n+2
-// K^T and the gate rows are double-buffered (K^T of n+1 is written while
-// phase 6 of n has yet to read K^T of n; the gate rows are read in every
-// interval); O has a staging buffer of its own.  The two roles run separate
-// loops with the same barrier count, so their registers do not add up.
+// Waves 0-3 carry the state chain; waves 4-7 move data: while the chain works
+// on chunk n they load later chunks from HBM into registers, write each LDS
+// buffer in an interval in which nobody reads it, and write the staged O rows
+// out.  (Issuing the loads costs the compute unit about 40 bytes per clock;
+// here it runs beside the MFMA chain instead of inside it.)
+//
+// The chain wave of row block rb and value block ib computes the X and O_inter
+// tiles (rb, ib) in phase 1.  After one barrier every chain wave computes U for
+// the value block of its state tiles, both row blocks, and keeps it in
+// registers: a 32x32 accumulator tile is the B operand of the next product as
+// it stands (frag_acc, with the A operand read in the matching k order by
+// frag_perm), so P U and the state update take U and the decay-weighted U
+// straight from the accumulators.  Two barriers per chunk:
+//   interval  chain waves                          data waves
+//   A         phase 1: X, O_inter (X^T -> LDS)     T, P of n; O(n-1) -> HBM;
+//                                                  load K, Q, V, gates of n+1
+//   B         U = T X; O += P U (staged);          K, Q rows, V^T, K^T, gates
+//             S^T <- decay S^T + K^T Uw            of n+1; load T, P of n+1
+// K^T and the gate rows are double-buffered (K^T of n+1 is written while the
+// chain reads K^T of n; the gates are read in both intervals); O has a staging
+// buffer of its own.  The chain issues all LDS fragment loads of interval B
+// before its first MFMA there.  The two roles run separate loops with the
+// same barrier count, so their registers do not add up.
 template <typename E, int DK, int DVS>
 struct WsPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
@@ -1169,16 +1179,14 @@ struct WsPlan {
   static constexpr size_t es = sizeof(E);
   static constexpr size_t kr = 0;
   static constexpr size_t qr = kr + (size_t)C * LDK * es;
-  static constexpr size_t kt = qr + (size_t)C * LDK * es;         // two buffers
+  static constexpr size_t kt = qr + (size_t)C * LDK * es;          // two buffers
   static constexpr size_t sb = kt + 2 * (size_t)DK * LDT * es;
   static constexpr size_t vt = sb + (size_t)DVS * LDSB * es;
   static constexpr size_t xt = vt + (size_t)DVS * LDT * es;
   static constexpr size_t os = xt + (size_t)DVS * LDT * es;
   static constexpr size_t pm = os + (size_t)C * OST * es;
   static constexpr size_t tm = pm + (size_t)C * LDT * es;
-  static constexpr size_t ut = tm + (size_t)C * LDT * es;
-  static constexpr size_t uw = ut + (size_t)DVS * LDT * es;
-  static constexpr size_t g = uw + (size_t)DVS * LDT * es;       // two buffers
+  static constexpr size_t g = tm + (size_t)C * LDT * es;   // two buffers
   static constexpr size_t total = g + 2 * kGateFloats * 4;
 };
 
@@ -1186,6 +1194,7 @@ constexpr int kWsThreads = 512;
 
 template <typename E, int DK, int DVS, int MODE>
 __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws) {
+  static_assert(sizeof(E) == 2, "the eight-wave kernel is bf16");
   using L = WsPlan<E, DK, DVS>;
   static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
   constexpr bool KDA = MODE == 2;
@@ -1194,7 +1203,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   constexpr int NC = DK / 32;        // 32-wide key blocks
   constexpr int NT = NC * NI;        // state tiles
   constexpr int NST = (NT + 3) / 4;  // state tiles per chain wave
-  constexpr int EPC = 16 / (int)sizeof(E);
+  constexpr int EPC = 8;
   constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB, OST = L::OST;
   // data-wave geometry (256 threads): blocks of 4 rows x one 16-byte chunk
   constexpr int PT = 256;
@@ -1211,19 +1220,17 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
   E* Kr = reinterpret_cast<E*>(smem + L::kr);
   E* Qr = reinterpret_cast<E*>(smem + L::qr);
-  E* Ktb = reinterpret_cast<E*>(smem + L::kt);          // two K^T buffers, DK * LDT apart
+  E* Ktb = reinterpret_cast<E*>(smem + L::kt);   // two K^T buffers, DK * LDT apart
   E* Sb = reinterpret_cast<E*>(smem + L::sb);
   E* Vt = reinterpret_cast<E*>(smem + L::vt);
   E* Xt = reinterpret_cast<E*>(smem + L::xt);
   E* Os = reinterpret_cast<E*>(smem + L::os);
   E* Pm = reinterpret_cast<E*>(smem + L::pm);
   E* Tm = reinterpret_cast<E*>(smem + L::tm);
-  E* Ut = reinterpret_cast<E*>(smem + L::ut);
-  E* Uw = reinterpret_cast<E*>(smem + L::uw);
   float* Gbuf = reinterpret_cast<float*>(smem + L::g);  // two gate blocks (or gC rows)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31;
+  const int col = lane & 31, hh = lane >> 5;
   const int H = a.H, T = a.T, dv = a.dv;
   const int nsl = dv / DVS;
   const int nheads = a.B * H;
@@ -1255,15 +1262,16 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
 
     u32x4 pk[KBT][4], pq[KBT][4], pv[VBT][4], pkc[KDA ? KBT : 1][4];   // rows of a chunk
-    u32x4 pt[TBT], pp[TBT], pg = u32x4{0u, 0u, 0u, 0u};                // T, P, gates of a chunk
+    u32x4 pg = u32x4{0u, 0u, 0u, 0u};
+    u32x4 pt[TBT], pp[TBT];                                             // T, P of a chunk
 
-    // Loads are unconditional; rows past the sequence end re-read its last
-    // row (T's rows and columns of those tokens are zero).
-    auto load_rows = [&](int n) __attribute__((always_inline)) {
+    // K, Q, V rows and the gates of chunk n (unconditional loads; rows past the
+    // sequence end re-read its last row, whose T rows and columns are zero).
+    auto load_a = [&](int n) __attribute__((always_inline)) {
       const int t0 = n * C;
       const int rmax = min(C, T - t0) - 1;
+      const E* rq = recs + (size_t)n * R::elems;
       if constexpr (KDA) {
-        const E* rq = recs + (size_t)n * R::elems;
 #pragma unroll
         for (int m = 0; m < KBT; ++m) {
           const int blk = ptid + PT * m;
@@ -1306,19 +1314,20 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
           }
         }
       }
+      if (ptid < NG4) pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * ptid);
     };
-    auto load_tp = [&](int n) __attribute__((always_inline)) {
+    auto load_b = [&](int n) __attribute__((always_inline)) {
       const E* rq = recs + (size_t)n * R::elems;
 #pragma unroll
       for (int m = 0; m < TBT; ++m) {
         pt[m] = *reinterpret_cast<const u32x4*>(rq + R::t + (ptid + PT * m) * EPC);
         pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (ptid + PT * m) * EPC);
       }
-      if (ptid < NG4) pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * ptid);
     };
-    // K and Q rows, V^T and K^T (buffer kb) of a chunk.
-    auto commit_rows = [&](int kb) __attribute__((always_inline)) {
-      E* Kt = Ktb + kb * DK * LDT;
+    // Rows of a chunk: K and Q rows, V^T, the gates and K^T (from the K rows,
+    // or the decay-scaled Kc rows), into buffers gb of the gates and K^T.
+    auto commit_a = [&](int gb) __attribute__((always_inline)) {
+      E* Kt = Ktb + gb * DK * LDT;
 #pragma unroll
       for (int m = 0; m < KBT; ++m) {
         const int blk = ptid + PT * m;
@@ -1345,21 +1354,16 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
             store_col4(Vt + (cc * EPC + e) * LDT + 4 * rb4, pv[m][0], pv[m][1], pv[m][2], pv[m][3], e);
         }
       }
+      if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * kGateFloats + 4 * ptid) = pg;
     };
-    auto commit_p = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int m = 0; m < TBT; ++m) {
-        const int q = ptid + PT * m, r = q / CPT, cc = q % CPT;
-        *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
-      }
-    };
-    auto commit_t = [&](int gb) __attribute__((always_inline)) {
+    // T and P of a chunk.
+    auto commit_b = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int m = 0; m < TBT; ++m) {
         const int q = ptid + PT * m, r = q / CPT, cc = q % CPT;
         *reinterpret_cast<u32x4*>(Tm + r * LDT + cc * EPC) = pt[m];
+        *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
       }
-      if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * kGateFloats + 4 * ptid) = pg;
     };
     // Staged O rows of a chunk -> HBM, 16-byte stores along each row.
     auto flush_o = [&](int t0f, int cnf) __attribute__((always_inline)) {
@@ -1373,28 +1377,20 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     };
 
     if (nchunks > 0) {
-      load_rows(0);
-      load_tp(0);
-      commit_rows(0);
-      commit_p();
-      commit_t(0);
-      load_rows(min(1, nchunks - 1));
+      load_a(0);
+      load_b(0);
+      commit_a(0);
     }
     __syncthreads();
     for (int n = 0; n < nchunks; ++n) {
-      // I1
-      if (n > 0) {
-        commit_p();                 // P(n), loaded during chunk n - 1
-        flush_o((n - 1) * C, C);
-      }
-      load_tp(min(n + 1, nchunks - 1));
+      // interval A: the chain runs phase 1 of chunk n
+      commit_b();                    // T, P of chunk n
+      if (n > 0) flush_o((n - 1) * C, C);
+      load_a(min(n + 1, nchunks - 1));
       __syncthreads();
-      // I4
-      if (n + 1 < nchunks) commit_rows((n + 1) & 1);
-      __syncthreads();
-      // I6
-      if (n + 1 < nchunks) commit_t((n + 1) & 1);
-      load_rows(min(n + 2, nchunks - 1));
+      // interval B: the chain runs U, O and S of chunk n
+      if (n + 1 < nchunks) commit_a((n + 1) & 1);
+      load_b(min(n + 1, nchunks - 1));
       __syncthreads();
     }
     if (nchunks > 0) flush_o((nchunks - 1) * C, T - (nchunks - 1) * C);
@@ -1402,8 +1398,8 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   }
 
   // ======================= chain waves =======================
-  // X, O_inter (phase 1), U (phase 4) and O (phase 5) tiles of row block own_rb
-  // and value block own_ib belong to one wave.
+  // X and O tiles of row block own_rb and value block own_ib belong to one
+  // wave; its state tiles t = wave + 4 st all lie in value block ub.
   int own_rb = -1, own_ib = 0;
   if (NI == 2) {
     own_rb = wave >> 1;
@@ -1411,6 +1407,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   } else if (wave < 2) {
     own_rb = wave;
   }
+  const int ub = NI == 2 ? (wave & 1) : 0;
 
   f32x16 Sacc[NST];
 #pragma unroll
@@ -1440,7 +1437,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     const float* Ec = G + 2 * C;
     const E* Kt = Ktb + (n & 1) * DK * LDT;
 
-    // ---- I1, phase 1: X and O_inter tiles (they share the S operand) ----
+    // ---- interval A, phase 1: X = V - diag(gamma) K S^T, O_inter = diag(gamma) Q S^T ----
     f32x16 xacc = zero16(), oacc = zero16();
     if (own_rb >= 0) {
       tile_nt2_shared_b<DK / 16>(xacc, oacc, Kr + own_rb * 32 * LDK, Qr + own_rb * 32 * LDK, LDK,
@@ -1461,29 +1458,77 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     }
     __syncthreads();
 
-    // ---- I4, phase 4: U = T X; U^T and the decay-weighted copy for the state ----
-    if (own_rb >= 0) {
-      f32x16 uacc = zero16();
-      if (own_rb == 0) tile_nt_k<2>(uacc, Tm, LDT, Xt + own_ib * 32 * LDT, LDT, lane);
-      else tile_nt_k<4>(uacc, Tm + 32 * LDT, LDT, Xt + own_ib * 32 * LDT, LDT, lane);
-      const int i = own_ib * 32 + col;
+    // ---- interval B: every LDS fragment of the interval first ----
+    Frag<E> ta0[2], ta1[4], xb[4];   // T rows 0..31 (k < 32), T rows 32..63, X^T of block ub
+    {
+      const int ko = (lane >> 5) * 8;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = own_rb * 32 + acc_row(g, 0, lane);
-        store4(Ut + i * LDT + r0, uacc[4 * g], uacc[4 * g + 1], uacc[4 * g + 2], uacc[4 * g + 3]);
-        if constexpr (!KDA) {
-          const float4 ec = *reinterpret_cast<const float4*>(Ec + r0);
-          store4(Uw + i * LDT + r0, uacc[4 * g] * ec.x, uacc[4 * g + 1] * ec.y,
-                 uacc[4 * g + 2] * ec.z, uacc[4 * g + 3] * ec.w);
-        }
+      for (int s = 0; s < 4; ++s) {
+        if (s < 2) ta0[s] = frag_load(Tm + col * LDT + ko + 16 * s);
+        ta1[s] = frag_load(Tm + (32 + col) * LDT + ko + 16 * s);
+        xb[s] = frag_load(Xt + (ub * 32 + col) * LDT + ko + 16 * s);
       }
     }
-    __syncthreads();
-
-    // ---- I6, phase 5: O = O_inter + P U, staged for the data waves ----
+    bf16x8 pa[2][2], ka[NST][2][2];  // P rows of the wave's O tile; K^T rows of its state tiles
     if (own_rb >= 0) {
-      if (own_rb == 0) tile_nt_k<2>(oacc, Pm, LDT, Ut + own_ib * 32 * LDT, LDT, lane);
-      else tile_nt_k<4>(oacc, Pm + 32 * LDT, LDT, Ut + own_ib * 32 * LDT, LDT, lane);
+      const E* prow = Pm + (own_rb * 32 + col) * LDT;
+#pragma unroll
+      for (int rj = 0; rj < 2; ++rj)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) pa[rj][s] = frag_perm(prow, 32 * rj + 16 * s, hh);
+    }
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int cb = min((wave + 4 * st) / NI, NC - 1);
+      const E* ktrow = Kt + (cb * 32 + col) * LDT;
+#pragma unroll
+      for (int rj = 0; rj < 2; ++rj)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ka[st][rj][s] = frag_perm(ktrow, 32 * rj + 16 * s, hh);
+    }
+    sched_fence();
+
+    // U = T X for value block ub, both row blocks, in registers (T is lower
+    // triangular: row block 0 needs k < 32)
+    f32x16 u0 = zero16(), u1 = zero16();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 2) mma16(u0, ta0[s], xb[s]);
+      mma16(u1, ta1[s], xb[s]);
+    }
+    bf16x8 uf[2][2], wf[2][2];   // U and the decay-weighted U as B fragments (k = token)
+    uf[0][0] = frag_acc(u0, 0);
+    uf[0][1] = frag_acc(u0, 1);
+    uf[1][0] = frag_acc(u1, 0);
+    uf[1][1] = frag_acc(u1, 1);
+    if constexpr (KDA) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        wf[q][0] = uf[q][0];
+        wf[q][1] = uf[q][1];
+      }
+    } else {   // rows r times exp(G_C - G_r)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 e0 = *reinterpret_cast<const float4*>(Ec + acc_row(g, 0, lane));
+        const float4 e1 = *reinterpret_cast<const float4*>(Ec + 32 + acc_row(g, 0, lane));
+        u0[4 * g + 0] *= e0.x; u0[4 * g + 1] *= e0.y; u0[4 * g + 2] *= e0.z; u0[4 * g + 3] *= e0.w;
+        u1[4 * g + 0] *= e1.x; u1[4 * g + 1] *= e1.y; u1[4 * g + 2] *= e1.z; u1[4 * g + 3] *= e1.w;
+      }
+      wf[0][0] = frag_acc(u0, 0);
+      wf[0][1] = frag_acc(u0, 1);
+      wf[1][0] = frag_acc(u1, 0);
+      wf[1][1] = frag_acc(u1, 1);
+    }
+
+    // ---- O = O_inter + P U for the wave's tile, staged for the data waves ----
+    if (own_rb >= 0) {
+#pragma unroll
+      for (int rj = 0; rj < 2; ++rj) {
+        if (rj > own_rb) break;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) mma_bf16(oacc, pa[rj][s], uf[rj][s]);
+      }
       const int i = own_ib * 32 + col;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
@@ -1491,56 +1536,37 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         for (int e = 0; e < 4; ++e)
           Os[(own_rb * 32 + acc_row(g, e, lane)) * OST + i] = to_elem<E>(oacc[4 * g + e]);
     }
-    // ---- phase 6: S^T <- gamma_C S^T + K^T Uw (per-channel: Diag(gC) S^T + Kc^T U) ----
-    {
+
+    // ---- S^T <- gamma_C S^T + K^T Uw (per-channel: Diag(gC) S^T + Kc^T U), refresh Sb ----
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int t = wave + 4 * st;
+      if (t >= NT) continue;
+      const int cb = t / NI;
       if constexpr (KDA) {
 #pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          const int cb = (wave + 4 * st) / NI;
-          if (cb < NC) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const float4 d = *reinterpret_cast<const float4*>(G + cb * 32 + acc_row(g, 0, lane));
-              Sacc[st][4 * g + 0] *= d.x;
-              Sacc[st][4 * g + 1] *= d.y;
-              Sacc[st][4 * g + 2] *= d.z;
-              Sacc[st][4 * g + 3] *= d.w;
-            }
-          }
+        for (int g = 0; g < 4; ++g) {
+          const float4 d = *reinterpret_cast<const float4*>(G + cb * 32 + acc_row(g, 0, lane));
+          Sacc[st][4 * g + 0] *= d.x;
+          Sacc[st][4 * g + 1] *= d.y;
+          Sacc[st][4 * g + 2] *= d.z;
+          Sacc[st][4 * g + 3] *= d.w;
         }
       } else {
         const float gC = Eg[C - 1];
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
-      }
-      const E* Ub = KDA ? Ut : Uw;
-      if (NST == 2 && wave + 4 < NT) {
-        tile_nt2_shared_b<C / 16>(Sacc[0], Sacc[NST - 1], Kt + (wave / NI) * 32 * LDT,
-                                  Kt + ((wave + 4) / NI) * 32 * LDT, LDT,
-                                  Ub + (wave % NI) * 32 * LDT, LDT, lane);
-      } else {
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          const int t = wave + 4 * st;
-          if (t < NT)
-            tile_nt_k<C / 16>(Sacc[st], Kt + (t / NI) * 32 * LDT, LDT, Ub + (t % NI) * 32 * LDT,
-                              LDT, lane);
-        }
+        for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
       }
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int t = wave + 4 * st;
-        if (t < NT) {
-          const int cb = t / NI, ib = t % NI, i = ib * 32 + col;
+      for (int rj = 0; rj < 2; ++rj)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int c0 = cb * 32 + acc_row(g, 0, lane);
-            store4(Sb + i * LDSB + c0, Sacc[st][4 * g], Sacc[st][4 * g + 1], Sacc[st][4 * g + 2],
-                   Sacc[st][4 * g + 3]);
-          }
-        }
+        for (int s = 0; s < 2; ++s) mma_bf16(Sacc[st], ka[st][rj][s], wf[rj][s]);
+      const int i = ub * 32 + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = cb * 32 + acc_row(g, 0, lane);
+        store4(Sb + i * LDSB + c0, Sacc[st][4 * g], Sacc[st][4 * g + 1], Sacc[st][4 * g + 2],
+               Sacc[st][4 * g + 3]);
       }
     }
     __syncthreads();

@@ -192,6 +192,37 @@ __device__ inline void tile_nt3(f32x16& x, f32x16& o, f32x16& p, const E* Ax, co
   }
 }
 
+// ---- products whose B operand is an accumulator tile (bf16) ----
+// A 32x32 accumulator tile can be the B operand of the next product as it
+// stands: lane l holds rows 8g + 4h + e (g, e = 0..3, h = l / 32) of column
+// l % 32, so the 16-row k step s takes the lane's rows 16s + 4h + 0..3 and
+// 16s + 8 + 4h + 0..3.  The A operand is then read from LDS in that same k
+// order; the sum over k is unchanged.
+
+// A fragment (row-major bf16 row of lane l % 32) for the k step covering
+// k0 .. k0 + 15, in the accumulator's k order.
+__device__ inline bf16x8 frag_perm(const __bf16* row, int k0, int h) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(row + k0 + 4 * h);
+  const uint2 hi = *reinterpret_cast<const uint2*>(row + k0 + 8 + 4 * h);
+  return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+// B fragment for k step s (rows 16s .. 16s + 15) of an fp32 accumulator tile,
+// rounded to bf16.
+__device__ inline bf16x8 frag_acc(const f32x16& acc, int s) {
+  bf16x8 f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = (__bf16)acc[8 * s + j];
+    f[4 + j] = (__bf16)acc[8 * s + 4 + j];
+  }
+  return f;
+}
+
+__device__ inline void mma_bf16(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
 // fp32 16x16 tile step, four k values: lane l supplies A[l % 16][kappa] and
 // B[kappa][l % 16] for one k index kappa of its choice (A and B must agree);
 // accumulator element v of lane l is C[4 (l / 16) + v][l % 16].
