@@ -42,6 +42,8 @@
 //   workgroup owns one (b, h, d_v slice).
 // chunk_state_kernel (fp32; the same phases with four waves that also move
 //   the data themselves)
+#include <type_traits>
+
 #include "gdn_internal.h"
 #include "gdn_mfma.h"
 
@@ -1152,37 +1154,47 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 // out.  (Issuing the loads costs the compute unit about 40 bytes per clock;
 // here it runs beside the MFMA chain instead of inside it.)
 //
-// The chain wave of row block rb and value block ib computes the X and O_inter
-// tiles (rb, ib) in phase 1.  After one barrier every chain wave computes U for
-// the value block of its state tiles, both row blocks, and keeps it in
-// registers: a 32x32 accumulator tile is the B operand of the next product as
-// it stands (frag_acc, with the A operand read in the matching k order by
-// frag_perm), so P U and the state update take U and the decay-weighted U
-// straight from the accumulators.  Two barriers per chunk:
+// Every buffer the data waves fill is row-major, written with 16-byte stores.
+// Where the chain needs a column-wise operand (K^T of the state update, V in
+// the X epilogue) it reads the rows with gfx950's transposed LDS read.
+//
+// The chain wave of row block rb and value block ib computes the X and the
+// O_inter^T tiles (rb, ib) in phase 1 (both from one S fragment, which serves
+// as the B operand of X = K S^T and the A operand of O^T = S Q^T).  After one
+// barrier every chain wave computes U for the value block of its state tiles,
+// both row blocks, and keeps it in registers: a 32x32 accumulator tile is an
+// operand of the next product as it stands (frag_acc, with the other operand
+// read in the matching k order), so O^T += U^T P^T and the state update take U
+// and the decay-weighted U straight from the accumulators.  O is staged
+// transposed-back in LDS with 8-byte stores.  Two barriers per chunk:
 //   interval  chain waves                          data waves
-//   A         phase 1: X, O_inter (X^T -> LDS)     T, P of n; O(n-1) -> HBM;
-//                                                  load K, Q, V, gates of n+1
-//   B         U = T X; O += P U (staged);          K, Q rows, V^T, K^T, gates
-//             S^T <- decay S^T + K^T Uw            of n+1; load T, P of n+1
-// K^T and the gate rows are double-buffered (K^T of n+1 is written while the
-// chain reads K^T of n; the gates are read in both intervals); O has a staging
-// buffer of its own.  The chain issues all LDS fragment loads of interval B
-// before its first MFMA there.  The two roles run separate loops with the
-// same barrier count, so their registers do not add up.
-template <typename E, int DK, int DVS>
+//   A         phase 1: X, O_inter^T (X^T -> LDS)   load K, gates of n+1;
+//                                                  T, P of n; O(n-1) -> HBM
+//   B         U = T X; O^T += U^T P^T (staged);    load T, P of n+1; K, Q, V
+//             S^T <- decay S^T + K^T Uw            rows, gates of n+1; load
+//                                                  Q, V of n+2
+// The rows of the state update's K operand (K, or the decay-scaled Kc) and the
+// gate rows are double-buffered (those of n+1 are written while the chain
+// reads those of n); O has a staging buffer of its own.  The chain issues all
+// LDS fragment loads of interval B before its first MFMA there.  The two roles
+// run separate loops with the same barrier count, so their registers do not
+// add up.
+template <typename E, int DK, int DVS, bool KDA>
 struct WsPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = DK + PAD;
   static constexpr int LDT = C + PAD;
   static constexpr int LDSB = DK + PAD;
+  static constexpr int LDV = DVS + 16;   // 4-row transposed reads fall in distinct banks
   static constexpr int OST = DVS + PAD;
   static constexpr size_t es = sizeof(E);
-  static constexpr size_t kr = 0;
-  static constexpr size_t qr = kr + (size_t)C * LDK * es;
-  static constexpr size_t kt = qr + (size_t)C * LDK * es;          // two buffers
-  static constexpr size_t sb = kt + 2 * (size_t)DK * LDT * es;
-  static constexpr size_t vt = sb + (size_t)DVS * LDSB * es;
-  static constexpr size_t xt = vt + (size_t)DVS * LDT * es;
+  static constexpr size_t rows = (size_t)C * LDK * es;                // one [C][LDK] row buffer
+  static constexpr size_t qr = 0;
+  static constexpr size_t ks = qr + rows;                             // two buffers
+  static constexpr size_t kr = ks + 2 * rows;                         // per-channel only
+  static constexpr size_t sb = kr + (KDA ? rows : 0);
+  static constexpr size_t vr = sb + (size_t)DVS * LDSB * es;
+  static constexpr size_t xt = vr + (size_t)C * LDV * es;
   static constexpr size_t os = xt + (size_t)DVS * LDT * es;
   static constexpr size_t pm = os + (size_t)C * OST * es;
   static constexpr size_t tm = pm + (size_t)C * LDT * es;
@@ -1195,34 +1207,35 @@ constexpr int kWsThreads = 512;
 template <typename E, int DK, int DVS, int MODE>
 __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws) {
   static_assert(sizeof(E) == 2, "the eight-wave kernel is bf16");
-  using L = WsPlan<E, DK, DVS>;
-  static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
   constexpr bool KDA = MODE == 2;
+  using L = WsPlan<E, DK, DVS, KDA>;
+  static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
   using R = typename RecOf<E, DK, MODE>::type;
   constexpr int NI = DVS / 32;       // 32-wide value blocks in the slice
   constexpr int NC = DK / 32;        // 32-wide key blocks
   constexpr int NT = NC * NI;        // state tiles
   constexpr int NST = (NT + 3) / 4;  // state tiles per chain wave
   constexpr int EPC = 8;
-  constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB, OST = L::OST;
-  // data-wave geometry (256 threads): blocks of 4 rows x one 16-byte chunk
+  constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB, LDV = L::LDV, OST = L::OST;
+  // data-wave geometry (256 threads): K / Q rows in blocks of 4 rows x one
+  // 16-byte chunk, V rows and T / P in 16-byte pieces along the rows
   constexpr int PT = 256;
   constexpr int CPR = DK / EPC;
   constexpr int NKB = 16 * CPR;
   constexpr int KBT = (NKB + PT - 1) / PT;
   constexpr int CPV = DVS / EPC;
-  constexpr int NVB = 16 * CPV;
-  constexpr int VBT = (NVB + PT - 1) / PT;
+  constexpr int VPT = C * CPV / PT;
+  static_assert(C * CPV % PT == 0, "V rows must split evenly over the data threads");
   constexpr int CPT = C / EPC;
   constexpr int TBT = C * CPT / PT;
   constexpr int NG4 = (KDA ? DK : (int)kGateFloats) / 4;   // 16-byte chunks of the fp32 rows
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
-  E* Kr = reinterpret_cast<E*>(smem + L::kr);
   E* Qr = reinterpret_cast<E*>(smem + L::qr);
-  E* Ktb = reinterpret_cast<E*>(smem + L::kt);   // two K^T buffers, DK * LDT apart
+  E* Ksb = reinterpret_cast<E*>(smem + L::ks);   // two row buffers, C * LDK apart
+  E* Kr = reinterpret_cast<E*>(smem + L::kr);    // per-channel: the K operand of phase 1
   E* Sb = reinterpret_cast<E*>(smem + L::sb);
-  E* Vt = reinterpret_cast<E*>(smem + L::vt);
+  E* Vr = reinterpret_cast<E*>(smem + L::vr);
   E* Xt = reinterpret_cast<E*>(smem + L::xt);
   E* Os = reinterpret_cast<E*>(smem + L::os);
   E* Pm = reinterpret_cast<E*>(smem + L::pm);
@@ -1261,60 +1274,66 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     const E* recs = tws + (size_t)head * nchunks * R::elems;
     E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
 
-    u32x4 pk[KBT][4], pq[KBT][4], pv[VBT][4], pkc[KDA ? KBT : 1][4];   // rows of a chunk
+    u32x4 pk[KBT][4], pq[KBT][4], pv[VPT], pkc[KDA ? KBT : 1][4];   // rows of a chunk
     u32x4 pg = u32x4{0u, 0u, 0u, 0u};
-    u32x4 pt[TBT], pp[TBT];                                             // T, P of a chunk
+    u32x4 pt[TBT], pp[TBT];                                          // T, P of a chunk
 
-    // K, Q, V rows and the gates of chunk n (unconditional loads; rows past the
-    // sequence end re-read its last row, whose T rows and columns are zero).
-    auto load_a = [&](int n) __attribute__((always_inline)) {
+    // The loads are split in two groups so that both intervals issue about
+    // the same number of bytes: the K operands and the gates of chunk n, and
+    // Q and V of chunk n (issued one chunk earlier).  Every thread issues the
+    // same loads (surplus threads repeat a valid block), so the wait counts
+    // the compiler derives are exact; rows past the sequence end re-read its
+    // last row, whose T rows and columns are zero.
+    auto load_k = [&](int n) __attribute__((always_inline)) {
       const int t0 = n * C;
       const int rmax = min(C, T - t0) - 1;
       const E* rq = recs + (size_t)n * R::elems;
-      if constexpr (KDA) {
+      const E* kq = kg + (size_t)t0 * qk_tok;
 #pragma unroll
-        for (int m = 0; m < KBT; ++m) {
-          const int blk = ptid + PT * m;
-          const int bq = blk < NKB ? blk : 0;
-          const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
+      for (int m = 0; m < KBT; ++m) {
+        const int blk = ptid + PT * m;
+        const int bq = blk < NKB ? blk : 0;
+        const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
+        for (int rr = 0; rr < 4; ++rr) {
+          if constexpr (KDA) {
             const uint32_t off = (uint32_t)(4 * rb4 + rr) * DK + cc * EPC;
             pk[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::kg + off);
-            pq[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::qg + off);
             pkc[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::kc + off);
-          }
-        }
-      } else {
-        const E* kq = kg + (size_t)t0 * qk_tok;
-        const E* qq = qg + (size_t)t0 * qk_tok;
-#pragma unroll
-        for (int m = 0; m < KBT; ++m) {
-          const int blk = ptid + PT * m;
-          const int bq = blk < NKB ? blk : 0;
-          const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
+          } else {
             const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)qk_tok + cc * EPC;
             pk[m][rr] = *reinterpret_cast<const u32x4*>(kq + off);
+          }
+        }
+      }
+      pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(ptid, NG4 - 1));
+    };
+    auto load_qv = [&](int n) __attribute__((always_inline)) {
+      const int t0 = n * C;
+      const int rmax = min(C, T - t0) - 1;
+      const E* rq = recs + (size_t)n * R::elems;
+      const E* qq = qg + (size_t)t0 * qk_tok;
+#pragma unroll
+      for (int m = 0; m < KBT; ++m) {
+        const int blk = ptid + PT * m;
+        const int bq = blk < NKB ? blk : 0;
+        const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          if constexpr (KDA) {
+            pq[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::qg + (uint32_t)(4 * rb4 + rr) * DK + cc * EPC);
+          } else {
+            const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)qk_tok + cc * EPC;
             pq[m][rr] = *reinterpret_cast<const u32x4*>(qq + off);
           }
         }
       }
       const E* vq = vg + (size_t)t0 * v_tok;
 #pragma unroll
-      for (int m = 0; m < VBT; ++m) {
-        const int blk = ptid + PT * m;
-        if (blk < NVB) {   // whole waves (NVB is a multiple of 64)
-          const int rb4 = blk_row(blk, CPV), cc = blk_col(blk, CPV);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)v_tok + cc * EPC;
-            pv[m][rr] = ld_once(vq + off);
-          }
-        }
+      for (int m = 0; m < VPT; ++m) {
+        const int q = ptid + PT * m, r = q / CPV, cc = q % CPV;
+        pv[m] = ld_once(vq + (uint32_t)min(r, rmax) * (uint32_t)v_tok + cc * EPC);
       }
-      if (ptid < NG4) pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * ptid);
     };
     auto load_b = [&](int n) __attribute__((always_inline)) {
       const E* rq = recs + (size_t)n * R::elems;
@@ -1324,10 +1343,10 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (ptid + PT * m) * EPC);
       }
     };
-    // Rows of a chunk: K and Q rows, V^T, the gates and K^T (from the K rows,
-    // or the decay-scaled Kc rows), into buffers gb of the gates and K^T.
+    // Rows of a chunk: Q, the state update's K operand (K, or Kc) into buffer
+    // gb, the per-channel phase-1 K operand, V, and the gates into buffer gb.
     auto commit_a = [&](int gb) __attribute__((always_inline)) {
-      E* Kt = Ktb + gb * DK * LDT;
+      E* Ks = Ksb + gb * C * LDK;
 #pragma unroll
       for (int m = 0; m < KBT; ++m) {
         const int blk = ptid + PT * m;
@@ -1335,24 +1354,17 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
           const int rb4 = blk_row(blk, CPR), cc = blk_col(blk, CPR);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            *reinterpret_cast<u32x4*>(Kr + (4 * rb4 + rr) * LDK + cc * EPC) = pk[m][rr];
-            *reinterpret_cast<u32x4*>(Qr + (4 * rb4 + rr) * LDK + cc * EPC) = pq[m][rr];
+            const int o = (4 * rb4 + rr) * LDK + cc * EPC;
+            *reinterpret_cast<u32x4*>(Qr + o) = pq[m][rr];
+            *reinterpret_cast<u32x4*>(Ks + o) = KDA ? pkc[m][rr] : pk[m][rr];
+            if constexpr (KDA) *reinterpret_cast<u32x4*>(Kr + o) = pk[m][rr];
           }
-          const auto& src = KDA ? pkc[m] : pk[m];
-#pragma unroll
-          for (int e = 0; e < EPC; ++e)
-            store_col4(Kt + (cc * EPC + e) * LDT + 4 * rb4, src[0], src[1], src[2], src[3], e);
         }
       }
 #pragma unroll
-      for (int m = 0; m < VBT; ++m) {
-        const int blk = ptid + PT * m;
-        if (blk < NVB) {
-          const int rb4 = blk_row(blk, CPV), cc = blk_col(blk, CPV);
-#pragma unroll
-          for (int e = 0; e < EPC; ++e)
-            store_col4(Vt + (cc * EPC + e) * LDT + 4 * rb4, pv[m][0], pv[m][1], pv[m][2], pv[m][3], e);
-        }
+      for (int m = 0; m < VPT; ++m) {
+        const int q = ptid + PT * m, r = q / CPV, cc = q % CPV;
+        *reinterpret_cast<u32x4*>(Vr + r * LDV + cc * EPC) = pv[m];
       }
       if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * kGateFloats + 4 * ptid) = pg;
     };
@@ -1365,35 +1377,52 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
       }
     };
-    // Staged O rows of a chunk -> HBM, 16-byte stores along each row.
-    auto flush_o = [&](int t0f, int cnf) __attribute__((always_inline)) {
-      constexpr int CPO = DVS / EPC;
+    // Staged O rows of a whole chunk -> HBM, 16-byte stores along each row.
+    constexpr int CPO = DVS / EPC;
+    static_assert(C * CPO % PT == 0, "O rows must split evenly over the data threads");
+    auto flush_o = [&](int t0f) __attribute__((always_inline)) {
+      E* oq = og + (size_t)t0f * v_tok;
+#pragma unroll
+      for (int m = 0; m < C * CPO / PT; ++m) {
+        const int q = ptid + PT * m, r = q / CPO, cc = q % CPO;
+        st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC));
+      }
+    };
+    // One chunk step.  Loads are issued before the LDS writes of an interval
+    // whose data arrived earlier; the first step (nothing to flush) is peeled
+    // so that no global access in the loop is conditional.
+    auto step = [&](int n, auto first) __attribute__((always_inline)) {
+      // interval A: the chain runs phase 1 of chunk n
+      load_k(min(n + 1, nchunks - 1));
+      commit_b();                    // T, P of chunk n
+      if constexpr (!decltype(first)::value) flush_o((n - 1) * C);
+      __syncthreads();
+      // interval B: the chain runs U, O and S of chunk n
+      load_b(min(n + 1, nchunks - 1));
+      if (n + 1 < nchunks) commit_a((n + 1) & 1);
+      load_qv(min(n + 2, nchunks - 1));
+      __syncthreads();
+    };
+
+    if (nchunks > 0) {
+      load_k(0);
+      load_qv(0);
+      load_b(0);
+      commit_a(0);
+      load_qv(min(1, nchunks - 1));
+    }
+    __syncthreads();
+    if (nchunks > 0) step(0, std::true_type{});
+    for (int n = 1; n < nchunks; ++n) step(n, std::false_type{});
+    if (nchunks > 0) {   // the last chunk's rows
+      const int t0f = (nchunks - 1) * C, cnf = T - t0f;
       E* oq = og + (size_t)t0f * v_tok;
       for (int q = ptid; q < C * CPO; q += PT) {
         const int r = q / CPO, cc = q % CPO;
         if (r < cnf)
           st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC));
       }
-    };
-
-    if (nchunks > 0) {
-      load_a(0);
-      load_b(0);
-      commit_a(0);
     }
-    __syncthreads();
-    for (int n = 0; n < nchunks; ++n) {
-      // interval A: the chain runs phase 1 of chunk n
-      commit_b();                    // T, P of chunk n
-      if (n > 0) flush_o((n - 1) * C, C);
-      load_a(min(n + 1, nchunks - 1));
-      __syncthreads();
-      // interval B: the chain runs U, O and S of chunk n
-      if (n + 1 < nchunks) commit_a((n + 1) & 1);
-      load_b(min(n + 1, nchunks - 1));
-      __syncthreads();
-    }
-    if (nchunks > 0) flush_o((nchunks - 1) * C, T - (nchunks - 1) * C);
     return;
   }
 
@@ -1435,25 +1464,30 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     const float* G = Gbuf + (n & 1) * kGateFloats;
     const float* Eg = G + C;
     const float* Ec = G + 2 * C;
-    const E* Kt = Ktb + (n & 1) * DK * LDT;
+    const E* Ks = Ksb + (n & 1) * C * LDK;
+    const E* K1 = KDA ? Kr : Ks;   // K operand of phase 1
 
-    // ---- interval A, phase 1: X = V - diag(gamma) K S^T, O_inter = diag(gamma) Q S^T ----
+    // ---- interval A, phase 1: X = V - diag(gamma) K S^T, O_inter^T = S (diag(gamma) Q)^T ----
     f32x16 xacc = zero16(), oacc = zero16();
     if (own_rb >= 0) {
-      tile_nt2_shared_b<DK / 16>(xacc, oacc, Kr + own_rb * 32 * LDK, Qr + own_rb * 32 * LDK, LDK,
-                                 Sb + own_ib * 32 * LDSB, LDSB, lane);
+      tile_nt2_shared_b<DK / 16, E, true>(xacc, oacc, K1 + own_rb * 32 * LDK, Qr + own_rb * 32 * LDK, LDK,
+                                          Sb + own_ib * 32 * LDSB, LDSB, lane);
       const int i = own_ib * 32 + col;
+      const int vc = own_ib * 32 + 16 * ((lane >> 4) & 1);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = own_rb * 32 + acc_row(g, 0, lane);
         const float4 eg = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
-        const float4 v4 = load4_elem(Vt + i * LDT + r0);
+        const uint2 vw = tr_read4(Vr, LDV, r0, vc, lane);   // V[r0 .. r0 + 3][i]
+        const float4 v4 = make_float4(__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u),
+                                      __uint_as_float(vw.y << 16), __uint_as_float(vw.y & 0xffff0000u));
         store4(Xt + i * LDT + r0, v4.x - eg.x * xacc[4 * g + 0], v4.y - eg.y * xacc[4 * g + 1],
                v4.z - eg.z * xacc[4 * g + 2], v4.w - eg.w * xacc[4 * g + 3]);
-        oacc[4 * g + 0] *= eg.x;
-        oacc[4 * g + 1] *= eg.y;
-        oacc[4 * g + 2] *= eg.z;
-        oacc[4 * g + 3] *= eg.w;
+      }
+      if constexpr (!KDA) {   // O^T columns are the chunk rows r
+        const float egr = Eg[own_rb * 32 + col];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[v] *= egr;
       }
     }
     __syncthreads();
@@ -1469,7 +1503,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         xb[s] = frag_load(Xt + (ub * 32 + col) * LDT + ko + 16 * s);
       }
     }
-    bf16x8 pa[2][2], ka[NST][2][2];  // P rows of the wave's O tile; K^T rows of its state tiles
+    bf16x8 pa[2][2], ka[NST][2][2];  // P rows of the wave's O tile; K^T of its state tiles
     if (own_rb >= 0) {
       const E* prow = Pm + (own_rb * 32 + col) * LDT;
 #pragma unroll
@@ -1480,11 +1514,10 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       const int cb = min((wave + 4 * st) / NI, NC - 1);
-      const E* ktrow = Kt + (cb * 32 + col) * LDT;
 #pragma unroll
       for (int rj = 0; rj < 2; ++rj)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) ka[st][rj][s] = frag_perm(ktrow, 32 * rj + 16 * s, hh);
+        for (int s = 0; s < 2; ++s) ka[st][rj][s] = frag_perm_tr(Ks, LDK, 32 * rj + 16 * s, cb * 32, lane);
     }
     sched_fence();
 
@@ -1496,7 +1529,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       if (s < 2) mma16(u0, ta0[s], xb[s]);
       mma16(u1, ta1[s], xb[s]);
     }
-    bf16x8 uf[2][2], wf[2][2];   // U and the decay-weighted U as B fragments (k = token)
+    bf16x8 uf[2][2], wf[2][2];   // U and the decay-weighted U as operands (k = token)
     uf[0][0] = frag_acc(u0, 0);
     uf[0][1] = frag_acc(u0, 1);
     uf[1][0] = frag_acc(u1, 0);
@@ -1521,20 +1554,19 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       wf[1][1] = frag_acc(u1, 1);
     }
 
-    // ---- O = O_inter + P U for the wave's tile, staged for the data waves ----
+    // ---- O^T = O_inter^T + U^T P^T for the wave's tile, staged for the data waves ----
     if (own_rb >= 0) {
 #pragma unroll
       for (int rj = 0; rj < 2; ++rj) {
         if (rj > own_rb) break;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) mma_bf16(oacc, pa[rj][s], uf[rj][s]);
+        for (int s = 0; s < 2; ++s) mma_bf16(oacc, uf[rj][s], pa[rj][s]);
       }
-      const int i = own_ib * 32 + col;
+      const int r = own_rb * 32 + col;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          Os[(own_rb * 32 + acc_row(g, e, lane)) * OST + i] = to_elem<E>(oacc[4 * g + e]);
+        store4(Os + r * OST + own_ib * 32 + acc_row(g, 0, lane), oacc[4 * g], oacc[4 * g + 1], oacc[4 * g + 2],
+               oacc[4 * g + 3]);
     }
 
     // ---- S^T <- gamma_C S^T + K^T Uw (per-channel: Diag(gC) S^T + Kc^T U), refresh Sb ----

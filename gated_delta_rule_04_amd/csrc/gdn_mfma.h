@@ -100,8 +100,10 @@ __device__ inline void tile_nt_k(f32x16& acc, const E* A, int lda, const E* B, i
   }
 }
 
-// Two tiles that share the B operand: acc0 += A0 B^T, acc1 += A1 B^T.
-template <int NK, typename E>
+// Two tiles that share the B operand: acc0 += A0 B^T, acc1 += A1 B^T, or with
+// T1 the second one transposed, acc1 += B A1^T (a fragment has the same
+// register layout as an A and as a B operand).
+template <int NK, typename E, bool T1 = false>
 __device__ inline void tile_nt2_shared_b(f32x16& acc0, f32x16& acc1, const E* A0, const E* A1,
                                          int lda, const E* B, int ldb, int lane) {
   const int ra = (lane & 31) * lda + (lane >> 5) * 8;
@@ -123,7 +125,8 @@ __device__ inline void tile_nt2_shared_b(f32x16& acc0, f32x16& acc1, const E* A0
     }
     sched_fence();
     mma16(acc0, f0[s], fb[s]);
-    mma16(acc1, f1[s], fb[s]);
+    if constexpr (T1) mma16(acc1, fb[s], f1[s]);
+    else mma16(acc1, f1[s], fb[s]);
     sched_fence();
   }
 }
@@ -217,6 +220,31 @@ __device__ inline bf16x8 frag_acc(const f32x16& acc, int s) {
     f[4 + j] = (__bf16)acc[8 * s + 4 + j];
   }
   return f;
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16, gfx950) of a row-major bf16 matrix:
+// every 16-lane group g of the wave receives a 4 x 16 block, lane l getting
+// M[r0 + e][c0 + (l & 15)] for e = 0..3, where r0 and c0 are the group's (the
+// same in all its lanes).  The instruction has lane s of a group read the 8
+// bytes at row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3, and hands element j
+// of that read to lane 4 (s % 4) + j of the group as its element s / 4.
+__device__ inline uint2 tr_read4(const __bf16* M, int ld, int r0, int c0, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int s = lane & 15;
+  const __bf16* p = M + (r0 + (s >> 2)) * ld + c0 + 4 * (s & 3);
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// A fragment for the k step covering k0 .. k0 + 15 in the accumulator's k order
+// (as frag_perm) taken down a column: lane l receives M[k][c0 + l % 32] for the
+// rows k of that order, out of a row-major matrix whose rows are the k index.
+__device__ inline bf16x8 frag_perm_tr(const __bf16* M, int ld, int k0, int c0, int lane) {
+  const int h = lane >> 5, c = c0 + 16 * ((lane >> 4) & 1);
+  const uint2 lo = tr_read4(M, ld, k0 + 4 * h, c, lane);
+  const uint2 hi = tr_read4(M, ld, k0 + 8 + 4 * h, c, lane);
+  return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
 __device__ inline void mma_bf16(f32x16& acc, const bf16x8& a, const bf16x8& b) {
