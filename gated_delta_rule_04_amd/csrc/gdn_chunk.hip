@@ -79,16 +79,17 @@ __device__ inline void st_once(void* p, const u32x4& v) {
 
 // Workspace: one record per chunk of every head (chunk index = head *
 // N_chunks + n).  Scalar or no decay, offsets in elements of the operand dtype:
-//   T [C][C], P [C][C] (row-major), then the gate rows, 3 x C fp32:
-//   G_r, exp(G_r), exp(G_C - G_r).
-// (The per-channel record is KdaRec below.)
+//   T [C][C] (row-major), in fp32 also P [C][C], then the gate rows, 3 x C
+//   fp32: G_r, exp(G_r), exp(G_C - G_r).
+// (The bf16 state kernel forms P itself; the per-channel record is KdaRec.)
 constexpr size_t kGateFloats = 3 * C;
 
 template <typename E>
 struct GateRec {
+  static constexpr bool has_p = sizeof(E) == 4;
   static constexpr size_t t = 0;
-  static constexpr size_t p = (size_t)C * C;
-  static constexpr size_t g = 2 * (size_t)C * C;   // fp32 region
+  static constexpr size_t p = (size_t)C * C;   // fp32 only
+  static constexpr size_t g = (has_p ? 2 : 1) * (size_t)C * C;   // fp32 region
   static constexpr size_t elems = g + kGateFloats * 4 / sizeof(E);
 };
 
@@ -226,9 +227,12 @@ __device__ __attribute__((always_inline)) inline void tri_solve(const float* Am,
 }
 
 // ---------------------------------------------------------------------------
-// chunk_prep_kernel: T = (I + A)^-1 diag(beta) and P for one chunk of one head.
+// chunk_prep_kernel: T = (I + A)^-1 diag(beta) (and in fp32 P) for one chunk of
+// one head.
 // ---------------------------------------------------------------------------
-// Neither depends on the state, so both leave the sequential kernel.
+// Neither depends on the state, so both leave the sequential kernel.  (The bf16
+// state kernel forms P from the K and Q rows it holds anyway, which spares
+// this kernel the Q reads and the record the P bytes.)
 // LDS: K rows [64][LDK] (then L^-1 fp32 [64][LDA]), Q rows [64][LDK] (then A
 // fp32 [64][LDA], then T [64][LDT]), Mt fp32 [32][LDM], G, beta.  P goes to
 // the record straight from the accumulators.
@@ -273,10 +277,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   const int h = bh % H, b = bh / H;
   const int t0 = n * C, cn = min(C, T - t0);
   const size_t tok0 = (size_t)b * T + t0;   // first token of the chunk in [B, T]
+  constexpr bool WP = R::has_p;
   E* rec = tws + (size_t)blockIdx.x * R::elems;
   E* Pw = rec + R::p;
 
-  // K and Q rows (rows past the sequence end repeat its last row: beta = 0
+  // K (and Q) rows (rows past the sequence end repeat its last row: beta = 0
   // there, so they never reach A or T, and P's rows of them are never used)
   {
     const E* kg = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
         const int r = 4 * rg + rr;
         const size_t off = (size_t)min(r, cn - 1) * ktok + cc * EPC;
         *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = ld_once(kg + off);
-        *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = ld_once(qg + off);
+        if constexpr (WP) *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = ld_once(qg + off);
       }
     }
   }
@@ -313,9 +318,13 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   // columns r; wave w < 3 takes tile w of both.
   const int jb = wave == 2 ? 1 : 0, rb = wave == 0 ? 0 : 1;
   f32x16 acca = zero16(), accp = zero16();
-  if (wave < 3)
-    tile_nt2_pairs<DK / 16>(acca, accp, Kr + jb * 32 * LDK, Kr + rb * 32 * LDK, Kr + jb * 32 * LDK,
-                            Qr + rb * 32 * LDK, LDK, lane);
+  if (wave < 3) {
+    if constexpr (WP)
+      tile_nt2_pairs<DK / 16>(acca, accp, Kr + jb * 32 * LDK, Kr + rb * 32 * LDK, Kr + jb * 32 * LDK,
+                              Qr + rb * 32 * LDK, LDK, lane);
+    else
+      tile_nt_k<DK / 16>(acca, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
+  }
   __syncthreads();   // Q is dead: A takes its bytes
   // A[r][j] = beta_r exp(G_r - G_j) k_r.k_j (j < r); P[r][j] = exp(G_r - G_j) q_r.k_j
   // (j <= r).  Masked entries are selected away (their weight may overflow).
@@ -335,9 +344,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
         y[e] = (j0 + e <= r) ? w * accp[4 * g + e] : 0.f;
       }
       store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
-      store4(Pw + r * C + j0, y[0], y[1], y[2], y[3]);
+      if constexpr (WP) store4(Pw + r * C + j0, y[0], y[1], y[2], y[3]);
     }
-  } else {   // P rows 0..31, columns 32..63 are zero
+  } else if (WP) {   // P rows 0..31, columns 32..63 are zero
     const int q = tid - 192, r = q >> 1, j0 = 32 + 16 * (q & 1);
 #pragma unroll
     for (int e = 0; e < 16; e += 4) store4(Pw + r * C + j0 + e, 0.f, 0.f, 0.f, 0.f);
@@ -997,7 +1006,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
     // ---- phase 1: X and O_inter tiles (they share the S operand) ----
     f32x16 xacc = zero16(), oacc = zero16();
     if (own_rb >= 0)
-      tile_nt2_shared_b<DK / 16>(xacc, oacc, Kr + own_rb * 32 * LDK, Qr + own_rb * 32 * LDK, LDK,
+      tile_nt2_shared_b<DK / 16>(xacc, oacc, Kr + own_rb * 32 * LDK, Qr + own_rb * 32 * LDK, LDK, LDK,
                                  Sb + own_ib * 32 * LDSB, LDSB, lane);
     if (own_rb >= 0) {
       const int i = own_ib * 32 + col;
@@ -1096,7 +1105,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
       if (NST == 2 && wave + 4 < NT) {
         // tiles wave and wave + 4 share the value block: one Uw fragment, two MFMAs
         tile_nt2_shared_b<C / 16>(Sacc[0], Sacc[NST - 1], Kt + (wave / NI) * 32 * LDT,
-                                  Kt + ((wave + 4) / NI) * 32 * LDT, LDT,
+                                  Kt + ((wave + 4) / NI) * 32 * LDT, LDT, LDT,
                                   Ub + (wave % NI) * 32 * LDT, LDT, lane);
       } else {
 #pragma unroll
@@ -1158,6 +1167,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 // Where the chain needs a column-wise operand (K^T of the state update, V in
 // the X epilogue) it reads the rows with gfx950's transposed LDS read.
 //
+// Scalar or no decay: three data waves form P = (Q K^T masked, times
+// exp(G_r - G_j)) for chunk n + 1 from the K and Q rows in LDS while the chain
+// is in interval B of chunk n (the per-channel P comes with the record).
+//
 // The chain wave of row block rb and value block ib computes the X and the
 // O_inter^T tiles (rb, ib) in phase 1 (both from one S fragment, which serves
 // as the B operand of X = K S^T and the A operand of O^T = S Q^T).  After one
@@ -1168,41 +1181,54 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 // and the decay-weighted U straight from the accumulators.  O is staged
 // transposed-back in LDS with 8-byte stores.  Two barriers per chunk:
 //   interval  chain waves                          data waves
-//   A         phase 1: X, O_inter^T (X^T -> LDS)   load K, gates of n+1;
-//                                                  T, P of n; O(n-1) -> HBM
-//   B         U = T X; O^T += U^T P^T (staged);    load T, P of n+1; K, Q, V
-//             S^T <- decay S^T + K^T Uw            rows, gates of n+1; load
-//                                                  Q, V of n+2
-// The rows of the state update's K operand (K, or the decay-scaled Kc) and the
-// gate rows are double-buffered (those of n+1 are written while the chain
-// reads those of n); O has a staging buffer of its own.  The chain issues all
-// LDS fragment loads of interval B before its first MFMA there.  The two roles
-// run separate loops with the same barrier count, so their registers do not
-// add up.
+//   A         phase 1: X, O_inter^T (X^T -> LDS)   K, Q, V rows, gates of n+1;
+//                                                  T (per-channel: P) of n;
+//                                                  O(n-1) -> HBM; load K,
+//                                                  gates of n+2
+//   B         U = T X; O^T += U^T P^T (staged);    load T (P) of n+1, Q, V of
+//             S^T <- decay S^T + K^T Uw            n+2; P of n+1 (scalar)
+// The row buffers are double-buffered (those of n+1 are written while the
+// chain reads those of n); O has a staging buffer of its own.  The chain
+// issues all LDS fragment loads of interval B before its first MFMA there.
+// The two roles run separate loops with the same barrier count, so their
+// registers do not add up.
 template <typename E, int DK, int DVS, bool KDA>
 struct WsPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = DK + PAD;
+  // The state update's K rows are also read transposed: a row stride of 16
+  // mod 64 dwords, with row-swizzled chunks, serves both read shapes.
+  static constexpr int LDKS = DK + 32;
   static constexpr int LDT = C + PAD;
   static constexpr int LDSB = DK + PAD;
-  static constexpr int LDV = DVS + 16;   // 4-row transposed reads fall in distinct banks
-  static constexpr int OST = DVS + PAD;
+  static constexpr int LDV = DVS + 16;   // 4-row transposed reads fall in fewer banks
+  // P and the O staging rows are accessed 8 bytes per lane, a row per lane:
+  // a row stride of 2 mod 4 dwords puts 32 rows in distinct banks.
+  static constexpr int LDP = C + 4;
+  static constexpr int OST = DVS + 4;
   static constexpr size_t es = sizeof(E);
-  static constexpr size_t rows = (size_t)C * LDK * es;                // one [C][LDK] row buffer
+  static constexpr size_t rows = (size_t)C * LDK * es;     // one [C][LDK] row buffer
+  static constexpr size_t srows = (size_t)C * LDKS * es;   // one [C][LDKS] row buffer
+  static constexpr size_t vrows = (size_t)C * LDV * es;    // one [C][LDV] V buffer
+  static constexpr size_t pmat = (size_t)C * LDP * es;     // one [C][LDP] P matrix
+  // Q rows, the state update's K rows and (per-channel) the phase-1 K rows, V
+  // rows, the gates: two buffers each (n and n + 1).  P: two buffers when the
+  // data waves form it during the chain's use of the previous one.
   static constexpr size_t qr = 0;
-  static constexpr size_t ks = qr + rows;                             // two buffers
-  static constexpr size_t kr = ks + 2 * rows;                         // per-channel only
-  static constexpr size_t sb = kr + (KDA ? rows : 0);
+  static constexpr size_t ks = qr + 2 * rows;
+  static constexpr size_t kr = ks + 2 * srows;
+  static constexpr size_t sb = kr + (KDA ? 2 * rows : 0);
   static constexpr size_t vr = sb + (size_t)DVS * LDSB * es;
-  static constexpr size_t xt = vr + (size_t)C * LDV * es;
+  static constexpr size_t xt = vr + 2 * vrows;
   static constexpr size_t os = xt + (size_t)DVS * LDT * es;
   static constexpr size_t pm = os + (size_t)C * OST * es;
-  static constexpr size_t tm = pm + (size_t)C * LDT * es;
-  static constexpr size_t g = tm + (size_t)C * LDT * es;   // two buffers
+  static constexpr size_t tm = pm + (KDA ? 1 : 2) * pmat;
+  static constexpr size_t g = tm + (size_t)C * LDT * es;
   static constexpr size_t total = g + 2 * kGateFloats * 4;
 };
 
 constexpr int kWsThreads = 512;
+constexpr int kP1Ahead = 2;   // phase-1 fragments loaded this many k steps ahead
 
 template <typename E, int DK, int DVS, int MODE>
 __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws) {
@@ -1216,13 +1242,14 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   constexpr int NT = NC * NI;        // state tiles
   constexpr int NST = (NT + 3) / 4;  // state tiles per chain wave
   constexpr int EPC = 8;
-  constexpr int LDK = L::LDK, LDT = L::LDT, LDSB = L::LDSB, LDV = L::LDV, OST = L::OST;
-  // data-wave geometry (256 threads): K / Q rows in blocks of 4 rows x one
-  // 16-byte chunk, V rows and T / P in 16-byte pieces along the rows
+  constexpr int LDK = L::LDK, LDKS = L::LDKS, LDT = L::LDT, LDSB = L::LDSB, LDV = L::LDV, LDP = L::LDP,
+                OST = L::OST;
+  // data-wave geometry (256 threads): every row buffer in 16-byte pieces,
+  // consecutive threads along a row (coalesced loads, conflict-free writes)
   constexpr int PT = 256;
   constexpr int CPR = DK / EPC;
-  constexpr int NKB = 16 * CPR;
-  constexpr int KBT = (NKB + PT - 1) / PT;
+  constexpr int KPT = C * CPR / PT;
+  static_assert(C * CPR % PT == 0, "K rows must split evenly over the data threads");
   constexpr int CPV = DVS / EPC;
   constexpr int VPT = C * CPV / PT;
   static_assert(C * CPV % PT == 0, "V rows must split evenly over the data threads");
@@ -1231,16 +1258,18 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   constexpr int NG4 = (KDA ? DK : (int)kGateFloats) / 4;   // 16-byte chunks of the fp32 rows
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
-  E* Qr = reinterpret_cast<E*>(smem + L::qr);
-  E* Ksb = reinterpret_cast<E*>(smem + L::ks);   // two row buffers, C * LDK apart
-  E* Kr = reinterpret_cast<E*>(smem + L::kr);    // per-channel: the K operand of phase 1
+  // Buffer pairs are C * LDK (rows; C * LDKS for Ks), C * LDV (V), C * LDP (P) elements and
+  // kGateFloats floats apart.
+  E* Qrb = reinterpret_cast<E*>(smem + L::qr);
+  E* Ksb = reinterpret_cast<E*>(smem + L::ks);   // K rows of the state update (K, or Kc), row-swizzled
+  E* Krb = reinterpret_cast<E*>(smem + L::kr);   // per-channel: the K operand of phase 1
   E* Sb = reinterpret_cast<E*>(smem + L::sb);
-  E* Vr = reinterpret_cast<E*>(smem + L::vr);
+  E* Vrb = reinterpret_cast<E*>(smem + L::vr);
   E* Xt = reinterpret_cast<E*>(smem + L::xt);
   E* Os = reinterpret_cast<E*>(smem + L::os);
-  E* Pm = reinterpret_cast<E*>(smem + L::pm);
+  E* Pmb = reinterpret_cast<E*>(smem + L::pm);
   E* Tm = reinterpret_cast<E*>(smem + L::tm);
-  float* Gbuf = reinterpret_cast<float*>(smem + L::g);  // two gate blocks (or gC rows)
+  float* Gbuf = reinterpret_cast<float*>(smem + L::g);  // gate rows (or gC rows)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
@@ -1274,9 +1303,9 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     const E* recs = tws + (size_t)head * nchunks * R::elems;
     E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
 
-    u32x4 pk[KBT][4], pq[KBT][4], pv[VPT], pkc[KDA ? KBT : 1][4];   // rows of a chunk
+    u32x4 pk[KPT], pq[KPT], pv[VPT], pkc[KDA ? KPT : 1];   // rows of a chunk
     u32x4 pg = u32x4{0u, 0u, 0u, 0u};
-    u32x4 pt[TBT], pp[TBT];                                          // T, P of a chunk
+    u32x4 pt[TBT], pp[KDA ? TBT : 1];                                // T (and P) of a chunk
 
     // The loads are split in two groups so that both intervals issue about
     // the same number of bytes: the K operands and the gates of chunk n, and
@@ -1290,20 +1319,14 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       const E* rq = recs + (size_t)n * R::elems;
       const E* kq = kg + (size_t)t0 * qk_tok;
 #pragma unroll
-      for (int m = 0; m < KBT; ++m) {
-        const int blk = ptid + PT * m;
-        const int bq = blk < NKB ? blk : 0;
-        const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if constexpr (KDA) {
-            const uint32_t off = (uint32_t)(4 * rb4 + rr) * DK + cc * EPC;
-            pk[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::kg + off);
-            pkc[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::kc + off);
-          } else {
-            const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)qk_tok + cc * EPC;
-            pk[m][rr] = *reinterpret_cast<const u32x4*>(kq + off);
-          }
+      for (int m = 0; m < KPT; ++m) {
+        const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
+        if constexpr (KDA) {
+          const uint32_t off = (uint32_t)r * DK + cc * EPC;
+          pk[m] = *reinterpret_cast<const u32x4*>(rq + R::kg + off);
+          pkc[m] = *reinterpret_cast<const u32x4*>(rq + R::kc + off);
+        } else {
+          pk[m] = *reinterpret_cast<const u32x4*>(kq + (uint32_t)min(r, rmax) * (uint32_t)qk_tok + cc * EPC);
         }
       }
       pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(ptid, NG4 - 1));
@@ -1314,19 +1337,12 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       const E* rq = recs + (size_t)n * R::elems;
       const E* qq = qg + (size_t)t0 * qk_tok;
 #pragma unroll
-      for (int m = 0; m < KBT; ++m) {
-        const int blk = ptid + PT * m;
-        const int bq = blk < NKB ? blk : 0;
-        const int rb4 = blk_row(bq, CPR), cc = blk_col(bq, CPR);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          if constexpr (KDA) {
-            pq[m][rr] = *reinterpret_cast<const u32x4*>(rq + R::qg + (uint32_t)(4 * rb4 + rr) * DK + cc * EPC);
-          } else {
-            const uint32_t off = (uint32_t)min(4 * rb4 + rr, rmax) * (uint32_t)qk_tok + cc * EPC;
-            pq[m][rr] = *reinterpret_cast<const u32x4*>(qq + off);
-          }
-        }
+      for (int m = 0; m < KPT; ++m) {
+        const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
+        if constexpr (KDA)
+          pq[m] = *reinterpret_cast<const u32x4*>(rq + R::qg + (uint32_t)r * DK + cc * EPC);
+        else
+          pq[m] = *reinterpret_cast<const u32x4*>(qq + (uint32_t)min(r, rmax) * (uint32_t)qk_tok + cc * EPC);
       }
       const E* vq = vg + (size_t)t0 * v_tok;
 #pragma unroll
@@ -1335,31 +1351,28 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         pv[m] = ld_once(vq + (uint32_t)min(r, rmax) * (uint32_t)v_tok + cc * EPC);
       }
     };
-    auto load_b = [&](int n) __attribute__((always_inline)) {
+    auto load_tp = [&](int n) __attribute__((always_inline)) {
       const E* rq = recs + (size_t)n * R::elems;
 #pragma unroll
       for (int m = 0; m < TBT; ++m) {
         pt[m] = *reinterpret_cast<const u32x4*>(rq + R::t + (ptid + PT * m) * EPC);
-        pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (ptid + PT * m) * EPC);
+        if constexpr (KDA) pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (ptid + PT * m) * EPC);
       }
     };
-    // Rows of a chunk: Q, the state update's K operand (K, or Kc) into buffer
-    // gb, the per-channel phase-1 K operand, V, and the gates into buffer gb.
-    auto commit_a = [&](int gb) __attribute__((always_inline)) {
-      E* Ks = Ksb + gb * C * LDK;
+    // Rows of a chunk into buffer gb: Q, the state update's K operand (K, or
+    // Kc), the per-channel phase-1 K operand, V, and the gates.
+    auto commit_rows = [&](int gb) __attribute__((always_inline)) {
+      E* Qr = Qrb + gb * C * LDK;
+      E* Ks = Ksb + gb * C * LDKS;
+      E* Kr = Krb + gb * C * LDK;
+      E* Vr = Vrb + gb * C * LDV;
 #pragma unroll
-      for (int m = 0; m < KBT; ++m) {
-        const int blk = ptid + PT * m;
-        if (blk < NKB) {
-          const int rb4 = blk_row(blk, CPR), cc = blk_col(blk, CPR);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int o = (4 * rb4 + rr) * LDK + cc * EPC;
-            *reinterpret_cast<u32x4*>(Qr + o) = pq[m][rr];
-            *reinterpret_cast<u32x4*>(Ks + o) = KDA ? pkc[m][rr] : pk[m][rr];
-            if constexpr (KDA) *reinterpret_cast<u32x4*>(Kr + o) = pk[m][rr];
-          }
-        }
+      for (int m = 0; m < KPT; ++m) {
+        const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
+        const int o = r * LDK + cc * EPC;
+        *reinterpret_cast<u32x4*>(Qr + o) = pq[m];
+        *reinterpret_cast<u32x4*>(Ks + r * LDKS + swz_col(r, cc * EPC)) = KDA ? pkc[m] : pk[m];
+        if constexpr (KDA) *reinterpret_cast<u32x4*>(Kr + o) = pk[m];
       }
 #pragma unroll
       for (int m = 0; m < VPT; ++m) {
@@ -1368,48 +1381,92 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       }
       if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * kGateFloats + 4 * ptid) = pg;
     };
-    // T and P of a chunk.
-    auto commit_b = [&]() __attribute__((always_inline)) {
+    // T (and the per-channel P) of a chunk.
+    auto commit_tp = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int m = 0; m < TBT; ++m) {
         const int q = ptid + PT * m, r = q / CPT, cc = q % CPT;
         *reinterpret_cast<u32x4*>(Tm + r * LDT + cc * EPC) = pt[m];
-        *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
+        if constexpr (KDA) {
+          uint2* d = reinterpret_cast<uint2*>(Pmb + r * LDP + cc * EPC);
+          d[0] = make_uint2(pp[m][0], pp[m][1]);
+          d[1] = make_uint2(pp[m][2], pp[m][3]);
+        }
+      }
+    };
+    // P of the chunk in row buffers gb (scalar or no decay): data wave d < 3
+    // takes the 32 x 32 tile (column block, row block) (0,0), (0,1), (1,1) of
+    // P^T = K Q^T, so that each lane holds four consecutive columns j of one
+    // row r: P[r][j] = exp(G_r - G_j) q_r.k_j for j <= r, else 0 (a select:
+    // the weight of a masked entry may overflow).
+    auto form_p = [&](int gb) __attribute__((always_inline)) {
+      const int d = wave - 4;
+      if (d >= 3) return;
+      const int jb = d == 2 ? 1 : 0, rb = d == 0 ? 0 : 1;
+      f32x16 acc = zero16();
+      tile_nt_k<DK / 16, E, true>(acc, Ksb + gb * C * LDKS + jb * 32 * LDKS, LDKS,
+                                  Qrb + gb * C * LDK + rb * 32 * LDK, LDK, lane);
+      const float* Gl = Gbuf + gb * kGateFloats;
+      E* Pm = Pmb + gb * C * LDP;
+      const int r = rb * 32 + col;
+      const float Gr = Gl[r];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = jb * 32 + acc_row(g, 0, lane);
+        const float4 gj = *reinterpret_cast<const float4*>(Gl + j0);
+        const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (j0 + e <= r) ? __expf(Gr - gjv[e]) * acc[4 * g + e] : 0.f;
+        store4(Pm + r * LDP + j0, y[0], y[1], y[2], y[3]);
       }
     };
     // Staged O rows of a whole chunk -> HBM, 16-byte stores along each row.
     constexpr int CPO = DVS / EPC;
+    auto os_piece = [&](int r, int cc) __attribute__((always_inline)) {   // rows are 8-byte aligned
+      const uint2* p = reinterpret_cast<const uint2*>(Os + r * OST + cc * EPC);
+      const uint2 lo = p[0], hi = p[1];
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    };
     static_assert(C * CPO % PT == 0, "O rows must split evenly over the data threads");
     auto flush_o = [&](int t0f) __attribute__((always_inline)) {
       E* oq = og + (size_t)t0f * v_tok;
 #pragma unroll
       for (int m = 0; m < C * CPO / PT; ++m) {
         const int q = ptid + PT * m, r = q / CPO, cc = q % CPO;
-        st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC));
+        st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, os_piece(r, cc));
       }
     };
-    // One chunk step.  Loads are issued before the LDS writes of an interval
-    // whose data arrived earlier; the first step (nothing to flush) is peeled
-    // so that no global access in the loop is conditional.
+    // One chunk step.  The LDS writes of interval A use data loaded at least
+    // one interval earlier; the first step (nothing to flush) is peeled so that
+    // no global access in the loop is conditional.
     auto step = [&](int n, auto first) __attribute__((always_inline)) {
       // interval A: the chain runs phase 1 of chunk n
-      load_k(min(n + 1, nchunks - 1));
-      commit_b();                    // T, P of chunk n
+      if (n + 1 < nchunks) commit_rows((n + 1) & 1);
+      commit_tp();                   // T (and P) of chunk n
       if constexpr (!decltype(first)::value) flush_o((n - 1) * C);
+      load_k(min(n + 2, nchunks - 1));
       __syncthreads();
       // interval B: the chain runs U, O and S of chunk n
-      load_b(min(n + 1, nchunks - 1));
-      if (n + 1 < nchunks) commit_a((n + 1) & 1);
+      load_tp(min(n + 1, nchunks - 1));
       load_qv(min(n + 2, nchunks - 1));
+      if constexpr (!KDA) {
+        if (n + 1 < nchunks) form_p((n + 1) & 1);
+      }
       __syncthreads();
     };
 
     if (nchunks > 0) {
       load_k(0);
       load_qv(0);
-      load_b(0);
-      commit_a(0);
+      commit_rows(0);
+      load_k(min(1, nchunks - 1));
       load_qv(min(1, nchunks - 1));
+      load_tp(0);
+    }
+    __syncthreads();
+    if constexpr (!KDA) {
+      if (nchunks > 0) form_p(0);
     }
     __syncthreads();
     if (nchunks > 0) step(0, std::true_type{});
@@ -1420,7 +1477,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       for (int q = ptid; q < C * CPO; q += PT) {
         const int r = q / CPO, cc = q % CPO;
         if (r < cnf)
-          st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, *reinterpret_cast<const u32x4*>(Os + r * OST + cc * EPC));
+          st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, os_piece(r, cc));
       }
     }
     return;
@@ -1459,18 +1516,24 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     }
   }
   __syncthreads();
+  __syncthreads();   // the data waves form P of the first chunk
 
   for (int n = 0; n < nchunks; ++n) {
-    const float* G = Gbuf + (n & 1) * kGateFloats;
+    const int nb = n & 1;
+    const float* G = Gbuf + nb * kGateFloats;
     const float* Eg = G + C;
     const float* Ec = G + 2 * C;
-    const E* Ks = Ksb + (n & 1) * C * LDK;
-    const E* K1 = KDA ? Kr : Ks;   // K operand of phase 1
+    const E* Ks = Ksb + nb * C * LDKS;
+    const E* K1 = KDA ? Krb + nb * C * LDK : Ks;   // K operand of phase 1 (scalar: swizzled)
+    const E* Qr = Qrb + nb * C * LDK;
+    const E* Vr = Vrb + nb * C * LDV;
+    const E* Pm = Pmb + (KDA ? 0 : nb) * C * LDP;
 
     // ---- interval A, phase 1: X = V - diag(gamma) K S^T, O_inter^T = S (diag(gamma) Q)^T ----
     f32x16 xacc = zero16(), oacc = zero16();
     if (own_rb >= 0) {
-      tile_nt2_shared_b<DK / 16, E, true>(xacc, oacc, K1 + own_rb * 32 * LDK, Qr + own_rb * 32 * LDK, LDK,
+      tile_nt2_shared_b<DK / 16, E, true, kP1Ahead, !KDA>(xacc, oacc, K1 + own_rb * 32 * (KDA ? LDK : LDKS),
+                                                           Qr + own_rb * 32 * LDK, KDA ? LDK : LDKS, LDK,
                                           Sb + own_ib * 32 * LDSB, LDSB, lane);
       const int i = own_ib * 32 + col;
       const int vc = own_ib * 32 + 16 * ((lane >> 4) & 1);
@@ -1505,7 +1568,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     }
     bf16x8 pa[2][2], ka[NST][2][2];  // P rows of the wave's O tile; K^T of its state tiles
     if (own_rb >= 0) {
-      const E* prow = Pm + (own_rb * 32 + col) * LDT;
+      const E* prow = Pm + (own_rb * 32 + col) * LDP;
 #pragma unroll
       for (int rj = 0; rj < 2; ++rj)
 #pragma unroll
@@ -1517,7 +1580,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
 #pragma unroll
       for (int rj = 0; rj < 2; ++rj)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) ka[st][rj][s] = frag_perm_tr(Ks, LDK, 32 * rj + 16 * s, cb * 32, lane);
+        for (int s = 0; s < 2; ++s) ka[st][rj][s] = frag_perm_tr<true>(Ks, LDKS, 32 * rj + 16 * s, cb * 32, lane);
     }
     sched_fence();
 
@@ -1630,8 +1693,10 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0>), grid, wblock, 0, stream, a, tws);
     else if (a.mode == 1)
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1>), grid, wblock, 0, stream, a, tws);
-    else
+    else if constexpr (DVS == 32)   // the per-channel buffers leave room for 32-row slices only
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2>), grid, wblock, 0, stream, a, tws);
+    else
+      return hipErrorInvalidConfiguration;
   } else {
     if (a.mode == 0)
       hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 0>), grid, block, 0, stream, a, tws);
@@ -1665,7 +1730,7 @@ hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) 
     return launch_state<E, DK, 32>(a, tws, stream);
   } else {
     const long long wg64 = (long long)a.B * a.H * (a.dv / 64);
-    if (wg64 >= 256) return launch_state<E, DK, 64>(a, tws, stream);
+    if (wg64 >= 256 && a.mode != 2) return launch_state<E, DK, 64>(a, tws, stream);
     return launch_state<E, DK, 32>(a, tws, stream);
   }
 }
@@ -1676,7 +1741,7 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dtype, int mode)
   const size_t chunks = (size_t)B * H * (((size_t)T + C - 1) / C);
   const size_t es = dtype == 1 ? 2 : 4;
   if (mode == 2) return chunks * ((2 * (size_t)C * C + 3 * (size_t)C * dk) * es + 4 * (size_t)dk);
-  return chunks * (2 * (size_t)C * C * es + kGateFloats * 4);
+  return chunks * ((es == 4 ? 2 : 1) * (size_t)C * C * es + kGateFloats * 4);   // bf16: no P
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream) {

@@ -41,10 +41,11 @@ struct DecodeArgs {
 };
 
 // Device workspace the prefill needs, per chunk of every head.  Scalar or no
-// decay: T = (I + A)^-1 diag(beta) and the masked intra-chunk attention P
-// (64 x 64 elements of the operand dtype each) and the chunk's decay factors
-// (3 x 64 fp32).  Per-channel decay: T and P, the decay-scaled K, Q and K
-// (64 x dk each, operand dtype) and the chunk's per-channel decay (dk fp32).
+// decay: T = (I + A)^-1 diag(beta) (64 x 64 elements of the operand dtype),
+// in fp32 also the masked intra-chunk attention P (64 x 64), and the chunk's
+// decay factors (3 x 64 fp32).  Per-channel decay: T and P, the decay-scaled
+// K, Q and K (64 x dk each, operand dtype) and the chunk's per-channel decay
+// (dk fp32).
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dtype, int mode);
 // Enqueue the prefill kernels; returns the launch status.
 hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);

@@ -76,22 +76,32 @@ constexpr int kAhead = 2;
 
 __device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Rows of a row-swizzled bf16 LDS buffer keep their 16-byte chunks at index
+// chunk ^ swz(row), swz(row) = (row / 4) % 4.  For a row stride of 16 mod 64
+// dwords this puts the 16-byte reads of 16 consecutive rows and the transposed
+// reads of 4 consecutive rows into distinct banks.
+__device__ inline int swz(int row) { return (row >> 2) & 3; }
+__device__ inline int swz_col(int row, int col) { return (((col >> 3) ^ swz(row)) << 3) | (col & 7); }
+
 // acc += A[0:32, 0:16 NK] * B[0:32, 0:16 NK]^T, A and B in LDS with leading
-// dimensions lda and ldb (elements), k contiguous.
-template <int NK, typename E>
+// dimensions lda and ldb (elements), k contiguous.  With SWA the rows of A are
+// row-swizzled (the tile's first row a multiple of 16).
+template <int NK, typename E, bool SWA = false>
 __device__ inline void tile_nt_k(f32x16& acc, const E* A, int lda, const E* B, int ldb, int lane) {
-  const E* pa = A + (lane & 31) * lda + (lane >> 5) * 8;
+  const int sa = SWA ? swz(lane & 31) : 0;
+  const E* pa = A + (lane & 31) * lda;
   const E* pb = B + (lane & 31) * ldb + (lane >> 5) * 8;
+  auto oa = [&](int s) { return (((2 * s + (lane >> 5)) ^ sa) << 3); };
   Frag<E> fa[NK], fb[NK];
 #pragma unroll
   for (int s = 0; s < kAhead && s < NK; ++s) {
-    fa[s] = frag_load(pa + 16 * s);
+    fa[s] = frag_load(pa + oa(s));
     fb[s] = frag_load(pb + 16 * s);
   }
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
     if (s + kAhead < NK) {
-      fa[s + kAhead] = frag_load(pa + 16 * (s + kAhead));
+      fa[s + kAhead] = frag_load(pa + oa(s + kAhead));
       fb[s + kAhead] = frag_load(pb + 16 * (s + kAhead));
     }
     sched_fence();
@@ -102,25 +112,30 @@ __device__ inline void tile_nt_k(f32x16& acc, const E* A, int lda, const E* B, i
 
 // Two tiles that share the B operand: acc0 += A0 B^T, acc1 += A1 B^T, or with
 // T1 the second one transposed, acc1 += B A1^T (a fragment has the same
-// register layout as an A and as a B operand).
-template <int NK, typename E, bool T1 = false>
+// register layout as an A and as a B operand).  Fragments are loaded AH k
+// steps ahead.  A0 has leading dimension lda0 and, with SW0, row-swizzled rows
+// (the tile's first row a multiple of 16).
+template <int NK, typename E, bool T1 = false, int AH = kAhead, bool SW0 = false>
 __device__ inline void tile_nt2_shared_b(f32x16& acc0, f32x16& acc1, const E* A0, const E* A1,
-                                         int lda, const E* B, int ldb, int lane) {
+                                         int lda0, int lda, const E* B, int ldb, int lane) {
   const int ra = (lane & 31) * lda + (lane >> 5) * 8;
   const E* pb = B + (lane & 31) * ldb + (lane >> 5) * 8;
+  const int s0 = SW0 ? swz(lane & 31) : 0;
+  const E* p0 = A0 + (lane & 31) * lda0;
+  auto o0 = [&](int s) { return (((2 * s + (lane >> 5)) ^ s0) << 3); };
   Frag<E> fb[NK], f0[NK], f1[NK];
 #pragma unroll
-  for (int s = 0; s < kAhead && s < NK; ++s) {
+  for (int s = 0; s < AH && s < NK; ++s) {
     fb[s] = frag_load(pb + 16 * s);
-    f0[s] = frag_load(A0 + ra + 16 * s);
+    f0[s] = frag_load(p0 + o0(s));
     f1[s] = frag_load(A1 + ra + 16 * s);
   }
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
-    if (s + kAhead < NK) {
-      const int t = s + kAhead;
+    if (s + AH < NK) {
+      const int t = s + AH;
       fb[t] = frag_load(pb + 16 * t);
-      f0[t] = frag_load(A0 + ra + 16 * t);
+      f0[t] = frag_load(p0 + o0(t));
       f1[t] = frag_load(A1 + ra + 16 * t);
     }
     sched_fence();
@@ -228,22 +243,25 @@ __device__ inline bf16x8 frag_acc(const f32x16& acc, int s) {
 // same in all its lanes).  The instruction has lane s of a group read the 8
 // bytes at row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3, and hands element j
 // of that read to lane 4 (s % 4) + j of the group as its element s / 4.
+template <bool SW = false>
 __device__ inline uint2 tr_read4(const __bf16* M, int ld, int r0, int c0, int lane) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const int s = lane & 15;
-  const __bf16* p = M + (r0 + (s >> 2)) * ld + c0 + 4 * (s & 3);
+  const int s = lane & 15, r = r0 + (s >> 2), c = c0 + 4 * (s & 3);
+  const __bf16* p = M + r * ld + (SW ? swz_col(r, c) : c);
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
   return __builtin_bit_cast(uint2, v);
 }
 
 // A fragment for the k step covering k0 .. k0 + 15 in the accumulator's k order
 // (as frag_perm) taken down a column: lane l receives M[k][c0 + l % 32] for the
-// rows k of that order, out of a row-major matrix whose rows are the k index.
+// rows k of that order, out of a row-major matrix whose rows are the k index
+// (with SW, row-swizzled).
+template <bool SW = false>
 __device__ inline bf16x8 frag_perm_tr(const __bf16* M, int ld, int k0, int c0, int lane) {
   const int h = lane >> 5, c = c0 + 16 * ((lane >> 4) & 1);
-  const uint2 lo = tr_read4(M, ld, k0 + 4 * h, c, lane);
-  const uint2 hi = tr_read4(M, ld, k0 + 8 + 4 * h, c, lane);
+  const uint2 lo = tr_read4<SW>(M, ld, k0 + 4 * h, c, lane);
+  const uint2 hi = tr_read4<SW>(M, ld, k0 + 8 + 4 * h, c, lane);
   return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 

@@ -107,7 +107,8 @@ def _ws_bytes(B, T, H, es, dk=128, mode=1):
     chunks = B * H * ((T + 63) // 64)
     if mode == 2:   # T, P, three scaled copies of K / Q, per-channel decay
         return chunks * ((2 * 64 * 64 + 3 * 64 * dk) * es + 4 * dk)
-    return chunks * (2 * 64 * 64 * es + 3 * 64 * 4)     # T and P per chunk + three fp32 gate rows
+    # T per chunk (and P in fp32: the bf16 state kernel forms P itself) + three fp32 gate rows
+    return chunks * ((2 if es == 4 else 1) * 64 * 64 * es + 3 * 64 * 4)
 
 
 def test_workspace_query(lib):
