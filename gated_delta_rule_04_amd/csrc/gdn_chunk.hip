@@ -1229,6 +1229,7 @@ struct WsPlan {
 
 constexpr int kWsThreads = 512;
 constexpr int kP1Ahead = 2;   // phase-1 fragments loaded this many k steps ahead
+constexpr int kFormPAhead = 2;   // fragments of P's product loaded this many k steps ahead
 
 template <typename E, int DK, int DVS, int MODE>
 __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws) {
@@ -1404,20 +1405,31 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       if (d >= 3) return;
       const int jb = d == 2 ? 1 : 0, rb = d == 0 ? 0 : 1;
       f32x16 acc = zero16();
-      tile_nt_k<DK / 16, E, true>(acc, Ksb + gb * C * LDKS + jb * 32 * LDKS, LDKS,
+      tile_nt_k<DK / 16, E, true, kFormPAhead>(acc, Ksb + gb * C * LDKS + jb * 32 * LDKS, LDKS,
                                   Qrb + gb * C * LDK + rb * 32 * LDK, LDK, lane);
       const float* Gl = Gbuf + gb * kGateFloats;
       E* Pm = Pmb + gb * C * LDP;
       const int r = rb * 32 + col;
       const float Gr = Gl[r];
+      // Every weight is formed (clamped to at most 1) before the mask selects:
+      // left conditional, the gate loads sink into per-element branches.
+      float w[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 gj = *reinterpret_cast<const float4*>(Gl + jb * 32 + acc_row(g, 0, lane));
+        w[4 * g + 0] = __expf(fminf(Gr - gj.x, 0.f));
+        w[4 * g + 1] = __expf(fminf(Gr - gj.y, 0.f));
+        w[4 * g + 2] = __expf(fminf(Gr - gj.z, 0.f));
+        w[4 * g + 3] = __expf(fminf(Gr - gj.w, 0.f));
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) asm volatile("" ::"v"(w[v]));
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int j0 = jb * 32 + acc_row(g, 0, lane);
-        const float4 gj = *reinterpret_cast<const float4*>(Gl + j0);
-        const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (j0 + e <= r) ? __expf(Gr - gjv[e]) * acc[4 * g + e] : 0.f;
+        for (int e = 0; e < 4; ++e) y[e] = (j0 + e <= r) ? w[4 * g + e] * acc[4 * g + e] : 0.f;
         store4(Pm + r * LDP + j0, y[0], y[1], y[2], y[3]);
       }
     };

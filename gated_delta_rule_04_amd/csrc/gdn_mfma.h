@@ -85,8 +85,9 @@ __device__ inline int swz_col(int row, int col) { return (((col >> 3) ^ swz(row)
 
 // acc += A[0:32, 0:16 NK] * B[0:32, 0:16 NK]^T, A and B in LDS with leading
 // dimensions lda and ldb (elements), k contiguous.  With SWA the rows of A are
-// row-swizzled (the tile's first row a multiple of 16).
-template <int NK, typename E, bool SWA = false>
+// row-swizzled (the tile's first row a multiple of 16).  Fragments are loaded
+// AH k steps ahead.
+template <int NK, typename E, bool SWA = false, int AH = kAhead>
 __device__ inline void tile_nt_k(f32x16& acc, const E* A, int lda, const E* B, int ldb, int lane) {
   const int sa = SWA ? swz(lane & 31) : 0;
   const E* pa = A + (lane & 31) * lda;
@@ -94,15 +95,15 @@ __device__ inline void tile_nt_k(f32x16& acc, const E* A, int lda, const E* B, i
   auto oa = [&](int s) { return (((2 * s + (lane >> 5)) ^ sa) << 3); };
   Frag<E> fa[NK], fb[NK];
 #pragma unroll
-  for (int s = 0; s < kAhead && s < NK; ++s) {
+  for (int s = 0; s < AH && s < NK; ++s) {
     fa[s] = frag_load(pa + oa(s));
     fb[s] = frag_load(pb + 16 * s);
   }
 #pragma unroll
   for (int s = 0; s < NK; ++s) {
-    if (s + kAhead < NK) {
-      fa[s + kAhead] = frag_load(pa + oa(s + kAhead));
-      fb[s + kAhead] = frag_load(pb + 16 * (s + kAhead));
+    if (s + AH < NK) {
+      fa[s + AH] = frag_load(pa + oa(s + AH));
+      fb[s + AH] = frag_load(pb + 16 * (s + AH));
     }
     sched_fence();
     mma16(acc, fa[s], fb[s]);
