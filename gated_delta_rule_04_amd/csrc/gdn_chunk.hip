@@ -118,9 +118,10 @@ __device__ inline float chunk_log_decay(float alpha, bool ok) {
 //   Am  A, fp32 [C][LDA]: read below the diagonal; inside the 16x16 diagonal
 //       blocks the entries on and above the diagonal must be zero
 //   Bt  beta [C] (zero for rows past the sequence end)
-//   Li  scratch for L^-1 = (I + A)^-1, fp32 [C][LDA]
+//   Li  scratch for L^-1 = (I + A)^-1, fp32 [C][LDA]; may be Am itself (every
+//       step overwrites only blocks of A that it has finished reading)
 //   Mt  scratch, fp32 [32][LDM]
-//   Tm  T in the operand dtype [C][LDT]; may share Am's bytes
+//   Tm  T in the operand dtype [C][LDT]; may share Am's bytes unless Li is Am
 // All threads of the workgroup take part; it ends with a barrier.
 template <typename E>
 struct SolveLd {
@@ -244,9 +245,16 @@ struct PrepPlan {
   static constexpr int LDT = SolveLd<E>::LDT;
   static constexpr int LDM = SolveLd<E>::LDM;
   static constexpr size_t es = sizeof(E);
-  static constexpr size_t kr = 0;   // also L^-1
-  static constexpr size_t am = cmax((size_t)C * LDK * es, (size_t)C * LDA * 4);   // Q, then A, then T
-  static constexpr size_t mt = am + cmax((size_t)C * LDK * es, cmax((size_t)C * LDA * 4, (size_t)C * LDT * es));
+  // bf16 (no Q): A takes the dead K rows' bytes and L^-1 overwrites A in
+  // place, T has bytes of its own; 31.7 KB, five workgroups per compute unit.
+  // fp32: L^-1 over the K rows; Q, then A, then T in a second region.
+  static constexpr bool inplace = sizeof(E) == 2;
+  static constexpr size_t r1 = cmax((size_t)C * LDK * es, (size_t)C * LDA * 4);
+  static constexpr size_t kr = 0;   // K rows, then L^-1
+  static constexpr size_t am = inplace ? 0 : r1;
+  static constexpr size_t tm = inplace ? r1 : am;
+  static constexpr size_t mt = inplace ? tm + (size_t)C * LDT * es
+                                       : am + cmax((size_t)C * LDK * es, cmax((size_t)C * LDA * 4, (size_t)C * LDT * es));
   static constexpr size_t g = mt + (size_t)32 * LDM * 4;
   static constexpr size_t total = g + 2 * C * 4;
 };
@@ -256,16 +264,16 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
                                                               int nchunks) {
   using L = PrepPlan<E, DK>;
   using R = GateRec<E>;
+  constexpr bool WP = R::has_p;
   constexpr int EPC = 16 / (int)sizeof(E);
   constexpr int CPR = DK / EPC;
-  constexpr int NKB = 16 * CPR;
   constexpr int LDK = L::LDK, LDA = L::LDA, LDT = L::LDT;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
   E* Kr = reinterpret_cast<E*>(smem + L::kr);
   float* Li = reinterpret_cast<float*>(smem + L::kr);
   E* Qr = reinterpret_cast<E*>(smem + L::am);
   float* Am = reinterpret_cast<float*>(smem + L::am);
-  E* Tm = reinterpret_cast<E*>(smem + L::am);
+  E* Tm = reinterpret_cast<E*>(smem + L::tm);
   float* Mt = reinterpret_cast<float*>(smem + L::mt);
   float* G = reinterpret_cast<float*>(smem + L::g);
   float* Bt = G + C;
@@ -277,25 +285,24 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   const int h = bh % H, b = bh / H;
   const int t0 = n * C, cn = min(C, T - t0);
   const size_t tok0 = (size_t)b * T + t0;   // first token of the chunk in [B, T]
-  constexpr bool WP = R::has_p;
   E* rec = tws + (size_t)blockIdx.x * R::elems;
   E* Pw = rec + R::p;
 
-  // K (and Q) rows (rows past the sequence end repeat its last row: beta = 0
-  // there, so they never reach A or T, and P's rows of them are never used)
+  // K (and Q) rows, consecutive threads along a row (rows past the sequence
+  // end repeat its last row: beta = 0 there, so they never reach A or T, and
+  // P's rows of them are never used)
   {
     const E* kg = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
     const E* qg = static_cast<const E*>(a.q) + (tok0 * H + h) * DK;
     const size_t ktok = (size_t)H * DK;
-    for (int blk = tid; blk < NKB; blk += kThreads) {
-      const int rg = blk_row(blk, CPR), cc = blk_col(blk, CPR);
+    static_assert(C * CPR % kThreads == 0, "K rows must split evenly over the threads");
+  static_assert(L::inplace == !WP, "the in-place plan has no room for Q");
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = 4 * rg + rr;
-        const size_t off = (size_t)min(r, cn - 1) * ktok + cc * EPC;
-        *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = ld_once(kg + off);
-        if constexpr (WP) *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = ld_once(qg + off);
-      }
+    for (int m = 0; m < C * CPR / kThreads; ++m) {
+      const int q = tid + kThreads * m, r = q / CPR, cc = q % CPR;
+      const size_t off = (size_t)min(r, cn - 1) * ktok + cc * EPC;
+      *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = ld_once(kg + off);
+      if constexpr (WP) *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = ld_once(qg + off);
     }
   }
   if (wave == 0) {
@@ -325,23 +332,32 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     else
       tile_nt_k<DK / 16>(acca, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
   }
-  __syncthreads();   // Q is dead: A takes its bytes
+  __syncthreads();   // K and Q are dead: A takes their bytes
   // A[r][j] = beta_r exp(G_r - G_j) k_r.k_j (j < r); P[r][j] = exp(G_r - G_j) q_r.k_j
-  // (j <= r).  Masked entries are selected away (their weight may overflow).
+  // (j <= r).  Every weight is formed clamped to at most 1 before the masks
+  // select (left conditional, its loads would sink into per-element branches).
   if (wave < 3) {
     const int r = rb * 32 + col;
     const float Gr = G[r], br = Bt[r];
+    float w[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 gj = *reinterpret_cast<const float4*>(G + jb * 32 + acc_row(g, 0, lane));
+      w[4 * g + 0] = __expf(fminf(Gr - gj.x, 0.f));
+      w[4 * g + 1] = __expf(fminf(Gr - gj.y, 0.f));
+      w[4 * g + 2] = __expf(fminf(Gr - gj.z, 0.f));
+      w[4 * g + 3] = __expf(fminf(Gr - gj.w, 0.f));
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) asm volatile("" ::"v"(w[v]));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int j0 = jb * 32 + acc_row(g, 0, lane);
-      const float4 gj = *reinterpret_cast<const float4*>(G + j0);
-      const float gjv[4] = {gj.x, gj.y, gj.z, gj.w};
       float x[4], y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float w = __expf(Gr - gjv[e]);
-        x[e] = (j0 + e < r) ? br * w * acca[4 * g + e] : 0.f;
-        y[e] = (j0 + e <= r) ? w * accp[4 * g + e] : 0.f;
+        x[e] = (j0 + e < r) ? br * w[4 * g + e] * acca[4 * g + e] : 0.f;
+        y[e] = (j0 + e <= r) ? w[4 * g + e] * accp[4 * g + e] : 0.f;
       }
       store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
       if constexpr (WP) store4(Pw + r * C + j0, y[0], y[1], y[2], y[3]);
@@ -357,8 +373,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   // T -> the record, 64 x 64 contiguous, 16-byte stores
   {
     constexpr int CPT = C / EPC;
-    for (int q = tid; q < C * CPT; q += kThreads) {
-      const int r = q / CPT, cc = q % CPT;
+    static_assert(C * CPT % kThreads == 0, "T must split evenly over the threads");
+#pragma unroll
+    for (int m = 0; m < C * CPT / kThreads; ++m) {
+      const int q = tid + kThreads * m, r = q / CPT, cc = q % CPT;
       st_once(rec + R::t + r * C + cc * EPC, *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC));
     }
   }
