@@ -23,21 +23,23 @@
 // per-channel decay the exponentials are per key channel; see chunk_prep_kda.)
 //
 // A, T and P depend only on the chunk's keys, queries and gates, never on the
-// state, so a first, fully parallel kernel (one workgroup per chunk of every
-// head) computes them and hands them to the sequential kernel through a
-// workspace record per chunk.  The sequential kernel then only carries the
-// state chain X -> U -> (O, S) per chunk.
+// state, so they leave the state chain: a first, fully parallel kernel (one
+// workgroup per chunk of every head) computes T (and P, except for scalar decay
+// in bf16, where the state kernel's data waves form P from the K and Q rows
+// they stage anyway) and hands it over through a workspace record per chunk.
+// The sequential kernel then only carries the chain X -> U -> (O, S) per chunk.
 //
 // chunk_prep_kernel  (none / scalar decay; grid B * H * N_chunks)
-//   K, Q tiles and gates -> A and P (MFMA) -> 16x16 diagonal inverses
-//   (quad-DPP forward substitution) -> two levels of fp32 MFMA block products
-//   -> T; T, P and the gate rows -> record.
+//   K (fp32: and Q) tiles and gates -> A (and P) (MFMA) -> 16x16 diagonal
+//   inverses (quad-DPP forward substitution) -> two levels of fp32 MFMA block
+//   products -> T; T (P) and the gate rows -> record.
 // chunk_prep_kda     (per-channel decay; grid B * H * N_chunks)
 //   per-channel prefix of log alpha -> anchor-split decay factors -> A and P
 //   (MFMA) -> T; T, P, the decay-scaled K / Q operands and exp(G_C) -> record.
 // chunk_state_ws     (bf16; grid B * H * d_v / DVS, chunks in order)
 //   Four chain waves carry the fp32 state slice in MFMA accumulators; four
-//   data waves stream the chunks into LDS and the outputs back out.  Value
+//   data waves stream the chunks into LDS (and form P) and the outputs back
+//   out.  Value
 //   rows are independent ("On State Reduction" notes, section 2.5), so each
 //   workgroup owns one (b, h, d_v slice).
 // chunk_state_kernel (fp32; the same phases with four waves that also move
@@ -57,13 +59,11 @@ constexpr float kLogFloor = -100.f;  // gates below e^-100 act as e^-100 (= 0 in
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // Tiles are moved between HBM, registers and LDS in blocks of 4 rows x one
-// 16-byte chunk.  Block blk of a tile with cpr chunks per row covers rows
+// 16-byte chunk (used by the fp32 state kernel, which transposes from
+// registers).  Block blk of a tile with cpr chunks per row covers rows
 // 4 blk_row .. 4 blk_row + 3 and chunk blk_col.  Four consecutive blocks take
-// four row groups of one chunk, the next four the next chunk: a wave's global
-// loads cover whole rows and its row-major 16-byte LDS writes hit distinct
-// banks.  (Its transposed 8-byte writes of K^T and V^T do collide: rows 8
-// chunks apart share banks.  Measured: remapping a wave to all row groups of
-// four chunks removes that but costs more on the global side.)
+// four row groups of one chunk, the next four the next chunk, so a wave's
+// global loads cover whole rows.
 __device__ inline int blk_row(int blk, int cpr) { return (blk & 3) + 4 * (blk / (4 * cpr)); }
 __device__ inline int blk_col(int blk, int cpr) { return (blk >> 2) % cpr; }
 
