@@ -1562,23 +1562,30 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     // ---- interval A, phase 1: X = V - diag(gamma) K S^T, O_inter^T = S (diag(gamma) Q)^T ----
     f32x16 xacc = zero16(), oacc = zero16();
     if (own_rb >= 0) {
+      // the V columns and gate rows of the epilogue are read before the product
+      const int vc = own_ib * 32 + 16 * ((lane >> 4) & 1);
+      uint2 vw[4];
+      float4 eg[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = own_rb * 32 + acc_row(g, 0, lane);
+        vw[g] = tr_read4(Vr, LDV, r0, vc, lane);   // V[r0 .. r0 + 3][i]
+        eg[g] = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
+      }
+      const float egr = KDA ? 1.f : Eg[own_rb * 32 + col];   // O^T columns are the chunk rows r
       tile_nt2_shared_b<DK / 16, E, true, kP1Ahead, !KDA>(xacc, oacc, K1 + own_rb * 32 * (KDA ? LDK : LDKS),
                                                            Qr + own_rb * 32 * LDK, KDA ? LDK : LDKS, LDK,
                                           Sb + own_ib * 32 * LDSB, LDSB, lane);
       const int i = own_ib * 32 + col;
-      const int vc = own_ib * 32 + 16 * ((lane >> 4) & 1);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = own_rb * 32 + acc_row(g, 0, lane);
-        const float4 eg = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
-        const uint2 vw = tr_read4(Vr, LDV, r0, vc, lane);   // V[r0 .. r0 + 3][i]
-        const float4 v4 = make_float4(__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u),
-                                      __uint_as_float(vw.y << 16), __uint_as_float(vw.y & 0xffff0000u));
-        store4(Xt + i * LDT + r0, v4.x - eg.x * xacc[4 * g + 0], v4.y - eg.y * xacc[4 * g + 1],
-               v4.z - eg.z * xacc[4 * g + 2], v4.w - eg.w * xacc[4 * g + 3]);
+        const float4 v4 = make_float4(__uint_as_float(vw[g].x << 16), __uint_as_float(vw[g].x & 0xffff0000u),
+                                      __uint_as_float(vw[g].y << 16), __uint_as_float(vw[g].y & 0xffff0000u));
+        store4(Xt + i * LDT + r0, v4.x - eg[g].x * xacc[4 * g + 0], v4.y - eg[g].y * xacc[4 * g + 1],
+               v4.z - eg[g].z * xacc[4 * g + 2], v4.w - eg[g].w * xacc[4 * g + 3]);
       }
-      if constexpr (!KDA) {   // O^T columns are the chunk rows r
-        const float egr = Eg[own_rb * 32 + col];
+      if constexpr (!KDA) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[v] *= egr;
       }
