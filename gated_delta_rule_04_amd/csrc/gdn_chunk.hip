@@ -120,7 +120,9 @@ __device__ inline float chunk_log_decay(float alpha, bool ok) {
 //   Bt  beta [C] (zero for rows past the sequence end)
 //   Li  scratch for L^-1 = (I + A)^-1, fp32 [C][LDA]; may be Am itself (every
 //       step overwrites only blocks of A that it has finished reading)
-//   Mt  scratch, fp32 [32][LDM]
+//   Mt  scratch, fp32 [32][ldm]; in place it may be Am + 32 with ldm = LDA
+//       (rows 0..31, columns 32..63 of L^-1 are above the diagonal and never
+//       read)
 //   Tm  T in the operand dtype [C][LDT]; may share Am's bytes unless Li is Am
 // All threads of the workgroup take part; it ends with a barrier.
 template <typename E>
@@ -130,10 +132,10 @@ struct SolveLd {
   static constexpr int LDM = 32 + 4;
 };
 
-template <typename E>
+template <typename E, int LDM = SolveLd<E>::LDM>
 __device__ __attribute__((always_inline)) inline void tri_solve(const float* Am, float* Li, float* Mt,
                                                                 const float* Bt, E* Tm, int tid) {
-  constexpr int LDA = SolveLd<E>::LDA, LDT = SolveLd<E>::LDT, LDM = SolveLd<E>::LDM;
+  constexpr int LDA = SolveLd<E>::LDA, LDT = SolveLd<E>::LDT;
   const int lane = tid & 63, wave = tid >> 6;
   // (a) inverse of each unit-lower 16x16 diagonal block: wave w owns block w;
   // lane 4c + p computes column c, rows 4p .. 4p + 3, summing its part of each
@@ -246,16 +248,18 @@ struct PrepPlan {
   static constexpr int LDM = SolveLd<E>::LDM;
   static constexpr size_t es = sizeof(E);
   // bf16 (no Q): A takes the dead K rows' bytes and L^-1 overwrites A in
-  // place, T has bytes of its own; 31.7 KB, five workgroups per compute unit.
+  // place, the solve's scratch tile sits in L^-1's unused upper-right block,
+  // T has bytes of its own; 27.1 KB, six workgroups per compute unit.
   // fp32: L^-1 over the K rows; Q, then A, then T in a second region.
   static constexpr bool inplace = sizeof(E) == 2;
   static constexpr size_t r1 = cmax((size_t)C * LDK * es, (size_t)C * LDA * 4);
   static constexpr size_t kr = 0;   // K rows, then L^-1
   static constexpr size_t am = inplace ? 0 : r1;
   static constexpr size_t tm = inplace ? r1 : am;
-  static constexpr size_t mt = inplace ? tm + (size_t)C * LDT * es
+  static constexpr int ldm = inplace ? LDA : LDM;
+  static constexpr size_t mt = inplace ? (size_t)32 * 4   // A + 32 floats, leading dimension LDA
                                        : am + cmax((size_t)C * LDK * es, cmax((size_t)C * LDA * 4, (size_t)C * LDT * es));
-  static constexpr size_t g = mt + (size_t)32 * LDM * 4;
+  static constexpr size_t g = inplace ? tm + (size_t)C * LDT * es : mt + (size_t)32 * LDM * 4;
   static constexpr size_t total = g + 2 * C * 4;
 };
 
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   }
   __syncthreads();
 
-  tri_solve<E>(Am, Li, Mt, Bt, Tm, tid);
+  tri_solve<E, L::ldm>(Am, Li, Mt, Bt, Tm, tid);
   // T -> the record, 64 x 64 contiguous, 16-byte stores
   {
     constexpr int CPT = C / EPC;
