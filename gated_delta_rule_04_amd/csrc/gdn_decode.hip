@@ -10,13 +10,14 @@
 // notes, section 2.5), so every row is handled by its own group of lanes with
 // no cross-row communication.
 //
-// Layout of the work: eight lanes share a state row and lane l owns its float4
-// columns {4l + 32j}, so each load instruction of a wave covers eight rows as
-// contiguous 128-byte segments (coalesced 128-bit accesses).  Every thread
-// holds four float4 of state: one row at d_k = 128, two rows at d_k = 64; one
-// 256-thread workgroup takes 32 or 64 rows of a (b, h) head.  The fp32 rows
-// are held in registers between the read and the write, and the two row dot
-// products are finished with xor-shuffles over the eight lanes.
+// Layout of the work: LPR lanes share a state row (8 at d_k = 128, 16 at
+// d_k = 64) and lane l owns its float4 columns {4l + 4 LPR j}, so each load
+// instruction of a wave covers whole rows as contiguous segments (coalesced
+// 128-bit accesses).  A thread holds one row at d_k = 128 (four float4) and two
+// rows at d_k = 64 (one float4 each); one 256-thread workgroup takes 32 rows
+// of a (b, h) head.  The fp32 rows are held in registers between the read and
+// the write, and the two row dot products are finished with xor-shuffles over
+// the row's lanes.
 // The state is touched once per step, so its loads and stores are marked
 // non-temporal (they do not displace cached lines); with more, smaller
 // workgroups than heads the reads of later workgroups overlap the writes of
@@ -28,8 +29,12 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLanesPerRow = 8;
-constexpr int kFloat4PerThread = 4;
+// Lanes that share a state row and 16-byte state pieces per thread: d_k = 128
+// takes 8 lanes per 512-byte row, one row per thread; d_k = 64 takes 16 lanes
+// per 256-byte row, two rows per thread (measured: 12.04 against 12.22 us per
+// step with 8 lanes, batch 64, 16 heads, d_v = 128).
+template <int DK> constexpr int lanes_per_row() { return DK == 64 ? 16 : 8; }
+template <int DK> constexpr int f4_per_thread() { return DK == 64 ? 2 : 4; }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -70,9 +75,9 @@ __device__ inline float group_sum(float x) {
 
 template <typename E, int DK, int DV, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  constexpr int LPR = kLanesPerRow;                      // lanes per row
+  constexpr int LPR = lanes_per_row<DK>();               // lanes per row
   constexpr int NQ = DK / (4 * LPR);                     // float4 per lane per row
-  constexpr int NR = kFloat4PerThread / NQ;              // rows per thread
+  constexpr int NR = f4_per_thread<DK>() / NQ;           // rows per thread
   constexpr int RPW = kThreads / LPR;                    // rows per pass of the workgroup
   constexpr int RPG = RPW * NR;                          // rows per workgroup
   constexpr int GPH = DV / RPG;                          // workgroups per head
@@ -162,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
 template <typename E, int DK, int DV>
 hipError_t launch_mode(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int RPG = kThreads / kLanesPerRow * (kFloat4PerThread / (DK / (4 * kLanesPerRow)));
+  constexpr int LPR = lanes_per_row<DK>();
+  constexpr int RPG = kThreads / LPR * (f4_per_thread<DK>() / (DK / (4 * LPR)));
   dim3 grid((unsigned)(a.B * a.H * (DV / RPG))), block(kThreads);
   switch (a.mode) {
     case 0: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 0>), grid, block, 0, stream, a); break;
