@@ -9,7 +9,8 @@ Contents
 --------
 ``gdn_oracle.c``     plain fp64 token-by-token loop (prefill and decode), the
                      definition of what the path computes.
-``loop.py``          ctypes loader for it: :func:`gdn_fwd`, :func:`gdn_decode`.
+``loop.py``          ctypes loader for it: :func:`gdn_fwd`, :func:`gdn_fwd_varlen`
+                     (packed sequences of varying length), :func:`gdn_decode`.
 ``chunk_form.py``    fp64 NumPy chunkwise (UT/WY) rewrite of the same loop;
                      it is checked against the loop and documents the algebra
                      the GPU path follows, but never produces expected values
@@ -20,8 +21,8 @@ all oracle functions are pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (worked example, closed forms, exact rational
 evaluation of the product form, invariants).
 """
-from .loop import (gdn_fwd, gdn_decode, build, num_threads, Oracle, compile_library,
+from .loop import (gdn_fwd, gdn_fwd_varlen, gdn_decode, build, num_threads, Oracle, compile_library,
                    SOURCE, MODE_NONE, MODE_SCALAR, MODE_CHANNEL)
 
-__all__ = ["gdn_fwd", "gdn_decode", "build", "num_threads", "Oracle", "compile_library", "SOURCE",
+__all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_decode", "build", "num_threads", "Oracle", "compile_library", "SOURCE",
            "MODE_NONE", "MODE_SCALAR", "MODE_CHANNEL"]

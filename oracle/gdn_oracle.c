@@ -120,6 +120,79 @@ int oracle_gdn_fwd_f64(const double* q, const double* k, const double* v,
   return fail ? -1 : 0;
 }
 
+/* Prefill over a packed batch of N sequences of varying length.
+ *
+ * The tokens of all sequences lie back to back along one axis of length T:
+ * sequence s holds tokens cu[s] .. cu[s+1]-1 (cu[0] = 0, non-decreasing,
+ * cu[N] = T; empty sequences allowed).  The state starts again from S0[s]
+ * (zeros when S0 is NULL) at the first token of every sequence and nowhere
+ * else: a token that opens a document inside a sequence does not reset it
+ * (NextTransformer "method sources" page, baseline section on the packed
+ * rows of the recurrent mixers).
+ *
+ * The loop runs once over the whole token axis per head and performs the reset
+ * when the token index reaches the next boundary; it is written independently
+ * of oracle_gdn_fwd_f64 so that the two can be checked against each other.
+ *
+ * Layouts: q, k [T, H, dk]; v, o [T, H, dv]; alpha [T, H] or [T, H, dk];
+ * beta [T, H]; S0, S_final [N, H, dv, dk].  Returns 0, or -1 on a bad argument
+ * (including cu_seqlens that do not run from 0 to T without decreasing). */
+int oracle_gdn_fwd_varlen_f64(const double* q, const double* k, const double* v,
+                              const double* alpha, const double* beta,
+                              const double* S0, double* o, double* S_final,
+                              const int* cu, int N, int T, int H, int dk, int dv,
+                              int mode) {
+  long h;
+  int s, fail = 0;
+  const size_t sz = (size_t)dv * dk;
+  if (N < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || cu == NULL) return -1;
+  if (mode < MODE_NONE || mode > MODE_CHANNEL) return -1;
+  if (mode != MODE_NONE && alpha == NULL && T > 0) return -1;
+  if (cu[0] != 0 || cu[N] != T) return -1;
+  for (s = 0; s < N; ++s)
+    if (cu[s + 1] < cu[s]) return -1;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+  for (h = 0; h < H; ++h) {
+    double* S = (double*)malloc(sizeof(double) * sz);
+    double* p = (double*)malloc(sizeof(double) * (size_t)dv);
+    int seq = 0;
+    long t;
+    if (S == NULL || p == NULL) {
+      free(S);
+      free(p);
+      fail |= 1;
+      continue;
+    }
+    if (N > 0) {
+      if (S0 != NULL) memcpy(S, S0 + (size_t)h * sz, sizeof(double) * sz);
+      else memset(S, 0, sizeof(double) * sz);
+    }
+    for (t = 0; t <= T; ++t) {
+      /* close every sequence that ends before token t, open the next one */
+      while (seq < N && cu[seq + 1] == t) {
+        if (S_final != NULL) memcpy(S_final + ((size_t)seq * H + h) * sz, S, sizeof(double) * sz);
+        ++seq;
+        if (seq < N) {
+          if (S0 != NULL) memcpy(S, S0 + ((size_t)seq * H + h) * sz, sizeof(double) * sz);
+          else memset(S, 0, sizeof(double) * sz);
+        }
+      }
+      if (t == T) break;
+      {
+        size_t tok = (size_t)t * H + h;
+        const double* a = NULL;
+        if (mode == MODE_SCALAR) a = alpha + tok;
+        if (mode == MODE_CHANNEL) a = alpha + tok * dk;
+        oracle_step(S, q + tok * dk, k + tok * dk, v + tok * dv, a, beta[tok], o + tok * dv, dk, dv,
+                    mode, p);
+      }
+    }
+    free(S);
+    free(p);
+  }
+  return fail ? -1 : 0;
+}
+
 /* One decode step on S in place.
  *   q, k [B, H, dk]; v, o [B, H, dv]; alpha [B, H] (mode 1) or [B, H, dk]
  *   (mode 2); beta [B, H]; S [B, H, dv, dk] in/out. */

@@ -68,6 +68,9 @@ class Oracle:
         dp = ctypes.POINTER(ctypes.c_double)
         lib.oracle_gdn_fwd_f64.argtypes = [dp] * 8 + [ctypes.c_int] * 6
         lib.oracle_gdn_fwd_f64.restype = ctypes.c_int
+        lib.oracle_gdn_fwd_varlen_f64.argtypes = ([dp] * 8 + [ctypes.POINTER(ctypes.c_int)]
+                                                  + [ctypes.c_int] * 6)
+        lib.oracle_gdn_fwd_varlen_f64.restype = ctypes.c_int
         lib.oracle_gdn_decode_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 5
         lib.oracle_gdn_decode_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
@@ -104,6 +107,45 @@ class Oracle:
         if rc != 0:
             raise RuntimeError("oracle_gdn_fwd_f64 failed (rc=%d)" % rc)
         return o, S
+
+    def gdn_fwd_varlen(self, q, k, v, alpha, beta, cu_seqlens, S0=None, mode: int = MODE_SCALAR):
+        """Prefill of a packed batch: sequence s holds tokens cu_seqlens[s] ..
+        cu_seqlens[s + 1] - 1 of the token axis, and its state starts from S0[s]
+        (zeros when S0 is None) at its first token.
+
+        q, k [T, H, dk]; v [T, H, dv]; alpha [T, H] (mode 1), [T, H, dk] (mode 2)
+        or None; beta [T, H]; cu_seqlens N + 1 integers; S0 [N, H, dv, dk] or None.
+        A leading axis of size 1 on the token tensors is accepted and kept.
+        Returns (o, S_final [N, H, dv, dk]) as fp64 ndarrays."""
+        q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+        alpha, S0 = _f64(alpha), _f64(S0)
+        lead = q.ndim == 4
+        if lead:
+            assert q.shape[0] == 1
+            q, k, v, beta = q[0], k[0], v[0], beta[0]
+            alpha = None if alpha is None else alpha[0]
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+        T, H, dk = q.shape
+        dv = v.shape[-1]
+        assert k.shape == q.shape and v.shape == (T, H, dv) and beta.shape == (T, H)
+        if mode == MODE_SCALAR:
+            assert alpha is not None and alpha.shape == (T, H)
+        elif mode == MODE_CHANNEL:
+            assert alpha is not None and alpha.shape == (T, H, dk)
+        else:
+            alpha = None
+        if S0 is not None:
+            assert S0.shape == (N, H, dv, dk)
+        o = np.zeros((T, H, dv), dtype=np.float64)
+        S = np.zeros((N, H, dv, dk), dtype=np.float64)
+        rc = self._lib.oracle_gdn_fwd_varlen_f64(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S),
+            cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), N, T, H, dk, dv, mode)
+        if rc != 0:
+            raise RuntimeError("oracle_gdn_fwd_varlen_f64 failed (rc=%d)" % rc)
+        return (o[None] if lead else o), S
 
     def gdn_decode(self, q, k, v, alpha, beta, S, mode: int = MODE_SCALAR):
         """One decode step.  q, k [B, H, dk]; v [B, H, dv]; alpha [B, H] or
@@ -142,6 +184,10 @@ def default() -> Oracle:
 
 def gdn_fwd(*args, **kw):
     return default().gdn_fwd(*args, **kw)
+
+
+def gdn_fwd_varlen(*args, **kw):
+    return default().gdn_fwd_varlen(*args, **kw)
 
 
 def gdn_decode(*args, **kw):

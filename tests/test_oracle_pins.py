@@ -411,11 +411,48 @@ def pin_decode_matches_prefill(orc):
         assert np.array_equal(np.concatenate([oa, ob], 1), o) and np.array_equal(Sb, S)
 
 
+def pin_varlen_resets_at_sequence_starts(orc):
+    """A packed batch (sequences back to back on one token axis) equals separate
+    runs of the sequences, each from its own initial state: the state restarts
+    at the first token of every sequence and nowhere else (NT, baseline section:
+    the recurrent mixers reset their state at the start of each packed row).
+    Covers empty sequences, lengths of one token, and a single sequence."""
+    rng = np.random.default_rng(27)
+    H, dk, dv = 2, 4, 3
+    for mode in MODES:
+        for lens in ([5, 0, 1, 7, 0, 3], [9], [0, 4], [3, 3, 3]):
+            cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            T, N = int(cu[-1]), len(lens)
+            q, k, v, alpha, beta, _ = _inputs(rng, 1, T, H, dk, dv, mode)
+            S0 = rng.standard_normal((N, H, dv, dk))
+            sq = lambda x: None if x is None else x[0]
+            for s0 in (S0, None):
+                o, S = orc.gdn_fwd_varlen(q[0], k[0], v[0], sq(alpha), beta[0], cu, s0, mode=mode)
+                assert o.shape == (T, H, dv) and S.shape == (N, H, dv, dk)
+                for s in range(N):
+                    a, b = int(cu[s]), int(cu[s + 1])
+                    sl = lambda x: None if x is None else x[:, a:b]
+                    init = None if s0 is None else s0[s:s + 1]
+                    os_, Ss = orc.gdn_fwd(q[:, a:b], k[:, a:b], v[:, a:b], sl(alpha), beta[:, a:b],
+                                          init, mode=mode)
+                    assert np.array_equal(o[a:b], os_[0])
+                    assert np.array_equal(S[s], Ss[0])
+        # equal lengths: the same as a batch of rows
+        L, N = 4, 3
+        q, k, v, alpha, beta, S0 = _inputs(rng, N, L, H, dk, dv, mode)
+        cu = np.arange(0, N * L + 1, L, dtype=np.int32)
+        flat = lambda x: None if x is None else x.reshape((N * L,) + x.shape[2:])
+        o, S = orc.gdn_fwd_varlen(flat(q), flat(k), flat(v), flat(alpha), flat(beta), cu, S0,
+                                  mode=mode)
+        ob, Sb = orc.gdn_fwd(q, k, v, alpha, beta, S0, mode=mode)
+        assert np.array_equal(o, flat(ob)) and np.array_equal(S, Sb)
+
+
 PINS = [pin_worked_example, pin_exact_recall, pin_orthonormal_closed_form,
         pin_kda_axis_keys_closed_form, pin_no_write, pin_exact_rational, pin_gradient_step,
         pin_orthogonal_invariance, pin_rank_bound, pin_value_channel_independence,
         pin_linearity, pin_contraction, pin_mode_reductions, pin_zero_gate_resets,
-        pin_decode_matches_prefill]
+        pin_decode_matches_prefill, pin_varlen_resets_at_sequence_starts]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -434,6 +471,14 @@ def test_oracle_empty_sequence_returns_initial_state():
     _, S = oracle.gdn_fwd(z, z, np.zeros((2, 0, 3, 4)), None, np.zeros((2, 0, 3)), None,
                           mode=MODE_NONE)
     assert np.array_equal(S, np.zeros((2, 3, 4, 5)))
+
+
+def test_oracle_varlen_rejects_bad_offsets():
+    """Offsets must run from 0 to T without decreasing."""
+    z, v, b = np.zeros((6, 1, 4)), np.zeros((6, 1, 3)), np.zeros((6, 1))
+    for cu in ([0, 4, 2, 6], [1, 6], [0, 5], [0, 3, 7]):
+        with pytest.raises(RuntimeError):
+            oracle.gdn_fwd_varlen(z, z, v, None, b, np.array(cu), mode=MODE_NONE)
 
 
 # ----------------------------------------------------------------------------------
@@ -481,6 +526,10 @@ MUTATIONS = {
     "read_uses_key": ("acc += S[i * dk + c] * q[c];", "acc += S[i * dk + c] * k[c];"),
     "write_uses_query": ("S[i * dk + c] += u * k[c];", "S[i * dk + c] += u * q[c];"),
     "error_without_beta": ("double u = beta * (v[i] - p[i]);", "double u = (v[i] - p[i]);"),
+    "varlen_wrong_initial_state": ("memcpy(S, S0 + ((size_t)seq * H + h) * sz",
+                                   "memcpy(S, S0 + ((size_t)(seq - 1) * H + h) * sz"),
+    "varlen_boundary_one_late": ("while (seq < N && cu[seq + 1] == t) {",
+                                 "while (seq < N && t > 0 && cu[seq + 1] == t - 1) {"),
 }
 
 
