@@ -10,7 +10,9 @@ the state it returns.  ``value`` is prefill throughput in tokens/s (B*T per
 step).  The decode step's own throughput (GB/s against HBM peak) is measured
 on the batch-64 x 16-head decode workload, 1024 steps captured in a HIP graph,
 both in place on one state (as the recurrence runs) and rotated over 16 state
-buffers so the 67 MB state cannot stay in the 256 MB Infinity Cache.
+buffers so the 67 MB state cannot stay in the 256 MB Infinity Cache.  The
+packed variable-length prefill (the same 32768 tokens x 16 heads split into 16
+rows of 593 to 5858 tokens) is timed alongside (``packed``).
 
 Printed: one JSON line (the contract below), preceded by progress lines on
 stderr.  Peaks are MI355X's published figures: HBM 8 TB/s, dense bf16 MFMA
@@ -165,6 +167,46 @@ def bench_step(w: W.Prefill, steps: int, warmup: int):
     launch_ms = b0.elapsed_time(b1) / steps
     # outputs of the last launch, for the parity spot check against the oracle
     return dict(wall_s=wall, kernel_ms=kern_ms, launch_ms=launch_ms, host=host, o=o, S=S)
+
+
+def packed_bytes(w: W.Packed) -> int:
+    """Algorithmic bytes of a packed prefill: the rows' tokens as one row, plus
+    one initial (if given) and one final state per sequence."""
+    rows = prefill_bytes(W.Prefill(w.name, 1, w.H, w.T, w.dk, w.dv, w.dtype, w.gate, 0.0, w.seed))
+    rows -= w.H * w.dv * w.dk * 4                                   # the single row's S_final
+    return rows + w.N * w.H * w.dv * w.dk * 4 * (2 if w.s0_std > 0 else 1) + (w.N + 1) * 4
+
+
+def bench_packed(w: W.Packed, steps: int):
+    """Average duration of one ``gdn_chunk_fwd_varlen`` launch: ``steps``
+    launches back to back between one event pair, behind a running launch."""
+    log("generating %s" % w.name)
+    host = W.make_packed(w)
+    d = {k: (None if v is None else v.cuda()) for k, v in host.items()}
+    o = torch.empty((1, w.T, w.H, w.dv), dtype=w.dtype, device="cuda")
+    S = torch.empty((w.N, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+
+    def launch():
+        gdn.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["cu_seqlens"],
+                             d["S0"], mode=w.mode, o=o, S_final=S)
+
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    launch()
+    b0.record()
+    for _ in range(steps):
+        launch()
+    b1.record()
+    torch.cuda.synchronize()
+    ms = b0.elapsed_time(b1) / steps
+    nbytes = packed_bytes(w)
+    lens = W.packed_lengths(w)
+    return dict(workload=w.name, N=w.N, T=w.T, H=w.H, lengths_min=min(lens), lengths_max=max(lens),
+                launch_us=ms * 1e3, tokens_per_s=w.T / (ms * 1e-3),
+                hbm_gbps=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                algorithmic_bytes=nbytes)
 
 
 def bench_decode(w: W.Decode, reps: int = 3, rotate: int = 1):
@@ -336,6 +378,8 @@ def main():
                     choices=[w.name for w in W.PREFILL_WORKLOADS])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="skip the packed variable-length prefill workload")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -391,6 +435,13 @@ def main():
             log("decode %s: in place %.2f us/step %.0f GB/s; rotated %.2f us/step %.0f GB/s" % (
                 dw.name, lit["us_per_step"], lit["gbps"], rot["us_per_step"], rot["gbps"]))
 
+    packed = None
+    if not args.no_packed:
+        packed = bench_packed(W.GDN_BF16_PACKED, args.steps)
+        log("packed %s: %.1f us per launch, %.3g tokens/s (rows %d..%d tokens)" % (
+            packed["workload"], packed["launch_us"], packed["tokens_per_s"], packed["lengths_min"],
+            packed["lengths_max"]))
+
     copy_gbps = device_copy_gbps()   # also the known-size reference for HBM byte counters
     log("device copy %.0f GB/s" % copy_gbps)
 
@@ -410,7 +461,7 @@ def main():
                            decay={0: "none", 1: "scalar", 2: "channel"}[w.mode],
                            step="chunked prefill + first decode token",
                            state="fp32", parallelism="single GPU"),
-               roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode,
+               roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode, packed=packed,
                device_copy_gbps=copy_gbps)
     print(json.dumps(out), flush=True)
 

@@ -6,6 +6,8 @@ device memory and the current HIP stream.  There is no CPU fallback: if the
 library is missing or does not load, every call raises.
 
     o, S_final = chunk_fwd(q, k, v, alpha, beta, S0)      # prefill
+    o, S_final = chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0)
+                                                           # packed sequences
     o = decode_step(q, k, v, alpha, beta, S)               # one token, S in place
 """
 from __future__ import annotations
@@ -16,14 +18,15 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "load", "lib_path", "GDNError",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "decode_step", "load", "lib_path", "GDNError",
            "DECAY_NONE", "DECAY_SCALAR", "DECAY_CHANNEL", "EXPORTED_SYMBOLS"]
 
 DECAY_NONE, DECAY_SCALAR, DECAY_CHANNEL = 0, 1, 2
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
-EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step",
-                    "gdn_status_string", "gdn_version")
+EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
+                    "gdn_chunk_fwd_varlen_workspace_bytes", "gdn_chunk_fwd_varlen",
+                    "gdn_decode_step", "gdn_status_string", "gdn_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -56,6 +59,10 @@ def load():
         lib.gdn_chunk_fwd_workspace_bytes.restype = sz
         lib.gdn_chunk_fwd.argtypes = [vp] * 8 + [vp, sz] + [i] * 8 + [vp]
         lib.gdn_chunk_fwd.restype = i
+        lib.gdn_chunk_fwd_varlen_workspace_bytes.argtypes = [i] * 8
+        lib.gdn_chunk_fwd_varlen_workspace_bytes.restype = sz
+        lib.gdn_chunk_fwd_varlen.argtypes = [vp] * 9 + [vp, sz] + [i] * 8 + [vp]
+        lib.gdn_chunk_fwd_varlen.restype = i
         lib.gdn_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.gdn_decode_step.restype = i
         lib.gdn_status_string.argtypes = [i]
@@ -136,6 +143,55 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, *, mode=None, chunk=64, o=None, S_f
     st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None), _ptr(beta),
                            _ptr(S0), _ptr(o), _ptr(S_final), _ptr(ws), ws_bytes,
                            B, T, H, dk, dv, chunk, _DTYPES[dtype], mode, _stream(stream))
+    _check(st)
+    return o, S_final
+
+
+def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, *, mode=None, chunk=64, o=None,
+                     S_final=None, need_final=True, stream=None):
+    """Chunked prefill of a packed batch through ``gdn_chunk_fwd_varlen``.
+
+    q, k [T, H, dk]; v [T, H, dv] (a leading axis of 1 is accepted and kept);
+    alpha fp32 [T, H], ``dtype`` [T, H, dk] or None; beta fp32 [T, H];
+    cu_seqlens int32 GPU tensor [N + 1] (0, ..., T, non-decreasing); S0 fp32
+    [N, H, dv, dk] or None.  Returns (o, S_final [N, H, dv, dk])."""
+    lib = load()
+    lead = q.dim() == 4
+    T, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    if lead and q.shape[0] != 1:
+        raise ValueError("a packed batch has a leading axis of 1, got %d" % q.shape[0])
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    _require(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens is None or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    N = cu_seqlens.shape[0] - 1
+    if mode is None:
+        mode = DECAY_NONE if alpha is None else (
+            DECAY_SCALAR if alpha.dim() == q.dim() - 1 else DECAY_CHANNEL)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, dtype)
+    _require(beta, "beta", torch.float32)
+    _require(S0, "S0", torch.float32)
+    if mode == DECAY_SCALAR:
+        _require(alpha, "alpha", torch.float32)
+    elif mode == DECAY_CHANNEL:
+        _require(alpha, "alpha", dtype)
+    if o is None:
+        o = torch.empty(tuple(q.shape[:-1]) + (dv,), dtype=dtype, device=q.device)
+    if S_final is None and need_final:
+        S_final = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    _require(o, "o", dtype)
+    _require(S_final, "S_final", torch.float32)
+    ws_bytes = int(lib.gdn_chunk_fwd_varlen_workspace_bytes(N, T, H, dk, dv, chunk,
+                                                            _DTYPES[dtype], mode))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    st = lib.gdn_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None),
+                                  _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens),
+                                  _ptr(ws), ws_bytes, N, T, H, dk, dv, chunk, _DTYPES[dtype], mode,
+                                  _stream(stream))
     _check(st)
     return o, S_final
 

@@ -55,7 +55,7 @@ gdn_status check_common(int B, int H, int dk, int dv, gdn_dtype dtype, gdn_decay
 
 extern "C" {
 
-int gdn_version(void) { return 100; }
+int gdn_version(void) { return 200; }
 
 const char* gdn_status_string(gdn_status s) {
   switch (s) {
@@ -126,6 +126,71 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void
 
   gdn::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_final, B, T, H, dk, dv, (int)dtype,
                      (int)mode};
+  return gdn::launch_prefill(a, workspace, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+size_t gdn_chunk_fwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv, int chunk,
+                                            gdn_dtype dtype, gdn_decay mode) {
+  if (check_common(N, H, dk, dv, dtype, mode) != GDN_OK || T < 0 || chunk != kChunk) return 0;
+  long long n;
+  if (!count4((long long)T / kChunk + N, H, 1, 1, &n) || (long long)T / kChunk + N > 0x7fffffffLL)
+    return 0;
+  return gdn::prefill_varlen_workspace_bytes(N, T, H, dk, (int)dtype, (int)mode);
+}
+
+gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                                const float* beta, const float* S0, void* o, float* S_final,
+                                const int* cu_seqlens, void* workspace, size_t workspace_bytes,
+                                int N, int T, int H, int dk, int dv, int chunk, gdn_dtype dtype,
+                                gdn_decay mode, hipStream_t stream) {
+  gdn_status st = check_common(N, H, dk, dv, dtype, mode);
+  if (st != GDN_OK) return st;
+  if (T < 0) return GDN_ERR_SHAPE;
+  if (chunk != kChunk) return GDN_ERR_UNSUPPORTED;
+  if (N == 0 && T > 0) return GDN_ERR_SHAPE;   // tokens outside every sequence
+  long long nqk, nv, ntok, nS;
+  if (!count4(1, T, H, dk, &nqk) || !count4(1, T, H, dv, &nv) || !count4(1, T, H, 1, &ntok) ||
+      !count4(N, H, dv, dk, &nS))
+    return GDN_ERR_SHAPE;
+  if ((long long)N * H * (dv / 32) > 0x7fffffffLL) return GDN_ERR_SHAPE;
+  if ((long long)T / kChunk + N > 0x7fffffffLL ||
+      ((long long)T / kChunk + N) * H > 0x7fffffffLL)
+    return GDN_ERR_SHAPE;
+  const size_t ws_need = gdn_chunk_fwd_varlen_workspace_bytes(N, T, H, dk, dv, chunk, dtype, mode);
+  if (workspace_bytes < ws_need) return GDN_ERR_WORKSPACE;
+  if (N == 0 || H == 0) return GDN_OK;
+  if (!cu_seqlens) return GDN_ERR_NULL;
+  if (ws_need > 0 && !workspace) return GDN_ERR_NULL;
+  const bool has_tokens = T > 0;
+  if (has_tokens) {
+    if (!q || !k || !v || !beta || !o) return GDN_ERR_NULL;
+    if (mode != GDN_DECAY_NONE && !alpha) return GDN_ERR_NULL;
+  }
+  if (!has_tokens && !S_final) return GDN_OK;  // nothing to write
+
+  const size_t es = elem_size(dtype);
+  const size_t a_bytes = mode == GDN_DECAY_SCALAR ? (size_t)ntok * 4
+                         : mode == GDN_DECAY_CHANNEL ? (size_t)nqk * es : 0;
+  Range rq = range_of(has_tokens ? q : nullptr, (size_t)nqk * es);
+  Range rk = range_of(has_tokens ? k : nullptr, (size_t)nqk * es);
+  Range rv = range_of(has_tokens ? v : nullptr, (size_t)nv * es);
+  Range ra = range_of(has_tokens && mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes);
+  Range rb = range_of(has_tokens ? beta : nullptr, (size_t)ntok * 4);
+  Range rs0 = range_of(S0, (size_t)nS * 4);
+  Range rcu = range_of(cu_seqlens, ((size_t)N + 1) * 4);
+  Range ro = range_of(has_tokens ? o : nullptr, (size_t)nv * es);
+  Range rsf = range_of(S_final, (size_t)nS * 4);
+  for (Range in : {rq, rk, rv, ra, rb, rs0, rcu})
+    if (overlaps(ro, in)) return GDN_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, ra, rb, ro, rcu})
+    if (overlaps(rsf, in)) return GDN_ERR_ALIAS;
+  if (overlaps(rsf, rs0) && (const void*)S_final != (const void*)S0) return GDN_ERR_ALIAS;
+  Range rw = range_of(ws_need > 0 ? workspace : nullptr, ws_need);
+  for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, ro, rsf})
+    if (overlaps(rw, in)) return GDN_ERR_ALIAS;
+
+  gdn::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_final, N, T, H, dk, dv, (int)dtype,
+                     (int)mode, cu_seqlens, gdn::varlen_slots(N, T)};
   return gdn::launch_prefill(a, workspace, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 

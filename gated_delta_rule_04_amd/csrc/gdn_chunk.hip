@@ -58,6 +58,77 @@ constexpr float kLogFloor = -100.f;  // gates below e^-100 act as e^-100 (= 0 in
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
+// Where the tokens of one sequence lie and where its chunk records start.
+//   B rows of T tokens: sequence b is row b; its chunk n of head h has record
+//     (b H + h) N_chunks + n.
+//   packed batch: sequence b holds tokens cu[b] .. cu[b + 1] - 1 of the token
+//     axis; its chunk n of head h has record h nslots + cu[b] / C + b + n.
+//     Sequence b's records end at slot floor(cu[b + 1] / C) + b at most, below
+//     the next sequence's first one, and every slot is below T / C + B.
+// Offsets are clamped into [0, T] (each sequence to a range of its own start):
+// malformed offsets then give unspecified results but never an access outside
+// the buffers.
+struct Span {
+  size_t tok0;   // first token on the token axis ([B * T] for rows of T tokens)
+  int len;       // tokens of the sequence
+  size_t rec0;   // record of its chunk 0
+};
+
+__device__ inline Span seq_span(const PrefillArgs& a, int b, int h) {
+  if (a.cu_seqlens) {
+    const int s0 = min(max(a.cu_seqlens[b], 0), a.T);
+    const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.T);
+    return Span{(size_t)s0, s1 - s0, (size_t)h * a.nslots + s0 / C + b};
+  }
+  return Span{(size_t)b * a.T, a.T, ((size_t)b * a.H + h) * (size_t)((a.T + C - 1) / C)};
+}
+
+// Packed batch: the sequence whose records may hold slot `slot`, i.e. the
+// largest b with cu[b] / C + b <= slot (that bound grows strictly with b).  A
+// 64-ary search, each wave on its own: 64 probes per round, as many rounds as
+// the base-64 digits of B.
+__device__ inline int seq_of_slot(const PrefillArgs& a, int slot) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, span = a.B;   // the answer lies in [lo, lo + span)
+  while (span > 1) {
+    const int stride = (span + 63) / 64;
+    const int bq = lo + lane * stride;
+    bool le = false;
+    if (bq < lo + span) le = min(max(a.cu_seqlens[bq], 0), a.T) / C + bq <= slot;
+    const int cnt = __popcll(__ballot(le));
+    if (cnt == 0) return lo;
+    const int nlo = lo + (cnt - 1) * stride;
+    span = min(stride, lo + span - nlo);
+    lo = nlo;
+  }
+  return lo;
+}
+
+// The chunk one prep workgroup handles: sequence b, head h, chunk n of the
+// sequence.  B rows of T tokens: workgroup (b H + h) N_chunks + n.  Packed
+// batch: workgroup h nslots + slot; false when no chunk falls on the slot.
+struct PrepAt {
+  int b, h, n;
+  Span sp;
+};
+
+__device__ inline bool prep_at(const PrefillArgs& a, int nchunks, PrepAt& p) {
+  if (!a.cu_seqlens) {
+    const int bh = blockIdx.x / nchunks;
+    p.n = blockIdx.x % nchunks;
+    p.h = bh % a.H;
+    p.b = bh / a.H;
+    p.sp = seq_span(a, p.b, p.h);
+    return true;
+  }
+  p.h = blockIdx.x / a.nslots;
+  const int slot = blockIdx.x % a.nslots;
+  p.b = seq_of_slot(a, slot);
+  p.sp = seq_span(a, p.b, p.h);
+  p.n = slot - (int)(p.sp.rec0 - (size_t)p.h * a.nslots);
+  return p.n >= 0 && p.n * C < p.sp.len;
+}
+
 // Tiles are moved between HBM, registers and LDS in blocks of 4 rows x one
 // 16-byte chunk (used by the fp32 state kernel, which transposes from
 // registers).  Block blk of a tile with cpr chunks per row covers rows
@@ -283,13 +354,12 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   float* Bt = G + C;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
-  const int H = a.H, T = a.T;
-  const int n = blockIdx.x % nchunks;
-  const int bh = blockIdx.x / nchunks;
-  const int h = bh % H, b = bh / H;
-  const int t0 = n * C, cn = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;   // first token of the chunk in [B, T]
-  E* rec = tws + (size_t)blockIdx.x * R::elems;
+  PrepAt at;
+  if (!prep_at(a, nchunks, at)) return;
+  const int H = a.H, h = at.h, n = at.n;
+  const int t0 = n * C, cn = min(C, at.sp.len - t0);
+  const size_t tok0 = at.sp.tok0 + t0;   // first token of the chunk on the token axis
+  E* rec = tws + (at.sp.rec0 + n) * R::elems;
   E* Pw = rec + R::p;
 
   // K (and Q) rows, consecutive threads along a row (rows past the sequence
@@ -526,16 +596,15 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   uint32_t* Msk = reinterpret_cast<uint32_t*>(smem + L::msk);   // [2][DK / 32]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
-  const int H = a.H, T = a.T;
-  const int n = blockIdx.x % nchunks;
-  const int bh = blockIdx.x / nchunks;
-  const int h = bh % H, b = bh / H;
-  const int t0 = n * C, cn = min(C, T - t0);
-  const size_t tok0 = (size_t)b * T + t0;
+  PrepAt at;
+  if (!prep_at(a, nchunks, at)) return;
+  const int H = a.H, h = at.h, n = at.n;
+  const int t0 = n * C, cn = min(C, at.sp.len - t0);
+  const size_t tok0 = at.sp.tok0 + t0;
   const size_t qk_tok = (size_t)H * DK;
   const E* kgl = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
   const E* qgl = static_cast<const E*>(a.q) + (tok0 * H + h) * DK;
-  E* rec = tws + (size_t)blockIdx.x * R::elems;
+  E* rec = tws + (at.sp.rec0 + n) * R::elems;
 
   // This thread's (row, 16-byte chunk) items of K and Q, loaded once for all
   // passes: item m is row (tid + kThreads m) / CPR (rows 0..31 for m < IPT,
@@ -836,7 +905,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31;
-  const int H = a.H, T = a.T, dv = a.dv;
+  const int H = a.H, dv = a.dv;
   const int nsl = dv / DVS;
   const int nheads = a.B * H;
   // Workgroups are dispatched round-robin over the eight XCDs: give the slices
@@ -852,15 +921,17 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   }
   const int h = head % H, b = head / H;
   const int i0 = sl * DVS;
+  const Span sp = seq_span(a, b, h);
+  const int T = sp.len;   // tokens of this sequence
   const int nchunks = (T + C - 1) / C;
 
   const size_t qk_tok = (size_t)H * DK;   // stride between tokens in q, k
   const size_t v_tok = (size_t)H * dv;    // stride between tokens in v, o
-  const E* qg = static_cast<const E*>(a.q) + ((size_t)b * T * H + h) * DK;
-  const E* kg = static_cast<const E*>(a.k) + ((size_t)b * T * H + h) * DK;
-  const E* vg = static_cast<const E*>(a.v) + ((size_t)b * T * H + h) * dv + i0;
-  const E* recs = tws + (size_t)head * nchunks * R::elems;   // per-chunk records
-  E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
+  const E* qg = static_cast<const E*>(a.q) + (sp.tok0 * H + h) * DK;
+  const E* kg = static_cast<const E*>(a.k) + (sp.tok0 * H + h) * DK;
+  const E* vg = static_cast<const E*>(a.v) + (sp.tok0 * H + h) * dv + i0;
+  const E* recs = tws + sp.rec0 * R::elems;   // per-chunk records
+  E* og = static_cast<E*>(a.o) + (sp.tok0 * H + h) * dv + i0;
   const size_t sbase = ((size_t)b * H + h) * dv + i0;  // first state row of the slice
 
   // Tile ownership: X, O_inter (phase 1), U (phase 4) and O (phase 5) tiles of
@@ -1296,7 +1367,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  const int H = a.H, T = a.T, dv = a.dv;
+  const int H = a.H, dv = a.dv;
   const int nsl = dv / DVS;
   const int nheads = a.B * H;
   // Workgroups are dispatched round-robin over the eight XCDs: give the slices
@@ -1312,6 +1383,8 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   }
   const int h = head % H, b = head / H;
   const int i0 = sl * DVS;
+  const Span sp = seq_span(a, b, h);
+  const int T = sp.len;   // tokens of this sequence
   const int nchunks = (T + C - 1) / C;
   const size_t v_tok = (size_t)H * dv;
   const size_t sbase = ((size_t)b * H + h) * dv + i0;
@@ -1320,11 +1393,11 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     // ======================= data waves =======================
     const int ptid = tid - 256;
     const size_t qk_tok = (size_t)H * DK;
-    const E* qg = static_cast<const E*>(a.q) + ((size_t)b * T * H + h) * DK;
-    const E* kg = static_cast<const E*>(a.k) + ((size_t)b * T * H + h) * DK;
-    const E* vg = static_cast<const E*>(a.v) + ((size_t)b * T * H + h) * dv + i0;
-    const E* recs = tws + (size_t)head * nchunks * R::elems;
-    E* og = static_cast<E*>(a.o) + ((size_t)b * T * H + h) * dv + i0;
+    const E* qg = static_cast<const E*>(a.q) + (sp.tok0 * H + h) * DK;
+    const E* kg = static_cast<const E*>(a.k) + (sp.tok0 * H + h) * DK;
+    const E* vg = static_cast<const E*>(a.v) + (sp.tok0 * H + h) * dv + i0;
+    const E* recs = tws + sp.rec0 * R::elems;
+    E* og = static_cast<E*>(a.o) + (sp.tok0 * H + h) * dv + i0;
 
     u32x4 pk[KPT], pq[KPT], pv[VPT], pkc[KDA ? KPT : 1];   // rows of a chunk
     u32x4 pg = u32x4{0u, 0u, 0u, 0u};
@@ -1755,9 +1828,12 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
 template <typename E, int DK>
 hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) {
   E* tws = static_cast<E*>(workspace);
-  const int nchunks = (a.T + C - 1) / C;
-  if (nchunks > 0) {
-    dim3 grid((unsigned)((size_t)a.B * a.H * nchunks)), block(kThreads);
+  // One prep workgroup per chunk of every head; a packed batch takes one per
+  // record slot (slots that no chunk falls on return at once).
+  const int nchunks = a.cu_seqlens ? a.nslots : (a.T + C - 1) / C;
+  const size_t nprep = a.cu_seqlens ? (a.T > 0 ? (size_t)a.H * a.nslots : 0) : (size_t)a.B * a.H * nchunks;
+  if (nprep > 0) {
+    dim3 grid((unsigned)nprep), block(kThreads);
     if (a.mode == 0)
       hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 0>), grid, block, 0, stream, a, tws, nchunks);
     else if (a.mode == 1)
@@ -1778,11 +1854,22 @@ hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) 
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dtype, int mode) {
-  const size_t chunks = (size_t)B * H * (((size_t)T + C - 1) / C);
+// Bytes of one chunk record.
+static size_t record_bytes(int dk, int dtype, int mode) {
   const size_t es = dtype == 1 ? 2 : 4;
-  if (mode == 2) return chunks * ((2 * (size_t)C * C + 3 * (size_t)C * dk) * es + 4 * (size_t)dk);
-  return chunks * ((es == 4 ? 2 : 1) * (size_t)C * C * es + kGateFloats * 4);   // bf16: no P
+  if (mode == 2) return (2 * (size_t)C * C + 3 * (size_t)C * dk) * es + 4 * (size_t)dk;
+  return (es == 4 ? 2 : 1) * (size_t)C * C * es + kGateFloats * 4;   // bf16: no P
+}
+
+size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dtype, int mode) {
+  return (size_t)B * H * (((size_t)T + C - 1) / C) * record_bytes(dk, dtype, mode);
+}
+
+int varlen_slots(int N, int T) { return T / C + N; }
+
+size_t prefill_varlen_workspace_bytes(int N, int T, int H, int dk, int dtype, int mode) {
+  if (T == 0) return 0;
+  return (size_t)H * varlen_slots(N, T) * record_bytes(dk, dtype, mode);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream) {

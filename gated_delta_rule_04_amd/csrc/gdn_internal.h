@@ -23,6 +23,12 @@ struct PrefillArgs {
   int B, T, H, dk, dv;
   int dtype;         // 0 fp32, 1 bf16
   int mode;          // 0 none, 1 scalar, 2 channel
+  // Packed batch of sequences of varying length: B sequences back to back on
+  // a token axis of length T (the layouts above with a leading batch of 1),
+  // sequence b holding tokens cu_seqlens[b] .. cu_seqlens[b + 1] - 1 (device
+  // int32 [B + 1]).  Null for B rows of T tokens each.
+  const int* cu_seqlens = nullptr;
+  int nslots = 0;    // packed batch: chunk records per head, T / 64 + B
 };
 
 // Arguments of one decode launch: q, k [B, H, dk]; v, o [B, H, dv];
@@ -47,6 +53,12 @@ struct DecodeArgs {
 // K, Q and K (64 x dk each, operand dtype) and the chunk's per-channel decay
 // (dk fp32).
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dtype, int mode);
+// The same for a packed batch of N sequences with T tokens in all.
+size_t prefill_varlen_workspace_bytes(int N, int T, int H, int dk, int dtype, int mode);
+// Chunk records per head of a packed batch (an upper bound of the chunks of
+// any N sequences with T tokens in all: sequence b's chunk n takes record
+// slot cu_seqlens[b] / 64 + b + n).
+int varlen_slots(int N, int T);
 // Enqueue the prefill kernels; returns the launch status.
 hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);
 // Enqueue one decode step; returns the launch status.

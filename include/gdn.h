@@ -117,6 +117,52 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
 
 /*
+ * Bytes of device workspace gdn_chunk_fwd_varlen needs for N sequences with T
+ * tokens in all (0 means the workspace pointer may be NULL).  It depends only
+ * on N and T, not on how the tokens are split.  Returns 0 for arguments
+ * gdn_chunk_fwd_varlen would reject.
+ */
+size_t gdn_chunk_fwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv, int chunk,
+                                            gdn_dtype dtype, gdn_decay mode);
+
+/*
+ * Chunked prefill of a packed batch: N sequences of varying length lie back to
+ * back on one token axis of length T, and the state starts again from S0[s]
+ * at the first token of sequence s (and nowhere else; the NextTransformer
+ * "method sources" page, baseline section, resets the recurrent state at the
+ * start of every packed row).  Each sequence is cut into chunks of 64 from its
+ * own first token; every sequence may end in a partial chunk.
+ *
+ *   q, k        [T, H, dk]   `dtype`   (the gdn_chunk_fwd layouts with B = 1)
+ *   v           [T, H, dv]   `dtype`
+ *   alpha       mode SCALAR: fp32 [T, H]; mode CHANNEL: `dtype` [T, H, dk];
+ *               mode NONE: ignored (may be NULL)
+ *   beta        fp32 [T, H]
+ *   S0          fp32 [N, H, dv, dk], sequence s's initial state; NULL means zeros
+ *   o           [T, H, dv]   `dtype`, written
+ *   S_final     fp32 [N, H, dv, dk], written: each sequence's state after its
+ *               last token (S0[s], or zeros, for an empty sequence); may be NULL.
+ *               S_final == S0 is allowed; no other output may alias an input.
+ *   cu_seqlens  DEVICE int32 [N + 1]: sequence s holds tokens cu_seqlens[s] ..
+ *               cu_seqlens[s + 1] - 1.  The caller guarantees cu_seqlens[0] = 0,
+ *               cu_seqlens[N] = T and no decrease (empty sequences are allowed).
+ *               The offsets are read only on the device, so they are not
+ *               validated; the kernels clamp them into [0, T], so malformed
+ *               offsets give unspecified results but no access outside the
+ *               buffers.  Must not alias o, S_final or the workspace.
+ *   workspace   at least gdn_chunk_fwd_varlen_workspace_bytes(...) bytes.
+ *
+ * N = 0 requires T = 0 (GDN_ERR_SHAPE otherwise) and does nothing.  Errors,
+ * asynchrony and numerics are those of gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                                const void* alpha, const float* beta, const float* S0,
+                                void* o, float* S_final, const int* cu_seqlens,
+                                void* workspace, size_t workspace_bytes,
+                                int N, int T, int H, int dk, int dv, int chunk,
+                                gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
+
+/*
  * One decode step (the recurrence body for a single token), S updated in place.
  *
  *   q, k      [B, H, dk]   `dtype`

@@ -37,6 +37,10 @@ def lib():
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_chunk_fwd_workspace_bytes.argtypes = [i] * 8
     lib.gdn_chunk_fwd_workspace_bytes.restype = sz
+    lib.gdn_chunk_fwd_varlen.argtypes = [vp] * 9 + [vp, sz] + [i] * 8 + [vp]
+    lib.gdn_chunk_fwd_varlen.restype = i
+    lib.gdn_chunk_fwd_varlen_workspace_bytes.argtypes = [i] * 8
+    lib.gdn_chunk_fwd_varlen_workspace_bytes.restype = sz
     return lib
 
 
@@ -55,7 +59,7 @@ def test_status_strings(lib):
         s = lib.gdn_status_string(st)
         assert s and s.startswith(b"GDN_")
     assert lib.gdn_status_string(12345) == b"unknown gdn_status"
-    assert lib.gdn_version() == 100
+    assert lib.gdn_version() == 200
 
 
 # fake, disjoint device addresses (never dereferenced: every call fails validation)
@@ -130,6 +134,76 @@ def test_chunk_fwd_checks_workspace(lib):
     assert _fwd(lib, ws=q + 128, ws_bytes=need) == E_ALIAS     # workspace over q
     need2 = _ws_bytes(2, 100, 3, 2, 128, 2)
     assert _fwd(lib, mode=2, ws=ws, ws_bytes=need2 - 1) == E_WS
+
+
+def _varlen_ws_bytes(N, T, H, es, dk=128, mode=1):
+    # one record per slot: T // 64 + N slots per head bound the chunks of any split
+    if T == 0:
+        return 0
+    slots = H * (T // 64 + N)
+    if mode == 2:
+        return slots * ((2 * 64 * 64 + 3 * 64 * dk) * es + 4 * dk)
+    return slots * ((2 if es == 4 else 1) * 64 * 64 * es + 3 * 64 * 4)
+
+
+def test_varlen_workspace_bounds_every_split():
+    """T // 64 + N chunk slots hold the chunks of any split of T tokens into N
+    sequences, and sequence s's chunk n at slot cu[s] // 64 + s + n never
+    collides with another sequence's (checked over random splits)."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for _ in range(2000):
+        N = int(rng.integers(1, 12))
+        T = int(rng.integers(0, 700))
+        cuts = np.sort(rng.integers(0, T + 1, N - 1))
+        cu = np.concatenate([[0], cuts, [T]])
+        used = set()
+        for s in range(N):
+            ln = cu[s + 1] - cu[s]
+            for n in range((ln + 63) // 64):
+                slot = cu[s] // 64 + s + n
+                assert slot < T // 64 + N and slot not in used
+                used.add(slot)
+
+
+def test_varlen_workspace_query(lib):
+    q = lib.gdn_chunk_fwd_varlen_workspace_bytes
+    assert q(16, 32768, 16, 128, 128, 64, 1, 1) == _varlen_ws_bytes(16, 32768, 16, 2)
+    assert q(3, 100, 2, 64, 64, 64, 0, 0) == _varlen_ws_bytes(3, 100, 2, 4, 64, 0)
+    assert q(5, 1000, 4, 128, 128, 64, 1, 2) == _varlen_ws_bytes(5, 1000, 4, 2, 128, 2)
+    assert q(4, 0, 2, 128, 128, 64, 1, 1) == 0
+    assert q(4, 10, 2, 96, 128, 64, 1, 1) == 0          # unsupported d_k
+    assert q(4, 10, 2, 128, 128, 32, 1, 1) == 0         # unsupported chunk
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    q, k, v, a, b, s0, o, sf = _bufs()
+    cu = (1 << 40) + 10 * (1 << 36)
+    ws = (1 << 40) + 11 * (1 << 36)
+
+    def fwd(ptrs=None, cu=cu, ws=ws, ws_bytes=1 << 30, N=4, T=300, H=2, dk=128, dv=128, chunk=64,
+            dtype=1, mode=1):
+        p = ptrs if ptrs is not None else (q, k, v, a, b, s0, o, sf)
+        return lib.gdn_chunk_fwd_varlen(*p, cu, ws, ws_bytes, N, T, H, dk, dv, chunk, dtype, mode,
+                                        None)
+
+    assert fwd(dk=96) == E_UNSUP
+    assert fwd(chunk=128) == E_UNSUP
+    assert fwd(T=-1) == E_SHAPE
+    assert fwd(N=-1) == E_SHAPE
+    assert fwd(N=0, T=10) == E_SHAPE                    # tokens outside every sequence
+    assert fwd(dtype=5) == E_DTYPE
+    assert fwd(cu=0) == E_NULL
+    assert fwd(ptrs=(q, k, v, 0, b, s0, o, sf)) == E_NULL
+    assert fwd(ptrs=(q, k, v, a, b, s0, 0, sf)) == E_NULL
+    assert fwd(ws=0) == E_NULL
+    assert fwd(ws_bytes=_varlen_ws_bytes(4, 300, 2, 2) - 1) == E_WS
+    assert fwd(ptrs=(q, k, v, a, b, s0, q + 64, sf)) == E_ALIAS     # o inside q
+    assert fwd(cu=o + 64) == E_ALIAS                                # offsets inside o
+    assert fwd(cu=sf + 64) == E_ALIAS                               # offsets inside S_final
+    assert fwd(ws=cu - 64) == E_ALIAS                               # workspace over the offsets
+    assert fwd(N=0, T=0, ptrs=(0, 0, 0, 0, 0, 0, 0, 0), cu=0, ws=0) == OK
+    assert fwd(H=0) == OK
 
 
 def test_decode_rejects_bad_arguments(lib):

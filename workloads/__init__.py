@@ -128,6 +128,70 @@ GDN_BF16_LONG = Prefill("gdn_bf16_b1_h32_t65536_d128", 1, 32, 65536, 128, 128, t
                         "range095", 0.0, seed=5)
 
 PREFILL_WORKLOADS = [GDN_FP32_SMALL, GDN_BF16_PREFILL, KDA_BF16_PREFILL, GDN_BF16_LONG]
+
+
+@dataclasses.dataclass(frozen=True)
+class Packed:
+    """N sequences of varying length packed back to back on one token axis of
+    T tokens (inputs [1, T, H, d], offsets cu_seqlens [N + 1]).  The lengths are
+    a seeded uniform random split of T into N parts (normalised Exp(1) draws,
+    rounded down, at least ``min_len`` each, the remainder spread one token at
+    a time from the first sequence on): a broad mix of short and long rows with
+    ragged tails.  ``lengths`` overrides the split."""
+    name: str
+    N: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    dtype: torch.dtype
+    gate: str
+    s0_std: float
+    seed: int
+    min_len: int = 1
+    lengths: Optional[tuple] = None
+
+    @property
+    def mode(self) -> int:
+        return GATES[self.gate][0]
+
+    def with_(self, **kw) -> "Packed":
+        return dataclasses.replace(self, **kw)
+
+
+# Same token count and head shape as the B=8 x T=4096 prefill, split into 16 rows.
+GDN_BF16_PACKED = Packed("gdn_bf16_packed_n16_t32768_h16_d128", 16, 32768, 16, 128, 128,
+                         torch.bfloat16, "range090", 0.1, seed=6)
+
+
+def packed_lengths(w: Packed) -> list:
+    """Sequence lengths of a packed workload (tensor number 6 of its seed)."""
+    if w.lengths is not None:
+        assert len(w.lengths) == w.N and sum(w.lengths) == w.T
+        return list(w.lengths)
+    assert w.T >= w.N * w.min_len
+    u = -torch.log1p(-torch.rand(w.N, generator=_gen(1000 * w.seed + 6), dtype=torch.float64))
+    spare = w.T - w.N * w.min_len
+    lens = [w.min_len + int(x) for x in torch.floor(spare * u / u.sum()).tolist()]
+    i = 0
+    while sum(lens) < w.T:
+        lens[i % w.N] += 1
+        i += 1
+    return lens
+
+
+def make_packed(w: Packed) -> dict:
+    """CPU tensors q, k [1, T, H, dk]; v [1, T, H, dv]; beta [1, T, H]; alpha
+    [1, T, H] or [1, T, H, dk] or None; S0 [N, H, dv, dk] or None; cu_seqlens
+    int32 [N + 1].  Same distributions and seeding as :func:`make_prefill`."""
+    base = make_prefill(Prefill(w.name, 1, w.H, w.T, w.dk, w.dv, w.dtype, w.gate, 0.0, w.seed))
+    if w.s0_std > 0:
+        base["S0"] = w.s0_std * _randn((w.N, w.H, w.dv, w.dk), 1000 * w.seed + 5)
+    lens = packed_lengths(w)
+    cu = torch.zeros(w.N + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    base["cu_seqlens"] = cu
+    return base
 DECODE_WORKLOADS = [DECODE_DK128, DECODE_DK64]
 
 
