@@ -549,3 +549,76 @@ def test_planted_mistakes_are_caught(name, tmp_path):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, "planted mistake %s escaped every pin" % name
+
+
+# ----------------------------------------------------------------------------------
+# the per-token prologue (oracle/prologue.py): closed forms
+# ----------------------------------------------------------------------------------
+
+def test_prologue_l2norm_closed_forms():
+    """(3, 4) has norm 5: eps = 0 gives (0.6, 0.8); eps = 11 gives (3, 4) / 6.
+    Every normalised vector has unit norm at eps = 0; scaling the input does
+    not change the result."""
+    from oracle import prologue as P
+    assert np.array_equal(P.l2norm(np.array([3.0, 4.0]), 0.0), [0.6, 0.8])
+    assert np.allclose(P.l2norm(np.array([3.0, 4.0]), 11.0), [0.5, 4.0 / 6.0], rtol=0, atol=1e-16)
+    x = np.random.default_rng(3).standard_normal((5, 7, 16))
+    n = np.linalg.norm(P.l2norm(x, 0.0), axis=-1)
+    assert np.max(np.abs(n - 1)) < 1e-15
+    assert np.max(np.abs(P.l2norm(7.5 * x, 0.0) - P.l2norm(x, 0.0))) < 1e-15
+
+
+def test_prologue_sigmoid_softplus_closed_forms():
+    """sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(x) + sigmoid(-x) = 1;
+    softplus(0) = ln 2, softplus(y) - softplus(-y) = y, softplus(ln 3) = ln 4,
+    and no overflow at |y| = 800."""
+    from oracle import prologue as P
+    assert P.sigmoid(np.array(0.0)) == 0.5
+    assert abs(P.sigmoid(np.array(np.log(3.0))) - 0.75) < 1e-15
+    y = np.linspace(-30, 30, 61)
+    assert np.max(np.abs(P.sigmoid(y) + P.sigmoid(-y) - 1)) < 1e-15
+    assert abs(P.softplus(np.array(0.0)) - np.log(2.0)) < 1e-16
+    assert abs(P.softplus(np.array(np.log(3.0))) - np.log(4.0)) < 1e-15
+    assert np.max(np.abs(P.softplus(y) - P.softplus(-y) - y)) < 1e-13
+    big = P.softplus(np.array([800.0, -800.0]))
+    assert big[0] == 800.0 and big[1] == 0.0
+
+
+def test_prologue_decay_closed_forms():
+    """exp(-a softplus(y)) = (1 + e^y)^(-a): a = 1 gives sigmoid(-y), a = 2 its
+    square; the bias shifts the argument (per head for a scalar gate, per head
+    and key channel for a per-channel gate); a -> 0 gives no decay."""
+    from oracle import prologue as P
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 5, 2))                      # [B, T, H]
+    b = np.array([0.5, -1.5])
+    A = np.array([1.0, 2.0])
+    al = P.decay_from_logits(x, A, b, MODE_SCALAR)
+    s = 1.0 / (1.0 + np.exp(x + b))                         # sigmoid(-(x + b))
+    assert np.max(np.abs(al[..., 0] - s[..., 0])) < 1e-15
+    assert np.max(np.abs(al[..., 1] - s[..., 1] ** 2)) < 1e-15
+    xc = rng.standard_normal((2, 4, 2, 3))                  # [B, T, H, dk]
+    bc = rng.standard_normal((2, 3))
+    alc = P.decay_from_logits(xc, A, bc, MODE_CHANNEL)
+    sc = 1.0 / (1.0 + np.exp(xc + bc))
+    assert np.max(np.abs(alc[:, :, 0] - sc[:, :, 0])) < 1e-15
+    assert np.max(np.abs(alc[:, :, 1] - sc[:, :, 1] ** 2)) < 1e-15
+    assert np.array_equal(P.decay_from_logits(x, np.zeros(2), None, MODE_SCALAR), np.ones_like(x))
+
+
+def test_prologue_feeds_the_loop():
+    """The prologue's outputs are exactly what the loop receives: with unit
+    keys, beta logit +inf (beta = 1) and no decay the key is recalled exactly
+    (exact-recall pin of the loop), whatever the keys' scale before the
+    normalisation."""
+    from oracle import prologue as P
+    rng = np.random.default_rng(5)
+    B, T, H, dk, dv = 1, 3, 1, 4, 2
+    q = rng.standard_normal((B, T, H, dk)) * 5
+    k = rng.standard_normal((B, T, H, dk)) * 3
+    v = rng.standard_normal((B, T, H, dv))
+    beta = np.full((B, T, H), 800.0)
+    o, S = P.gdn_fwd(q, k, v, None, beta, None, mode=MODE_NONE, l2norm_qk=True, eps=0.0,
+                     beta_logits=True)
+    kn = k[0, -1, 0] / np.linalg.norm(k[0, -1, 0])
+    assert np.max(np.abs(S[0, 0] @ kn - v[0, -1, 0])) < 1e-12
