@@ -12,7 +12,9 @@ on the batch-64 x 16-head decode workload, 1024 steps captured in a HIP graph,
 both in place on one state (as the recurrence runs) and rotated over 16 state
 buffers so the 67 MB state cannot stay in the 256 MB Infinity Cache.  The
 packed variable-length prefill (the same 32768 tokens x 16 heads split into 16
-rows of 593 to 5858 tokens) is timed alongside (``packed``).
+rows of 593 to 5858 tokens) is timed alongside (``packed``), and so is the
+prefill with the per-token prologue fused in (``fused_prologue``: raw q and k
+normalised in the kernels, beta and alpha from logits).
 
 Printed: one JSON line (the contract below), preceded by progress lines on
 stderr.  Peaks are MI355X's published figures: HBM 8 TB/s, dense bf16 MFMA
@@ -209,6 +211,39 @@ def bench_packed(w: W.Packed, steps: int):
                 algorithmic_bytes=nbytes)
 
 
+def bench_fused(w: W.Prefill, steps: int):
+    """Average duration of one ``gdn_chunk_fwd_fused`` launch on raw inputs of
+    the workload's shape (q, k not normalised, beta and alpha logits, per-head
+    rates and biases), every part of the prologue on."""
+    log("generating raw inputs for the fused prologue (%s shape)" % w.name)
+    d = {k: (None if v is None else v.cuda()) for k, v in
+         W.make_prologue(w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.mode, seed=w.seed + 200,
+                         s0_std=w.s0_std).items()}
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=w.dtype, device="cuda")
+    S = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+
+    def launch():
+        gdn.chunk_fwd_fused(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], mode=w.mode,
+                            l2norm_qk=True, beta_logits=True, alpha_logits=True, A=d["A"],
+                            dt_bias=d["dt_bias"], o=o, S_final=S)
+
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    launch()
+    b0.record()
+    for _ in range(steps):
+        launch()
+    b1.record()
+    torch.cuda.synchronize()
+    ms = b0.elapsed_time(b1) / steps
+    nbytes = prefill_bytes(w) + w.H * 4 * (2 if w.mode == W.MODE_SCALAR else 1 + w.dk)
+    return dict(workload=w.name + "_fused_prologue", launch_us=ms * 1e3,
+                tokens_per_s=w.B * w.T / (ms * 1e-3), hbm_gbps=nbytes / (ms * 1e-3) / 1e9,
+                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, algorithmic_bytes=nbytes)
+
+
 def bench_decode(w: W.Decode, reps: int = 3, rotate: int = 1):
     """``w.steps`` decode steps captured in one HIP graph; per-step time from
     the median replay.  ``rotate`` > 1 cycles the steps over that many state
@@ -380,6 +415,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-packed", action="store_true",
                     help="skip the packed variable-length prefill workload")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the prefill with the fused per-token prologue")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -442,6 +479,12 @@ def main():
             packed["workload"], packed["launch_us"], packed["tokens_per_s"], packed["lengths_min"],
             packed["lengths_max"]))
 
+    fused = None
+    if not args.no_fused and w.mode != W.MODE_NONE:
+        fused = bench_fused(w, args.steps)
+        log("fused prologue: %.1f us per launch (plain %.1f us)" % (fused["launch_us"],
+                                                                   kern_ms * 1e3))
+
     copy_gbps = device_copy_gbps()   # also the known-size reference for HBM byte counters
     log("device copy %.0f GB/s" % copy_gbps)
 
@@ -462,6 +505,7 @@ def main():
                            step="chunked prefill + first decode token",
                            state="fp32", parallelism="single GPU"),
                roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode, packed=packed,
+               fused_prologue=fused,
                device_copy_gbps=copy_gbps)
     print(json.dumps(out), flush=True)
 

@@ -9,6 +9,9 @@ library is missing or does not load, every call raises.
     o, S_final = chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0)
                                                            # packed sequences
     o = decode_step(q, k, v, alpha, beta, S)               # one token, S in place
+    o, S_final = chunk_fwd_fused(q, k, v, alpha, beta, S0, l2norm_qk=True,
+                                 beta_logits=True, alpha_logits=True, A=A)
+                                                           # prologue in the kernels
 """
 from __future__ import annotations
 
@@ -18,7 +21,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "decode_step", "load", "lib_path", "GDNError",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_fused", "decode_step", "decode_step_fused", "load", "lib_path", "GDNError",
            "DECAY_NONE", "DECAY_SCALAR", "DECAY_CHANNEL", "EXPORTED_SYMBOLS"]
 
 DECAY_NONE, DECAY_SCALAR, DECAY_CHANNEL = 0, 1, 2
@@ -26,7 +29,15 @@ _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                     "gdn_chunk_fwd_varlen_workspace_bytes", "gdn_chunk_fwd_varlen",
-                    "gdn_decode_step", "gdn_status_string", "gdn_version")
+                    "gdn_chunk_fwd_fused", "gdn_decode_step", "gdn_decode_step_fused",
+                    "gdn_status_string", "gdn_version")
+
+
+class Prologue(ctypes.Structure):
+    """``gdn_prologue`` of include/gdn.h."""
+    _fields_ = [("l2norm_qk", ctypes.c_int), ("eps", ctypes.c_float),
+                ("beta_logits", ctypes.c_int), ("alpha_logits", ctypes.c_int),
+                ("A", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +74,10 @@ def load():
         lib.gdn_chunk_fwd_varlen_workspace_bytes.restype = sz
         lib.gdn_chunk_fwd_varlen.argtypes = [vp] * 9 + [vp, sz] + [i] * 8 + [vp]
         lib.gdn_chunk_fwd_varlen.restype = i
+        lib.gdn_chunk_fwd_fused.argtypes = [vp] * 10 + [vp, sz] + [i] * 8 + [vp]
+        lib.gdn_chunk_fwd_fused.restype = i
+        lib.gdn_decode_step_fused.argtypes = [vp] * 8 + [i] * 6 + [vp]
+        lib.gdn_decode_step_fused.restype = i
         lib.gdn_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.gdn_decode_step.restype = i
         lib.gdn_status_string.argtypes = [i]
@@ -221,5 +236,96 @@ def decode_step(q, k, v, alpha, beta, S, *, mode=None, o=None, stream=None):
     _require(o, "o", dtype)
     st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None), _ptr(beta),
                              _ptr(S), _ptr(o), B, H, dk, dv, _DTYPES[dtype], mode, _stream(stream))
+    _check(st)
+    return o
+
+
+def _prologue(l2norm_qk, eps, beta_logits, alpha_logits, A, dt_bias):
+    _require(A, "A", torch.float32)
+    _require(dt_bias, "dt_bias", torch.float32)
+    return Prologue(int(bool(l2norm_qk)), float(eps), int(bool(beta_logits)),
+                    int(bool(alpha_logits)), None if A is None else A.data_ptr(),
+                    None if dt_bias is None else dt_bias.data_ptr())
+
+
+def chunk_fwd_fused(q, k, v, alpha, beta, S0=None, *, cu_seqlens=None, l2norm_qk=False,
+                    eps=1e-6, beta_logits=False, alpha_logits=False, A=None, dt_bias=None,
+                    mode=None, chunk=64, o=None, S_final=None, need_final=True, stream=None):
+    """Prefill with the per-token prologue in the kernels (``gdn_chunk_fwd_fused``).
+
+    The tensors are those of :func:`chunk_fwd` (``cu_seqlens`` None) or of
+    :func:`chunk_fwd_varlen` (``cu_seqlens`` given); with ``alpha_logits`` the
+    alpha tensor holds logits x and log alpha = -A[h] softplus(x + dt_bias),
+    A fp32 [H], dt_bias fp32 [H] or [H, dk]; with ``beta_logits`` beta holds
+    logits; ``l2norm_qk`` normalises q and k per (token, head) with ``eps``."""
+    lib = load()
+    packed = cu_seqlens is not None
+    T, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    if packed:
+        _require(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() == 4 and q.shape[0] != 1:
+            raise ValueError("a packed batch has a leading axis of 1, got %d" % q.shape[0])
+        B = cu_seqlens.shape[0] - 1
+    else:
+        B = q.shape[0]
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    if mode is None:
+        mode = DECAY_NONE if alpha is None else (
+            DECAY_SCALAR if alpha.dim() == q.dim() - 1 else DECAY_CHANNEL)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, dtype)
+    _require(beta, "beta", torch.float32)
+    _require(S0, "S0", torch.float32)
+    if mode == DECAY_SCALAR:
+        _require(alpha, "alpha", torch.float32)
+    elif mode == DECAY_CHANNEL:
+        _require(alpha, "alpha", dtype)
+    pro = _prologue(l2norm_qk, eps, beta_logits, alpha_logits, A, dt_bias)
+    if o is None:
+        o = torch.empty(tuple(q.shape[:-1]) + (dv,), dtype=dtype, device=q.device)
+    if S_final is None and need_final:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _require(o, "o", dtype)
+    _require(S_final, "S_final", torch.float32)
+    wsf = lib.gdn_chunk_fwd_varlen_workspace_bytes if packed else lib.gdn_chunk_fwd_workspace_bytes
+    ws_bytes = int(wsf(B, T, H, dk, dv, chunk, _DTYPES[dtype], mode))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    st = lib.gdn_chunk_fwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None),
+                                 _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens),
+                                 ctypes.byref(pro), _ptr(ws), ws_bytes, B, T, H, dk, dv, chunk,
+                                 _DTYPES[dtype], mode, _stream(stream))
+    _check(st)
+    return o, S_final
+
+
+def decode_step_fused(q, k, v, alpha, beta, S, *, l2norm_qk=False, eps=1e-6, beta_logits=False,
+                      alpha_logits=False, A=None, dt_bias=None, mode=None, o=None, stream=None):
+    """One decode step with the prologue in the kernel (``gdn_decode_step_fused``);
+    tensors as in :func:`decode_step`, prologue as in :func:`chunk_fwd_fused`."""
+    lib = load()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, dtype)
+    _require(beta, "beta", torch.float32)
+    _require(S, "S", torch.float32)
+    if mode == DECAY_SCALAR:
+        _require(alpha, "alpha", torch.float32)
+    elif mode == DECAY_CHANNEL:
+        _require(alpha, "alpha", dtype)
+    pro = _prologue(l2norm_qk, eps, beta_logits, alpha_logits, A, dt_bias)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dtype, device=q.device)
+    _require(o, "o", dtype)
+    st = lib.gdn_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None),
+                                   _ptr(beta), _ptr(S), _ptr(o), ctypes.byref(pro), B, H, dk, dv,
+                                   _DTYPES[dtype], mode, _stream(stream))
     _check(st)
     return o

@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <cmath>
+
 #include "gdn_internal.h"
 
 namespace {
@@ -55,7 +57,7 @@ gdn_status check_common(int B, int H, int dk, int dv, gdn_dtype dtype, gdn_decay
 
 extern "C" {
 
-int gdn_version(void) { return 200; }
+int gdn_version(void) { return 300; }
 
 const char* gdn_status_string(gdn_status s) {
   switch (s) {
@@ -67,6 +69,7 @@ const char* gdn_status_string(gdn_status s) {
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace too small";
     case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: the HIP runtime refused the launch";
     case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: forbidden aliasing between arguments";
+    case GDN_ERR_VALUE: return "GDN_ERR_VALUE: a scalar argument is out of range";
   }
   return "unknown gdn_status";
 }
@@ -79,56 +82,6 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
   return gdn::prefill_workspace_bytes(B, T, H, dk, (int)dtype, (int)mode);
 }
 
-gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
-                         const float* beta, const float* S0, void* o, float* S_final,
-                         void* workspace, size_t workspace_bytes, int B, int T, int H, int dk,
-                         int dv, int chunk, gdn_dtype dtype, gdn_decay mode,
-                         hipStream_t stream) {
-  gdn_status st = check_common(B, H, dk, dv, dtype, mode);
-  if (st != GDN_OK) return st;
-  if (T < 0) return GDN_ERR_SHAPE;
-  if (chunk != kChunk) return GDN_ERR_UNSUPPORTED;
-  long long nqk, nv, ntok, nS;
-  if (!count4(B, T, H, dk, &nqk) || !count4(B, T, H, dv, &nv) || !count4(B, T, H, 1, &ntok) ||
-      !count4(B, H, dv, dk, &nS))
-    return GDN_ERR_SHAPE;
-  if ((long long)B * H * (dv / 32) > 0x7fffffffLL) return GDN_ERR_SHAPE;
-  const size_t ws_need = gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, mode);
-  if (workspace_bytes < ws_need) return GDN_ERR_WORKSPACE;
-  if (B == 0 || H == 0) return GDN_OK;
-  if (ws_need > 0 && !workspace) return GDN_ERR_NULL;
-  const bool has_tokens = T > 0;
-  if (has_tokens) {
-    if (!q || !k || !v || !beta || !o) return GDN_ERR_NULL;
-    if (mode != GDN_DECAY_NONE && !alpha) return GDN_ERR_NULL;
-  }
-  if (!has_tokens && !S_final) return GDN_OK;  // nothing to write
-
-  const size_t es = elem_size(dtype);
-  const size_t a_bytes = mode == GDN_DECAY_SCALAR ? (size_t)ntok * 4
-                         : mode == GDN_DECAY_CHANNEL ? (size_t)nqk * es : 0;
-  Range rq = range_of(has_tokens ? q : nullptr, (size_t)nqk * es);
-  Range rk = range_of(has_tokens ? k : nullptr, (size_t)nqk * es);
-  Range rv = range_of(has_tokens ? v : nullptr, (size_t)nv * es);
-  Range ra = range_of(has_tokens && mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes);
-  Range rb = range_of(has_tokens ? beta : nullptr, (size_t)ntok * 4);
-  Range rs0 = range_of(S0, (size_t)nS * 4);
-  Range ro = range_of(has_tokens ? o : nullptr, (size_t)nv * es);
-  Range rsf = range_of(S_final, (size_t)nS * 4);
-  for (Range in : {rq, rk, rv, ra, rb, rs0})
-    if (overlaps(ro, in)) return GDN_ERR_ALIAS;
-  for (Range in : {rq, rk, rv, ra, rb, ro})
-    if (overlaps(rsf, in)) return GDN_ERR_ALIAS;
-  if (overlaps(rsf, rs0) && (const void*)S_final != (const void*)S0) return GDN_ERR_ALIAS;
-  Range rw = range_of(ws_need > 0 ? workspace : nullptr, ws_need);
-  for (Range in : {rq, rk, rv, ra, rb, rs0, ro, rsf})
-    if (overlaps(rw, in)) return GDN_ERR_ALIAS;
-
-  gdn::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_final, B, T, H, dk, dv, (int)dtype,
-                     (int)mode};
-  return gdn::launch_prefill(a, workspace, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
-}
-
 size_t gdn_chunk_fwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv, int chunk,
                                             gdn_dtype dtype, gdn_decay mode) {
   if (check_common(N, H, dk, dv, dtype, mode) != GDN_OK || T < 0 || chunk != kChunk) return 0;
@@ -138,30 +91,66 @@ size_t gdn_chunk_fwd_varlen_workspace_bytes(int N, int T, int H, int dk, int dv,
   return gdn::prefill_varlen_workspace_bytes(N, T, H, dk, (int)dtype, (int)mode);
 }
 
-gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* alpha,
-                                const float* beta, const float* S0, void* o, float* S_final,
-                                const int* cu_seqlens, void* workspace, size_t workspace_bytes,
-                                int N, int T, int H, int dk, int dv, int chunk, gdn_dtype dtype,
-                                gdn_decay mode, hipStream_t stream) {
-  gdn_status st = check_common(N, H, dk, dv, dtype, mode);
+}  // extern "C"
+
+namespace {
+
+// The prologue's arguments, checked; `reads_gates` says whether the kernels
+// will read the gates (A is then required when alpha comes from logits).
+gdn_status take_prologue(const gdn_prologue* pro, gdn_decay mode, bool reads_gates, int H, int dk,
+                         gdn::Prologue* out, Range* ra, Range* rb) {
+  *out = gdn::Prologue{};
+  *ra = Range{0, 0};
+  *rb = Range{0, 0};
+  if (!pro) return GDN_OK;
+  if (!(pro->eps >= 0.f) || !std::isfinite(pro->eps)) return GDN_ERR_VALUE;
+  out->qk_norm = pro->l2norm_qk != 0;
+  out->norm_eps = pro->eps;
+  out->beta_logits = pro->beta_logits != 0;
+  out->alpha_logits = pro->alpha_logits != 0 && mode != GDN_DECAY_NONE;
+  if (out->alpha_logits) {
+    if (reads_gates && !pro->A) return GDN_ERR_NULL;
+    out->A = pro->A;
+    out->dt_bias = pro->dt_bias;
+    *ra = range_of(pro->A, (size_t)H * 4);
+    *rb = range_of(pro->dt_bias, (size_t)H * (mode == GDN_DECAY_CHANNEL ? dk : 1) * 4);
+  }
+  return GDN_OK;
+}
+
+// Prefill over B rows of T tokens (cu_seqlens NULL and packed false) or over a
+// packed batch of B sequences with T tokens in all.
+gdn_status prefill(const void* q, const void* k, const void* v, const void* alpha,
+                   const float* beta, const float* S0, void* o, float* S_final,
+                   const int* cu_seqlens, bool packed, const gdn_prologue* pro, void* workspace,
+                   size_t workspace_bytes, int B, int T, int H, int dk, int dv, int chunk,
+                   gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
+  gdn_status st = check_common(B, H, dk, dv, dtype, mode);
   if (st != GDN_OK) return st;
   if (T < 0) return GDN_ERR_SHAPE;
   if (chunk != kChunk) return GDN_ERR_UNSUPPORTED;
-  if (N == 0 && T > 0) return GDN_ERR_SHAPE;   // tokens outside every sequence
+  if (packed && B == 0 && T > 0) return GDN_ERR_SHAPE;   // tokens outside every sequence
+  const int rows = packed ? 1 : B;   // leading axis of the token tensors
   long long nqk, nv, ntok, nS;
-  if (!count4(1, T, H, dk, &nqk) || !count4(1, T, H, dv, &nv) || !count4(1, T, H, 1, &ntok) ||
-      !count4(N, H, dv, dk, &nS))
+  if (!count4(rows, T, H, dk, &nqk) || !count4(rows, T, H, dv, &nv) ||
+      !count4(rows, T, H, 1, &ntok) || !count4(B, H, dv, dk, &nS))
     return GDN_ERR_SHAPE;
-  if ((long long)N * H * (dv / 32) > 0x7fffffffLL) return GDN_ERR_SHAPE;
-  if ((long long)T / kChunk + N > 0x7fffffffLL ||
-      ((long long)T / kChunk + N) * H > 0x7fffffffLL)
+  if ((long long)B * H * (dv / 32) > 0x7fffffffLL) return GDN_ERR_SHAPE;
+  if (packed && ((long long)T / kChunk + B > 0x7fffffffLL ||
+                 ((long long)T / kChunk + B) * H > 0x7fffffffLL))
     return GDN_ERR_SHAPE;
-  const size_t ws_need = gdn_chunk_fwd_varlen_workspace_bytes(N, T, H, dk, dv, chunk, dtype, mode);
+  const size_t ws_need = packed
+                             ? gdn_chunk_fwd_varlen_workspace_bytes(B, T, H, dk, dv, chunk, dtype, mode)
+                             : gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, mode);
   if (workspace_bytes < ws_need) return GDN_ERR_WORKSPACE;
-  if (N == 0 || H == 0) return GDN_OK;
-  if (!cu_seqlens) return GDN_ERR_NULL;
-  if (ws_need > 0 && !workspace) return GDN_ERR_NULL;
   const bool has_tokens = T > 0;
+  gdn::Prologue pa;
+  Range rA, rbias;
+  st = take_prologue(pro, mode, has_tokens, H, dk, &pa, &rA, &rbias);
+  if (st != GDN_OK) return st;
+  if (B == 0 || H == 0) return GDN_OK;
+  if (packed && !cu_seqlens) return GDN_ERR_NULL;
+  if (ws_need > 0 && !workspace) return GDN_ERR_NULL;
   if (has_tokens) {
     if (!q || !k || !v || !beta || !o) return GDN_ERR_NULL;
     if (mode != GDN_DECAY_NONE && !alpha) return GDN_ERR_NULL;
@@ -177,26 +166,32 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
   Range ra = range_of(has_tokens && mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes);
   Range rb = range_of(has_tokens ? beta : nullptr, (size_t)ntok * 4);
   Range rs0 = range_of(S0, (size_t)nS * 4);
-  Range rcu = range_of(cu_seqlens, ((size_t)N + 1) * 4);
+  Range rcu = range_of(packed ? cu_seqlens : nullptr, ((size_t)B + 1) * 4);
   Range ro = range_of(has_tokens ? o : nullptr, (size_t)nv * es);
   Range rsf = range_of(S_final, (size_t)nS * 4);
-  for (Range in : {rq, rk, rv, ra, rb, rs0, rcu})
+  if (!has_tokens) rA = rbias = Range{0, 0};
+  for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, rA, rbias})
     if (overlaps(ro, in)) return GDN_ERR_ALIAS;
-  for (Range in : {rq, rk, rv, ra, rb, ro, rcu})
+  for (Range in : {rq, rk, rv, ra, rb, ro, rcu, rA, rbias})
     if (overlaps(rsf, in)) return GDN_ERR_ALIAS;
   if (overlaps(rsf, rs0) && (const void*)S_final != (const void*)S0) return GDN_ERR_ALIAS;
   Range rw = range_of(ws_need > 0 ? workspace : nullptr, ws_need);
-  for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, ro, rsf})
+  for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, ro, rsf, rA, rbias})
     if (overlaps(rw, in)) return GDN_ERR_ALIAS;
 
-  gdn::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_final, N, T, H, dk, dv, (int)dtype,
-                     (int)mode, cu_seqlens, gdn::varlen_slots(N, T)};
+  gdn::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_final, B, T, H, dk, dv, (int)dtype,
+                     (int)mode};
+  if (packed) {
+    a.cu_seqlens = cu_seqlens;
+    a.nslots = gdn::varlen_slots(B, T);
+  }
+  a.pro = pa;
   return gdn::launch_prefill(a, workspace, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
-gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const void* alpha,
-                           const float* beta, float* S, void* o, int B, int H, int dk, int dv,
-                           gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
+gdn_status decode(const void* q, const void* k, const void* v, const void* alpha,
+                  const float* beta, float* S, void* o, const gdn_prologue* pro, int B, int H,
+                  int dk, int dv, gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
   gdn_status st = check_common(B, H, dk, dv, dtype, mode);
   if (st != GDN_OK) return st;
   long long nqk, nv, nh, nS;
@@ -204,6 +199,10 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const vo
       !count4(B, H, dv, dk, &nS))
     return GDN_ERR_SHAPE;
   if ((long long)B * H > 0x7fffffffLL) return GDN_ERR_SHAPE;
+  gdn::Prologue pa;
+  Range rA, rbias;
+  st = take_prologue(pro, mode, B > 0 && H > 0, H, dk, &pa, &rA, &rbias);
+  if (st != GDN_OK) return st;
   if (B == 0 || H == 0) return GDN_OK;
   if (!q || !k || !v || !beta || !S || !o) return GDN_ERR_NULL;
   if (mode != GDN_DECAY_NONE && !alpha) return GDN_ERR_NULL;
@@ -216,13 +215,59 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const vo
   Range ra = range_of(mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes);
   Range rb = range_of(beta, (size_t)nh * 4);
   Range rs = range_of(S, (size_t)nS * 4), ro = range_of(o, (size_t)nv * es);
-  for (Range in : {rq, rk, rv, ra, rb, rs})
+  for (Range in : {rq, rk, rv, ra, rb, rs, rA, rbias})
     if (overlaps(ro, in)) return GDN_ERR_ALIAS;
-  for (Range in : {rq, rk, rv, ra, rb})
+  for (Range in : {rq, rk, rv, ra, rb, rA, rbias})
     if (overlaps(rs, in)) return GDN_ERR_ALIAS;
 
   gdn::DecodeArgs a{q, k, v, alpha, beta, S, o, B, H, dk, dv, (int)dtype, (int)mode};
+  a.pro = pa;
   return gdn::launch_decode(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                         const float* beta, const float* S0, void* o, float* S_final,
+                         void* workspace, size_t workspace_bytes, int B, int T, int H, int dk,
+                         int dv, int chunk, gdn_dtype dtype, gdn_decay mode,
+                         hipStream_t stream) {
+  return prefill(q, k, v, alpha, beta, S0, o, S_final, nullptr, false, nullptr, workspace,
+                 workspace_bytes, B, T, H, dk, dv, chunk, dtype, mode, stream);
+}
+
+gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* alpha,
+                                const float* beta, const float* S0, void* o, float* S_final,
+                                const int* cu_seqlens, void* workspace, size_t workspace_bytes,
+                                int N, int T, int H, int dk, int dv, int chunk, gdn_dtype dtype,
+                                gdn_decay mode, hipStream_t stream) {
+  return prefill(q, k, v, alpha, beta, S0, o, S_final, cu_seqlens, true, nullptr, workspace,
+                 workspace_bytes, N, T, H, dk, dv, chunk, dtype, mode, stream);
+}
+
+gdn_status gdn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* alpha,
+                               const float* beta, const float* S0, void* o, float* S_final,
+                               const int* cu_seqlens, const gdn_prologue* prologue,
+                               void* workspace, size_t workspace_bytes, int B, int T, int H,
+                               int dk, int dv, int chunk, gdn_dtype dtype, gdn_decay mode,
+                               hipStream_t stream) {
+  return prefill(q, k, v, alpha, beta, S0, o, S_final, cu_seqlens, cu_seqlens != nullptr,
+                 prologue, workspace, workspace_bytes, B, T, H, dk, dv, chunk, dtype, mode, stream);
+}
+
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                           const float* beta, float* S, void* o, int B, int H, int dk, int dv,
+                           gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
+  return decode(q, k, v, alpha, beta, S, o, nullptr, B, H, dk, dv, dtype, mode, stream);
+}
+
+gdn_status gdn_decode_step_fused(const void* q, const void* k, const void* v, const void* alpha,
+                                 const float* beta, float* S, void* o,
+                                 const gdn_prologue* prologue, int B, int H, int dk, int dv,
+                                 gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
+  return decode(q, k, v, alpha, beta, S, o, prologue, B, H, dk, dv, dtype, mode, stream);
 }
 
 }  // extern "C"

@@ -150,10 +150,18 @@ __device__ inline void st_once(void* p, const u32x4& v) {
 
 // Workspace: one record per chunk of every head (chunk index = head *
 // N_chunks + n).  Scalar or no decay, offsets in elements of the operand dtype:
-//   T [C][C] (row-major), in fp32 also P [C][C], then the gate rows, 3 x C
-//   fp32: G_r, exp(G_r), exp(G_C - G_r).
-// (The bf16 state kernel forms P itself; the per-channel record is KdaRec.)
-constexpr size_t kGateFloats = 3 * C;
+//   T [C][C] (row-major), in fp32 also P [C][C], then five fp32 gate rows:
+//     0  G_r
+//     1  exp(G_r) nk_r          X = V - diag(row 1) K S^T
+//     2  exp(G_C - G_r) nk_r    S_{n+1} = gamma_C S_n + U^T diag(row 2) K
+//     3  exp(G_r) nq_r          O_inter = diag(row 3) Q S^T
+//     4  nk_r                   P[r][j] = exp(G_r - G_j) nq_r nk_j (q_r . k_j)
+//   nk_r and nq_r are 1 / sqrt(|k_r|^2 + eps) and 1 / sqrt(|q_r|^2 + eps) when
+//   the kernels normalise q and k, else 1.  The bf16 records hold nq = 1: that
+//   state kernel forms P itself and applies nq to its output rows.
+// (The per-channel record is KdaRec.)
+constexpr int kGateRows = 5;
+constexpr size_t kGateFloats = kGateRows * C;
 
 template <typename E>
 struct GateRec {
@@ -171,11 +179,53 @@ __device__ inline float quad_sum(float x) {
   return x;
 }
 
+// Sum over aligned groups of N lanes (N = 4, 8, 16, 32), result in all of them.
+template <int N>
+__device__ inline float lane_group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "group of 4, 8, 16 or 32 lanes");
+  x = quad_sum(x);
+  if constexpr (N >= 8)   // row_half_mirror: lane i of 8 takes lane 7 - i
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+  if constexpr (N >= 16)  // row_mirror: lane i of 16 takes lane 15 - i
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// Sum of squares of a 16-byte piece of the operand dtype.
+template <typename E>
+__device__ inline float sumsq16(const u32x4& u) {
+  float s = 0.f;
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float lo = __uint_as_float(u[w] << 16), hi = __uint_as_float(u[w] & 0xffff0000u);
+      s += lo * lo + hi * hi;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float x = __uint_as_float(u[w]);
+      s += x * x;
+    }
+  }
+  return s;
+}
+
+// log alpha of one gate value of head h (channel c for a per-channel gate): the
+// value itself, or a logit x with log alpha = -A[h] softplus(x + dt_bias)
+// (a Mamba2-style decay); floored at kLogFloor.
+template <bool FASTLOG>
+__device__ inline float log_alpha(const Prologue& p, float x, int h, int bias_index) {
+  const float la = p.alpha_logits
+                       ? -p.A[h] * softplus_f(x + (p.dt_bias ? p.dt_bias[bias_index] : 0.f))
+                       : (FASTLOG ? __logf(x) : logf(x));
+  return fmaxf(la, kLogFloor);
+}
+
 // Gates of one chunk, lane r of the wave holding token r: inclusive prefix G of
-// log alpha (0 past the sequence end).
-template <int MODE>
-__device__ inline float chunk_log_decay(float alpha, bool ok) {
-  float la = (MODE == 1 && ok) ? fmaxf(logf(alpha), kLogFloor) : 0.f;
+// log alpha (la = 0 past the sequence end).
+__device__ inline float chunk_prefix(float la) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -308,9 +358,10 @@ __device__ __attribute__((always_inline)) inline void tri_solve(const float* Am,
 // state kernel forms P from the K and Q rows it holds anyway, which spares
 // this kernel the Q reads and the record the P bytes.)
 // LDS: K rows [64][LDK] (then L^-1 fp32 [64][LDA]), Q rows [64][LDK] (then A
-// fp32 [64][LDA], then T [64][LDT]), Mt fp32 [32][LDM], G, beta.  P goes to
-// the record straight from the accumulators.
-template <typename E, int DK>
+// fp32 [64][LDA], then T [64][LDT]), Mt fp32 [32][LDM], G, beta (and, when q
+// and k are normalised, the inverse norms of the K and Q rows).  P goes to the
+// record straight from the accumulators.
+template <typename E, int DK, bool NORM>
 struct PrepPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = DK + PAD;
@@ -331,13 +382,16 @@ struct PrepPlan {
   static constexpr size_t mt = inplace ? (size_t)32 * 4   // A + 32 floats, leading dimension LDA
                                        : am + cmax((size_t)C * LDK * es, cmax((size_t)C * LDA * 4, (size_t)C * LDT * es));
   static constexpr size_t g = inplace ? tm + (size_t)C * LDT * es : mt + (size_t)32 * LDM * 4;
-  static constexpr size_t total = g + 2 * C * 4;
+  // inverse norms (K, then Q in fp32): in place they use T's bytes, which the
+  // solve writes only after its last read of them
+  static constexpr size_t nk = inplace ? tm : g + 2 * C * 4;
+  static constexpr size_t total = g + (NORM && !inplace ? 4 : 2) * C * 4;
 };
 
-template <typename E, int DK, int MODE>
+template <typename E, int DK, int MODE, bool NORM>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* __restrict__ tws,
                                                               int nchunks) {
-  using L = PrepPlan<E, DK>;
+  using L = PrepPlan<E, DK, NORM>;
   using R = GateRec<E>;
   constexpr bool WP = R::has_p;
   constexpr int EPC = 16 / (int)sizeof(E);
@@ -352,6 +406,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   float* Mt = reinterpret_cast<float*>(smem + L::mt);
   float* G = reinterpret_cast<float*>(smem + L::g);
   float* Bt = G + C;
+  float* Nk = reinterpret_cast<float*>(smem + L::nk);   // NORM only
+  float* Nq = Nk + C;                                   // NORM, fp32 only
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
   PrepAt at;
@@ -383,15 +439,22 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     const bool ok = lane < cn;
     const size_t tok = (tok0 + min(lane, cn - 1)) * H + h;
     const float al = MODE == 1 ? static_cast<const float*>(a.alpha)[tok] : 1.f;
-    const float bt = a.beta[tok];
-    const float g = chunk_log_decay<MODE>(al, ok);
+    const float braw = a.beta[tok];
+    const float la = MODE == 1 ? log_alpha<false>(a.pro, al, h, h) : 0.f;
+    const float bt = a.pro.beta_logits ? sigmoid_f(braw) : braw;
+    const float g = chunk_prefix(ok ? la : 0.f);
     const float gC = __shfl(g, C - 1);
     G[lane] = g;
     Bt[lane] = ok ? bt : 0.f;
     float* gw = reinterpret_cast<float*>(rec + R::g);
     gw[lane] = g;
-    gw[C + lane] = __expf(g);
-    gw[2 * C + lane] = __expf(gC - g);
+    if constexpr (!NORM) {   // (normalised: the rows with norms follow once they are known)
+      const float eg = __expf(g);
+      gw[C + lane] = eg;
+      gw[2 * C + lane] = __expf(gC - g);
+      gw[3 * C + lane] = eg;
+      gw[4 * C + lane] = 1.f;
+    }
   }
   __syncthreads();
 
@@ -406,13 +469,40 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     else
       tile_nt_k<DK / 16>(acca, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
   }
+  if constexpr (NORM) {
+    // the diagonals of the K K^T tiles (0,0) and (1,1) are |k_r|^2
+    if (wave == 0 || wave == 2) {
+      const int r = rb * 32 + col;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (acc_row(v >> 2, v & 3, lane) == col) Nk[r] = rsqrtf(acca[v] + a.pro.norm_eps);
+    }
+    if constexpr (WP) {   // |q_r|^2, four threads per row
+      const int r = tid >> 2, qd = tid & 3;
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < DK / 4; c += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(Qr + r * LDK + qd * (DK / 4) + c);
+        ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+      }
+      ss = quad_sum(ss);
+      if (qd == 0) Nq[r] = rsqrtf(ss + a.pro.norm_eps);
+    }
+  }
   __syncthreads();   // K and Q are dead: A takes their bytes
   // A[r][j] = beta_r exp(G_r - G_j) k_r.k_j (j < r); P[r][j] = exp(G_r - G_j) q_r.k_j
   // (j <= r).  Every weight is formed clamped to at most 1 before the masks
   // select (left conditional, its loads would sink into per-element branches).
+  // Normalised q and k: A takes nk_r nk_j, P nq_r nk_j (the row factor joins
+  // beta_r, the column factor the weight).
   if (wave < 3) {
     const int r = rb * 32 + col;
-    const float Gr = G[r], br = Bt[r];
+    const float Gr = G[r];
+    float br = Bt[r], pr = 1.f;
+    if constexpr (NORM) {
+      br *= Nk[r];
+      if constexpr (WP) pr = Nq[r];
+    }
     float w[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -421,6 +511,13 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
       w[4 * g + 1] = __expf(fminf(Gr - gj.y, 0.f));
       w[4 * g + 2] = __expf(fminf(Gr - gj.z, 0.f));
       w[4 * g + 3] = __expf(fminf(Gr - gj.w, 0.f));
+      if constexpr (NORM) {
+        const float4 nj = *reinterpret_cast<const float4*>(Nk + jb * 32 + acc_row(g, 0, lane));
+        w[4 * g + 0] *= nj.x;
+        w[4 * g + 1] *= nj.y;
+        w[4 * g + 2] *= nj.z;
+        w[4 * g + 3] *= nj.w;
+      }
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) asm volatile("" ::"v"(w[v]));
@@ -431,15 +528,25 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[e] = (j0 + e < r) ? br * w[4 * g + e] * acca[4 * g + e] : 0.f;
-        y[e] = (j0 + e <= r) ? w[4 * g + e] * accp[4 * g + e] : 0.f;
+        y[e] = (j0 + e <= r) ? pr * w[4 * g + e] * accp[4 * g + e] : 0.f;
       }
       store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
       if constexpr (WP) store4(Pw + r * C + j0, y[0], y[1], y[2], y[3]);
     }
-  } else if (WP) {   // P rows 0..31, columns 32..63 are zero
-    const int q = tid - 192, r = q >> 1, j0 = 32 + 16 * (q & 1);
+  } else {
+    if constexpr (WP) {   // P rows 0..31, columns 32..63 are zero
+      const int q = tid - 192, r = q >> 1, j0 = 32 + 16 * (q & 1);
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) store4(Pw + r * C + j0 + e, 0.f, 0.f, 0.f, 0.f);
+      for (int e = 0; e < 16; e += 4) store4(Pw + r * C + j0 + e, 0.f, 0.f, 0.f, 0.f);
+    }
+    if constexpr (NORM) {   // the gate rows that carry the norms
+      const float g = G[lane], eg = __expf(g), nk = Nk[lane];
+      float* gw = reinterpret_cast<float*>(rec + R::g);
+      gw[C + lane] = eg * nk;
+      gw[2 * C + lane] = __expf(G[C - 1] - g) * nk;
+      gw[3 * C + lane] = WP ? eg * Nq[lane] : eg;
+      gw[4 * C + lane] = nk;
+    }
   }
   __syncthreads();
 
@@ -544,7 +651,7 @@ constexpr float kSplitLimit = 64.f;
 // tiles, then L^-1 and Mt of the solve; then the unscaled K and Q rows of the
 // current diagonal block, prefix segment totals, beta and the bit masks of
 // the channels left out of each diagonal block's MFMA.
-template <typename E, int DK>
+template <typename E, int DK, bool NORM>
 struct KdaPrepPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = DK + PAD;
@@ -565,13 +672,14 @@ struct KdaPrepPlan {
   static constexpr size_t tot = raw + (size_t)2 * 32 * LDK * sizeof(E);
   static constexpr size_t bt = tot + (size_t)NSEG * DK * 4;
   static constexpr size_t msk = bt + C * 4;
-  static constexpr size_t total = msk + (size_t)2 * (DK / 32) * 4;
+  static constexpr size_t nrm = msk + (size_t)2 * (DK / 32) * 4;   // inverse norms of K, Q rows
+  static constexpr size_t total = nrm + (NORM ? 2 * C * 4 : 0);
 };
 
-template <typename E, int DK>
+template <typename E, int DK, bool NORM>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __restrict__ tws,
                                                            int nchunks) {
-  using L = KdaPrepPlan<E, DK>;
+  using L = KdaPrepPlan<E, DK, NORM>;
   using R = KdaRec<E, DK>;
   constexpr int EPC = 16 / (int)sizeof(E);
   constexpr int CPR = DK / EPC;
@@ -594,6 +702,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   float* Tot = reinterpret_cast<float*>(smem + L::tot);
   float* Bt = reinterpret_cast<float*>(smem + L::bt);
   uint32_t* Msk = reinterpret_cast<uint32_t*>(smem + L::msk);   // [2][DK / 32]
+  float* Nk = reinterpret_cast<float*>(smem + L::nrm);            // NORM only
+  float* Nq = Nk + C;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
   PrepAt at;
@@ -611,6 +721,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   // 32..63 above), channels c0 = ((tid + kThreads m) % CPR) EPC.  Rows past the
   // sequence end repeat its last row.
   u32x4 kreg[2 * IPT], qreg[2 * IPT];
+  float nkm[2 * IPT], nqm[2 * IPT];   // inverse norms of those rows (NORM)
   // G, per channel: thread (segment s, channel c) scans RPS rows, then adds the
   // totals of the segments before it.  Rows past the sequence end add nothing.
   {
@@ -630,13 +741,30 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
     }
 #pragma unroll
     for (int i = 0; i < RPS; ++i) {
-      const float la = fmaxf(__logf(g[i]), kLogFloor);
+      const float la = log_alpha<true>(a.pro, g[i], h, h * DK + c);
       g[i] = s * RPS + i < cn ? la : 0.f;
     }
 #pragma unroll
     for (int i = 1; i < RPS; ++i) g[i] += g[i - 1];
     Tot[s * DK + c] = g[RPS - 1];
-    if (tid < C) Bt[tid] = tid < cn ? a.beta[(tok0 + tid) * H + h] : 0.f;
+    if (tid < C) {
+      const float bt = a.beta[(tok0 + min(tid, cn - 1)) * H + h];
+      Bt[tid] = tid < cn ? (a.pro.beta_logits ? sigmoid_f(bt) : bt) : 0.f;
+    }
+    if constexpr (NORM) {
+      // inverse norms of this thread's K and Q rows: a row's CPR pieces sit in
+      // CPR consecutive lanes
+#pragma unroll
+      for (int m = 0; m < 2 * IPT; ++m) {
+        const int it = tid + kThreads * m;
+        nkm[m] = rsqrtf(lane_group_sum<CPR>(sumsq16<E>(kreg[m])) + a.pro.norm_eps);
+        nqm[m] = rsqrtf(lane_group_sum<CPR>(sumsq16<E>(qreg[m])) + a.pro.norm_eps);
+        if (it % CPR == 0) {
+          Nk[it / CPR] = nkm[m];
+          Nq[it / CPR] = nqm[m];
+        }
+      }
+    }
     __syncthreads();
     float off = 0.f;
     for (int s2 = 0; s2 < s; ++s2) off += Tot[s2 * DK + c];
@@ -679,6 +807,13 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
       const u32x4 qraw = qreg[m];
       unpack16<E>(kraw, kf);
       unpack16<E>(qraw, qf);
+      if constexpr (NORM) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          kf[e] *= nkm[m];
+          qf[e] *= nqm[m];
+        }
+      }
       const int anchor = pass == 2 ? 31 : (pass == 0 ? 15 : 47);
 #pragma unroll
       for (int e = 0; e < EPC; e += 4) {
@@ -739,6 +874,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
       // exact contributions of the channels left out of this diagonal block
       const int r = 32 * pass + col;
       const E* xr = ((wave & 1) ? Qraw : Kraw) + col * LDK;
+      const float xn = NORM ? ((wave & 1) ? Nq[r] : Nk[r]) : 1.f;   // the rows are unscaled
 #pragma unroll 1
       for (int wd = 0; wd < DK / 32; ++wd) {
         uint32_t bits = __builtin_amdgcn_readfirstlane(Msk[pass * (DK / 32) + wd]);
@@ -746,11 +882,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
           const int c = 32 * wd + __builtin_ctz(bits);
           bits &= bits - 1;
           const float gr = Gl[r * LDG + c];
-          const float xv = (float)xr[c];
+          const float xv = (float)xr[c] * xn;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int jl = acc_row(v >> 2, v & 3, lane), j = 32 * pass + jl;
-            const float w = __expf(fminf(gr - Gl[j * LDG + c], 0.f));
+            const float w = __expf(fminf(gr - Gl[j * LDG + c], 0.f)) * (NORM ? Nk[j] : 1.f);
             const float t = xv * (float)Kraw[jl * LDK + c] * w;
             acc0[v] += j <= r ? t : 0.f;
           }
@@ -837,7 +973,7 @@ struct StatePlan {
   static constexpr size_t ut = tm + (size_t)C * LDT * es;
   static constexpr size_t uw = ut + (size_t)DVS * LDT * es;
   static constexpr size_t g = uw + (size_t)DVS * LDT * es;
-  static constexpr size_t total = g + 3 * C * 4;
+  static constexpr size_t total = g + 4 * C * 4;   // gate rows 0..3 (or DK per-channel values)
 };
 
 template <typename E, int DK, int DVS>
@@ -894,9 +1030,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   E* Tm = reinterpret_cast<E*>(smem + L::tm);
   E* Ut = reinterpret_cast<E*>(smem + L::ut);
   E* Uw = reinterpret_cast<E*>(smem + L::uw);
-  float* G = reinterpret_cast<float*>(smem + L::g);   // gate block, as in the workspace
-  float* Eg = G + C;       // exp(G_r)
-  float* Ec = G + 2 * C;   // exp(G_C - G_r)
+  float* G = reinterpret_cast<float*>(smem + L::g);   // gate rows 0..3 of the record
+  float* Eg = G + C;       // exp(G_r) nk_r
+  float* Ec = G + 2 * C;   // exp(G_C - G_r) nk_r
+  float* Eo = G + 3 * C;   // exp(G_r) nq_r
   float* Gc = G;           // per-channel decay: exp(G_C[c]), DK values
   // O staging (rows r, OST elements apart) reuses X^T's region, free after phase 4
   constexpr int OST = (sizeof(E) == 2 && DVS == 64) ? 72 : DVS;
@@ -1029,7 +1166,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
         pt[m] = *reinterpret_cast<const u32x4*>(rq + R::t + (tid + kThreads * m) * EPC);
         pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (tid + kThreads * m) * EPC);
       }
-      constexpr int NG4 = (KDA ? DK : (int)kGateFloats) / 4;   // 16-byte chunks of the fp32 rows
+      constexpr int NG4 = (KDA ? DK : 4 * C) / 4;   // 16-byte chunks of the fp32 rows used
       pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(tid, NG4 - 1));
     }
   };
@@ -1069,7 +1206,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
       *reinterpret_cast<u32x4*>(Tm + r * LDT + cc * EPC) = pt[m];
       *reinterpret_cast<u32x4*>(Pm + r * LDT + cc * EPC) = pp[m];
     }
-    if (tid < (KDA ? DK / 4 : (int)kGateFloats / 4)) *reinterpret_cast<u32x4*>(G + 4 * tid) = pg;
+    if (tid < (KDA ? DK / 4 : C)) *reinterpret_cast<u32x4*>(G + 4 * tid) = pg;
   };
 
   // Staged O rows of a chunk -> HBM, 16-byte stores along each row.
@@ -1107,13 +1244,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
       for (int g = 0; g < 4; ++g) {
         const int r0 = own_rb * 32 + acc_row(g, 0, lane);
         const float4 eg = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
+        const float4 eo = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eo + r0);
         const float4 v4 = load4_elem(Vt + i * LDT + r0);
         store4(Xt + i * LDT + r0, v4.x - eg.x * xacc[4 * g + 0], v4.y - eg.y * xacc[4 * g + 1],
                v4.z - eg.z * xacc[4 * g + 2], v4.w - eg.w * xacc[4 * g + 3]);
-        oacc[4 * g + 0] *= eg.x;
-        oacc[4 * g + 1] *= eg.y;
-        oacc[4 * g + 2] *= eg.z;
-        oacc[4 * g + 3] *= eg.w;
+        oacc[4 * g + 0] *= eo.x;
+        oacc[4 * g + 1] *= eo.y;
+        oacc[4 * g + 2] *= eo.z;
+        oacc[4 * g + 3] *= eo.w;
       }
     }
     __syncthreads();
@@ -1188,7 +1326,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
           }
         }
       } else {
-        const float gC = Eg[C - 1];
+        const float gC = __expf(G[C - 1]);
 #pragma unroll
         for (int st = 0; st < NST; ++st)
 #pragma unroll
@@ -1285,7 +1423,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
 // issues all LDS fragment loads of interval B before its first MFMA there.
 // The two roles run separate loops with the same barrier count, so their
 // registers do not add up.
-template <typename E, int DK, int DVS, bool KDA>
+template <typename E, int DK, int DVS, bool KDA, bool NORM>
 struct WsPlan {
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = DK + PAD;
@@ -1317,18 +1455,24 @@ struct WsPlan {
   static constexpr size_t pm = os + (size_t)C * OST * es;
   static constexpr size_t tm = pm + (KDA ? 1 : 2) * pmat;
   static constexpr size_t g = tm + (size_t)C * LDT * es;
-  static constexpr size_t total = g + 2 * kGateFloats * 4;
+  // per buffer: gate rows 0..2 of the record (normalised q, k: rows 0..4 and
+  // the chunk's inverse Q norms); per-channel: exp(G_C), DK values
+  static constexpr int gstride = NORM ? 6 * C : 3 * C;
+  static_assert(DK <= 3 * C, "per-channel decay row must fit a gate buffer");
+  static constexpr size_t total = g + 2 * (size_t)gstride * 4;
 };
 
 constexpr int kWsThreads = 512;
 constexpr int kP1Ahead = 2;   // phase-1 fragments loaded this many k steps ahead
 constexpr int kFormPAhead = 2;   // fragments of P's product loaded this many k steps ahead
 
-template <typename E, int DK, int DVS, int MODE>
+template <typename E, int DK, int DVS, int MODE, bool NORM>
 __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws) {
   static_assert(sizeof(E) == 2, "the eight-wave kernel is bf16");
   constexpr bool KDA = MODE == 2;
-  using L = WsPlan<E, DK, DVS, KDA>;
+  static_assert(!(KDA && NORM), "per-channel records carry normalised operands already");
+  using L = WsPlan<E, DK, DVS, KDA, NORM>;
+  constexpr int GS = L::gstride;
   static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
   using R = typename RecOf<E, DK, MODE>::type;
   constexpr int NI = DVS / 32;       // 32-wide value blocks in the slice
@@ -1349,11 +1493,11 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   static_assert(C * CPV % PT == 0, "V rows must split evenly over the data threads");
   constexpr int CPT = C / EPC;
   constexpr int TBT = C * CPT / PT;
-  constexpr int NG4 = (KDA ? DK : (int)kGateFloats) / 4;   // 16-byte chunks of the fp32 rows
+  constexpr int NG4 = (KDA ? DK : (NORM ? 5 : 3) * C) / 4;   // 16-byte chunks of the fp32 rows
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
   // Buffer pairs are C * LDK (rows; C * LDKS for Ks), C * LDV (V), C * LDP (P) elements and
-  // kGateFloats floats apart.
+  // GS floats apart.
   E* Qrb = reinterpret_cast<E*>(smem + L::qr);
   E* Ksb = reinterpret_cast<E*>(smem + L::ks);   // K rows of the state update (K, or Kc), row-swizzled
   E* Krb = reinterpret_cast<E*>(smem + L::kr);   // per-channel: the K operand of phase 1
@@ -1475,7 +1619,15 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         const int q = ptid + PT * m, r = q / CPV, cc = q % CPV;
         *reinterpret_cast<u32x4*>(Vr + r * LDV + cc * EPC) = pv[m];
       }
-      if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * kGateFloats + 4 * ptid) = pg;
+      if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * GS + 4 * ptid) = pg;
+      if constexpr (NORM) {   // inverse norms of the Q rows: a row's CPR pieces sit in CPR lanes
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+          const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
+          const float nq = rsqrtf(lane_group_sum<CPR>(sumsq16<E>(pq[m])) + a.pro.norm_eps);
+          if (cc == 0) Gbuf[gb * GS + 5 * C + r] = nq;
+        }
+      }
     };
     // T (and the per-channel P) of a chunk.
     auto commit_tp = [&]() __attribute__((always_inline)) {
@@ -1502,12 +1654,14 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       f32x16 acc = zero16();
       tile_nt_k<DK / 16, E, true, kFormPAhead>(acc, Ksb + gb * C * LDKS + jb * 32 * LDKS, LDKS,
                                   Qrb + gb * C * LDK + rb * 32 * LDK, LDK, lane);
-      const float* Gl = Gbuf + gb * kGateFloats;
+      const float* Gl = Gbuf + gb * GS;
       E* Pm = Pmb + gb * C * LDP;
       const int r = rb * 32 + col;
       const float Gr = Gl[r];
       // Every weight is formed (clamped to at most 1) before the mask selects:
       // left conditional, the gate loads sink into per-element branches.
+      // Normalised q and k: the column factor nk_j joins the weight (nq_r is
+      // applied to the output rows).
       float w[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -1516,6 +1670,13 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         w[4 * g + 1] = __expf(fminf(Gr - gj.y, 0.f));
         w[4 * g + 2] = __expf(fminf(Gr - gj.z, 0.f));
         w[4 * g + 3] = __expf(fminf(Gr - gj.w, 0.f));
+        if constexpr (NORM) {
+          const float4 nj = *reinterpret_cast<const float4*>(Gl + 4 * C + jb * 32 + acc_row(g, 0, lane));
+          w[4 * g + 0] *= nj.x;
+          w[4 * g + 1] *= nj.y;
+          w[4 * g + 2] *= nj.z;
+          w[4 * g + 3] *= nj.w;
+        }
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) asm volatile("" ::"v"(w[v]));
@@ -1627,9 +1788,9 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
 
   for (int n = 0; n < nchunks; ++n) {
     const int nb = n & 1;
-    const float* G = Gbuf + nb * kGateFloats;
-    const float* Eg = G + C;
-    const float* Ec = G + 2 * C;
+    const float* G = Gbuf + nb * GS;
+    const float* Eg = G + C;       // exp(G_r) nk_r
+    const float* Ec = G + 2 * C;   // exp(G_C - G_r) nk_r
     const E* Ks = Ksb + nb * C * LDKS;
     const E* K1 = KDA ? Krb + nb * C * LDK : Ks;   // K operand of phase 1 (scalar: swizzled)
     const E* Qr = Qrb + nb * C * LDK;
@@ -1649,7 +1810,9 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         vw[g] = tr_read4(Vr, LDV, r0, vc, lane);   // V[r0 .. r0 + 3][i]
         eg[g] = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
       }
-      const float egr = KDA ? 1.f : Eg[own_rb * 32 + col];   // O^T columns are the chunk rows r
+      // O^T columns are the chunk rows r: exp(G_r) (normalised q: exp(G_r) and,
+      // after the intra-chunk part, nq_r)
+      const float egr = KDA ? 1.f : (NORM ? G[3 * C + own_rb * 32 + col] : Eg[own_rb * 32 + col]);
       tile_nt2_shared_b<DK / 16, E, true, kP1Ahead, !KDA>(xacc, oacc, K1 + own_rb * 32 * (KDA ? LDK : LDKS),
                                                            Qr + own_rb * 32 * LDK, KDA ? LDK : LDKS, LDK,
                                           Sb + own_ib * 32 * LDSB, LDSB, lane);
@@ -1740,6 +1903,11 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         for (int s = 0; s < 2; ++s) mma_bf16(oacc, uf[rj][s], pa[rj][s]);
       }
       const int r = own_rb * 32 + col;
+      if constexpr (NORM) {
+        const float nq = G[5 * C + r];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[v] *= nq;
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         store4(Os + r * OST + own_ib * 32 + acc_row(g, 0, lane), oacc[4 * g], oacc[4 * g + 1], oacc[4 * g + 2],
@@ -1762,7 +1930,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
           Sacc[st][4 * g + 3] *= d.w;
         }
       } else {
-        const float gC = Eg[C - 1];
+        const float gC = NORM ? __expf(G[C - 1]) : Eg[C - 1];
 #pragma unroll
         for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
       }
@@ -1803,12 +1971,19 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
   dim3 grid((unsigned)((size_t)a.B * a.H * (a.dv / DVS))), block(kThreads);
   if constexpr (sizeof(E) == 2) {
     dim3 wblock(kWsThreads);
-    if (a.mode == 0)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0>), grid, wblock, 0, stream, a, tws);
+    // (normalised q and k: the per-channel records carry normalised operands, so
+    // only the scalar / no-decay state kernel has a variant of its own)
+    const bool nrm = a.pro.qk_norm != 0;
+    if (a.mode == 0 && !nrm)
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, false>), grid, wblock, 0, stream, a, tws);
+    else if (a.mode == 0)
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, true>), grid, wblock, 0, stream, a, tws);
+    else if (a.mode == 1 && !nrm)
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws);
     else if (a.mode == 1)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1>), grid, wblock, 0, stream, a, tws);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws);
     else if constexpr (DVS == 32)   // the per-channel buffers leave room for 32-row slices only
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2>), grid, wblock, 0, stream, a, tws);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws);
     else
       return hipErrorInvalidConfiguration;
   } else {
@@ -1834,12 +2009,21 @@ hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) 
   const size_t nprep = a.cu_seqlens ? (a.T > 0 ? (size_t)a.H * a.nslots : 0) : (size_t)a.B * a.H * nchunks;
   if (nprep > 0) {
     dim3 grid((unsigned)nprep), block(kThreads);
-    if (a.mode == 0)
-      hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 0>), grid, block, 0, stream, a, tws, nchunks);
-    else if (a.mode == 1)
-      hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 1>), grid, block, 0, stream, a, tws, nchunks);
-    else
-      hipLaunchKernelGGL((chunk_prep_kda<E, DK>), grid, block, 0, stream, a, tws, nchunks);
+    if (a.pro.qk_norm) {
+      if (a.mode == 0)
+        hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 0, true>), grid, block, 0, stream, a, tws, nchunks);
+      else if (a.mode == 1)
+        hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 1, true>), grid, block, 0, stream, a, tws, nchunks);
+      else
+        hipLaunchKernelGGL((chunk_prep_kda<E, DK, true>), grid, block, 0, stream, a, tws, nchunks);
+    } else {
+      if (a.mode == 0)
+        hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 0, false>), grid, block, 0, stream, a, tws, nchunks);
+      else if (a.mode == 1)
+        hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 1, false>), grid, block, 0, stream, a, tws, nchunks);
+      else
+        hipLaunchKernelGGL((chunk_prep_kda<E, DK, false>), grid, block, 0, stream, a, tws, nchunks);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -18,6 +18,9 @@
 // of a (b, h) head.  The fp32 rows are held in registers between the read and
 // the write, and the two row dot products are finished with xor-shuffles over
 // the row's lanes.
+// With the prologue on, q and k are normalised in fp32 registers (their norms
+// are sums over the row's lanes like the dot products) and beta, alpha come
+// from logits; the state traffic is unchanged.
 // The state is touched once per step, so its loads and stores are marked
 // non-temporal (they do not displace cached lines); with more, smaller
 // workgroups than heads the reads of later workgroups overlap the writes of
@@ -73,7 +76,7 @@ __device__ inline float group_sum(float x) {
   return x;
 }
 
-template <typename E, int DK, int DV, int MODE>
+template <typename E, int DK, int DV, int MODE, bool PRO>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int LPR = lanes_per_row<DK>();               // lanes per row
   constexpr int NQ = DK / (4 * LPR);                     // float4 per lane per row
@@ -108,9 +111,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     qf[j] = load4(q + 4 * l8 + 4 * LPR * j);
     if (MODE == 2) af[j] = load4(static_cast<const E*>(a.alpha) + bh * DK + 4 * l8 + 4 * LPR * j);
   }
-  const float beta = a.beta[bh];
+  float beta = a.beta[bh];
   float alpha = 1.f;
   if (MODE == 1) alpha = static_cast<const float*>(a.alpha)[bh];
+  if constexpr (PRO) {
+    const Prologue& p = a.pro;
+    const int h = (int)(bh % a.H);
+    if (p.beta_logits) beta = sigmoid_f(beta);
+    if (MODE == 1 && p.alpha_logits)
+      alpha = __expf(fmaxf(-p.A[h] * softplus_f(alpha + (p.dt_bias ? p.dt_bias[h] : 0.f)), -100.f));
+    if (MODE == 2 && p.alpha_logits) {
+      const float ah = p.A[h];
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const int c = 4 * l8 + 4 * LPR * j;
+        float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.dt_bias) {
+          const float* bp = p.dt_bias + (size_t)h * DK + c;
+          b4 = make_float4(bp[0], bp[1], bp[2], bp[3]);
+        }
+        af[j].x = __expf(fmaxf(-ah * softplus_f(af[j].x + b4.x), -100.f));
+        af[j].y = __expf(fmaxf(-ah * softplus_f(af[j].y + b4.y), -100.f));
+        af[j].z = __expf(fmaxf(-ah * softplus_f(af[j].z + b4.z), -100.f));
+        af[j].w = __expf(fmaxf(-ah * softplus_f(af[j].w + b4.w), -100.f));
+      }
+    }
+    if (p.qk_norm) {   // fp32, exact scaling of the loaded values
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        sk += kf[j].x * kf[j].x + kf[j].y * kf[j].y + kf[j].z * kf[j].z + kf[j].w * kf[j].w;
+        sq += qf[j].x * qf[j].x + qf[j].y * qf[j].y + qf[j].z * qf[j].z + qf[j].w * qf[j].w;
+      }
+      const float nk = rsqrtf(group_sum<LPR>(sk) + p.norm_eps);
+      const float nq = rsqrtf(group_sum<LPR>(sq) + p.norm_eps);
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        kf[j] = make_float4(kf[j].x * nk, kf[j].y * nk, kf[j].z * nk, kf[j].w * nk);
+        qf[j] = make_float4(qf[j].x * nq, qf[j].y * nq, qf[j].z * nq, qf[j].w * nq);
+      }
+    }
+  }
   float vr[NR];
 #pragma unroll
   for (int m = 0; m < NR; ++m) vr[m] = load1(v + g + RPW * m);
@@ -170,10 +211,14 @@ hipError_t launch_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int LPR = lanes_per_row<DK>();
   constexpr int RPG = kThreads / LPR * (f4_per_thread<DK>() / (DK / (4 * LPR)));
   dim3 grid((unsigned)(a.B * a.H * (DV / RPG))), block(kThreads);
-  switch (a.mode) {
-    case 0: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 0>), grid, block, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 1>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 2>), grid, block, 0, stream, a); break;
+  const bool pro = a.pro.qk_norm || a.pro.beta_logits || a.pro.alpha_logits;
+  switch (a.mode * 2 + (pro ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 0, false>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 0, true>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 1, false>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 1, true>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 2, false>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 2, true>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }

@@ -8,6 +8,21 @@
 
 namespace gdn {
 
+// Per-token prologue of the mixer layers, applied inside the kernels (all off
+// by default).
+struct Prologue {
+  int qk_norm = 0;                  // q, k <- x / sqrt(|x|^2 + norm_eps) per (token, head)
+  float norm_eps = 0.f;
+  int beta_logits = 0;              // beta <- sigmoid(beta)
+  int alpha_logits = 0;             // log alpha <- -A[h] softplus(alpha + dt_bias)
+  const float* A = nullptr;         // [H]
+  const float* dt_bias = nullptr;   // [H] (scalar decay) or [H, dk] (per channel); may be null
+};
+
+// log(1 + e^y) without overflow, and the logistic function (fp32).
+__device__ inline float softplus_f(float y) { return fmaxf(y, 0.f) + log1pf(__expf(-fabsf(y))); }
+__device__ inline float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+
 // Arguments of one prefill launch.  Pointers are device pointers; layouts are
 // the C-ABI's: q, k [B, T, H, dk]; v, o [B, T, H, dv]; alpha [B, T, H] or
 // [B, T, H, dk]; beta [B, T, H]; S0, S_final [B, H, dv, dk].
@@ -29,6 +44,7 @@ struct PrefillArgs {
   // int32 [B + 1]).  Null for B rows of T tokens each.
   const int* cu_seqlens = nullptr;
   int nslots = 0;    // packed batch: chunk records per head, T / 64 + B
+  Prologue pro;
 };
 
 // Arguments of one decode launch: q, k [B, H, dk]; v, o [B, H, dv];
@@ -44,6 +60,7 @@ struct DecodeArgs {
   int B, H, dk, dv;
   int dtype;
   int mode;
+  Prologue pro;
 };
 
 // Device workspace the prefill needs, per chunk of every head.  Scalar or no

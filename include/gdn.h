@@ -62,7 +62,8 @@ typedef enum gdn_status {
   GDN_ERR_UNSUPPORTED = -4,  /* d_k, d_v or chunk outside the supported set     */
   GDN_ERR_WORKSPACE = -5,    /* workspace smaller than the size queried         */
   GDN_ERR_LAUNCH = -6,       /* the HIP runtime refused a launch or a copy      */
-  GDN_ERR_ALIAS = -7         /* forbidden aliasing between inputs and outputs   */
+  GDN_ERR_ALIAS = -7,        /* forbidden aliasing between inputs and outputs   */
+  GDN_ERR_VALUE = -8         /* a scalar argument is out of range               */
 } gdn_status;
 
 /* Element type of q, k, v and o (and of a per-channel alpha). */
@@ -74,6 +75,38 @@ typedef enum gdn_decay {
   GDN_DECAY_SCALAR = 1,   /* alpha fp32, one value per (b, t, h)                */
   GDN_DECAY_CHANNEL = 2   /* alpha in `dtype`, one value per (b, t, h, key chan)*/
 } gdn_decay;
+
+/*
+ * Per-token prologue of the mixer layers, fused into the kernels by the
+ * *_fused entry points (a NULL prologue there means none of it).
+ *
+ *   l2norm_qk     nonzero: q_t <- q_t / sqrt(|q_t|^2 + eps) and k_t likewise,
+ *                 per (token, head), in fp32 on the values as loaded (the layers
+ *                 normalise queries and keys per head: "Don't Read Everything"
+ *                 notes, section 2.1; residual-learning notes, section 2.2;
+ *                 NextTransformer "method sources" page, baseline section).
+ *                 With eps = 0 a zero vector gives NaN.
+ *   eps           >= 0 and finite (GDN_ERR_VALUE otherwise); the pages leave it open.
+ *   beta_logits   nonzero: `beta` holds logits x and the recurrence uses
+ *                 sigmoid(x) (NextTransformer page, DeltaNet entry).
+ *   alpha_logits  nonzero, decay modes only (ignored for GDN_DECAY_NONE):
+ *                 `alpha` holds x and log alpha = -A[h] softplus(x + dt_bias),
+ *                 a Mamba2-style decay (residual-learning notes, section 2.2);
+ *                 floored at -100 like every log alpha here.
+ *   A             DEVICE fp32 [H], the per-head rates (positive); required when
+ *                 alpha_logits is set and the call reads gates (GDN_ERR_NULL).
+ *   dt_bias       DEVICE fp32 [H] for a scalar decay, [H, dk] for a per-channel
+ *                 decay; NULL means zero.
+ * A and dt_bias must not alias any output or the workspace.
+ */
+typedef struct gdn_prologue {
+  int l2norm_qk;
+  float eps;
+  int beta_logits;
+  int alpha_logits;
+  const float* A;
+  const float* dt_bias;
+} gdn_prologue;
 
 /*
  * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 means the
@@ -163,6 +196,24 @@ gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                 gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
 
 /*
+ * Chunked prefill with the prologue fused in: gdn_chunk_fwd when cu_seqlens is
+ * NULL (B rows of T tokens), gdn_chunk_fwd_varlen when it is not (B packed
+ * sequences with T tokens in all); arguments, layouts, workspace size and
+ * errors are those of that entry point, plus the prologue's (see
+ * gdn_prologue).  Normalised q and k are never materialised: the kernels fold
+ * the inverse norms into the per-row factors they already apply (the decay
+ * weights of K K^T, Q K^T and the chunk's state products), so no extra pass
+ * over q or k is made.
+ */
+gdn_status gdn_chunk_fwd_fused(const void* q, const void* k, const void* v,
+                               const void* alpha, const float* beta, const float* S0,
+                               void* o, float* S_final, const int* cu_seqlens,
+                               const gdn_prologue* prologue,
+                               void* workspace, size_t workspace_bytes,
+                               int B, int T, int H, int dk, int dv, int chunk,
+                               gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
+
+/*
  * One decode step (the recurrence body for a single token), S updated in place.
  *
  *   q, k      [B, H, dk]   `dtype`
@@ -184,6 +235,17 @@ gdn_status gdn_decode_step(const void* q, const void* k, const void* v,
                            const void* alpha, const float* beta, float* S, void* o,
                            int B, int H, int dk, int dv,
                            gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
+
+/*
+ * gdn_decode_step with the prologue fused in (q and k normalised in fp32,
+ * beta and alpha from logits); alpha logits are [B, H] (scalar) or [B, H, dk]
+ * (per channel), dt_bias [H] or [H, dk].  A NULL prologue is gdn_decode_step.
+ */
+gdn_status gdn_decode_step_fused(const void* q, const void* k, const void* v,
+                                 const void* alpha, const float* beta, float* S, void* o,
+                                 const gdn_prologue* prologue,
+                                 int B, int H, int dk, int dv,
+                                 gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(gdn_status s);

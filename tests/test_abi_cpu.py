@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "gated_delta_rule_04_amd", "libgdn.so")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_WS, E_LAUNCH, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_WS, E_LAUNCH, E_ALIAS, E_VALUE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 def _declared():
@@ -41,6 +41,10 @@ def lib():
     lib.gdn_chunk_fwd_varlen.restype = i
     lib.gdn_chunk_fwd_varlen_workspace_bytes.argtypes = [i] * 8
     lib.gdn_chunk_fwd_varlen_workspace_bytes.restype = sz
+    lib.gdn_chunk_fwd_fused.argtypes = [vp] * 10 + [vp, sz] + [i] * 8 + [vp]
+    lib.gdn_chunk_fwd_fused.restype = i
+    lib.gdn_decode_step_fused.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    lib.gdn_decode_step_fused.restype = i
     return lib
 
 
@@ -55,11 +59,11 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_WS, E_LAUNCH, E_ALIAS):
+    for st in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_WS, E_LAUNCH, E_ALIAS, E_VALUE):
         s = lib.gdn_status_string(st)
         assert s and s.startswith(b"GDN_")
     assert lib.gdn_status_string(12345) == b"unknown gdn_status"
-    assert lib.gdn_version() == 200
+    assert lib.gdn_version() == 300
 
 
 # fake, disjoint device addresses (never dereferenced: every call fails validation)
@@ -111,8 +115,8 @@ def _ws_bytes(B, T, H, es, dk=128, mode=1):
     chunks = B * H * ((T + 63) // 64)
     if mode == 2:   # T, P, three scaled copies of K / Q, per-channel decay
         return chunks * ((2 * 64 * 64 + 3 * 64 * dk) * es + 4 * dk)
-    # T per chunk (and P in fp32: the bf16 state kernel forms P itself) + three fp32 gate rows
-    return chunks * ((2 if es == 4 else 1) * 64 * 64 * es + 3 * 64 * 4)
+    # T per chunk (and P in fp32: the bf16 state kernel forms P itself) + five fp32 gate rows
+    return chunks * ((2 if es == 4 else 1) * 64 * 64 * es + 5 * 64 * 4)
 
 
 def test_workspace_query(lib):
@@ -143,7 +147,7 @@ def _varlen_ws_bytes(N, T, H, es, dk=128, mode=1):
     slots = H * (T // 64 + N)
     if mode == 2:
         return slots * ((2 * 64 * 64 + 3 * 64 * dk) * es + 4 * dk)
-    return slots * ((2 if es == 4 else 1) * 64 * 64 * es + 3 * 64 * 4)
+    return slots * ((2 if es == 4 else 1) * 64 * 64 * es + 5 * 64 * 4)
 
 
 def test_varlen_workspace_bounds_every_split():
@@ -228,3 +232,46 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gdn, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         gdn.load()
+
+
+def _pro(l2=1, eps=1e-6, bl=1, al=1, A=(1 << 40) + 12 * (1 << 36), bias=0):
+    import gated_delta_rule_04_amd as gdn
+    return gdn.Prologue(l2, eps, bl, al, A, bias or None)
+
+
+def test_fused_prologue_validation(lib):
+    q, k, v, a, b, s0, o, sf = _bufs()
+    ws = (1 << 40) + 9 * (1 << 36)
+
+    def fwd(pro, cu=None, mode=1, T=100, B=2, H=3):
+        return lib.gdn_chunk_fwd_fused(q, k, v, a, b, s0, o, sf, cu,
+                                       None if pro is None else ctypes.byref(pro), ws, 1 << 30,
+                                       B, T, H, 128, 128, 64, 1, mode, None)
+
+    assert fwd(_pro(eps=-1.0)) == E_VALUE
+    assert fwd(_pro(eps=float("nan"))) == E_VALUE
+    assert fwd(_pro(eps=float("inf"))) == E_VALUE
+    assert fwd(_pro(A=0)) == E_NULL                        # alpha logits need A
+    assert fwd(_pro(A=o + 4)) == E_ALIAS                   # A inside o
+    assert fwd(_pro(bias=sf + 4)) == E_ALIAS               # dt_bias inside S_final
+    assert fwd(_pro(bias=ws + 4)) == E_ALIAS               # dt_bias inside the workspace
+    assert fwd(_pro(), mode=1, B=-1) == E_SHAPE
+    assert fwd(_pro(), cu=None, B=0, T=10) == OK            # fixed rows: B = 0, nothing to do
+    assert fwd(_pro(), cu=(1 << 40) + 13 * (1 << 36), B=0, T=10) == E_SHAPE   # packed: tokens, no rows
+    assert fwd(None, B=0) == OK
+    assert fwd(_pro(A=0, al=1), mode=0, B=0) == OK          # nothing to compute
+
+
+def test_fused_decode_validation(lib):
+    q, k, v, a, b, S, o, _ = _bufs()
+
+    def dec(pro, mode=1, B=4, H=2):
+        return lib.gdn_decode_step_fused(q, k, v, a, b, S, o,
+                                         None if pro is None else ctypes.byref(pro),
+                                         B, H, 128, 64, 1, mode, None)
+
+    assert dec(_pro(eps=-0.5)) == E_VALUE
+    assert dec(_pro(A=0)) == E_NULL
+    assert dec(_pro(A=S + 8)) == E_ALIAS                   # A inside the state
+    assert dec(_pro(A=o)) == E_ALIAS                       # A at o
+    assert dec(_pro(), B=0) == OK

@@ -280,3 +280,43 @@ def per_head_rel_err(x, ref, head_axes) -> float:
     den = np.max(np.abs(rs), axis=1)
     r = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
     return float(np.max(r))
+
+
+
+def make_prologue(B: int, T: int, H: int, dk: int, dv: int, dtype: torch.dtype, mode: int,
+                  seed: int, s0_std: float = 0.1) -> dict:
+    """Raw inputs for the fused prologue (the values a mixer layer's projections
+    produce before its normalisations and gates):
+      q, k      z ~ N(0, 1) times a per-(b, t, h) scale exp(N(0, 0.5^2)), not
+                normalised; cast to ``dtype``
+      v         z, cast
+      beta      logits z, fp32 [B, T, H]
+      alpha     logits z, fp32 [B, T, H] (scalar decay) or ``dtype``
+                [B, T, H, dk] (per channel); None without decay
+      A         per-head rates U(1, 16), fp32 [H]
+      dt_bias   inverse softplus of dt = exp(U(ln 0.001, ln 0.1)), fp32 [H]
+                (scalar) or [H, dk] (per channel): a Mamba2-style initialisation
+                of the decay, softplus(x + dt_bias) near dt
+      S0        N(0, s0_std^2) fp32 [B, H, dv, dk], or None for s0_std = 0.
+    Tensor j of the seed: q 0, k 1, v 2, beta 3, alpha 4, S0 5, scales 7, A 8,
+    dt_bias 9."""
+    s = 1000 * seed
+    scale = torch.exp(0.5 * _randn((2, B, T, H, 1), s + 7))
+    q = (_randn((B, T, H, dk), s + 0) * scale[0]).to(dtype)
+    k = (_randn((B, T, H, dk), s + 1) * scale[1]).to(dtype)
+    v = _randn((B, T, H, dv), s + 2).to(dtype)
+    beta = _randn((B, T, H), s + 3)
+    alpha = A = dt_bias = None
+    if mode != MODE_NONE:
+        A = 1.0 + 15.0 * torch.rand(H, generator=_gen(s + 8))
+        bshape = (H,) if mode == MODE_SCALAR else (H, dk)
+        dt = torch.exp(torch.empty(bshape).uniform_(float(torch.log(torch.tensor(1e-3))),
+                                                    float(torch.log(torch.tensor(1e-1))),
+                                                    generator=_gen(s + 9)))
+        dt_bias = torch.log(torch.expm1(dt))
+        if mode == MODE_SCALAR:
+            alpha = _randn((B, T, H), s + 4)
+        else:
+            alpha = _randn((B, T, H, dk), s + 4).to(dtype)
+    S0 = s0_std * _randn((B, H, dv, dk), s + 5) if s0_std > 0 else None
+    return dict(q=q, k=k, v=v, beta=beta, alpha=alpha, S0=S0, A=A, dt_bias=dt_bias)
