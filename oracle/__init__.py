@@ -26,7 +26,7 @@ evaluation of the product form, invariants).
 """
 from . import prologue  # noqa: F401
 from .loop import (gdn_fwd, gdn_fwd_varlen, gdn_decode, build, num_threads, Oracle, compile_library,
-                   SOURCE, MODE_NONE, MODE_SCALAR, MODE_CHANNEL)
+                   SOURCE, MODE_NONE, MODE_SCALAR, MODE_CHANNEL, MODE_GDN2)
 
 __all__ = ["gdn_fwd", "gdn_fwd_varlen", "gdn_decode", "build", "num_threads", "Oracle", "compile_library", "SOURCE",
-           "MODE_NONE", "MODE_SCALAR", "MODE_CHANNEL"]
+           "MODE_NONE", "MODE_SCALAR", "MODE_CHANNEL", "MODE_GDN2"]

@@ -25,12 +25,18 @@ and o_r = S_r q_r gives the two terms of O.
 
 All decay ratios are formed as explicit products of the per-token gates (no
 division, no logarithm), so gates equal to 0 or 1 are handled exactly.
+
+Gated DeltaNet-2 (mode 3; "Linear Attention Architectures" notes, section 2.6)
+changes two things: the prediction reads the erase direction e_r = b_r * k_r
+and the target is z_r = w_r * v_r, with no beta.  The same unrolling gives
+(I + A) U = Z - (E Gam) S_n^T with A[r, j] = e_r^T R(r, j) k_j, so Tm = (I + A)^{-1},
+W = Tm (E Gam), Ut = Tm Z; the output and the state update keep k.
 """
 from __future__ import annotations
 
 import numpy as np
 
-MODE_NONE, MODE_SCALAR, MODE_CHANNEL = 0, 1, 2
+MODE_NONE, MODE_SCALAR, MODE_CHANNEL, MODE_GDN2 = 0, 1, 2, 3
 
 
 def _decay_vectors(alpha_c, mode, C, dk):
@@ -50,10 +56,12 @@ def _ratio(dec, r, j):
     return out
 
 
-def chunk_step(S, Q, K, V, beta_c, alpha_c, mode):
+def chunk_step(S, Q, K, V, beta_c, alpha_c, mode, erase_c=None, write_c=None):
     """One chunk: returns (O (C, dv), S_next (dv, dk)).  All fp64."""
     C, dk = K.shape
-    dec = _decay_vectors(alpha_c, mode, C, dk)
+    dec = _decay_vectors(alpha_c, MODE_CHANNEL if mode == MODE_GDN2 else mode, C, dk)
+    gdn2 = mode == MODE_GDN2
+    Er = K * erase_c if gdn2 else K * np.asarray(beta_c)[:, None]   # row side of A
     gam = np.stack([_ratio(dec, r, -1) for r in range(C)])         # Gam_r, (C, dk)
     A = np.zeros((C, C))
     P = np.zeros((C, C))
@@ -61,11 +69,16 @@ def chunk_step(S, Q, K, V, beta_c, alpha_c, mode):
         for j in range(r + 1):
             rr = _ratio(dec, r, j)
             if j < r:
-                A[r, j] = beta_c[r] * np.dot(K[r] * rr, K[j])
+                A[r, j] = np.dot(Er[r] * rr, K[j])
             P[r, j] = np.dot(Q[r] * rr, K[j])
-    Tm = np.linalg.solve(np.eye(C) + A, np.diag(beta_c))
-    W = Tm @ (K * gam)
-    Ut = Tm @ V
+    if gdn2:
+        Tm = np.linalg.solve(np.eye(C) + A, np.eye(C))
+        W = Tm @ (Er * gam)
+        Ut = Tm @ (V * write_c)
+    else:
+        Tm = np.linalg.solve(np.eye(C) + A, np.diag(beta_c))
+        W = Tm @ (K * gam)
+        Ut = Tm @ V
     U = Ut - W @ S.T
     O = (Q * gam) @ S.T + P @ U
     Ktail = np.stack([K[r] * _ratio(dec, C - 1, r) for r in range(C)])
@@ -73,9 +86,10 @@ def chunk_step(S, Q, K, V, beta_c, alpha_c, mode):
     return O, S_next
 
 
-def gdn_fwd(q, k, v, alpha, beta, S0=None, mode=MODE_SCALAR, chunk=64):
+def gdn_fwd(q, k, v, alpha, beta, S0=None, mode=MODE_SCALAR, chunk=64, erase=None, write=None):
     """Chunked prefill, same layouts and meaning as ``oracle.gdn_fwd``."""
-    q, k, v, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta))
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    beta = None if beta is None else np.asarray(beta, dtype=np.float64)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     alpha = None if mode == MODE_NONE else np.asarray(alpha, dtype=np.float64)
@@ -87,8 +101,10 @@ def gdn_fwd(q, k, v, alpha, beta, S0=None, mode=MODE_SCALAR, chunk=64):
             for n0 in range(0, T, chunk):
                 sl = slice(n0, min(n0 + chunk, T))
                 a_c = None if alpha is None else alpha[b, sl, h]
-                O, S = chunk_step(S, q[b, sl, h], k[b, sl, h], v[b, sl, h],
-                                  beta[b, sl, h], a_c, mode)
+                b_c = None if beta is None else beta[b, sl, h]
+                e_c = None if erase is None else np.asarray(erase[b, sl, h], dtype=np.float64)
+                w_c = None if write is None else np.asarray(write[b, sl, h], dtype=np.float64)
+                O, S = chunk_step(S, q[b, sl, h], k[b, sl, h], v[b, sl, h], b_c, a_c, mode, e_c, w_c)
                 o[b, sl, h] = O
             S_final[b, h] = S
     return o, S_final

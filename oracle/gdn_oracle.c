@@ -32,6 +32,10 @@
  *
  * The decode step is the loop body run once with S in/out.
  *
+ * Mode 3 (Gated DeltaNet-2, see oracle_step_gdn2) replaces beta by an erase
+ * gate b [.., dk] on the key side and a write gate w [.., dv] on the value
+ * side; its alpha is per key channel.
+ *
  * Layouts (row-major, contiguous):
  *   q, k   [B, T, H, dk]      v, o [B, T, H, dv]
  *   alpha  mode 0: unused (may be NULL); mode 1: [B, T, H]; mode 2: [B, T, H, dk]
@@ -47,6 +51,7 @@
 #define MODE_NONE 0
 #define MODE_SCALAR 1
 #define MODE_CHANNEL 2
+#define MODE_GDN2 3
 
 /* One recurrence step on the state S (dv x dk) of one head. */
 static void oracle_step(double* S, const double* q, const double* k,
@@ -79,16 +84,75 @@ static void oracle_step(double* S, const double* q, const double* k,
   }
 }
 
-/* Prefill over T tokens.  Returns 0 on success, -1 on a bad argument. */
+/* One Gated DeltaNet-2 step on the state W (dv x dk) of one head, in the
+ * notation of the "Linear Attention Architectures" notes, section 2.6
+ * (Eqs. 21-24): the erase and write controls of the delta rule are separate
+ * vectors.
+ *   W~ = W D_alpha          per-key-channel decay, from the right
+ *   e  = b (.) kappa        erase direction, key side
+ *   z  = w (.) v            new content, value side
+ *   r  = z - W~ e           residual against the erase read-out
+ *   W  = W~ + r kappa^T     the outer product takes the key itself, not e
+ *   o  = W q                the query reads the updated state
+ * With b = beta 1 and w = beta 1 this is the per-channel (KDA) step. */
+static void oracle_step_gdn2(double* W, const double* q, const double* kappa,
+                             const double* v, const double* alpha, const double* b,
+                             const double* w, double* o, int dk, int dv, double* res) {
+  int i, c;
+  for (i = 0; i < dv; ++i)
+    for (c = 0; c < dk; ++c) W[i * dk + c] *= alpha[c];
+  for (i = 0; i < dv; ++i) {
+    double read = 0.0;
+    for (c = 0; c < dk; ++c) read += W[i * dk + c] * (b[c] * kappa[c]);
+    res[i] = w[i] * v[i] - read;
+  }
+  for (i = 0; i < dv; ++i)
+    for (c = 0; c < dk; ++c) W[i * dk + c] += res[i] * kappa[c];
+  for (i = 0; i < dv; ++i) {
+    double acc = 0.0;
+    for (c = 0; c < dk; ++c) acc += W[i * dk + c] * q[c];
+    o[i] = acc;
+  }
+}
+
+/* One token of any variant: GDN2 reads the erase and write gates of the
+ * token, the others its beta. */
+static void oracle_token(double* S, const double* q, const double* k, const double* v,
+                         const double* alpha, const double* beta, const double* erase,
+                         const double* write, size_t tok, double* o, int dk, int dv, int mode,
+                         double* p) {
+  const double* a = NULL;
+  if (mode == MODE_SCALAR) a = alpha + tok;
+  if (mode == MODE_CHANNEL || mode == MODE_GDN2) a = alpha + tok * dk;
+  if (mode == MODE_GDN2)
+    oracle_step_gdn2(S, q + tok * dk, k + tok * dk, v + tok * dv, a, erase + tok * dk,
+                     write + tok * dv, o + tok * dv, dk, dv, p);
+  else
+    oracle_step(S, q + tok * dk, k + tok * dk, v + tok * dv, a, beta[tok], o + tok * dv, dk, dv,
+                mode, p);
+}
+
+/* Arguments every entry point checks the same way. */
+static int bad_mode_args(int mode, const double* alpha, const double* beta, const double* erase,
+                         const double* write, int has_tokens) {
+  if (mode < MODE_NONE || mode > MODE_GDN2) return 1;
+  if (!has_tokens) return 0;
+  if (mode != MODE_NONE && alpha == NULL) return 1;
+  if (mode == MODE_GDN2) return erase == NULL || write == NULL;
+  return beta == NULL;
+}
+
+/* Prefill over T tokens.  Returns 0 on success, -1 on a bad argument.
+ * erase [B, T, H, dk] and write [B, T, H, dv] are read by mode GDN2 only
+ * (which ignores beta; its alpha is [B, T, H, dk]). */
 int oracle_gdn_fwd_f64(const double* q, const double* k, const double* v,
-                       const double* alpha, const double* beta,
-                       const double* S0, double* o, double* S_final,
+                       const double* alpha, const double* beta, const double* erase,
+                       const double* write, const double* S0, double* o, double* S_final,
                        int B, int T, int H, int dk, int dv, int mode) {
   long bh;
   int fail = 0;
   if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
-  if (mode < MODE_NONE || mode > MODE_CHANNEL) return -1;
-  if (mode != MODE_NONE && alpha == NULL && T > 0) return -1;
+  if (bad_mode_args(mode, alpha, beta, erase, write, T > 0)) return -1;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
   for (bh = 0; bh < (long)B * H; ++bh) {
     long b = bh / H, h = bh % H;
@@ -106,11 +170,7 @@ int oracle_gdn_fwd_f64(const double* q, const double* k, const double* v,
       memset(S, 0, sizeof(double) * (size_t)dv * dk);
     for (long t = 0; t < T; ++t) {
       size_t tok = ((size_t)b * T + t) * H + h; /* index of (b, t, h) */
-      const double* a = NULL;
-      if (mode == MODE_SCALAR) a = alpha + tok;
-      if (mode == MODE_CHANNEL) a = alpha + tok * dk;
-      oracle_step(S, q + tok * dk, k + tok * dk, v + tok * dv, a, beta[tok],
-                  o + tok * dv, dk, dv, mode, p);
+      oracle_token(S, q, k, v, alpha, beta, erase, write, tok, o, dk, dv, mode, p);
     }
     if (S_final != NULL)
       memcpy(S_final + (size_t)bh * dv * dk, S, sizeof(double) * (size_t)dv * dk);
@@ -138,16 +198,15 @@ int oracle_gdn_fwd_f64(const double* q, const double* k, const double* v,
  * beta [T, H]; S0, S_final [N, H, dv, dk].  Returns 0, or -1 on a bad argument
  * (including cu_seqlens that do not run from 0 to T without decreasing). */
 int oracle_gdn_fwd_varlen_f64(const double* q, const double* k, const double* v,
-                              const double* alpha, const double* beta,
-                              const double* S0, double* o, double* S_final,
-                              const int* cu, int N, int T, int H, int dk, int dv,
-                              int mode) {
+                              const double* alpha, const double* beta, const double* erase,
+                              const double* write, const double* S0, double* o,
+                              double* S_final, const int* cu, int N, int T, int H, int dk,
+                              int dv, int mode) {
   long h;
   int s, fail = 0;
   const size_t sz = (size_t)dv * dk;
   if (N < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0 || cu == NULL) return -1;
-  if (mode < MODE_NONE || mode > MODE_CHANNEL) return -1;
-  if (mode != MODE_NONE && alpha == NULL && T > 0) return -1;
+  if (bad_mode_args(mode, alpha, beta, erase, write, T > 0)) return -1;
   if (cu[0] != 0 || cu[N] != T) return -1;
   for (s = 0; s < N; ++s)
     if (cu[s + 1] < cu[s]) return -1;
@@ -178,14 +237,7 @@ int oracle_gdn_fwd_varlen_f64(const double* q, const double* k, const double* v,
         }
       }
       if (t == T) break;
-      {
-        size_t tok = (size_t)t * H + h;
-        const double* a = NULL;
-        if (mode == MODE_SCALAR) a = alpha + tok;
-        if (mode == MODE_CHANNEL) a = alpha + tok * dk;
-        oracle_step(S, q + tok * dk, k + tok * dk, v + tok * dv, a, beta[tok], o + tok * dv, dk, dv,
-                    mode, p);
-      }
+      oracle_token(S, q, k, v, alpha, beta, erase, write, (size_t)t * H + h, o, dk, dv, mode, p);
     }
     free(S);
     free(p);
@@ -197,25 +249,23 @@ int oracle_gdn_fwd_varlen_f64(const double* q, const double* k, const double* v,
  *   q, k [B, H, dk]; v, o [B, H, dv]; alpha [B, H] (mode 1) or [B, H, dk]
  *   (mode 2); beta [B, H]; S [B, H, dv, dk] in/out. */
 int oracle_gdn_decode_f64(const double* q, const double* k, const double* v,
-                          const double* alpha, const double* beta, double* S,
-                          double* o, int B, int H, int dk, int dv, int mode) {
+                          const double* alpha, const double* beta, const double* erase,
+                          const double* write, double* S, double* o, int B, int H, int dk,
+                          int dv, int mode) {
   long bh;
   int fail = 0;
   if (B < 0 || H < 0 || dk <= 0 || dv <= 0) return -1;
-  if (mode < MODE_NONE || mode > MODE_CHANNEL) return -1;
-  if (mode != MODE_NONE && alpha == NULL) return -1;
+  if (bad_mode_args(mode, alpha, beta, erase, write, B > 0 && H > 0)) return -1;
 #pragma omp parallel for schedule(static) reduction(| : fail)
   for (bh = 0; bh < (long)B * H; ++bh) {
     double* p = (double*)malloc(sizeof(double) * (size_t)dv);
-    const double* a = NULL;
     if (p == NULL) {
       fail |= 1;
       continue;
     }
-    if (mode == MODE_SCALAR) a = alpha + bh;
-    if (mode == MODE_CHANNEL) a = alpha + (size_t)bh * dk;
-    oracle_step(S + (size_t)bh * dv * dk, q + (size_t)bh * dk, k + (size_t)bh * dk,
-                v + (size_t)bh * dv, a, beta[bh], o + (size_t)bh * dv, dk, dv, mode, p);
+    /* one token per head: the token index is the head index */
+    oracle_token(S + (size_t)bh * dv * dk, q, k, v, alpha, beta, erase, write, (size_t)bh, o, dk,
+                 dv, mode, p);
     free(p);
   }
   return fail ? -1 : 0;

@@ -14,7 +14,7 @@ import threading
 
 import numpy as np
 
-MODE_NONE, MODE_SCALAR, MODE_CHANNEL = 0, 1, 2
+MODE_NONE, MODE_SCALAR, MODE_CHANNEL, MODE_GDN2 = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "gdn_oracle.c")
@@ -60,18 +60,31 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def _check_gates(mode, alpha, beta, erase, write, lead, dk, dv):
+    """Shapes of the gates of a decay mode (``lead`` = the token axes)."""
+    if mode == MODE_SCALAR:
+        assert alpha is not None and alpha.shape == lead
+    elif mode in (MODE_CHANNEL, MODE_GDN2):
+        assert alpha is not None and alpha.shape == lead + (dk,)
+    if mode == MODE_GDN2:
+        assert erase is not None and erase.shape == lead + (dk,)
+        assert write is not None and write.shape == lead + (dv,)
+    else:
+        assert beta is not None and beta.shape == lead
+
+
 class Oracle:
     """One loaded build of the oracle library."""
 
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
-        lib.oracle_gdn_fwd_f64.argtypes = [dp] * 8 + [ctypes.c_int] * 6
+        lib.oracle_gdn_fwd_f64.argtypes = [dp] * 10 + [ctypes.c_int] * 6
         lib.oracle_gdn_fwd_f64.restype = ctypes.c_int
-        lib.oracle_gdn_fwd_varlen_f64.argtypes = ([dp] * 8 + [ctypes.POINTER(ctypes.c_int)]
+        lib.oracle_gdn_fwd_varlen_f64.argtypes = ([dp] * 10 + [ctypes.POINTER(ctypes.c_int)]
                                                   + [ctypes.c_int] * 6)
         lib.oracle_gdn_fwd_varlen_f64.restype = ctypes.c_int
-        lib.oracle_gdn_decode_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 5
+        lib.oracle_gdn_decode_f64.argtypes = [dp] * 9 + [ctypes.c_int] * 5
         lib.oracle_gdn_decode_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -80,35 +93,36 @@ class Oracle:
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())
 
-    def gdn_fwd(self, q, k, v, alpha, beta, S0=None, mode: int = MODE_SCALAR):
+    def gdn_fwd(self, q, k, v, alpha, beta, S0=None, mode: int = MODE_SCALAR, erase=None,
+                write=None):
         """Prefill: token loop over T for every (b, h).
 
         q, k [B, T, H, dk]; v [B, T, H, dv]; alpha [B, T, H] (mode 1) or
-        [B, T, H, dk] (mode 2) or None (mode 0); beta [B, T, H];
-        S0 [B, H, dv, dk] or None (= zeros).
+        [B, T, H, dk] (modes 2, 3) or None (mode 0); beta [B, T, H] (modes
+        0-2); erase [B, T, H, dk] and write [B, T, H, dv] (mode 3, Gated
+        DeltaNet-2); S0 [B, H, dv, dk] or None (= zeros).
         Returns (o [B, T, H, dv], S_final [B, H, dv, dk]) as fp64 ndarrays."""
         q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
-        alpha, S0 = _f64(alpha), _f64(S0)
+        alpha, S0, erase, write = _f64(alpha), _f64(S0), _f64(erase), _f64(write)
         B, T, H, dk = q.shape
         dv = v.shape[-1]
-        assert k.shape == q.shape and v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
-        if mode == MODE_SCALAR:
-            assert alpha is not None and alpha.shape == (B, T, H)
-        elif mode == MODE_CHANNEL:
-            assert alpha is not None and alpha.shape == (B, T, H, dk)
-        else:
+        assert k.shape == q.shape and v.shape == (B, T, H, dv)
+        _check_gates(mode, alpha, beta, erase, write, (B, T, H), dk, dv)
+        if mode == MODE_NONE:
             alpha = None
         if S0 is not None:
             assert S0.shape == (B, H, dv, dk)
         o = np.zeros((B, T, H, dv), dtype=np.float64)
         S = np.zeros((B, H, dv, dk), dtype=np.float64)
         rc = self._lib.oracle_gdn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                          _ptr(S0), _ptr(o), _ptr(S), B, T, H, dk, dv, mode)
+                                          _ptr(erase), _ptr(write), _ptr(S0), _ptr(o), _ptr(S),
+                                          B, T, H, dk, dv, mode)
         if rc != 0:
             raise RuntimeError("oracle_gdn_fwd_f64 failed (rc=%d)" % rc)
         return o, S
 
-    def gdn_fwd_varlen(self, q, k, v, alpha, beta, cu_seqlens, S0=None, mode: int = MODE_SCALAR):
+    def gdn_fwd_varlen(self, q, k, v, alpha, beta, cu_seqlens, S0=None, mode: int = MODE_SCALAR,
+                       erase=None, write=None):
         """Prefill of a packed batch: sequence s holds tokens cu_seqlens[s] ..
         cu_seqlens[s + 1] - 1 of the token axis, and its state starts from S0[s]
         (zeros when S0 is None) at its first token.
@@ -118,55 +132,54 @@ class Oracle:
         A leading axis of size 1 on the token tensors is accepted and kept.
         Returns (o, S_final [N, H, dv, dk]) as fp64 ndarrays."""
         q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
-        alpha, S0 = _f64(alpha), _f64(S0)
+        alpha, S0, erase, write = _f64(alpha), _f64(S0), _f64(erase), _f64(write)
         lead = q.ndim == 4
         if lead:
             assert q.shape[0] == 1
-            q, k, v, beta = q[0], k[0], v[0], beta[0]
-            alpha = None if alpha is None else alpha[0]
+            first = lambda x: None if x is None else x[0]
+            q, k, v, beta = q[0], k[0], v[0], first(beta)
+            alpha, erase, write = first(alpha), first(erase), first(write)
         cu = np.ascontiguousarray(np.asarray(
             cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int32))
         N = cu.shape[0] - 1
         T, H, dk = q.shape
         dv = v.shape[-1]
-        assert k.shape == q.shape and v.shape == (T, H, dv) and beta.shape == (T, H)
-        if mode == MODE_SCALAR:
-            assert alpha is not None and alpha.shape == (T, H)
-        elif mode == MODE_CHANNEL:
-            assert alpha is not None and alpha.shape == (T, H, dk)
-        else:
+        assert k.shape == q.shape and v.shape == (T, H, dv)
+        _check_gates(mode, alpha, beta, erase, write, (T, H), dk, dv)
+        if mode == MODE_NONE:
             alpha = None
         if S0 is not None:
             assert S0.shape == (N, H, dv, dk)
         o = np.zeros((T, H, dv), dtype=np.float64)
         S = np.zeros((N, H, dv, dk), dtype=np.float64)
         rc = self._lib.oracle_gdn_fwd_varlen_f64(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(erase), _ptr(write),
+            _ptr(S0), _ptr(o), _ptr(S),
             cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), N, T, H, dk, dv, mode)
         if rc != 0:
             raise RuntimeError("oracle_gdn_fwd_varlen_f64 failed (rc=%d)" % rc)
         return (o[None] if lead else o), S
 
-    def gdn_decode(self, q, k, v, alpha, beta, S, mode: int = MODE_SCALAR):
+    def gdn_decode(self, q, k, v, alpha, beta, S, mode: int = MODE_SCALAR, erase=None,
+                   write=None):
         """One decode step.  q, k [B, H, dk]; v [B, H, dv]; alpha [B, H] or
-        [B, H, dk] or None; beta [B, H]; S [B, H, dv, dk].
+        [B, H, dk] or None; beta [B, H] (modes 0-2); erase [B, H, dk] and write
+        [B, H, dv] (mode 3); S [B, H, dv, dk].
         Returns (o [B, H, dv], S_new); the input S is not modified."""
         q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
-        alpha = _f64(alpha)
+        alpha, erase, write = _f64(alpha), _f64(erase), _f64(write)
         S = _f64(S).copy()
         B, H, dk = q.shape
         dv = v.shape[-1]
-        assert k.shape == q.shape and v.shape == (B, H, dv) and beta.shape == (B, H)
+        assert k.shape == q.shape and v.shape == (B, H, dv)
         assert S.shape == (B, H, dv, dk)
-        if mode == MODE_SCALAR:
-            assert alpha is not None and alpha.shape == (B, H)
-        elif mode == MODE_CHANNEL:
-            assert alpha is not None and alpha.shape == (B, H, dk)
-        else:
+        _check_gates(mode, alpha, beta, erase, write, (B, H), dk, dv)
+        if mode == MODE_NONE:
             alpha = None
         o = np.zeros((B, H, dv), dtype=np.float64)
         rc = self._lib.oracle_gdn_decode_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                             _ptr(S), _ptr(o), B, H, dk, dv, mode)
+                                             _ptr(erase), _ptr(write), _ptr(S), _ptr(o),
+                                             B, H, dk, dv, mode)
         if rc != 0:
             raise RuntimeError("oracle_gdn_decode_f64 failed (rc=%d)" % rc)
         return o, S

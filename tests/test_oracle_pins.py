@@ -448,11 +448,84 @@ def pin_varlen_resets_at_sequence_starts(orc):
         assert np.array_equal(o, flat(ob)) and np.array_equal(S, Sb)
 
 
+def _gdn2_inputs(rng, B, T, H, dk, dv, lo=0.5):
+    q, k, v, alpha, beta, S0 = _inputs(rng, B, T, H, dk, dv, MODE_CHANNEL, lo=lo)
+    erase = rng.uniform(0.0, 1.0, (B, T, H, dk))
+    write = rng.uniform(0.0, 1.0, (B, T, H, dv))
+    return q, k, v, alpha, erase, write, S0
+
+
+def pin_gdn2_reduces_to_kda(orc):
+    """Gated DeltaNet-2 with erase gate b = beta 1 and write gate w = beta 1 is the
+    per-channel (KDA) recurrence (LAA section 2.6), and with equal channels the
+    scalar-gate one (up to the rounding order of beta (v - p) against
+    beta v - beta p)."""
+    rng = np.random.default_rng(28)
+    B, T, H, dk, dv = 2, 9, 2, 5, 4
+    q, k, v, alpha, beta, S0 = _inputs(rng, B, T, H, dk, dv, MODE_CHANNEL)
+    erase = np.repeat(beta[..., None], dk, axis=-1)
+    write = np.repeat(beta[..., None], dv, axis=-1)
+    o2, S2 = orc.gdn_fwd(q, k, v, alpha, None, S0, mode=oracle.MODE_GDN2, erase=erase, write=write)
+    o1, S1 = orc.gdn_fwd(q, k, v, alpha, beta, S0, mode=MODE_CHANNEL)
+    assert _rel(o2, o1) < 1e-13 and _rel(S2, S1) < 1e-13
+    a1 = alpha[..., 0]
+    o2, S2 = orc.gdn_fwd(q, k, v, np.repeat(a1[..., None], dk, axis=-1), None, S0,
+                         mode=oracle.MODE_GDN2, erase=erase, write=write)
+    o1, S1 = orc.gdn_fwd(q, k, v, a1, beta, S0, mode=MODE_SCALAR)
+    assert _rel(o2, o1) < 1e-13 and _rel(S2, S1) < 1e-13
+
+
+def pin_gdn2_orthonormal_closed_form(orc):
+    """Orthonormal keys, no decay, S0 = 0, an erase gate equal over the channels
+    (b_t = c_t 1): every erase read-out S e_t = c_t S k_t is zero (the state's rows
+    lie in the span of the earlier keys), so S_T = sum_t (w_t * v_t) k_t^T and
+    o_t = sum_{j<=t} (w_j * v_j)(k_j . q_t): the write gate alone scales what is
+    stored, along the key itself."""
+    rng = np.random.default_rng(29)
+    T, dk, dv = 5, 6, 3
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm[:T][None, :, None, :]
+    q = rng.standard_normal((1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, dv))
+    alpha = np.ones((1, T, 1, dk))
+    erase = np.repeat(rng.uniform(0.1, 2.0, (1, T, 1, 1)), dk, axis=-1)
+    write = rng.uniform(0.1, 1.0, (1, T, 1, dv))
+    o, S = orc.gdn_fwd(q, k, v, alpha, None, None, mode=oracle.MODE_GDN2, erase=erase, write=write)
+    z = (write * v)[0, :, 0]
+    kk = k[0, :, 0]
+    assert np.max(np.abs(S[0, 0] - z.T @ kk)) < 1e-14
+    for t in range(T):
+        want = sum(z[j] * float(kk[j] @ q[0, t, 0]) for j in range(t + 1))
+        assert np.max(np.abs(o[0, t, 0] - want)) < 1e-13
+
+
+def pin_gdn2_product_form(orc):
+    """The unrolled form of the page's expansion S_t = S_{t-1} D_t (I - e_t k_t^T)
+    + z_t k_t^T (LAA section 2.6): S_T = S0 prod_t D_t (I - e_t k_t^T)
+    + sum_t z_t k_t^T prod_{j>t} D_j (I - e_j k_j^T), as matrix products."""
+    rng = np.random.default_rng(30)
+    T, dk, dv = 6, 4, 3
+    q, k, v, alpha, erase, write, S0 = _gdn2_inputs(rng, 1, T, 1, dk, dv)
+    o, S = orc.gdn_fwd(q, k, v, alpha, None, S0, mode=oracle.MODE_GDN2, erase=erase, write=write)
+    M = [np.diag(alpha[0, t, 0]) @ (np.eye(dk) - np.outer(erase[0, t, 0] * k[0, t, 0], k[0, t, 0]))
+         for t in range(T)]
+    want = S0[0, 0].copy()
+    for t in range(T):
+        want = want @ M[t]
+    for t in range(T):
+        term = np.outer(write[0, t, 0] * v[0, t, 0], k[0, t, 0])
+        for j in range(t + 1, T):
+            term = term @ M[j]
+        want = want + term
+    assert _rel(S[0, 0], want) < 1e-13
+
+
 PINS = [pin_worked_example, pin_exact_recall, pin_orthonormal_closed_form,
         pin_kda_axis_keys_closed_form, pin_no_write, pin_exact_rational, pin_gradient_step,
         pin_orthogonal_invariance, pin_rank_bound, pin_value_channel_independence,
         pin_linearity, pin_contraction, pin_mode_reductions, pin_zero_gate_resets,
-        pin_decode_matches_prefill, pin_varlen_resets_at_sequence_starts]
+        pin_decode_matches_prefill, pin_varlen_resets_at_sequence_starts, pin_gdn2_reduces_to_kda,
+        pin_gdn2_orthonormal_closed_form, pin_gdn2_product_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -484,6 +557,16 @@ def test_oracle_varlen_rejects_bad_offsets():
 # ----------------------------------------------------------------------------------
 # chunk form (the algebra the GPU kernels follow) against the pinned loop
 # ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,C", [(1, 64), (63, 16), (65, 64), (37, 3)])
+def test_chunk_form_gdn2_equals_loop(T, C):
+    rng = np.random.default_rng(2000 + T * 7 + C)
+    q, k, v, alpha, erase, write, S0 = _gdn2_inputs(rng, 1, T, 2, 8, 6, lo=0.6)
+    o, S = oracle.gdn_fwd(q, k, v, alpha, None, S0, mode=oracle.MODE_GDN2, erase=erase, write=write)
+    oc, Sc = chunk_form.gdn_fwd(q, k, v, alpha, None, S0, mode=oracle.MODE_GDN2, chunk=C,
+                                erase=erase, write=write)
+    assert _rel(oc, o) < 1e-12 and _rel(Sc, S) < 1e-12
+
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("T,C", [(1, 64), (2, 1), (63, 16), (64, 64), (65, 64), (130, 64),
@@ -526,6 +609,13 @@ MUTATIONS = {
     "read_uses_key": ("acc += S[i * dk + c] * q[c];", "acc += S[i * dk + c] * k[c];"),
     "write_uses_query": ("S[i * dk + c] += u * k[c];", "S[i * dk + c] += u * q[c];"),
     "error_without_beta": ("double u = beta * (v[i] - p[i]);", "double u = (v[i] - p[i]);"),
+    "gdn2_write_along_erase": ("W[i * dk + c] += res[i] * kappa[c];",
+                               "W[i * dk + c] += res[i] * b[c] * kappa[c];"),
+    "gdn2_no_write_gate": ("res[i] = w[i] * v[i] - read;", "res[i] = v[i] - read;"),
+    "gdn2_erase_without_gate": ("read += W[i * dk + c] * (b[c] * kappa[c]);",
+                                "read += W[i * dk + c] * kappa[c];"),
+    "gdn2_decay_on_value_rows": ("for (c = 0; c < dk; ++c) W[i * dk + c] *= alpha[c];",
+                                 "for (c = 0; c < dk; ++c) W[i * dk + c] *= alpha[i % dk];"),
     "varlen_wrong_initial_state": ("memcpy(S, S0 + ((size_t)seq * H + h) * sz",
                                    "memcpy(S, S0 + ((size_t)(seq - 1) * H + h) * sz"),
     "varlen_boundary_one_late": ("while (seq < N && cu[seq + 1] == t) {",
