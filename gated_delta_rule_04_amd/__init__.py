@@ -21,7 +21,8 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_fused", "decode_step", "decode_step_fused", "load", "lib_path", "GDNError",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_fused", "decode_step", "decode_step_fused",
+           "gdn2_chunk_fwd", "gdn2_decode_step", "load", "lib_path", "GDNError",
            "DECAY_NONE", "DECAY_SCALAR", "DECAY_CHANNEL", "EXPORTED_SYMBOLS"]
 
 DECAY_NONE, DECAY_SCALAR, DECAY_CHANNEL = 0, 1, 2
@@ -30,7 +31,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so"
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                     "gdn_chunk_fwd_varlen_workspace_bytes", "gdn_chunk_fwd_varlen",
                     "gdn_chunk_fwd_fused", "gdn_decode_step", "gdn_decode_step_fused",
-                    "gdn_status_string", "gdn_version")
+                    "gdn2_chunk_fwd", "gdn2_decode_step", "gdn_status_string", "gdn_version")
 
 
 class Prologue(ctypes.Structure):
@@ -78,6 +79,10 @@ def load():
         lib.gdn_chunk_fwd_fused.restype = i
         lib.gdn_decode_step_fused.argtypes = [vp] * 8 + [i] * 6 + [vp]
         lib.gdn_decode_step_fused.restype = i
+        lib.gdn2_chunk_fwd.argtypes = [vp] * 10 + [vp, sz] + [i] * 7 + [vp]
+        lib.gdn2_chunk_fwd.restype = i
+        lib.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
+        lib.gdn2_decode_step.restype = i
         lib.gdn_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.gdn_decode_step.restype = i
         lib.gdn_status_string.argtypes = [i]
@@ -327,5 +332,66 @@ def decode_step_fused(q, k, v, alpha, beta, S, *, l2norm_qk=False, eps=1e-6, bet
     st = lib.gdn_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None),
                                    _ptr(beta), _ptr(S), _ptr(o), ctypes.byref(pro), B, H, dk, dv,
                                    _DTYPES[dtype], mode, _stream(stream))
+    _check(st)
+    return o
+
+
+def gdn2_chunk_fwd(q, k, v, alpha, erase, write, S0=None, *, cu_seqlens=None, chunk=64, o=None,
+                   S_final=None, need_final=True, stream=None):
+    """Gated DeltaNet-2 prefill (``gdn2_chunk_fwd``): per-channel decay alpha and
+    erase gate [.., T, H, dk], write gate [.., T, H, dv], all in q's dtype;
+    batched ([B, T, H, d]) or packed (``cu_seqlens``, [1, T, H, d] or [T, H, d])."""
+    lib = load()
+    packed = cu_seqlens is not None
+    T, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    if packed:
+        _require(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() == 4 and q.shape[0] != 1:
+            raise ValueError("a packed batch has a leading axis of 1, got %d" % q.shape[0])
+        B = cu_seqlens.shape[0] - 1
+    else:
+        B = q.shape[0]
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (erase, "erase"),
+                 (write, "write")):
+        _require(t, n, dtype)
+    _require(S0, "S0", torch.float32)
+    if o is None:
+        o = torch.empty(tuple(q.shape[:-1]) + (dv,), dtype=dtype, device=q.device)
+    if S_final is None and need_final:
+        S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    _require(o, "o", dtype)
+    _require(S_final, "S_final", torch.float32)
+    wsf = lib.gdn_chunk_fwd_varlen_workspace_bytes if packed else lib.gdn_chunk_fwd_workspace_bytes
+    ws_bytes = int(wsf(B, T, H, dk, dv, chunk, _DTYPES[dtype], DECAY_CHANNEL))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    st = lib.gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                            _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens), _ptr(ws), ws_bytes,
+                            B, T, H, dk, dv, chunk, _DTYPES[dtype], _stream(stream))
+    _check(st)
+    return o, S_final
+
+
+def gdn2_decode_step(q, k, v, alpha, erase, write, S, *, o=None, stream=None):
+    """One Gated DeltaNet-2 decode step (``gdn2_decode_step``); S updated in place.
+    q, k, alpha, erase [B, H, dk]; v, write [B, H, dv]; S fp32 [B, H, dv, dk]."""
+    lib = load()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (alpha, "alpha"), (erase, "erase"),
+                 (write, "write")):
+        _require(t, n, dtype)
+    _require(S, "S", torch.float32)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dtype, device=q.device)
+    _require(o, "o", dtype)
+    st = lib.gdn2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                              _ptr(S), _ptr(o), B, H, dk, dv, _DTYPES[dtype], _stream(stream))
     _check(st)
     return o

@@ -120,11 +120,14 @@ gdn_status take_prologue(const gdn_prologue* pro, gdn_decay mode, bool reads_gat
 
 // Prefill over B rows of T tokens (cu_seqlens NULL and packed false) or over a
 // packed batch of B sequences with T tokens in all.
+// Gated DeltaNet-2 (erase and write gates given): mode is GDN_DECAY_CHANNEL
+// for every check and 3 for the kernels, and beta is not read.
 gdn_status prefill(const void* q, const void* k, const void* v, const void* alpha,
                    const float* beta, const float* S0, void* o, float* S_final,
                    const int* cu_seqlens, bool packed, const gdn_prologue* pro, void* workspace,
                    size_t workspace_bytes, int B, int T, int H, int dk, int dv, int chunk,
-                   gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
+                   gdn_dtype dtype, gdn_decay mode, hipStream_t stream,
+                   const void* erase = nullptr, const void* write = nullptr, bool gdn2 = false) {
   gdn_status st = check_common(B, H, dk, dv, dtype, mode);
   if (st != GDN_OK) return st;
   if (T < 0) return GDN_ERR_SHAPE;
@@ -152,7 +155,8 @@ gdn_status prefill(const void* q, const void* k, const void* v, const void* alph
   if (packed && !cu_seqlens) return GDN_ERR_NULL;
   if (ws_need > 0 && !workspace) return GDN_ERR_NULL;
   if (has_tokens) {
-    if (!q || !k || !v || !beta || !o) return GDN_ERR_NULL;
+    if (!q || !k || !v || !o) return GDN_ERR_NULL;
+    if (gdn2 ? (!erase || !write) : !beta) return GDN_ERR_NULL;
     if (mode != GDN_DECAY_NONE && !alpha) return GDN_ERR_NULL;
   }
   if (!has_tokens && !S_final) return GDN_OK;  // nothing to write
@@ -164,23 +168,27 @@ gdn_status prefill(const void* q, const void* k, const void* v, const void* alph
   Range rk = range_of(has_tokens ? k : nullptr, (size_t)nqk * es);
   Range rv = range_of(has_tokens ? v : nullptr, (size_t)nv * es);
   Range ra = range_of(has_tokens && mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes);
-  Range rb = range_of(has_tokens ? beta : nullptr, (size_t)ntok * 4);
+  Range rb = range_of(has_tokens && !gdn2 ? beta : nullptr, (size_t)ntok * 4);
+  Range re = range_of(has_tokens && gdn2 ? erase : nullptr, (size_t)nqk * es);
+  Range rwg = range_of(has_tokens && gdn2 ? write : nullptr, (size_t)nv * es);
   Range rs0 = range_of(S0, (size_t)nS * 4);
   Range rcu = range_of(packed ? cu_seqlens : nullptr, ((size_t)B + 1) * 4);
   Range ro = range_of(has_tokens ? o : nullptr, (size_t)nv * es);
   Range rsf = range_of(S_final, (size_t)nS * 4);
   if (!has_tokens) rA = rbias = Range{0, 0};
-  for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, rA, rbias})
+  for (Range in : {rq, rk, rv, ra, rb, re, rwg, rs0, rcu, rA, rbias})
     if (overlaps(ro, in)) return GDN_ERR_ALIAS;
-  for (Range in : {rq, rk, rv, ra, rb, ro, rcu, rA, rbias})
+  for (Range in : {rq, rk, rv, ra, rb, re, rwg, ro, rcu, rA, rbias})
     if (overlaps(rsf, in)) return GDN_ERR_ALIAS;
   if (overlaps(rsf, rs0) && (const void*)S_final != (const void*)S0) return GDN_ERR_ALIAS;
   Range rw = range_of(ws_need > 0 ? workspace : nullptr, ws_need);
-  for (Range in : {rq, rk, rv, ra, rb, rs0, rcu, ro, rsf, rA, rbias})
+  for (Range in : {rq, rk, rv, ra, rb, re, rwg, rs0, rcu, ro, rsf, rA, rbias})
     if (overlaps(rw, in)) return GDN_ERR_ALIAS;
 
-  gdn::PrefillArgs a{q, k, v, alpha, beta, S0, o, S_final, B, T, H, dk, dv, (int)dtype,
-                     (int)mode};
+  gdn::PrefillArgs a{q, k, v, alpha, gdn2 ? nullptr : beta, S0, o, S_final, B, T, H, dk, dv,
+                     (int)dtype, gdn2 ? 3 : (int)mode};
+  a.erase = erase;
+  a.write = write;
   if (packed) {
     a.cu_seqlens = cu_seqlens;
     a.nslots = gdn::varlen_slots(B, T);
@@ -191,7 +199,8 @@ gdn_status prefill(const void* q, const void* k, const void* v, const void* alph
 
 gdn_status decode(const void* q, const void* k, const void* v, const void* alpha,
                   const float* beta, float* S, void* o, const gdn_prologue* pro, int B, int H,
-                  int dk, int dv, gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
+                  int dk, int dv, gdn_dtype dtype, gdn_decay mode, hipStream_t stream,
+                  const void* erase = nullptr, const void* write = nullptr, bool gdn2 = false) {
   gdn_status st = check_common(B, H, dk, dv, dtype, mode);
   if (st != GDN_OK) return st;
   long long nqk, nv, nh, nS;
@@ -204,7 +213,8 @@ gdn_status decode(const void* q, const void* k, const void* v, const void* alpha
   st = take_prologue(pro, mode, B > 0 && H > 0, H, dk, &pa, &rA, &rbias);
   if (st != GDN_OK) return st;
   if (B == 0 || H == 0) return GDN_OK;
-  if (!q || !k || !v || !beta || !S || !o) return GDN_ERR_NULL;
+  if (!q || !k || !v || !S || !o) return GDN_ERR_NULL;
+  if (gdn2 ? (!erase || !write) : !beta) return GDN_ERR_NULL;
   if (mode != GDN_DECAY_NONE && !alpha) return GDN_ERR_NULL;
 
   const size_t es = elem_size(dtype);
@@ -213,15 +223,20 @@ gdn_status decode(const void* q, const void* k, const void* v, const void* alpha
   Range rq = range_of(q, (size_t)nqk * es), rk = range_of(k, (size_t)nqk * es);
   Range rv = range_of(v, (size_t)nv * es);
   Range ra = range_of(mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes);
-  Range rb = range_of(beta, (size_t)nh * 4);
+  Range rb = range_of(gdn2 ? nullptr : beta, (size_t)nh * 4);
+  Range re = range_of(gdn2 ? erase : nullptr, (size_t)nqk * es);
+  Range rwg = range_of(gdn2 ? write : nullptr, (size_t)nv * es);
   Range rs = range_of(S, (size_t)nS * 4), ro = range_of(o, (size_t)nv * es);
-  for (Range in : {rq, rk, rv, ra, rb, rs, rA, rbias})
+  for (Range in : {rq, rk, rv, ra, rb, re, rwg, rs, rA, rbias})
     if (overlaps(ro, in)) return GDN_ERR_ALIAS;
-  for (Range in : {rq, rk, rv, ra, rb, rA, rbias})
+  for (Range in : {rq, rk, rv, ra, rb, re, rwg, rA, rbias})
     if (overlaps(rs, in)) return GDN_ERR_ALIAS;
 
-  gdn::DecodeArgs a{q, k, v, alpha, beta, S, o, B, H, dk, dv, (int)dtype, (int)mode};
+  gdn::DecodeArgs a{q, k, v, alpha, gdn2 ? nullptr : beta, S, o, B, H, dk, dv, (int)dtype,
+                    gdn2 ? 3 : (int)mode};
   a.pro = pa;
+  a.erase = erase;
+  a.write = write;
   return gdn::launch_decode(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
@@ -268,6 +283,23 @@ gdn_status gdn_decode_step_fused(const void* q, const void* k, const void* v, co
                                  const gdn_prologue* prologue, int B, int H, int dk, int dv,
                                  gdn_dtype dtype, gdn_decay mode, hipStream_t stream) {
   return decode(q, k, v, alpha, beta, S, o, prologue, B, H, dk, dv, dtype, mode, stream);
+}
+
+gdn_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                          const void* erase, const void* write, const float* S0, void* o,
+                          float* S_final, const int* cu_seqlens, void* workspace,
+                          size_t workspace_bytes, int B, int T, int H, int dk, int dv, int chunk,
+                          gdn_dtype dtype, hipStream_t stream) {
+  return prefill(q, k, v, alpha, nullptr, S0, o, S_final, cu_seqlens, cu_seqlens != nullptr,
+                 nullptr, workspace, workspace_bytes, B, T, H, dk, dv, chunk, dtype,
+                 GDN_DECAY_CHANNEL, stream, erase, write, true);
+}
+
+gdn_status gdn2_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                            const void* erase, const void* write, float* S, void* o, int B,
+                            int H, int dk, int dv, gdn_dtype dtype, hipStream_t stream) {
+  return decode(q, k, v, alpha, nullptr, S, o, nullptr, B, H, dk, dv, dtype, GDN_DECAY_CHANNEL,
+                stream, erase, write, true);
 }
 
 }  // extern "C"

@@ -582,6 +582,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
 // exp(G_r - G_j) <= 1 taken directly, is added by the wave that owns the tile.
 // Masked entries (j > r) of the diagonal blocks may overflow; the epilogues
 // replace them by zero with a select, never with arithmetic.
+// Gated DeltaNet-2 ("Linear Attention Architectures" notes, section 2.6) runs
+// through the same kernel: its erase direction e_r = b_r * k_r takes k_r's place
+// on the row side of A and in Kg (the prediction reads e), beta is 1, and the
+// state kernel scales V by the write gate (z = w * v); P, Kc and the state
+// update keep k.
 // Instead of gates, the state kernel gets decay-scaled operands (the chunk form
 // with Diag(exp(G_r)) in place of gamma_r):
 //   Kg = K . exp(G)          X = V - Kg S^T
@@ -610,6 +615,10 @@ struct RecOf {
 };
 template <typename E, int DK>
 struct RecOf<E, DK, 2> {
+  using type = KdaRec<E, DK>;
+};
+template <typename E, int DK>
+struct RecOf<E, DK, 3> {   // Gated DeltaNet-2: Kg holds the decay-scaled erase rows
   using type = KdaRec<E, DK>;
 };
 
@@ -644,6 +653,18 @@ __device__ inline u32x4 pack16<float>(const float* f) {
   return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
 }
 
+// Element-wise product of two 16-byte pieces (rounded to the operand dtype).
+template <typename E>
+__device__ inline u32x4 mul16(const u32x4& a, const u32x4& b) {
+  constexpr int N = 16 / (int)sizeof(E);
+  float x[N], y[N];
+  unpack16<E>(a, x);
+  unpack16<E>(b, y);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] *= y[i];
+  return pack16<E>(x);
+}
+
 constexpr float kSplitLimit = 64.f;
 
 // LDS: region 1 holds G (fp32 [C][LDG]) while the operands are built, then A
@@ -676,9 +697,10 @@ struct KdaPrepPlan {
   static constexpr size_t total = nrm + (NORM ? 2 * C * 4 : 0);
 };
 
-template <typename E, int DK, bool NORM>
+template <typename E, int DK, bool NORM, bool G2>
 __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __restrict__ tws,
                                                            int nchunks) {
+  static_assert(!(NORM && G2), "the erase-gate variant takes no prologue");
   using L = KdaPrepPlan<E, DK, NORM>;
   using R = KdaRec<E, DK>;
   constexpr int EPC = 16 / (int)sizeof(E);
@@ -714,13 +736,14 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   const size_t qk_tok = (size_t)H * DK;
   const E* kgl = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
   const E* qgl = static_cast<const E*>(a.q) + (tok0 * H + h) * DK;
+  const E* bgl = G2 ? static_cast<const E*>(a.erase) + (tok0 * H + h) * DK : nullptr;
   E* rec = tws + (at.sp.rec0 + n) * R::elems;
 
   // This thread's (row, 16-byte chunk) items of K and Q, loaded once for all
   // passes: item m is row (tid + kThreads m) / CPR (rows 0..31 for m < IPT,
   // 32..63 above), channels c0 = ((tid + kThreads m) % CPR) EPC.  Rows past the
   // sequence end repeat its last row.
-  u32x4 kreg[2 * IPT], qreg[2 * IPT];
+  u32x4 kreg[2 * IPT], qreg[2 * IPT], breg[G2 ? 2 * IPT : 1];   // (erase gate rows: G2)
   float nkm[2 * IPT], nqm[2 * IPT];   // inverse norms of those rows (NORM)
   // G, per channel: thread (segment s, channel c) scans RPS rows, then adds the
   // totals of the segments before it.  Rows past the sequence end add nothing.
@@ -738,6 +761,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
       const uint32_t off = (uint32_t)min(it / CPR, cn - 1) * (uint32_t)qk_tok + (it % CPR) * EPC;
       kreg[m] = ld_once(kgl + off);
       qreg[m] = ld_once(qgl + off);
+      if constexpr (G2) breg[m] = ld_once(bgl + off);
     }
 #pragma unroll
     for (int i = 0; i < RPS; ++i) {
@@ -747,8 +771,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
 #pragma unroll
     for (int i = 1; i < RPS; ++i) g[i] += g[i - 1];
     Tot[s * DK + c] = g[RPS - 1];
-    if (tid < C) {
-      const float bt = a.beta[(tok0 + min(tid, cn - 1)) * H + h];
+    if (tid < C) {   // (G2: beta is 1, the gates sit in the operands)
+      const float bt = G2 ? 1.f : a.beta[(tok0 + min(tid, cn - 1)) * H + h];
       Bt[tid] = tid < cn ? (a.pro.beta_logits ? sigmoid_f(bt) : bt) : 0.f;
     }
     if constexpr (NORM) {
@@ -807,6 +831,13 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
       const u32x4 qraw = qreg[m];
       unpack16<E>(kraw, kf);
       unpack16<E>(qraw, qf);
+      // the row side of A and Kg: the key, or (G2) the erase direction b * k
+      float ef[EPC];
+      if constexpr (G2) {
+        unpack16<E>(breg[m], ef);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ef[e] *= kf[e];
+      }
       if constexpr (NORM) {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
@@ -832,7 +863,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
           const float w = __expf(gr[e]);
-          x[e] = kf[e] * w;
+          x[e] = (G2 ? ef[e] : kf[e]) * w;
           y[e] = qf[e] * w;
           z[e] = kf[e] * __expf(gl[e] - gr[e]);
         }
@@ -854,7 +885,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
         for (int e = 0; e < EPC; ++e) {
           const float w = __expf(gr[e] - ga[e]);
           const bool k1 = (keep >> e) & 1u;
-          x[e] = k1 ? kf[e] * w : 0.f;
+          x[e] = k1 ? (G2 ? ef[e] : kf[e]) * w : 0.f;
           y[e] = k1 ? qf[e] * w : 0.f;
         }
         *reinterpret_cast<u32x4*>(Rop + lr * LDK + c0) = pack16<E>(x);
@@ -882,7 +913,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
           const int c = 32 * wd + __builtin_ctz(bits);
           bits &= bits - 1;
           const float gr = Gl[r * LDG + c];
-          const float xv = (float)xr[c] * xn;
+          float xv = (float)xr[c] * xn;
+          // G2, A tiles: the row side is the erase direction; its gate comes
+          // from HBM (a channel taking this path is rare)
+          if (G2 && !(wave & 1)) xv *= (float)bgl[(size_t)min(r, cn - 1) * qk_tok + c];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int jl = acc_row(v >> 2, v & 3, lane), j = 32 * pass + jl;
@@ -999,7 +1033,8 @@ __device__ inline void store_col4(float* dst, const u32x4& r0, const u32x4& r1, 
 template <typename E, int DK, int DVS, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, const E* __restrict__ tws) {
   constexpr bool SEPKT = sep_kt_fits<E, DK, DVS>();
-  constexpr bool KDA = MODE == 2;   // per-channel decay: operands come pre-scaled
+  constexpr bool KDA = MODE >= 2;   // per-channel decay: operands come pre-scaled
+  constexpr bool G2 = MODE == 3;    // Gated DeltaNet-2: V is scaled by the write gate
   using L = StatePlan<E, DK, DVS, SEPKT>;
   using R = typename RecOf<E, DK, MODE>::type;
   static_assert(L::total <= 160 * 1024, "LDS plan exceeds 160 KiB");
@@ -1067,6 +1102,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   const E* qg = static_cast<const E*>(a.q) + (sp.tok0 * H + h) * DK;
   const E* kg = static_cast<const E*>(a.k) + (sp.tok0 * H + h) * DK;
   const E* vg = static_cast<const E*>(a.v) + (sp.tok0 * H + h) * dv + i0;
+  const E* wg = G2 ? static_cast<const E*>(a.write) + (sp.tok0 * H + h) * dv + i0 : nullptr;
   const E* recs = tws + sp.rec0 * R::elems;   // per-chunk records
   E* og = static_cast<E*>(a.o) + (sp.tok0 * H + h) * dv + i0;
   const size_t sbase = ((size_t)b * H + h) * dv + i0;  // first state row of the slice
@@ -1109,7 +1145,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
   // columns of those tokens are zero (their beta is zero), so they never reach
   // U, O or S, and their O rows are not written.
   u32x4 pk[KBT][4], pq[KBT][4], pv[VBT][4], pt[TBT];
-  u32x4 pg = u32x4{0u, 0u, 0u, 0u};   // gate block: 48 chunks, threads 0..47 (gC: DK / 4)
+  u32x4 pw[G2 ? VBT : 1][4];   // write-gate rows (G2)
+  u32x4 pg = u32x4{0u, 0u, 0u, 0u};   // gate block: rows 0..3, threads 0..63 (gC: DK / 4)
   u32x4 pkc[KDA && SEPKT ? KBT : 1][4], pp[TBT];   // Kc rows (per-channel decay) and P
 
   auto prefetch = [&](int n) __attribute__((always_inline)) {
@@ -1157,6 +1194,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
       for (int rr = 0; rr < 4; ++rr) {
         const uint32_t off = (uint32_t)min(4 * rg + rr, rmax) * (uint32_t)v_tok + cc * EPC;
         pv[m][rr] = ld_once(vq + off);
+        if constexpr (G2) pw[m][rr] = ld_once(wg + (size_t)t0 * v_tok + off);
       }
     }
     {
@@ -1195,6 +1233,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_kernel(PrefillArgs a, co
       const int blk = tid + kThreads * m;
       if (blk < NVB) {
         const int rg = blk_row(blk, CPV), cc = blk_col(blk, CPV);
+        if constexpr (G2) {   // z = w * v
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) pv[m][rr] = mul16<E>(pv[m][rr], pw[m][rr]);
+        }
 #pragma unroll
         for (int e = 0; e < EPC; ++e)
           store_col4(Vt + (cc * EPC + e) * LDT + 4 * rg, pv[m][0], pv[m][1], pv[m][2], pv[m][3], e);
@@ -1469,7 +1511,8 @@ constexpr int kFormPAhead = 2;   // fragments of P's product loaded this many k 
 template <typename E, int DK, int DVS, int MODE, bool NORM>
 __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws) {
   static_assert(sizeof(E) == 2, "the eight-wave kernel is bf16");
-  constexpr bool KDA = MODE == 2;
+  constexpr bool KDA = MODE >= 2;
+  constexpr bool G2 = MODE == 3;   // Gated DeltaNet-2: V is scaled by the write gate
   static_assert(!(KDA && NORM), "per-channel records carry normalised operands already");
   using L = WsPlan<E, DK, DVS, KDA, NORM>;
   constexpr int GS = L::gstride;
@@ -1540,10 +1583,12 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     const E* qg = static_cast<const E*>(a.q) + (sp.tok0 * H + h) * DK;
     const E* kg = static_cast<const E*>(a.k) + (sp.tok0 * H + h) * DK;
     const E* vg = static_cast<const E*>(a.v) + (sp.tok0 * H + h) * dv + i0;
+    const E* wg = G2 ? static_cast<const E*>(a.write) + (sp.tok0 * H + h) * dv + i0 : nullptr;
     const E* recs = tws + sp.rec0 * R::elems;
     E* og = static_cast<E*>(a.o) + (sp.tok0 * H + h) * dv + i0;
 
     u32x4 pk[KPT], pq[KPT], pv[VPT], pkc[KDA ? KPT : 1];   // rows of a chunk
+    u32x4 pw[G2 ? VPT : 1];                                  // write-gate rows (G2)
     u32x4 pg = u32x4{0u, 0u, 0u, 0u};
     u32x4 pt[TBT], pp[KDA ? TBT : 1];                                // T (and P) of a chunk
 
@@ -1589,6 +1634,8 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       for (int m = 0; m < VPT; ++m) {
         const int q = ptid + PT * m, r = q / CPV, cc = q % CPV;
         pv[m] = ld_once(vq + (uint32_t)min(r, rmax) * (uint32_t)v_tok + cc * EPC);
+        if constexpr (G2)
+          pw[m] = ld_once(wg + (size_t)t0 * v_tok + (uint32_t)min(r, rmax) * (uint32_t)v_tok + cc * EPC);
       }
     };
     auto load_tp = [&](int n) __attribute__((always_inline)) {
@@ -1617,7 +1664,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
 #pragma unroll
       for (int m = 0; m < VPT; ++m) {
         const int q = ptid + PT * m, r = q / CPV, cc = q % CPV;
-        *reinterpret_cast<u32x4*>(Vr + r * LDV + cc * EPC) = pv[m];
+        *reinterpret_cast<u32x4*>(Vr + r * LDV + cc * EPC) = G2 ? mul16<E>(pv[m], pw[m]) : pv[m];
       }
       if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * GS + 4 * ptid) = pg;
       if constexpr (NORM) {   // inverse norms of the Q rows: a row's CPR pieces sit in CPR lanes
@@ -1982,17 +2029,23 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws);
     else if (a.mode == 1)
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws);
-    else if constexpr (DVS == 32)   // the per-channel buffers leave room for 32-row slices only
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws);
-    else
+    else if constexpr (DVS == 32) {   // the per-channel buffers leave room for 32-row slices only
+      if (a.mode == 2)
+        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws);
+      else
+        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws);
+    } else {
       return hipErrorInvalidConfiguration;
+    }
   } else {
     if (a.mode == 0)
       hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 0>), grid, block, 0, stream, a, tws);
     else if (a.mode == 1)
       hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 1>), grid, block, 0, stream, a, tws);
-    else
+    else if (a.mode == 2)
       hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 2>), grid, block, 0, stream, a, tws);
+    else
+      hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 3>), grid, block, 0, stream, a, tws);
   }
   return hipGetLastError();
 }
@@ -2015,14 +2068,16 @@ hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) 
       else if (a.mode == 1)
         hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 1, true>), grid, block, 0, stream, a, tws, nchunks);
       else
-        hipLaunchKernelGGL((chunk_prep_kda<E, DK, true>), grid, block, 0, stream, a, tws, nchunks);
+        hipLaunchKernelGGL((chunk_prep_kda<E, DK, true, false>), grid, block, 0, stream, a, tws, nchunks);
     } else {
       if (a.mode == 0)
         hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 0, false>), grid, block, 0, stream, a, tws, nchunks);
       else if (a.mode == 1)
         hipLaunchKernelGGL((chunk_prep_kernel<E, DK, 1, false>), grid, block, 0, stream, a, tws, nchunks);
+      else if (a.mode == 2)
+        hipLaunchKernelGGL((chunk_prep_kda<E, DK, false, false>), grid, block, 0, stream, a, tws, nchunks);
       else
-        hipLaunchKernelGGL((chunk_prep_kda<E, DK, false>), grid, block, 0, stream, a, tws, nchunks);
+        hipLaunchKernelGGL((chunk_prep_kda<E, DK, false, true>), grid, block, 0, stream, a, tws, nchunks);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -2031,7 +2086,7 @@ hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) 
     return launch_state<E, DK, 32>(a, tws, stream);
   } else {
     const long long wg64 = (long long)a.B * a.H * (a.dv / 64);
-    if (wg64 >= 256 && a.mode != 2) return launch_state<E, DK, 64>(a, tws, stream);
+    if (wg64 >= 256 && a.mode < 2) return launch_state<E, DK, 64>(a, tws, stream);
     return launch_state<E, DK, 32>(a, tws, stream);
   }
 }
@@ -2041,7 +2096,7 @@ hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) 
 // Bytes of one chunk record.
 static size_t record_bytes(int dk, int dtype, int mode) {
   const size_t es = dtype == 1 ? 2 : 4;
-  if (mode == 2) return (2 * (size_t)C * C + 3 * (size_t)C * dk) * es + 4 * (size_t)dk;
+  if (mode >= 2) return (2 * (size_t)C * C + 3 * (size_t)C * dk) * es + 4 * (size_t)dk;
   return (es == 4 ? 2 : 1) * (size_t)C * C * es + kGateFloats * 4;   // bf16: no P
 }
 

@@ -18,6 +18,10 @@
 // of a (b, h) head.  The fp32 rows are held in registers between the read and
 // the write, and the two row dot products are finished with xor-shuffles over
 // the row's lanes.
+// Gated DeltaNet-2 (MODE 3; "Linear Attention Architectures" notes, section
+// 2.6): the prediction reads the erase direction e = b * k, the target is
+// w_i v_i and there is no beta: s_k = S_i D e, u_i = w_i v_i - s_k; the write
+// and the output keep k.
 // With the prologue on, q and k are normalised in fp32 registers (their norms
 // are sums over the row's lanes like the dot products) and beta, alpha come
 // from logits; the state traffic is unchanged.
@@ -104,14 +108,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) s[m][j] = load_state(S + (size_t)(g + RPW * m) * DK + 4 * l8 + 4 * LPR * j);
 
-  float4 kf[NQ], qf[NQ], af[NQ];
+  float4 kf[NQ], qf[NQ], af[NQ], bf[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     kf[j] = load4(k + 4 * l8 + 4 * LPR * j);
     qf[j] = load4(q + 4 * l8 + 4 * LPR * j);
-    if (MODE == 2) af[j] = load4(static_cast<const E*>(a.alpha) + bh * DK + 4 * l8 + 4 * LPR * j);
+    if (MODE >= 2) af[j] = load4(static_cast<const E*>(a.alpha) + bh * DK + 4 * l8 + 4 * LPR * j);
+    if (MODE == 3) bf[j] = load4(static_cast<const E*>(a.erase) + bh * DK + 4 * l8 + 4 * LPR * j);
   }
-  float beta = a.beta[bh];
+  float beta = MODE == 3 ? 1.f : a.beta[bh];
   float alpha = 1.f;
   if (MODE == 1) alpha = static_cast<const float*>(a.alpha)[bh];
   if constexpr (PRO) {
@@ -155,6 +160,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   float vr[NR];
 #pragma unroll
   for (int m = 0; m < NR; ++m) vr[m] = load1(v + g + RPW * m);
+  if constexpr (MODE == 3) {   // target w_i v_i
+    const E* wr = static_cast<const E*>(a.write) + bh * DV + r0;
+#pragma unroll
+    for (int m = 0; m < NR; ++m) vr[m] *= load1(wr + g + RPW * m);
+  }
 
   // k . q over the head (every group computes it; it is tiny)
   float kq = 0.f;
@@ -167,7 +177,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   float4 kd[NQ], qd[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    if (MODE == 2) {
+    if (MODE == 3) {   // the prediction reads D e = D (b * k)
+      kd[j] = make_float4(kf[j].x * bf[j].x * af[j].x, kf[j].y * bf[j].y * af[j].y,
+                          kf[j].z * bf[j].z * af[j].z, kf[j].w * bf[j].w * af[j].w);
+      qd[j] = make_float4(qf[j].x * af[j].x, qf[j].y * af[j].y, qf[j].z * af[j].z, qf[j].w * af[j].w);
+    } else if (MODE == 2) {
       kd[j] = make_float4(kf[j].x * af[j].x, kf[j].y * af[j].y, kf[j].z * af[j].z, kf[j].w * af[j].w);
       qd[j] = make_float4(qf[j].x * af[j].x, qf[j].y * af[j].y, qf[j].z * af[j].z, qf[j].w * af[j].w);
     } else {
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (l8 == 0) store1(o + g + RPW * m, out);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      float4 d = MODE == 2 ? af[j] : make_float4(alpha, alpha, alpha, alpha);
+      float4 d = MODE >= 2 ? af[j] : make_float4(alpha, alpha, alpha, alpha);
       float4 r;
       r.x = s[m][j].x * d.x + u * kf[j].x;
       r.y = s[m][j].y * d.y + u * kf[j].y;
@@ -218,7 +232,8 @@ hipError_t launch_mode(const DecodeArgs& a, hipStream_t stream) {
     case 2: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 1, false>), grid, block, 0, stream, a); break;
     case 3: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 1, true>), grid, block, 0, stream, a); break;
     case 4: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 2, false>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 2, true>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 2, true>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<E, DK, DV, 3, false>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }

@@ -37,7 +37,10 @@ struct PrefillArgs {
   float* S_final;    // may be null
   int B, T, H, dk, dv;
   int dtype;         // 0 fp32, 1 bf16
-  int mode;          // 0 none, 1 scalar, 2 channel
+  int mode;          // 0 none, 1 scalar, 2 channel, 3 Gated DeltaNet-2 (channel decay,
+                     // erase gate [B, T, H, dk] and write gate [B, T, H, dv] in place of beta)
+  const void* erase = nullptr;   // mode 3, operand dtype
+  const void* write = nullptr;   // mode 3, operand dtype
   // Packed batch of sequences of varying length: B sequences back to back on
   // a token axis of length T (the layouts above with a leading batch of 1),
   // sequence b holding tokens cu_seqlens[b] .. cu_seqlens[b + 1] - 1 (device
@@ -61,6 +64,8 @@ struct DecodeArgs {
   int dtype;
   int mode;
   Prologue pro;
+  const void* erase = nullptr;   // mode 3: [B, H, dk]
+  const void* write = nullptr;   // mode 3: [B, H, dv]
 };
 
 // Device workspace the prefill needs, per chunk of every head.  Scalar or no

@@ -247,6 +247,41 @@ gdn_status gdn_decode_step_fused(const void* q, const void* k, const void* v,
                                  int B, int H, int dk, int dv,
                                  gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
 
+/*
+ * Gated DeltaNet-2 ("Linear Attention Architectures" notes, section 2.6,
+ * Eqs. 21-24): the delta rule with its erase and write controls split into a
+ * key-side vector b_t and a value-side vector w_t, and a per-key-channel decay:
+ *
+ *     S~ = S_{t-1} Diag(alpha_t),  e_t = b_t * k_t,  z_t = w_t * v_t,
+ *     S_t = S~ + (z_t - S~ e_t) k_t^T,              o_t = S_t q_t
+ *
+ * (the outer product takes k_t itself).  b_t = w_t = beta_t 1 gives the
+ * per-channel rule of gdn_chunk_fwd.  Prefill, batched (cu_seqlens NULL, the
+ * gdn_chunk_fwd layouts) or packed (the gdn_chunk_fwd_varlen layouts):
+ *
+ *   alpha     `dtype` [.., T, H, dk]   per-channel decay in [0, 1]
+ *   erase     `dtype` [.., T, H, dk]   b_t
+ *   write     `dtype` [.., T, H, dv]   w_t
+ * and q, k, v, S0, o, S_final, workspace as for GDN_DECAY_CHANNEL (the
+ * workspace size is gdn_chunk_fwd(_varlen)_workspace_bytes with that mode).
+ * Errors as for gdn_chunk_fwd; erase and write are required when T > 0.
+ */
+gdn_status gdn2_chunk_fwd(const void* q, const void* k, const void* v, const void* alpha,
+                          const void* erase, const void* write, const float* S0, void* o,
+                          float* S_final, const int* cu_seqlens, void* workspace,
+                          size_t workspace_bytes, int B, int T, int H, int dk, int dv, int chunk,
+                          gdn_dtype dtype, hipStream_t stream);
+
+/*
+ * One Gated DeltaNet-2 decode step, S updated in place: q, k, alpha, erase
+ * [B, H, dk]; v, write, o [B, H, dv]; S fp32 [B, H, dv, dk].  Per state row i:
+ * s_e = S_i D e, s_q = S_i D q, u_i = w_i v_i - s_e, o_i = s_q + u_i (k . q),
+ * S_i <- S_i D + u_i k^T.
+ */
+gdn_status gdn2_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                            const void* erase, const void* write, float* S, void* o,
+                            int B, int H, int dk, int dv, gdn_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(gdn_status s);
 

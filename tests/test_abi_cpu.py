@@ -20,7 +20,7 @@ OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_WS, E_LAUNCH, E_ALIAS, E_VALUE = 0, -1,
 def _declared():
     text = open(os.path.join(ROOT, "include", "gdn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn2?_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -45,6 +45,10 @@ def lib():
     lib.gdn_chunk_fwd_fused.restype = i
     lib.gdn_decode_step_fused.argtypes = [vp] * 8 + [i] * 6 + [vp]
     lib.gdn_decode_step_fused.restype = i
+    lib.gdn2_chunk_fwd.argtypes = [vp] * 10 + [vp, sz] + [i] * 7 + [vp]
+    lib.gdn2_chunk_fwd.restype = i
+    lib.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
+    lib.gdn2_decode_step.restype = i
     return lib
 
 
@@ -275,3 +279,31 @@ def test_fused_decode_validation(lib):
     assert dec(_pro(A=S + 8)) == E_ALIAS                   # A inside the state
     assert dec(_pro(A=o)) == E_ALIAS                       # A at o
     assert dec(_pro(), B=0) == OK
+
+
+def test_gdn2_validation(lib):
+    q, k, v, a, s0, o, sf, _ = _bufs()
+    e, w = (1 << 40) + 14 * (1 << 36), (1 << 40) + 15 * (1 << 36)
+    ws = (1 << 40) + 9 * (1 << 36)
+
+    def fwd(ptrs=None, cu=None, B=2, T=100, H=3, dk=128, dv=128, ws_bytes=1 << 30):
+        p = ptrs if ptrs is not None else (q, k, v, a, e, w, s0, o, sf)
+        return lib.gdn2_chunk_fwd(*p, cu, ws, ws_bytes, B, T, H, dk, dv, 64, 1, None)
+
+    assert fwd(ptrs=(q, k, v, a, 0, w, s0, o, sf)) == E_NULL     # no erase gate
+    assert fwd(ptrs=(q, k, v, a, e, 0, s0, o, sf)) == E_NULL     # no write gate
+    assert fwd(ptrs=(q, k, v, 0, e, w, s0, o, sf)) == E_NULL     # no decay
+    assert fwd(ptrs=(q, k, v, a, e, o + 2, s0, o, sf)) == E_ALIAS
+    assert fwd(ptrs=(q, k, v, a, sf, w, s0, o, sf)) == E_ALIAS
+    assert fwd(dk=96) == E_UNSUP
+    assert fwd(ws_bytes=_ws_bytes(2, 100, 3, 2, 128, 2) - 1) == E_WS
+    assert fwd(B=0) == OK
+
+    def dec(ptrs=None, B=4, H=2):
+        p = ptrs if ptrs is not None else (q, k, v, a, e, w, s0, o)
+        return lib.gdn2_decode_step(*p, B, H, 128, 64, 1, None)
+
+    assert dec(ptrs=(q, k, v, a, 0, w, s0, o)) == E_NULL
+    assert dec(ptrs=(q, k, v, a, e, w, s0, e)) == E_ALIAS           # o over the erase gate
+    assert dec(ptrs=(q, k, v, a, e, s0 + 8, s0, o)) == E_ALIAS      # write gate inside S
+    assert dec(B=0) == OK

@@ -320,3 +320,18 @@ def make_prologue(B: int, T: int, H: int, dk: int, dv: int, dtype: torch.dtype, 
             alpha = _randn((B, T, H, dk), s + 4).to(dtype)
     S0 = s0_std * _randn((B, H, dv, dk), s + 5) if s0_std > 0 else None
     return dict(q=q, k=k, v=v, beta=beta, alpha=alpha, S0=S0, A=A, dt_bias=dt_bias)
+
+
+
+def make_gdn2(w: Prefill) -> dict:
+    """Inputs of a Gated DeltaNet-2 run with the shape and per-channel decay of a
+    workload ``w`` (gate recipe of ``w``): q, k, v, alpha, S0 as
+    :func:`make_prefill`, and instead of beta an erase gate sigmoid(z) per key
+    channel [B, T, H, dk] (tensor 10 of the seed) and a write gate sigmoid(z) per
+    value channel [B, T, H, dv] (tensor 11), both in the input dtype."""
+    d = make_prefill(w)
+    s = 1000 * w.seed
+    d["erase"] = torch.sigmoid(_randn((w.B, w.T, w.H, w.dk), s + 10)).to(w.dtype)
+    d["write"] = torch.sigmoid(_randn((w.B, w.T, w.H, w.dv), s + 11)).to(w.dtype)
+    d["beta"] = None
+    return d
