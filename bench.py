@@ -14,7 +14,9 @@ buffers so the 67 MB state cannot stay in the 256 MB Infinity Cache.  The
 packed variable-length prefill (the same 32768 tokens x 16 heads split into 16
 rows of 593 to 5858 tokens) is timed alongside (``packed``), and so is the
 prefill with the per-token prologue fused in (``fused_prologue``: raw q and k
-normalised in the kernels, beta and alpha from logits).
+normalised in the kernels, beta and alpha from logits), and Gated DeltaNet-2
+(``gdn2``: erase and write gates, per-channel decay) at the B=4, H=16, T=8192
+shape.
 
 Printed: one JSON line (the contract below), preceded by progress lines on
 stderr.  Peaks are MI355X's published figures: HBM 8 TB/s, dense bf16 MFMA
@@ -214,18 +216,64 @@ def bench_packed(w: W.Packed, steps: int):
 def bench_fused(w: W.Prefill, steps: int):
     """Average duration of one ``gdn_chunk_fwd_fused`` launch on raw inputs of
     the workload's shape (q, k not normalised, beta and alpha logits, per-head
-    rates and biases), every part of the prologue on."""
+    rates and biases), every part of the prologue on; timed in alternation
+    with the plain call on the workload's own inputs (three rounds each, mean),
+    so that both see the same clock."""
     log("generating raw inputs for the fused prologue (%s shape)" % w.name)
     d = {k: (None if v is None else v.cuda()) for k, v in
          W.make_prologue(w.B, w.T, w.H, w.dk, w.dv, w.dtype, w.mode, seed=w.seed + 200,
                          s0_std=w.s0_std).items()}
+    p = {k: (None if v is None else v.cuda()) for k, v in W.make_prefill(w).items()}
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=w.dtype, device="cuda")
+    S = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
+
+    def fused():
+        gdn.chunk_fwd_fused(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], mode=w.mode,
+                            l2norm_qk=True, beta_logits=True, alpha_logits=True, A=d["A"],
+                            dt_bias=d["dt_bias"], o=o, S_final=S)
+
+    def plain():
+        gdn.chunk_fwd(p["q"], p["k"], p["v"], p["alpha"], p["beta"], p["S0"], mode=w.mode,
+                      o=o, S_final=S)
+
+    def timed(f):
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f()
+        b0.record()
+        for _ in range(steps):
+            f()
+        b1.record()
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) / steps
+
+    for _ in range(3):
+        fused()
+        plain()
+    torch.cuda.synchronize()
+    tf, tp = [], []
+    for r in range(6):
+        order = (fused, plain) if r % 2 == 0 else (plain, fused)
+        for f in order:
+            (tf if f is fused else tp).append(timed(f))
+    ms, ms_plain = sum(tf) / len(tf), sum(tp) / len(tp)
+    nbytes = prefill_bytes(w) + w.H * 4 * (2 if w.mode == W.MODE_SCALAR else 1 + w.dk)
+    return dict(workload=w.name + "_fused_prologue", launch_us=ms * 1e3,
+                plain_launch_us_same_period=ms_plain * 1e3,
+                tokens_per_s=w.B * w.T / (ms * 1e-3), hbm_gbps=nbytes / (ms * 1e-3) / 1e9,
+                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, algorithmic_bytes=nbytes)
+
+
+def bench_gdn2(w: W.Prefill, steps: int):
+    """Average duration of one ``gdn2_chunk_fwd`` launch (erase and write gates)
+    at the shape and per-channel decay of ``w``."""
+    log("generating Gated DeltaNet-2 inputs (%s shape)" % w.name)
+    d = {k: (None if v is None else v.cuda()) for k, v in W.make_gdn2(w.with_(seed=w.seed + 300)).items()}
     o = torch.empty((w.B, w.T, w.H, w.dv), dtype=w.dtype, device="cuda")
     S = torch.empty((w.B, w.H, w.dv, w.dk), dtype=torch.float32, device="cuda")
 
     def launch():
-        gdn.chunk_fwd_fused(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], mode=w.mode,
-                            l2norm_qk=True, beta_logits=True, alpha_logits=True, A=d["A"],
-                            dt_bias=d["dt_bias"], o=o, S_final=S)
+        gdn.gdn2_chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["erase"], d["write"], d["S0"],
+                           o=o, S_final=S)
 
     for _ in range(3):
         launch()
@@ -238,10 +286,13 @@ def bench_fused(w: W.Prefill, steps: int):
     b1.record()
     torch.cuda.synchronize()
     ms = b0.elapsed_time(b1) / steps
-    nbytes = prefill_bytes(w) + w.H * 4 * (2 if w.mode == W.MODE_SCALAR else 1 + w.dk)
-    return dict(workload=w.name + "_fused_prologue", launch_us=ms * 1e3,
-                tokens_per_s=w.B * w.T / (ms * 1e-3), hbm_gbps=nbytes / (ms * 1e-3) / 1e9,
-                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, algorithmic_bytes=nbytes)
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    tok = w.B * w.T * w.H
+    nbytes = prefill_bytes(w) - tok * 4 + tok * (w.dk + w.dv) * es   # gates instead of beta
+    del d
+    return dict(workload="gdn2_" + w.name, launch_us=ms * 1e3, tokens_per_s=w.B * w.T / (ms * 1e-3),
+                hbm_gbps=nbytes / (ms * 1e-3) / 1e9, hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                algorithmic_bytes=nbytes)
 
 
 def bench_decode(w: W.Decode, reps: int = 3, rotate: int = 1):
@@ -417,6 +468,8 @@ def main():
                     help="skip the packed variable-length prefill workload")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the prefill with the fused per-token prologue")
+    ap.add_argument("--no-gdn2", action="store_true",
+                    help="skip the Gated DeltaNet-2 prefill")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -482,8 +535,13 @@ def main():
     fused = None
     if not args.no_fused and w.mode != W.MODE_NONE:
         fused = bench_fused(w, args.steps)
-        log("fused prologue: %.1f us per launch (plain %.1f us)" % (fused["launch_us"],
-                                                                   kern_ms * 1e3))
+        log("fused prologue: %.1f us per launch (plain call in alternation: %.1f us)" % (
+            fused["launch_us"], fused["plain_launch_us_same_period"]))
+
+    gdn2 = None
+    if not args.no_gdn2:
+        gdn2 = bench_gdn2(W.KDA_BF16_PREFILL, args.steps)
+        log("gated deltanet-2 %s: %.1f us per launch" % (gdn2["workload"], gdn2["launch_us"]))
 
     copy_gbps = device_copy_gbps()   # also the known-size reference for HBM byte counters
     log("device copy %.0f GB/s" % copy_gbps)
@@ -505,7 +563,7 @@ def main():
                            step="chunked prefill + first decode token",
                            state="fp32", parallelism="single GPU"),
                roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode, packed=packed,
-               fused_prologue=fused,
+               fused_prologue=fused, gdn2=gdn2,
                device_copy_gbps=copy_gbps)
     print(json.dumps(out), flush=True)
 

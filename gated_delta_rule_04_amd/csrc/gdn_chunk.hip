@@ -212,6 +212,17 @@ __device__ inline float sumsq16(const u32x4& u) {
   return s;
 }
 
+// 1 / sqrt(|x|^2 + eps) of a row of N elements of the operand dtype in LDS,
+// 16 bytes at a time (one lane per row).
+template <typename E, int N>
+__device__ inline float inv_norm_row(const E* row, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < N * (int)sizeof(E) / 16; ++i)
+    ss += sumsq16<E>(*reinterpret_cast<const u32x4*>(row + i * (16 / (int)sizeof(E))));
+  return __builtin_amdgcn_rsqf(ss + eps);
+}
+
 // log alpha of one gate value of head h (channel c for a per-channel gate): the
 // value itself, or a logit x with log alpha = -A[h] softplus(x + dt_bias)
 // (a Mamba2-style decay); floored at kLogFloor.
@@ -470,23 +481,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
       tile_nt_k<DK / 16>(acca, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
   }
   if constexpr (NORM) {
-    // the diagonals of the K K^T tiles (0,0) and (1,1) are |k_r|^2
-    if (wave == 0 || wave == 2) {
-      const int r = rb * 32 + col;
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (acc_row(v >> 2, v & 3, lane) == col) Nk[r] = rsqrtf(acca[v] + a.pro.norm_eps);
-    }
-    if constexpr (WP) {   // |q_r|^2, four threads per row
-      const int r = tid >> 2, qd = tid & 3;
-      float ss = 0.f;
-#pragma unroll
-      for (int c = 0; c < DK / 4; c += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(Qr + r * LDK + qd * (DK / 4) + c);
-        ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
-      }
-      ss = quad_sum(ss);
-      if (qd == 0) Nq[r] = rsqrtf(ss + a.pro.norm_eps);
+    // wave 3, idle during the tile products: inverse norms, lane r takes row r
+    if (wave == 3) {
+      Nk[lane] = inv_norm_row<E, DK>(Kr + lane * LDK, a.pro.norm_eps);
+      if constexpr (WP) Nq[lane] = inv_norm_row<E, DK>(Qr + lane * LDK, a.pro.norm_eps);
     }
   }
   __syncthreads();   // K and Q are dead: A takes their bytes
@@ -1667,14 +1665,6 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         *reinterpret_cast<u32x4*>(Vr + r * LDV + cc * EPC) = G2 ? mul16<E>(pv[m], pw[m]) : pv[m];
       }
       if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * GS + 4 * ptid) = pg;
-      if constexpr (NORM) {   // inverse norms of the Q rows: a row's CPR pieces sit in CPR lanes
-#pragma unroll
-        for (int m = 0; m < KPT; ++m) {
-          const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
-          const float nq = rsqrtf(lane_group_sum<CPR>(sumsq16<E>(pq[m])) + a.pro.norm_eps);
-          if (cc == 0) Gbuf[gb * GS + 5 * C + r] = nq;
-        }
-      }
     };
     // T (and the per-channel P) of a chunk.
     auto commit_tp = [&]() __attribute__((always_inline)) {
@@ -1696,7 +1686,13 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     // the weight of a masked entry may overflow).
     auto form_p = [&](int gb) __attribute__((always_inline)) {
       const int d = wave - 4;
-      if (d >= 3) return;
+      if (d >= 3) {
+        // normalised q: the fourth data wave takes the inverse norms of the
+        // chunk's Q rows meanwhile (lane r reads row r), for the chain's output
+        if constexpr (NORM)
+          Gbuf[gb * GS + 5 * C + lane] = inv_norm_row<E, DK>(Qrb + gb * C * LDK + lane * LDK, a.pro.norm_eps);
+        return;
+      }
       const int jb = d == 2 ? 1 : 0, rb = d == 0 ? 0 : 1;
       f32x16 acc = zero16();
       tile_nt_k<DK / 16, E, true, kFormPAhead>(acc, Ksb + gb * C * LDKS + jb * 32 * LDKS, LDKS,
