@@ -226,11 +226,10 @@ __device__ inline float inv_norm_row(const E* row, float eps) {
 // log alpha of one gate value of head h (channel c for a per-channel gate): the
 // value itself, or a logit x with log alpha = -A[h] softplus(x + dt_bias)
 // (a Mamba2-style decay); floored at kLogFloor.
-template <bool FASTLOG>
 __device__ inline float log_alpha(const Prologue& p, float x, int h, int bias_index) {
   const float la = p.alpha_logits
                        ? -p.A[h] * softplus_f(x + (p.dt_bias ? p.dt_bias[bias_index] : 0.f))
-                       : (FASTLOG ? __logf(x) : logf(x));
+                       : logf(x);
   return fmaxf(la, kLogFloor);
 }
 
@@ -451,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     const size_t tok = (tok0 + min(lane, cn - 1)) * H + h;
     const float al = MODE == 1 ? static_cast<const float*>(a.alpha)[tok] : 1.f;
     const float braw = a.beta[tok];
-    const float la = MODE == 1 ? log_alpha<false>(a.pro, al, h, h) : 0.f;
+    const float la = MODE == 1 ? log_alpha(a.pro, al, h, h) : 0.f;
     const float bt = a.pro.beta_logits ? sigmoid_f(braw) : braw;
     const float g = chunk_prefix(ok ? la : 0.f);
     const float gC = __shfl(g, C - 1);
@@ -761,10 +760,21 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
       qreg[m] = ld_once(qgl + off);
       if constexpr (G2) breg[m] = ld_once(bgl + off);
     }
+    // (one branch around the loop: with the choice inside, both the logarithm
+    // and the softplus would be formed for every value)
+    if (a.pro.alpha_logits) {
+      const float ah = a.pro.A[h], bc = a.pro.dt_bias ? a.pro.dt_bias[h * DK + c] : 0.f;
 #pragma unroll
-    for (int i = 0; i < RPS; ++i) {
-      const float la = log_alpha<true>(a.pro, g[i], h, h * DK + c);
-      g[i] = s * RPS + i < cn ? la : 0.f;
+      for (int i = 0; i < RPS; ++i) {
+        const float la = fmaxf(-ah * softplus_f(g[i] + bc), kLogFloor);
+        g[i] = s * RPS + i < cn ? la : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPS; ++i) {
+        const float la = fmaxf(__logf(g[i]), kLogFloor);
+        g[i] = s * RPS + i < cn ? la : 0.f;
+      }
     }
 #pragma unroll
     for (int i = 1; i < RPS; ++i) g[i] += g[i - 1];
