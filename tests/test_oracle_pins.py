@@ -712,3 +712,45 @@ def test_prologue_feeds_the_loop():
                      beta_logits=True)
     kn = k[0, -1, 0] / np.linalg.norm(k[0, -1, 0])
     assert np.max(np.abs(S[0, 0] @ kn - v[0, -1, 0])) < 1e-12
+
+
+# ----------------------------------------------------------------------------------
+# reference gradients (oracle/backward.py) against finite differences of the C loop
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", MODES)
+def test_backward_matches_finite_differences(mode):
+    """Every entry of dq, dk, dv, dalpha, dbeta and dS0 equals the central
+    difference of L = sum(do * o) + sum(dS_T * S_T) computed with the C loop
+    (step 1e-6, fp64): the reverse-mode gradients are pinned to the pinned
+    forward, not to a retyped copy of it."""
+    from oracle import backward
+    rng = np.random.default_rng(300 + mode)
+    B, T, H, dk, dv = 1, 5, 2, 3, 2
+    q, k, v, alpha, beta, S0 = _inputs(rng, B, T, H, dk, dv, mode, lo=0.3)
+    do = rng.standard_normal((B, T, H, dv))
+    dST = rng.standard_normal((B, H, dv, dk))
+    g = backward.gdn_bwd(q, k, v, alpha, beta, S0, do, dST, mode=mode)
+
+    def loss(**kw):
+        args = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
+        args.update(kw)
+        o, S = oracle.gdn_fwd(args["q"], args["k"], args["v"], args["alpha"], args["beta"],
+                              args["S0"], mode=mode)
+        return float(np.sum(o * do) + np.sum(S * dST))
+
+    h = 1e-6
+    names = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("beta", "dbeta"), ("S0", "dS0")]
+    if mode != MODE_NONE:
+        names.append(("alpha", "dalpha"))
+    base = dict(q=q, k=k, v=v, alpha=alpha, beta=beta, S0=S0)
+    for name, gname in names:
+        x = base[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd[idx] = (loss(**{name: xp}) - loss(**{name: xm})) / (2 * h)
+        err = np.max(np.abs(g[gname] - fd)) / max(1.0, np.max(np.abs(fd)))
+        assert err < 1e-7, (name, err)
