@@ -441,9 +441,14 @@ def summarize_pmc(fetch_dir, write_dir, out_json):
                note="FETCH_SIZE / WRITE_SIZE KiB per dispatch, scaled so the 1 GiB device "
                     "copy reads 1 GiB and writes 1 GiB")
     total = 0.0
-    for name in ("chunk_prep", "chunk_state"):   # the two kernels of one gdn_chunk_fwd call
-        fk, nf = kernel_kib(fetch, name)
-        wk, nw = kernel_kib(write, name)
+    # the two kernels of one gdn_chunk_fwd call on the bf16 d_k = 128 scalar-decay
+    # workload (mangled names: bf16, d_k 128, scalar decay, no normalisation; the
+    # state kernel with 64-row value slices)
+    kernels = (("chunk_prep", "chunk_prep_kernelIDF16bLi128ELi1ELb0E"),
+               ("chunk_state", "chunk_state_wsIDF16bLi128ELi64ELi1ELb0E"))
+    for name, mangled in kernels:
+        fk, nf = kernel_kib(fetch, mangled)
+        wk, nw = kernel_kib(write, mangled)
         rec[name] = dict(fetch_kib=fk, write_kib=wk, dispatches=[nf, nw],
                          hbm_read_bytes=fk * 1024 * fs, hbm_write_bytes=wk * 1024 * ws)
         total += fk * 1024 * fs + wk * 1024 * ws

@@ -22,7 +22,7 @@ import threading
 import torch
 
 __all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_fused", "decode_step", "decode_step_fused",
-           "gdn2_chunk_fwd", "gdn2_decode_step", "load", "lib_path", "GDNError",
+           "gdn2_chunk_fwd", "gdn2_decode_step", "chunk_bwd", "load", "lib_path", "GDNError",
            "DECAY_NONE", "DECAY_SCALAR", "DECAY_CHANNEL", "EXPORTED_SYMBOLS"]
 
 DECAY_NONE, DECAY_SCALAR, DECAY_CHANNEL = 0, 1, 2
@@ -31,7 +31,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so"
 EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
                     "gdn_chunk_fwd_varlen_workspace_bytes", "gdn_chunk_fwd_varlen",
                     "gdn_chunk_fwd_fused", "gdn_decode_step", "gdn_decode_step_fused",
-                    "gdn2_chunk_fwd", "gdn2_decode_step", "gdn_status_string", "gdn_version")
+                    "gdn2_chunk_fwd", "gdn2_decode_step", "gdn_chunk_bwd_workspace_bytes",
+                    "gdn_chunk_bwd", "gdn_status_string", "gdn_version")
 
 
 class Prologue(ctypes.Structure):
@@ -83,6 +84,10 @@ def load():
         lib.gdn2_chunk_fwd.restype = i
         lib.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
         lib.gdn2_decode_step.restype = i
+        lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i] * 8
+        lib.gdn_chunk_bwd_workspace_bytes.restype = sz
+        lib.gdn_chunk_bwd.argtypes = [vp] * 14 + [vp, sz] + [i] * 8 + [vp]
+        lib.gdn_chunk_bwd.restype = i
         lib.gdn_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.gdn_decode_step.restype = i
         lib.gdn_status_string.argtypes = [i]
@@ -395,3 +400,42 @@ def gdn2_decode_step(q, k, v, alpha, erase, write, S, *, o=None, stream=None):
                               _ptr(S), _ptr(o), B, H, dk, dv, _DTYPES[dtype], _stream(stream))
     _check(st)
     return o
+
+
+def chunk_bwd(q, k, v, alpha, beta, S0, dout, dS_final=None, *, mode=None, chunk=64,
+              need_dS0=True, stream=None):
+    """Gradients of L = sum(dout * o) + sum(dS_final * S_T) through ``gdn_chunk_bwd``.
+
+    Inputs as :func:`chunk_fwd`; dout [B, T, H, dv] in q's dtype; dS_final fp32
+    [B, H, dv, dk] or None.  Returns a dict: dq, dk, dv (q's dtype), dalpha (fp32,
+    alpha's shape; None without decay), dbeta (fp32), dS0 (fp32, or None when
+    ``need_dS0`` is False)."""
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _require(t, n, dtype)
+    _require(beta, "beta", torch.float32)
+    _require(S0, "S0", torch.float32)
+    _require(dS_final, "dS_final", torch.float32)
+    if mode == DECAY_SCALAR:
+        _require(alpha, "alpha", torch.float32)
+    elif mode == DECAY_CHANNEL:
+        _require(alpha, "alpha", dtype)
+    dev = q.device
+    dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dalpha = None if mode == DECAY_NONE else torch.empty(alpha.shape, dtype=torch.float32, device=dev)
+    dbeta = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dS0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev) if need_dS0 else None
+    ws_bytes = int(lib.gdn_chunk_bwd_workspace_bytes(B, T, H, dk, dv, chunk, _DTYPES[dtype], mode))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None), _ptr(beta),
+                           _ptr(S0), _ptr(dout), _ptr(dS_final), _ptr(dq), _ptr(dk_), _ptr(dv_),
+                           _ptr(dalpha), _ptr(dbeta), _ptr(dS0), _ptr(ws), ws_bytes,
+                           B, T, H, dk, dv, chunk, _DTYPES[dtype], mode, _stream(stream))
+    _check(st)
+    return dict(dq=dq, dk=dk_, dv=dv_, dalpha=dalpha, dbeta=dbeta, dS0=dS0)

@@ -6,6 +6,7 @@
 
 #include <cmath>
 
+#include "gdn_backward.h"
 #include "gdn_internal.h"
 
 namespace {
@@ -300,6 +301,74 @@ gdn_status gdn2_decode_step(const void* q, const void* k, const void* v, const v
                             int H, int dk, int dv, gdn_dtype dtype, hipStream_t stream) {
   return decode(q, k, v, alpha, nullptr, S, o, nullptr, B, H, dk, dv, dtype, GDN_DECAY_CHANNEL,
                 stream, erase, write, true);
+}
+
+size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                     gdn_dtype dtype, gdn_decay mode) {
+  if (check_common(B, H, dk, dv, dtype, mode) != GDN_OK || T < 0 || chunk != kChunk) return 0;
+  long long n;
+  if (!count4(B, T, H, dk, &n) || !count4(B, H, dv, dk, &n)) return 0;
+  return gdn::backward_workspace_bytes(B, T, H, dk, dv, (int)mode);
+}
+
+gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha,
+                         const float* beta, const float* S0, const void* dout,
+                         const float* dS_final, void* dq, void* dk, void* dv, float* dalpha,
+                         float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
+                         int B, int T, int H, int dk_, int dv_, int chunk, gdn_dtype dtype,
+                         gdn_decay mode, hipStream_t stream) {
+  gdn_status st = check_common(B, H, dk_, dv_, dtype, mode);
+  if (st != GDN_OK) return st;
+  if (T < 0) return GDN_ERR_SHAPE;
+  if (chunk != kChunk) return GDN_ERR_UNSUPPORTED;
+  long long nqk, nv, ntok, nS;
+  if (!count4(B, T, H, dk_, &nqk) || !count4(B, T, H, dv_, &nv) || !count4(B, T, H, 1, &ntok) ||
+      !count4(B, H, dv_, dk_, &nS))
+    return GDN_ERR_SHAPE;
+  if ((long long)B * H * (dv_ / 32) > 0x7fffffffLL || nqk / 4 / 256 > 0x7fffffffLL)
+    return GDN_ERR_SHAPE;
+  const size_t ws_need = gdn_chunk_bwd_workspace_bytes(B, T, H, dk_, dv_, chunk, dtype, mode);
+  if (workspace_bytes < ws_need) return GDN_ERR_WORKSPACE;
+  if (B == 0 || H == 0) return GDN_OK;
+  if (ws_need > 0 && !workspace) return GDN_ERR_NULL;
+  const bool has_tokens = T > 0;
+  if (has_tokens) {
+    if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta) return GDN_ERR_NULL;
+    if (mode != GDN_DECAY_NONE && (!alpha || !dalpha)) return GDN_ERR_NULL;
+  }
+  if (!has_tokens && !dS0) return GDN_OK;   // nothing to write
+
+  const size_t es = elem_size(dtype);
+  const size_t a_bytes = mode == GDN_DECAY_SCALAR ? (size_t)ntok * 4
+                         : mode == GDN_DECAY_CHANNEL ? (size_t)nqk * es : 0;
+  const size_t da_bytes = mode == GDN_DECAY_SCALAR ? (size_t)ntok * 4
+                          : mode == GDN_DECAY_CHANNEL ? (size_t)nqk * 4 : 0;
+  const bool t = has_tokens;
+  const Range ins[] = {range_of(t ? q : nullptr, (size_t)nqk * es),
+                       range_of(t ? k : nullptr, (size_t)nqk * es),
+                       range_of(t ? v : nullptr, (size_t)nv * es),
+                       range_of(t && mode != GDN_DECAY_NONE ? alpha : nullptr, a_bytes),
+                       range_of(t ? beta : nullptr, (size_t)ntok * 4),
+                       range_of(S0, (size_t)nS * 4),
+                       range_of(t ? dout : nullptr, (size_t)nv * es),
+                       range_of(dS_final, (size_t)nS * 4)};
+  const Range outs[] = {range_of(t ? dq : nullptr, (size_t)nqk * es),
+                        range_of(t ? dk : nullptr, (size_t)nqk * es),
+                        range_of(t ? dv : nullptr, (size_t)nv * es),
+                        range_of(t && mode != GDN_DECAY_NONE ? (void*)dalpha : nullptr, da_bytes),
+                        range_of(t ? (void*)dbeta : nullptr, (size_t)ntok * 4),
+                        range_of(dS0, (size_t)nS * 4),
+                        range_of(ws_need > 0 ? workspace : nullptr, ws_need)};
+  for (const Range& o : outs) {
+    for (const Range& in : ins)
+      if (overlaps(o, in)) return GDN_ERR_ALIAS;
+    for (const Range& o2 : outs)
+      if (&o2 != &o && overlaps(o, o2)) return GDN_ERR_ALIAS;
+  }
+
+  gdn::BackwardArgs a{q, k, v, alpha, beta, S0, dout, dS_final, dq, dk, dv, dalpha, dbeta, dS0,
+                      B, T, H, dk_, dv_, (int)dtype, (int)mode};
+  return gdn::launch_backward(a, workspace, stream) == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 }  // extern "C"

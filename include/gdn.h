@@ -282,6 +282,42 @@ gdn_status gdn2_decode_step(const void* q, const void* k, const void* v, const v
                             const void* erase, const void* write, float* S, void* o,
                             int B, int H, int dk, int dv, gdn_dtype dtype, hipStream_t stream);
 
+/*
+ * Bytes of device workspace gdn_chunk_bwd needs (0: the pointer may be NULL):
+ * the chunk-start states (d_v x d_k fp32 per 64 tokens of every head) and one
+ * partial of the row sums per 32-row value slice.  0 for rejected arguments.
+ */
+size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                     gdn_dtype dtype, gdn_decay mode);
+
+/*
+ * Backward of gdn_chunk_fwd: the gradients of
+ *     L = sum(dout * o) + sum(dS_final * S_T)
+ * with respect to every input (the pages' KDA training keeps a custom
+ * first-order backward: NextTransformer "method sources" page, KDA entry).
+ *
+ *   q, k, v, alpha, beta, S0   as given to gdn_chunk_fwd (S0 may be NULL)
+ *   dout      [B, T, H, dv] `dtype`: dL/do
+ *   dS_final  fp32 [B, H, dv, dk] or NULL (zeros): dL/dS_T
+ *   dq, dk    [B, T, H, dk] `dtype`, written
+ *   dv        [B, T, H, dv] `dtype`, written
+ *   dalpha    fp32 in alpha's shape ([B, T, H] or [B, T, H, dk]), written;
+ *             ignored for GDN_DECAY_NONE
+ *   dbeta     fp32 [B, T, H], written
+ *   dS0       fp32 [B, H, dv, dk], written (also when S0 is NULL: the
+ *             gradient at the zero state); may be NULL
+ *   workspace gdn_chunk_bwd_workspace_bytes(...) bytes
+ * No output may alias an input, another output or the workspace.  The
+ * computation is deterministic (no atomics).  Gradients are accumulated in
+ * fp32 and rounded once to `dtype`.  Errors as for gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha,
+                         const float* beta, const float* S0, const void* dout,
+                         const float* dS_final, void* dq, void* dk, void* dv, float* dalpha,
+                         float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
+                         int B, int T, int H, int dk_, int dv_, int chunk, gdn_dtype dtype,
+                         gdn_decay mode, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(gdn_status s);
 

@@ -49,6 +49,10 @@ def lib():
     lib.gdn2_chunk_fwd.restype = i
     lib.gdn2_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
     lib.gdn2_decode_step.restype = i
+    lib.gdn_chunk_bwd.argtypes = [vp] * 14 + [vp, sz] + [i] * 8 + [vp]
+    lib.gdn_chunk_bwd.restype = i
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i] * 8
+    lib.gdn_chunk_bwd_workspace_bytes.restype = sz
     return lib
 
 
@@ -307,3 +311,27 @@ def test_gdn2_validation(lib):
     assert dec(ptrs=(q, k, v, a, e, w, s0, e)) == E_ALIAS           # o over the erase gate
     assert dec(ptrs=(q, k, v, a, e, s0 + 8, s0, o)) == E_ALIAS      # write gate inside S
     assert dec(B=0) == OK
+
+
+def test_backward_validation(lib):
+    base = 1 << 40
+    p = [base + i * (1 << 36) for i in range(16)]
+    q, k, v, a, b, s0, do, dst, dq, dk, dv, da, db, ds0, ws = p[:15]
+
+    def bwd(ptrs=None, B=2, T=100, H=3, dk_=128, dv_=128, mode=1, ws_bytes=1 << 34, w=ws):
+        args = ptrs if ptrs is not None else (q, k, v, a, b, s0, do, dst, dq, dk, dv, da, db, ds0)
+        return lib.gdn_chunk_bwd(*args, w, ws_bytes, B, T, H, dk_, dv_, 64, 1, mode, None)
+
+    assert bwd(dk_=96) == E_UNSUP
+    assert bwd(T=-1) == E_SHAPE
+    assert bwd(mode=4) == E_DTYPE
+    assert bwd(ptrs=(q, k, v, a, b, s0, 0, dst, dq, dk, dv, da, db, ds0)) == E_NULL    # no dout
+    assert bwd(ptrs=(q, k, v, a, b, s0, do, dst, dq, dk, dv, 0, db, ds0)) == E_NULL    # no dalpha
+    assert bwd(ptrs=(q, k, v, a, b, s0, do, dst, q, dk, dv, da, db, ds0)) == E_ALIAS   # dq over q
+    assert bwd(ptrs=(q, k, v, a, b, s0, do, dst, dq, dq + 64, dv, da, db, ds0)) == E_ALIAS   # dk in dq
+    assert bwd(w=dq + 128) == E_ALIAS                                                 # ws in dq
+    need = lib.gdn_chunk_bwd_workspace_bytes(2, 100, 3, 128, 128, 64, 1, 1)
+    chunks, nth = 2, 2 * 100 * 3
+    assert need == 2 * 3 * chunks * 128 * 128 * 4 + 2 * 4 * nth * 128 * 4 + 2 * 4 * nth * 4
+    assert bwd(ws_bytes=need - 1) == E_WS
+    assert bwd(B=0) == OK
