@@ -16,7 +16,7 @@ rows of 593 to 5858 tokens) is timed alongside (``packed``), and so is the
 prefill with the per-token prologue fused in (``fused_prologue``: raw q and k
 normalised in the kernels, beta and alpha from logits), and Gated DeltaNet-2
 (``gdn2``: erase and write gates, per-channel decay) at the B=4, H=16, T=8192
-shape.
+shape, and the prefill backward (``backward``: all input gradients).
 
 Printed: one JSON line (the contract below), preceded by progress lines on
 stderr.  Peaks are MI355X's published figures: HBM 8 TB/s, dense bf16 MFMA
@@ -295,6 +295,38 @@ def bench_gdn2(w: W.Prefill, steps: int):
                 algorithmic_bytes=nbytes)
 
 
+def bench_backward(w: W.Prefill, steps: int):
+    """Average duration of one ``gdn_chunk_bwd`` launch on the workload's inputs
+    with a random output gradient (and final-state gradient)."""
+    log("backward inputs (%s)" % w.name)
+    d = {k: (None if v is None else v.cuda()) for k, v in W.make_prefill(w).items()}
+    g = torch.Generator().manual_seed(w.seed + 400)
+    do = torch.randn(w.B, w.T, w.H, w.dv, generator=g).to(w.dtype).cuda()
+    dST = torch.randn(w.B, w.H, w.dv, w.dk, generator=g).cuda()
+
+    def launch():
+        gdn.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], do, dST, mode=w.mode)
+
+    launch()
+    torch.cuda.synchronize()
+    n = max(2, steps // 4)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    launch()
+    b0.record()
+    for _ in range(n):
+        launch()
+    b1.record()
+    torch.cuda.synchronize()
+    ms = b0.elapsed_time(b1) / n
+    es = 2 if w.dtype == torch.bfloat16 else 4
+    tok = w.B * w.T * w.H
+    state = w.B * w.H * w.dv * w.dk * 4
+    nbytes = 2 * prefill_bytes(w) + tok * w.dv * es + state   # inputs + dout, dS_final; the same again out
+    return dict(workload=w.name + "_backward", launch_us=ms * 1e3, launches=n,
+                tokens_per_s=w.B * w.T / (ms * 1e-3), hbm_gbps=nbytes / (ms * 1e-3) / 1e9,
+                hbm_frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, algorithmic_bytes=nbytes)
+
+
 def bench_decode(w: W.Decode, reps: int = 3, rotate: int = 1):
     """``w.steps`` decode steps captured in one HIP graph; per-step time from
     the median replay.  ``rotate`` > 1 cycles the steps over that many state
@@ -475,6 +507,7 @@ def main():
                     help="skip the prefill with the fused per-token prologue")
     ap.add_argument("--no-gdn2", action="store_true",
                     help="skip the Gated DeltaNet-2 prefill")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
@@ -548,6 +581,11 @@ def main():
         gdn2 = bench_gdn2(W.KDA_BF16_PREFILL, args.steps)
         log("gated deltanet-2 %s: %.1f us per launch" % (gdn2["workload"], gdn2["launch_us"]))
 
+    bwd = None
+    if not args.no_backward:
+        bwd = bench_backward(w, args.steps)
+        log("backward: %.1f us per launch" % bwd["launch_us"])
+
     copy_gbps = device_copy_gbps()   # also the known-size reference for HBM byte counters
     log("device copy %.0f GB/s" % copy_gbps)
 
@@ -568,7 +606,7 @@ def main():
                            step="chunked prefill + first decode token",
                            state="fp32", parallelism="single GPU"),
                roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode, packed=packed,
-               fused_prologue=fused, gdn2=gdn2,
+               fused_prologue=fused, gdn2=gdn2, backward=bwd,
                device_copy_gbps=copy_gbps)
     print(json.dumps(out), flush=True)
 

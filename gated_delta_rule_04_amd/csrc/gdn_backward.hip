@@ -18,23 +18,26 @@
 //   dS_{t-1,i} = dS~_i D_t
 //
 // Three kernels:
-//   bwd_checkpoint  the forward token loop from S0, storing S at the start of
-//                   every chunk of 64 tokens (one workgroup per (b, h, 32-row
-//                   value slice); rows are independent: "On State Reduction"
-//                   notes, section 2.5)
-//   bwd_reverse     chunks in reverse order: the chunk's K, V, dO and gates are
-//                   staged in LDS, each 8-token block's states are recomputed
-//                   into registers from the chunk's checkpoint, then the
-//                   reverse steps run over the block.  dv and dS0 are complete
+//   bwd_checkpoint  the forward token loop from S0, storing S every 16 tokens
+//                   (one workgroup per (b, h, 32-row value slice); rows are
+//                   independent: "On State Reduction" notes, section 2.5)
+//   bwd_reverse     chunks of 64 tokens in reverse order: the chunk's K, V, dO
+//                   and gates are staged in LDS, each 8-token block's states
+//                   are recomputed into registers from the checkpoint at most
+//                   8 tokens before it, then the reverse steps run over the
+//                   block.  dv and dS0 are complete
 //                   per slice; the sums over rows (dq, dk, per-channel dalpha,
 //                   dbeta, scalar dalpha) are complete per slice and go to a
 //                   workspace, one partial per value slice
 //   bwd_reduce      adds the slices' partials in a fixed order (deterministic,
 //                   no atomics) and writes dq, dk, dalpha, dbeta.
-// Layout of the work inside a workgroup: 8 lanes per state row (lane l owns the
-// columns 4 l + 32 j .. + 3), 8 rows per wave, 32 rows per workgroup; dot
-// products over a row are DPP sums over its 8 lanes, sums over rows are lane
-// shuffles within a wave and LDS across the four waves.
+// Layout of the work inside a workgroup: 8 rows per wave, 32 rows per
+// workgroup, 8 lanes per state row; lane 8 c + r of a wave holds row r of the
+// wave and the columns 4 c + 32 j .. + 3.  The sums over rows (three per token,
+// 4 d_k / 32 values each) are then DPP sums over 8 adjacent lanes, and only
+// the dot products over a row (two or three per token) need lane shuffles;
+// across the four waves the sums go through LDS.  (Measured: 22 ms against
+// 25 ms with 8 adjacent lanes per row, at B=8, H=16, T=4096, d=128.)
 #include <stdint.h>
 
 #include "gdn_backward.h"
@@ -42,8 +45,10 @@
 namespace gdn {
 namespace {
 
-constexpr int C = 64;                  // tokens between state checkpoints
+constexpr int C = 64;                  // tokens staged in LDS at a time
+constexpr int CK = 16;                 // tokens between state checkpoints
 constexpr int SUB = 8;                 // tokens whose states are held in registers at a time
+static_assert(C % CK == 0 && CK % SUB == 0, "checkpoints at block boundaries");
 constexpr int kThreads = 256;
 constexpr int LPR = 8;                 // lanes per state row
 constexpr int DVS = kThreads / LPR;    // state rows per workgroup
@@ -53,19 +58,20 @@ __device__ inline float to_f32(__bf16 x) { return (float)x; }
 __device__ inline void from_f32(float* p, float x) { *p = x; }
 __device__ inline void from_f32(__bf16* p, float x) { *p = (__bf16)x; }
 
-// Sum over the 8 lanes of a row (aligned groups of 8), result in all of them.
+// Sum over the 8 lanes of a row (lanes 8 apart), result in all of them: lanes
+// 8 apart inside a 16-lane DPP row (row_ror:8), then across the DPP rows.
 __device__ inline float row_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
   return x;
 }
 
-// Sum over the 8 rows of a wave (lanes 8 apart), result in all of them.
+// Sum over the 8 rows of a wave (aligned groups of 8 lanes), result in all of them.
 __device__ inline float rows_sum(float x) {
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
   return x;
 }
 
@@ -102,7 +108,7 @@ struct BwdLds {
 };
 
 // Where a workgroup works: head (b, h), value rows i0 .. i0 + 31, and the
-// thread's row g and lane l8 inside them.
+// thread's row g inside them and its column group l8 (columns 4 l8 + 32 j).
 struct Place {
   int b, h, sl, i0, g, l8, wave, lane;
 };
@@ -114,10 +120,10 @@ __device__ inline Place place(const BackwardArgs& a) {
   p.h = bh % a.H;
   p.b = bh / a.H;
   p.i0 = p.sl * DVS;
-  p.g = threadIdx.x / LPR;
-  p.l8 = threadIdx.x % LPR;
   p.wave = threadIdx.x >> 6;
   p.lane = threadIdx.x & 63;
+  p.g = p.wave * 8 + (p.lane & 7);
+  p.l8 = p.lane >> 3;
   return p;
 }
 
@@ -185,16 +191,20 @@ __global__ __launch_bounds__(kThreads) void bwd_checkpoint(BackwardArgs a, float
   for (int j = 0; j < NQ; ++j)
     S[j] = a.S0 ? *reinterpret_cast<const float4*>(a.S0 + row * DK + 4 * P.l8 + 32 * j)
                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  const int nck = (a.T + CK - 1) / CK;
   for (int n = 0; n < nch; ++n) {
     const int t0 = n * C, cn = min(C, a.T - t0);
-    // checkpoint n: the state before the chunk, [B, H][chunk][dv][dk]
-    float* cp = ck + ((((size_t)P.b * a.H + P.h) * nch + n) * a.dv_ + P.i0 + P.g) * DK;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) *reinterpret_cast<float4*>(cp + 4 * P.l8 + 32 * j) = S[j];
     __syncthreads();
     stage_chunk<E, DK, MODE, false>(a, P, t0, cn, kst, ast, vst, nullptr, gst);
     __syncthreads();
-    for (int r = 0; r < cn; ++r) fstep<DK, MODE>(S, r, P.g, P.l8, kst, ast, vst, gst);
+    for (int r = 0; r < cn; ++r) {
+      if ((r & (CK - 1)) == 0) {   // checkpoint: the state before token t0 + r, [B, H][t / CK][dv][dk]
+        float* cp = ck + ((((size_t)P.b * a.H + P.h) * nck + (t0 + r) / CK) * a.dv_ + P.i0 + P.g) * DK;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) *reinterpret_cast<float4*>(cp + 4 * P.l8 + 32 * j) = S[j];
+      }
+      fstep<DK, MODE>(S, r, P.g, P.l8, kst, ast, vst, gst);
+    }
   }
 }
 
@@ -217,6 +227,7 @@ __global__ __launch_bounds__(kThreads) void bwd_reverse(BackwardArgs a, const fl
   const Place P = place(a);
   const int nsl = a.dv_ / DVS;
   const int nch = (a.T + C - 1) / C;
+  const int nck = (a.T + CK - 1) / CK;
   const size_t NTH = (size_t)a.B * a.T * a.H;   // token-heads
   const size_t row = ((size_t)P.b * a.H + P.h) * a.dv_ + P.i0 + P.g;
   float4 dS[NQ];
@@ -231,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void bwd_reverse(BackwardArgs a, const fl
     x.y = rows_sum(x.y);
     x.z = rows_sum(x.z);
     x.w = rows_sum(x.w);
-    if (P.lane < LPR) *reinterpret_cast<float4*>(dstp) = x;
+    if ((P.lane & 7) == 0) *reinterpret_cast<float4*>(dstp) = x;
   };
 
   // One reverse token step: Sp is the state before token r (chunk row r), jb
@@ -288,13 +299,16 @@ __global__ __launch_bounds__(kThreads) void bwd_reverse(BackwardArgs a, const fl
     const int t0 = n * C, cn = min(C, a.T - t0);
     __syncthreads();   // the previous chunk's readers are done with LDS
     stage_chunk<E, DK, MODE, true>(a, P, t0, cn, kst, ast, vst, dst, gst);
-    float4 Sc[NQ];
-    const float* cp = ck + ((((size_t)P.b * a.H + P.h) * nch + n) * a.dv_ + P.i0 + P.g) * DK;
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) Sc[j] = *reinterpret_cast<const float4*>(cp + 4 * P.l8 + 32 * j);
     const int nsub = (cn + SUB - 1) / SUB;
     for (int sb = nsub - 1; sb >= 0; --sb) {
       const int r0 = sb * SUB, nv = min(SUB, cn - r0);
+      const int rs = r0 & ~(CK - 1);   // the checkpoint at or before the block
+      float4 Sc[NQ];
+      {
+        const float* cp = ck + ((((size_t)P.b * a.H + P.h) * nck + (t0 + rs) / CK) * a.dv_ + P.i0 + P.g) * DK;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) Sc[j] = *reinterpret_cast<const float4*>(cp + 4 * P.l8 + 32 * j);
+      }
       {   // the block's Q rows
         const size_t tok0 = (size_t)P.b * a.T + t0 + r0;
         for (int idx = threadIdx.x; idx < SUB * DK; idx += kThreads) {
@@ -307,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void bwd_reverse(BackwardArgs a, const fl
       float4 S[NQ];
 #pragma unroll
       for (int j = 0; j < NQ; ++j) S[j] = Sc[j];
-      for (int r = 0; r < r0; ++r) fstep<DK, MODE>(S, r, P.g, P.l8, kst, ast, vst, gst);
+      for (int r = rs; r < r0; ++r) fstep<DK, MODE>(S, r, P.g, P.l8, kst, ast, vst, gst);
       float4 Sp[SUB][NQ];
 #pragma unroll
       for (int jb = 0; jb < SUB; ++jb) {
@@ -390,11 +404,11 @@ struct BwdWs {
   size_t ck, part, spart, total;
 };
 BwdWs bwd_ws(int B, int T, int H, int dk, int dv, int mode) {
-  const size_t nch = ((size_t)T + C - 1) / C, NTH = (size_t)B * T * H, nsl = dv / DVS;
+  const size_t nck = ((size_t)T + CK - 1) / CK, NTH = (size_t)B * T * H, nsl = dv / DVS;
   const size_t ncol = mode == 2 ? 3 : 2;
   BwdWs w;
   w.ck = 0;
-  w.part = w.ck + (size_t)B * H * nch * dv * dk * 4;
+  w.part = w.ck + (size_t)B * H * nck * dv * dk * 4;
   w.spart = w.part + ncol * nsl * NTH * dk * 4;
   w.total = w.spart + 2 * nsl * NTH * 4;
   return w;
