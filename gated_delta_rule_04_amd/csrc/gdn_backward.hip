@@ -18,14 +18,16 @@
 //   dS_{t-1,i} = dS~_i D_t
 //
 // Three kernels:
-//   bwd_checkpoint  the forward token loop from S0, storing S every 16 tokens
+//   bwd_checkpoint  the forward token loop from S0, storing S every 8 tokens
 //                   (one workgroup per (b, h, 32-row value slice); rows are
 //                   independent: "On State Reduction" notes, section 2.5)
 //   bwd_reverse     chunks of 64 tokens in reverse order: the chunk's K, V, dO
-//                   and gates are staged in LDS, each 8-token block's states
+//                   and gates are staged in LDS, each 4-token block's states
 //                   are recomputed into registers from the checkpoint at most
-//                   8 tokens before it, then the reverse steps run over the
-//                   block.  dv and dS0 are complete
+//                   4 tokens before it, then the reverse steps run over the
+//                   block.  (Blocks of 4 and LDS below 80 KB let two
+//                   workgroups share a compute unit and hide each other's
+//                   latency.)  dv and dS0 are complete
 //                   per slice; the sums over rows (dq, dk, per-channel dalpha,
 //                   dbeta, scalar dalpha) are complete per slice and go to a
 //                   workspace, one partial per value slice
@@ -36,8 +38,9 @@
 // wave and the columns 4 c + 32 j .. + 3.  The sums over rows (three per token,
 // 4 d_k / 32 values each) are then DPP sums over 8 adjacent lanes, and only
 // the dot products over a row (two or three per token) need lane shuffles;
-// across the four waves the sums go through LDS.  (Measured: 22 ms against
-// 25 ms with 8 adjacent lanes per row, at B=8, H=16, T=4096, d=128.)
+// across the four waves the sums go through LDS.  (Measured with 8-token
+// blocks: 21 ms against 25 ms with 8 adjacent lanes per row, at B=8, H=16,
+// T=4096, d=128.)
 #include <stdint.h>
 
 #include "gdn_backward.h"
@@ -46,8 +49,8 @@ namespace gdn {
 namespace {
 
 constexpr int C = 64;                  // tokens staged in LDS at a time
-constexpr int CK = 16;                 // tokens between state checkpoints
-constexpr int SUB = 8;                 // tokens whose states are held in registers at a time
+constexpr int CK = 8;                  // tokens between state checkpoints
+constexpr int SUB = 4;                 // tokens whose states are held in registers at a time
 static_assert(C % CK == 0 && CK % SUB == 0, "checkpoints at block boundaries");
 constexpr int kThreads = 256;
 constexpr int LPR = 8;                 // lanes per state row
@@ -75,6 +78,13 @@ __device__ inline float rows_sum(float x) {
   return x;
 }
 
+__device__ inline float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ inline float4 ld4(const __bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 __device__ inline float dot4(const float4& a, const float4& b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
@@ -88,15 +98,18 @@ __device__ inline float4 fma4(float s, const float4& a, const float4& b) {   // 
   return make_float4(s * a.x + b.x, s * a.y + b.y, s * a.z + b.z, s * a.w + b.w);
 }
 
-// LDS of the two sequential kernels (fp32): the chunk's K rows, per-channel
-// gates, V and dO slices, the gate scalars; then (reverse kernel) the block's
-// Q rows, the four waves' partial sums over rows and the block's dv.
-template <int DK, int MODE>
+// LDS of the two sequential kernels: the chunk's K rows and per-channel gates
+// (operand dtype), V and dO slices and the gate scalars (fp32); then (reverse
+// kernel) the block's Q rows, the four waves' partial sums over rows and the
+// block's dv.  Below 80 KB (bf16; fp32 without per-channel gates): two
+// workgroups per compute unit.
+template <typename E, int DK, int MODE>
 struct BwdLds {
   static constexpr int NCOL = MODE == 2 ? 3 : 2;   // dq, dk (, dalpha per channel)
-  static constexpr size_t k = 0;
-  static constexpr size_t a = k + (size_t)C * DK * 4;
-  static constexpr size_t v = a + (MODE == 2 ? (size_t)C * DK * 4 : 0);
+  static constexpr size_t es = sizeof(E);
+  static constexpr size_t k = 0;                   // K and per-channel gates in the operand dtype
+  static constexpr size_t a = k + (size_t)C * DK * es;
+  static constexpr size_t v = a + (MODE == 2 ? (size_t)C * DK * es : 0);
   static constexpr size_t d = v + (size_t)C * DVS * 4;
   static constexpr size_t g = d + (size_t)C * DVS * 4;   // beta [C], scalar alpha [C]
   static constexpr size_t q = g + 2 * C * 4;
@@ -130,15 +143,15 @@ __device__ inline Place place(const BackwardArgs& a) {
 // The chunk's rows into LDS (rows past the sequence end repeat its last row;
 // the loops below never reach them).
 template <typename E, int DK, int MODE, bool WITH_DO>
-__device__ inline void stage_chunk(const BackwardArgs& a, const Place& P, int t0, int cn, float* kst,
-                                   float* ast, float* vst, float* dst, float* gst) {
+__device__ inline void stage_chunk(const BackwardArgs& a, const Place& P, int t0, int cn, E* kst,
+                                   E* ast, float* vst, float* dst, float* gst) {
   const size_t tok0 = (size_t)P.b * a.T + t0;
   const int H = a.H;
   for (int idx = threadIdx.x; idx < C * DK; idx += kThreads) {
     const int r = idx / DK, c = idx % DK;
     const size_t tk = ((tok0 + min(r, cn - 1)) * H + P.h) * DK + c;
-    kst[idx] = to_f32(static_cast<const E*>(a.k)[tk]);
-    if constexpr (MODE == 2) ast[idx] = to_f32(static_cast<const E*>(a.alpha)[tk]);
+    kst[idx] = static_cast<const E*>(a.k)[tk];
+    if constexpr (MODE == 2) ast[idx] = static_cast<const E*>(a.alpha)[tk];
   }
   for (int idx = threadIdx.x; idx < C * DVS; idx += kThreads) {
     const int r = idx / DVS, i = idx % DVS;
@@ -154,17 +167,17 @@ __device__ inline void stage_chunk(const BackwardArgs& a, const Place& P, int t0
 }
 
 // One forward token step on this lane's piece of its row.
-template <int DK, int MODE>
-__device__ inline void fstep(float4 (&S)[DK / 32], int r, int g, int l8, const float* kst,
-                             const float* ast, const float* vst, const float* gst) {
+template <typename E, int DK, int MODE>
+__device__ inline void fstep(float4 (&S)[DK / 32], int r, int g, int l8, const E* kst,
+                             const E* ast, const float* vst, const float* gst) {
   constexpr int NQ = DK / 32;
   float4 kk[NQ];
   float p = 0.f;
   const float as = gst[C + r];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    kk[j] = *reinterpret_cast<const float4*>(kst + r * DK + 4 * l8 + 32 * j);
-    if constexpr (MODE == 2) S[j] = mul4(S[j], *reinterpret_cast<const float4*>(ast + r * DK + 4 * l8 + 32 * j));
+    kk[j] = ld4(kst + r * DK + 4 * l8 + 32 * j);
+    if constexpr (MODE == 2) S[j] = mul4(S[j], ld4(ast + r * DK + 4 * l8 + 32 * j));
     if constexpr (MODE == 1) S[j] = scale4(S[j], as);
     p += dot4(S[j], kk[j]);
   }
@@ -175,12 +188,12 @@ __device__ inline void fstep(float4 (&S)[DK / 32], int r, int g, int l8, const f
 }
 
 template <typename E, int DK, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_checkpoint(BackwardArgs a, float* __restrict__ ck) {
-  using L = BwdLds<DK, MODE>;
+__global__ __launch_bounds__(kThreads, 2) void bwd_checkpoint(BackwardArgs a, float* __restrict__ ck) {
+  using L = BwdLds<E, DK, MODE>;
   constexpr int NQ = DK / 32;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
-  float* kst = reinterpret_cast<float*>(smem + L::k);
-  float* ast = reinterpret_cast<float*>(smem + L::a);
+  E* kst = reinterpret_cast<E*>(smem + L::k);
+  E* ast = reinterpret_cast<E*>(smem + L::a);
   float* vst = reinterpret_cast<float*>(smem + L::v);
   float* gst = reinterpret_cast<float*>(smem + L::g);
   const Place P = place(a);
@@ -203,19 +216,19 @@ __global__ __launch_bounds__(kThreads) void bwd_checkpoint(BackwardArgs a, float
 #pragma unroll
         for (int j = 0; j < NQ; ++j) *reinterpret_cast<float4*>(cp + 4 * P.l8 + 32 * j) = S[j];
       }
-      fstep<DK, MODE>(S, r, P.g, P.l8, kst, ast, vst, gst);
+      fstep<E, DK, MODE>(S, r, P.g, P.l8, kst, ast, vst, gst);
     }
   }
 }
 
 template <typename E, int DK, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_reverse(BackwardArgs a, const float* __restrict__ ck,
+__global__ __launch_bounds__(kThreads, 2) void bwd_reverse(BackwardArgs a, const float* __restrict__ ck,
                                                         float* __restrict__ part, float* __restrict__ spart) {
-  using L = BwdLds<DK, MODE>;
+  using L = BwdLds<E, DK, MODE>;
   constexpr int NQ = DK / 32, NCOL = L::NCOL;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
-  float* kst = reinterpret_cast<float*>(smem + L::k);
-  float* ast = reinterpret_cast<float*>(smem + L::a);
+  E* kst = reinterpret_cast<E*>(smem + L::k);
+  E* ast = reinterpret_cast<E*>(smem + L::a);
   float* vst = reinterpret_cast<float*>(smem + L::v);
   float* dst = reinterpret_cast<float*>(smem + L::d);
   float* gst = reinterpret_cast<float*>(smem + L::g);
@@ -253,10 +266,9 @@ __global__ __launch_bounds__(kThreads) void bwd_reverse(BackwardArgs a, const fl
     float p = 0.f;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      kk[j] = *reinterpret_cast<const float4*>(kst + r * DK + 4 * P.l8 + 32 * j);
+      kk[j] = ld4(kst + r * DK + 4 * P.l8 + 32 * j);
       qq[j] = *reinterpret_cast<const float4*>(qst + jb * DK + 4 * P.l8 + 32 * j);
-      dd[j] = MODE == 2 ? *reinterpret_cast<const float4*>(ast + r * DK + 4 * P.l8 + 32 * j)
-                        : make_float4(as, as, as, as);
+      dd[j] = MODE == 2 ? ld4(ast + r * DK + 4 * P.l8 + 32 * j) : make_float4(as, as, as, as);
       Sd[j] = MODE == 0 ? Sp[j] : mul4(Sp[j], dd[j]);   // S~
       p += dot4(Sd[j], kk[j]);
     }
@@ -321,13 +333,13 @@ __global__ __launch_bounds__(kThreads) void bwd_reverse(BackwardArgs a, const fl
       float4 S[NQ];
 #pragma unroll
       for (int j = 0; j < NQ; ++j) S[j] = Sc[j];
-      for (int r = rs; r < r0; ++r) fstep<DK, MODE>(S, r, P.g, P.l8, kst, ast, vst, gst);
+      for (int r = rs; r < r0; ++r) fstep<E, DK, MODE>(S, r, P.g, P.l8, kst, ast, vst, gst);
       float4 Sp[SUB][NQ];
 #pragma unroll
       for (int jb = 0; jb < SUB; ++jb) {
 #pragma unroll
         for (int j = 0; j < NQ; ++j) Sp[jb][j] = S[j];
-        if (jb < nv) fstep<DK, MODE>(S, r0 + jb, P.g, P.l8, kst, ast, vst, gst);
+        if (jb < nv) fstep<E, DK, MODE>(S, r0 + jb, P.g, P.l8, kst, ast, vst, gst);
       }
 #pragma unroll
       for (int jb = SUB - 1; jb >= 0; --jb)
@@ -365,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void bwd_reverse(BackwardArgs a, const fl
 template <typename E, int DK, int MODE>
 __global__ __launch_bounds__(256) void bwd_reduce(BackwardArgs a, const float* __restrict__ part,
                                                   const float* __restrict__ spart) {
-  constexpr int NCOL = BwdLds<DK, MODE>::NCOL;
+  constexpr int NCOL = BwdLds<E, DK, MODE>::NCOL;
   const int nsl = a.dv_ / DVS;
   const size_t NTH = (size_t)a.B * a.T * a.H;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -284,7 +284,7 @@ gdn_status gdn2_decode_step(const void* q, const void* k, const void* v, const v
 
 /*
  * Bytes of device workspace gdn_chunk_bwd needs (0: the pointer may be NULL):
- * state checkpoints (d_v x d_k fp32 per 16 tokens of every head) and one
+ * state checkpoints (d_v x d_k fp32 per 8 tokens of every head) and one
  * partial of the row sums per 32-row value slice.  0 for rejected arguments.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,

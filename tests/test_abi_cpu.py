@@ -331,7 +331,7 @@ def test_backward_validation(lib):
     assert bwd(ptrs=(q, k, v, a, b, s0, do, dst, dq, dq + 64, dv, da, db, ds0)) == E_ALIAS   # dk in dq
     assert bwd(w=dq + 128) == E_ALIAS                                                 # ws in dq
     need = lib.gdn_chunk_bwd_workspace_bytes(2, 100, 3, 128, 128, 64, 1, 1)
-    chunks, nth = 7, 2 * 100 * 3   # state checkpoints every 16 tokens
+    chunks, nth = 13, 2 * 100 * 3   # state checkpoints every 8 tokens
     assert need == 2 * 3 * chunks * 128 * 128 * 4 + 2 * 4 * nth * 128 * 4 + 2 * 4 * nth * 4
     assert bwd(ws_bytes=need - 1) == E_WS
     assert bwd(B=0) == OK
