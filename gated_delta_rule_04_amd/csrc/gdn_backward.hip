@@ -307,28 +307,40 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_reverse(BackwardArgs a, const
     }
   };
 
+  // The checkpoint and the Q rows of a block, into registers: the next block's
+  // are loaded while the current one is computed.
+  constexpr int QPT = SUB * DK / kThreads;
+  static_assert(SUB * DK % kThreads == 0, "Q rows of a block must split evenly");
+  auto load_block = [&](int t0, int cn, int sb, E (&qv)[QPT], float4 (&sc4)[NQ]) __attribute__((always_inline)) {
+    const int r0 = sb * SUB, nv = min(SUB, cn - r0), rs = r0 & ~(CK - 1);
+    const float* cp = ck + ((((size_t)P.b * a.H + P.h) * nck + (t0 + rs) / CK) * a.dv_ + P.i0 + P.g) * DK;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) sc4[j] = *reinterpret_cast<const float4*>(cp + 4 * P.l8 + 32 * j);
+    const size_t tok0 = (size_t)P.b * a.T + t0 + r0;
+#pragma unroll
+    for (int m = 0; m < QPT; ++m) {
+      const int idx = threadIdx.x + kThreads * m, j = idx / DK, c = idx % DK;
+      qv[m] = static_cast<const E*>(a.q)[((tok0 + min(j, nv - 1)) * a.H + P.h) * DK + c];
+    }
+  };
+
   for (int n = nch - 1; n >= 0; --n) {
     const int t0 = n * C, cn = min(C, a.T - t0);
     __syncthreads();   // the previous chunk's readers are done with LDS
     stage_chunk<E, DK, MODE, true>(a, P, t0, cn, kst, ast, vst, dst, gst);
     const int nsub = (cn + SUB - 1) / SUB;
+    E qv[QPT];
+    float4 Sc[NQ];
+    load_block(t0, cn, nsub - 1, qv, Sc);
     for (int sb = nsub - 1; sb >= 0; --sb) {
       const int r0 = sb * SUB, nv = min(SUB, cn - r0);
       const int rs = r0 & ~(CK - 1);   // the checkpoint at or before the block
-      float4 Sc[NQ];
-      {
-        const float* cp = ck + ((((size_t)P.b * a.H + P.h) * nck + (t0 + rs) / CK) * a.dv_ + P.i0 + P.g) * DK;
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) Sc[j] = *reinterpret_cast<const float4*>(cp + 4 * P.l8 + 32 * j);
-      }
-      {   // the block's Q rows
-        const size_t tok0 = (size_t)P.b * a.T + t0 + r0;
-        for (int idx = threadIdx.x; idx < SUB * DK; idx += kThreads) {
-          const int j = idx / DK, c = idx % DK;
-          qst[idx] = to_f32(static_cast<const E*>(a.q)[((tok0 + min(j, nv - 1)) * a.H + P.h) * DK + c]);
-        }
-      }
+      for (int m = 0; m < QPT; ++m) qst[threadIdx.x + kThreads * m] = to_f32(qv[m]);
       __syncthreads();
+      E qn[QPT];
+      float4 Sn[NQ];
+      load_block(t0, cn, max(sb - 1, 0), qn, Sn);   // the next block's (unconditional: exact waits)
       // states before each token of the block, recomputed from the checkpoint
       float4 S[NQ];
 #pragma unroll
@@ -364,6 +376,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_reverse(BackwardArgs a, const
         const int jb = idx / DVS, i = idx % DVS;
         from_f32(static_cast<E*>(a.dv) + (th0 + (size_t)jb * a.H) * a.dv_ + P.i0 + i, dvb[idx]);
       }
+#pragma unroll
+      for (int m = 0; m < QPT; ++m) qv[m] = qn[m];
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) Sc[j] = Sn[j];
     }
   }
   if (a.dS0) {
