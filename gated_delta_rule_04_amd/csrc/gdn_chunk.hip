@@ -254,8 +254,10 @@ __device__ inline float chunk_prefix(float la) {
 //   Mt  scratch, fp32 [32][ldm]; in place it may be Am + 32 with ldm = LDA
 //       (rows 0..31, columns 32..63 of L^-1 are above the diagonal and never
 //       read)
-//   Tm  T in the operand dtype [C][LDT]; may share Am's bytes unless Li is Am
-// All threads of the workgroup take part; it ends with a barrier.
+//   Tm  T in the operand dtype: LDS [C][LDT] (it may
+//       share Am's bytes unless Li is Am), or (DIRECT) the chunk record in
+//       global memory, [C][C]
+// All threads of the workgroup take part; it ends with a barrier unless DIRECT.
 template <typename E>
 struct SolveLd {
   static constexpr int LDA = C + 4;
@@ -263,10 +265,10 @@ struct SolveLd {
   static constexpr int LDM = 32 + 4;
 };
 
-template <typename E, int LDM = SolveLd<E>::LDM>
+template <typename E, int LDM = SolveLd<E>::LDM, bool DIRECT = false>
 __device__ __attribute__((always_inline)) inline void tri_solve(const float* Am, float* Li, float* Mt,
                                                                 const float* Bt, E* Tm, int tid) {
-  constexpr int LDA = SolveLd<E>::LDA, LDT = SolveLd<E>::LDT;
+  constexpr int LDA = SolveLd<E>::LDA, LDT = DIRECT ? C : SolveLd<E>::LDT;
   const int lane = tid & 63, wave = tid >> 6;
   // (a) inverse of each unit-lower 16x16 diagonal block: wave w owns block w;
   // lane 4c + p computes column c, rows 4p .. 4p + 3, summing its part of each
@@ -357,7 +359,7 @@ __device__ __attribute__((always_inline)) inline void tri_solve(const float* Am,
       store4(Tm + r * LDT + 36 + (tid & 3) * 8, 0.f, 0.f, 0.f, 0.f);
     }
   }
-  __syncthreads();
+  if constexpr (!DIRECT) __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -381,21 +383,21 @@ struct PrepPlan {
   static constexpr size_t es = sizeof(E);
   // bf16 (no Q): A takes the dead K rows' bytes and L^-1 overwrites A in
   // place, the solve's scratch tile sits in L^-1's unused upper-right block,
-  // T has bytes of its own; 27.1 KB, six workgroups per compute unit.
+  // and T goes from the solve straight to the record; 17.9 KB, eight
+  // workgroups per compute unit.
   // fp32: L^-1 over the K rows; Q, then A, then T in a second region.
   static constexpr bool inplace = sizeof(E) == 2;
   static constexpr size_t r1 = cmax((size_t)C * LDK * es, (size_t)C * LDA * 4);
   static constexpr size_t kr = 0;   // K rows, then L^-1
   static constexpr size_t am = inplace ? 0 : r1;
-  static constexpr size_t tm = inplace ? r1 : am;
+  static constexpr size_t tm = inplace ? r1 : am;   // (in place: no T in LDS)
   static constexpr int ldm = inplace ? LDA : LDM;
   static constexpr size_t mt = inplace ? (size_t)32 * 4   // A + 32 floats, leading dimension LDA
                                        : am + cmax((size_t)C * LDK * es, cmax((size_t)C * LDA * 4, (size_t)C * LDT * es));
-  static constexpr size_t g = inplace ? tm + (size_t)C * LDT * es : mt + (size_t)32 * LDM * 4;
-  // inverse norms (K, then Q in fp32): in place they use T's bytes, which the
-  // solve writes only after its last read of them
-  static constexpr size_t nk = inplace ? tm : g + 2 * C * 4;
-  static constexpr size_t total = g + (NORM && !inplace ? 4 : 2) * C * 4;
+  static constexpr size_t g = inplace ? r1 : mt + (size_t)32 * LDM * 4;
+  // inverse norms (K, then Q in fp32)
+  static constexpr size_t nk = g + 2 * C * 4;
+  static constexpr size_t total = g + (NORM ? (inplace ? 3 : 4) : 2) * C * 4;
 };
 
 template <typename E, int DK, int MODE, bool NORM>
@@ -547,9 +549,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   }
   __syncthreads();
 
-  tri_solve<E, L::ldm>(Am, Li, Mt, Bt, Tm, tid);
-  // T -> the record, 64 x 64 contiguous, 16-byte stores
-  {
+  if constexpr (L::inplace) {
+    tri_solve<E, L::ldm, true>(Am, Li, Mt, Bt, rec + R::t, tid);   // T straight to the record
+  } else {
+    tri_solve<E, L::ldm>(Am, Li, Mt, Bt, Tm, tid);
+    // T -> the record, 64 x 64 contiguous, 16-byte stores
     constexpr int CPT = C / EPC;
     static_assert(C * CPT % kThreads == 0, "T must split evenly over the threads");
 #pragma unroll
