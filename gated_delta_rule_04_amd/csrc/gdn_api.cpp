@@ -308,7 +308,7 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
   if (check_common(B, H, dk, dv, dtype, mode) != GDN_OK || T < 0 || chunk != kChunk) return 0;
   long long n;
   if (!count4(B, T, H, dk, &n) || !count4(B, H, dv, dk, &n)) return 0;
-  return gdn::backward_workspace_bytes(B, T, H, dk, dv, (int)mode);
+  return gdn::backward_workspace_bytes(B, T, H, dk, dv, (int)dtype, (int)mode);
 }
 
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha,

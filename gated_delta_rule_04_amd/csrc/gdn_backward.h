@@ -32,7 +32,13 @@ struct BackwardArgs {
   int mode;    // 0 none, 1 scalar, 2 channel
 };
 
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int mode);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, int mode);
 hipError_t launch_backward(const BackwardArgs& a, void* workspace, hipStream_t stream);
+
+// The chunk-level backward (gdn_bwd_chunk.hip): bf16, no or scalar decay,
+// T > 0.  The token-level kernels take every other case.
+bool chunk_backward_applies(int T, int dk, int dv, int dtype, int mode);
+size_t chunk_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+hipError_t launch_chunk_backward(const BackwardArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace gdn

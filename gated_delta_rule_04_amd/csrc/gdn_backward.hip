@@ -468,11 +468,13 @@ hipError_t launch_dk(const BackwardArgs& a, void* ws, hipStream_t stream) {
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int mode) {
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, int mode) {
+  if (chunk_backward_applies(T, dk, dv, dtype, mode)) return chunk_backward_workspace_bytes(B, T, H, dk, dv);
   return bwd_ws(B, T, H, dk, dv, mode).total;
 }
 
 hipError_t launch_backward(const BackwardArgs& a, void* workspace, hipStream_t stream) {
+  if (chunk_backward_applies(a.T, a.dk_, a.dv_, a.dtype, a.mode)) return launch_chunk_backward(a, workspace, stream);
   if (a.dtype == 1)
     return a.dk_ == 128 ? launch_dk<__bf16, 128>(a, workspace, stream) : launch_dk<__bf16, 64>(a, workspace, stream);
   return a.dk_ == 128 ? launch_dk<float, 128>(a, workspace, stream) : launch_dk<float, 64>(a, workspace, stream);

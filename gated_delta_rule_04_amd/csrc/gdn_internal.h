@@ -83,6 +83,13 @@ size_t prefill_varlen_workspace_bytes(int N, int T, int H, int dk, int dtype, in
 int varlen_slots(int N, int T);
 // Enqueue the prefill kernels; returns the launch status.
 hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);
+// Bytes of one chunk record of the prefill workspace.  bf16 with scalar or no
+// decay, unnormalised q and k: T [64][64] bf16 (row-major), then five fp32
+// rows of 64: G_r (the running sum of log alpha inside the chunk, the same
+// past the sequence end), exp(G_r), exp(G_C - G_r), exp(G_r) again and ones.
+size_t prefill_record_bytes(int dk, int dtype, int mode);
+// Enqueue only the first prefill kernel, which writes the chunk records.
+hipError_t launch_prefill_prep(const PrefillArgs& a, void* workspace, hipStream_t stream);
 // Enqueue one decode step; returns the launch status.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

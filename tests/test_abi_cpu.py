@@ -330,8 +330,15 @@ def test_backward_validation(lib):
     assert bwd(ptrs=(q, k, v, a, b, s0, do, dst, q, dk, dv, da, db, ds0)) == E_ALIAS   # dq over q
     assert bwd(ptrs=(q, k, v, a, b, s0, do, dst, dq, dq + 64, dv, da, db, ds0)) == E_ALIAS   # dk in dq
     assert bwd(w=dq + 128) == E_ALIAS                                                 # ws in dq
-    need = lib.gdn_chunk_bwd_workspace_bytes(2, 100, 3, 128, 128, 64, 1, 1)
-    chunks, nth = 13, 2 * 100 * 3   # state checkpoints every 8 tokens
+    # fp32 (and per-channel decay): the token-level kernels, state checkpoints every 8 tokens
+    need = lib.gdn_chunk_bwd_workspace_bytes(2, 100, 3, 128, 128, 64, 0, 1)
+    chunks, nth = 13, 2 * 100 * 3
     assert need == 2 * 3 * chunks * 128 * 128 * 4 + 2 * 4 * nth * 128 * 4 + 2 * 4 * nth * 4
+    # bf16, scalar or no decay: the chunk-level kernels; per chunk of every head the
+    # forward's record (T bf16 + five fp32 gate rows), a bf16 state and a bf16 state gradient
+    nch = 2 * 3 * 2
+    need = lib.gdn_chunk_bwd_workspace_bytes(2, 100, 3, 128, 128, 64, 1, 1)
+    assert need == nch * (64 * 64 * 2 + 5 * 64 * 4) + 2 * nch * 128 * 128 * 2
+    assert lib.gdn_chunk_bwd_workspace_bytes(2, 100, 3, 128, 128, 64, 1, 0) == need
     assert bwd(ws_bytes=need - 1) == E_WS
     assert bwd(B=0) == OK

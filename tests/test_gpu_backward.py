@@ -77,11 +77,21 @@ def test_backward_empty_sequence(gpu):
     assert np.array_equal(g["dS0"], d["dST"].numpy())
 
 
-def test_backward_is_deterministic(gpu):
-    d = _inputs(2, 150, 2, 128, 128, torch.bfloat16, 2, seed=122)
-    a, b = _gpu(gpu, d, 2), _gpu(gpu, d, 2)
+@pytest.mark.parametrize("mode", [1, 2], ids=["chunk_level", "token_level"])
+def test_backward_is_deterministic(gpu, mode):
+    d = _inputs(2, 150, 2, 128, 128, torch.bfloat16, mode, seed=122)
+    a, b = _gpu(gpu, d, mode), _gpu(gpu, d, mode)
     for k in a:
         assert a[k] is None or np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_backward_eight_heads(gpu, mode):
+    """B * H a multiple of 8 (the chains group a head's value slices by XCD):
+    every head against the reference, several chunks and a ragged tail."""
+    d = _inputs(2, 200, 4, 128, 128, torch.bfloat16, mode, seed=124)
+    print("backward bf16 mode %d B 2 H 4 T 200" % mode, flush=True)
+    _check(_gpu(gpu, d, mode), _ref(d, mode), mode, TOL[torch.bfloat16])
 
 
 def test_backward_workload_sampled(gpu):
