@@ -110,34 +110,38 @@ __device__ inline void store4_split(bf* hi, bf* lo, float a, float b, float c, f
   store4(lo, r[0], r[1], r[2], r[3]);
 }
 
-// Sum over the 32 lanes of each half of the wave (result in all of them).
+// Sum over the 32 lanes of each half of the wave (result in all of them):
+// quads, then row_half_mirror and row_mirror DPP, then one swap of 16.
 __device__ inline float half_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+  x = quad_sum(x);
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
   x += __shfl_xor(x, 16);
   return x;
 }
 
 // Row sums of a 32x32 accumulator tile (rows r0 + acc_row) added to rows[],
 // then, if COLS, column sums (columns c0 + lane % 32) subtracted from cols[].
-// Only the calling wave touches rows[] and cols[]; the row writes and the
-// column writes are separate instructions, so the order of the sums is fixed.
+// The 16 row sums are independent reductions; lane j < 16 of each half then
+// adds the one of row acc_row(j / 4, j % 4) in a single read-modify-write.
+// Only the calling wave touches rows[] and cols[], and the row and column
+// updates are separate instructions, so the order of the sums is fixed.
 template <bool COLS>
 __device__ inline void tile_row_col_sums(const f32x16& x, float* rows, int r0, float* cols, int c0, int lane) {
-  const int h = lane >> 5;
+  float s[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float s = half_sum(x[v]);
-    if ((lane & 31) == 0) rows[r0 + acc_row(v >> 2, v & 3, lane)] += s;
-  }
+  for (int v = 0; v < 16; ++v) s[v] = half_sum(x[v]);
+  const int j = lane & 31;
+  float mine = s[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mine = j == v ? s[v] : mine;
+  if (j < 16) rows[r0 + acc_row(j >> 2, j & 3, lane)] += mine;
   if constexpr (COLS) {
     float c = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) c += x[v];
     c += __shfl_xor(c, 32);
-    if (h == 0) cols[c0 + lane] -= c;
+    if (lane < 32) cols[c0 + lane] -= c;
   }
 }
 
@@ -204,6 +208,10 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_states(BackwardArgs a, co
 #pragma unroll
     for (int v = 0; v < 16; ++v) S[v] = s0[acc_row(v >> 2, v & 3, lane)];
   }
+  // Wait for those loads here: a load pending on entry to the loop would make
+  // the compiler wait for every later load (the prefetches too) at the first
+  // use of S in each step.
+  __builtin_amdgcn_s_waitcnt(0);
 
   u32x4 kreg[KPT], treg[2], vreg;
   float greg = 0.f;
@@ -239,9 +247,14 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_states(BackwardArgs a, co
     st16(Vb + vrow * LDO + vcc * 8, vreg);
   };
 
-  if (NC > 0) load(0);
-  for (int n = 0; n < NC; ++n) {
+  // The next chunk's registers go to LDS at the end of each step, after its
+  // last barrier: the loads were issued at the step's start and only its own
+  // stores follow them, so the wait for them is exact.
+  if (NC > 0) {
+    load(0);
     commit();
+  }
+  for (int n = 0; n < NC; ++n) {
     if (n + 1 < NC) load(n + 1);
     if (wave < DK / 32) {
 #pragma unroll
@@ -290,6 +303,7 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_states(BackwardArgs a, co
         mma_bf16(S, frag_perm_tr(Kb, LDK, 16 * s, 32 * wave, lane), frag_perm(Ut + col * LDT, 16 * s, hh));
     }
     __syncthreads();
+    if (n + 1 < NC) commit();
   }
 }
 
@@ -351,6 +365,7 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_rev(BackwardArgs a, const
 #pragma unroll
     for (int v = 0; v < 16; ++v) dS[v] = s[acc_row(v >> 2, v & 3, lane)];
   }
+  __builtin_amdgcn_s_waitcnt(0);   // (as in bc_states)
 
   u32x4 kreg[KPT], qreg[KPT], treg[2], oreg;
   float greg = 0.f, ograte = 0.f;
@@ -397,10 +412,13 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_rev(BackwardArgs a, const
 #pragma unroll
     for (int g = 0; g < 4; ++g) store4(Pt + (32 + col) * LDT + 8 * g + 4 * hh, 0.f, 0.f, 0.f, 0.f);
   }
-  if (NC > 0) load(NC - 1);
+  // (the next chunk's registers go to LDS at the end of each step, as in bc_states)
+  if (NC > 0) {
+    load(NC - 1);
+    commit();
+  }
   for (int n = NC - 1; n >= 0; --n) {
     const int t0 = n * C, cn = min(C, T - t0);
-    commit();
     if (n > 0) load(n - 1);
     if (wave < DK / 32) {
 #pragma unroll
@@ -447,7 +465,7 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_rev(BackwardArgs a, const
         store4(dUt + col * LDT + 32 * wave + 8 * g + 4 * hh, du[4 * g], du[4 * g + 1], du[4 * g + 2], du[4 * g + 3]);
     }
     __syncthreads();
-    if (wave < 2) {   // dX = T^T dU = dV
+    if (wave < 2) {   // dX = T^T dU = dV, row-major into dO's bytes (dO is dead)
       f32x16 dx = zero16();
 #pragma unroll
       for (int t = 0; t < C / 16; ++t)
@@ -456,13 +474,14 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_rev(BackwardArgs a, const
       for (int g = 0; g < 4; ++g) {
         const int s0 = 32 * wave + 8 * g + 4 * hh;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (s0 + e < cn) dvg[((size_t)(b * T + t0 + s0 + e) * H + h) * DV + i0 + col] = (bf)dx[4 * g + e];
+        for (int e = 0; e < 4; ++e) dOb[(s0 + e) * LDO + col] = (bf)dx[4 * g + e];
         store4(Xn + col * LDT + s0, -eG[s0] * dx[4 * g], -eG[s0 + 1] * dx[4 * g + 1], -eG[s0 + 2] * dx[4 * g + 2],
                -eG[s0 + 3] * dx[4 * g + 3]);
       }
     }
     __syncthreads();
+    // dV rows -> HBM, one 16-byte piece per thread
+    if (orow < cn) st16(dvg + ((size_t)(b * T + t0 + orow) * H + h) * DV + i0 + occ * 8, ld16(dOb + orow * LDO + occ * 8));
     if (wave < DK / 32) {   // dS^T <- gamma_C dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dX
       const float gC = eG[C - 1];
 #pragma unroll
@@ -475,6 +494,7 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_rev(BackwardArgs a, const
         mma_bf16(dS, frag_perm_tr(Kb, LDK, 16 * t, 32 * wave, lane), frag_perm(Xn + col * LDT, 16 * t, hh));
     }
     __syncthreads();
+    if (n > 0) commit();
   }
   if (wave < DK / 32 && a.dS0) {
     float* d = a.dS0 + ((size_t)head * DV + i0 + col) * DK + 32 * wave;
@@ -605,21 +625,32 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
     pO0 = piece(tid, i0);
     if (tid < 3 * C * SL / 8 - kGradThreads) pO1 = piece(tid + kGradThreads, i0);
   };
-  load_slice(0);
-
-  // ---- stage K, Q, gates; clear the partial sums ----
+  // ---- stage K, Q, gates (their loads go out before the first slice's); clear the partial sums ----
   {
     const bf* kg = static_cast<const bf*>(a.k);
     const bf* qg = static_cast<const bf*>(a.q);
-    for (int q = tid; q < C * CPR; q += kGradThreads) {
-      const int r = q / CPR, cc = q % CPR;
+    constexpr int KQ = (C * CPR + kGradThreads - 1) / kGradThreads;
+    static_assert(C * CPR % kGradThreads == 0, "K rows split evenly");
+    u32x4 kr[KQ], qr[KQ];
+#pragma unroll
+    for (int m = 0; m < KQ; ++m) {
+      const int q = tid + kGradThreads * m, r = q / CPR, cc = q % CPR;
       const bool ok = r < cn;
-      st16(Kb + r * LDK + cc * 8, ok ? ld16(kg + tok(r) * DK + cc * 8) : zero_u4());
-      st16(Qb + r * LDK + cc * 8, ok ? ld16(qg + tok(r) * DK + cc * 8) : zero_u4());
+      kr[m] = ok ? ld16(kg + tok(r) * DK + cc * 8) : zero_u4();
+      qr[m] = ok ? ld16(qg + tok(r) * DK + cc * 8) : zero_u4();
     }
-    if (tid < 3 * C) Gs[tid] = rg[tid];
+    const float gr = tid < 3 * C ? rg[tid] : 0.f;
+    const float br = tid < cn ? a.beta[tok(tid)] : 0.f;
+    load_slice(0);
+#pragma unroll
+    for (int m = 0; m < KQ; ++m) {
+      const int q = tid + kGradThreads * m, r = q / CPR, cc = q % CPR;
+      st16(Kb + r * LDK + cc * 8, kr[m]);
+      st16(Qb + r * LDK + cc * 8, qr[m]);
+    }
+    if (tid < 3 * C) Gs[tid] = gr;
     if (tid < C) {
-      Bt[tid] = tid < cn ? a.beta[tok(tid)] : 0.f;
+      Bt[tid] = br;
       ones[tid] = 1.f;
     }
     for (int q = tid; q < 12 * C + 16; q += kGradThreads) dGp[q] = 0.f;   // dGp, dBp, misc
