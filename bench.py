@@ -45,7 +45,7 @@ BF16_PEAK_TFLOPS = 2500.0
 CHUNK = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_gdn_bf16_b8_h16_t4096_d128_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc", f)
-                  for f in ("gdn_chunk.hip", "gdn_mfma.h", "gdn_internal.h")]
+                  for f in ("gdn_chunk.hip", "gdn_mfma.h", "gdn_internal.h", "gdn_solve.h")]
 
 
 def log(msg):
