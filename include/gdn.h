@@ -283,9 +283,14 @@ gdn_status gdn2_decode_step(const void* q, const void* k, const void* v, const v
                             int B, int H, int dk, int dv, gdn_dtype dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace gdn_chunk_bwd needs (0: the pointer may be NULL):
- * state checkpoints (d_v x d_k fp32 per 8 tokens of every head) and one
- * partial of the row sums per 32-row value slice.  0 for rejected arguments.
+ * Bytes of device workspace gdn_chunk_bwd needs (0: the pointer may be NULL).
+ * bf16 with no or scalar decay (the chunk-level kernels): per chunk of 64
+ * tokens of every head, the forward's chunk record (T and five gate rows,
+ * 9,472 bytes), the bf16 entry state and the bf16 end-of-chunk state
+ * gradient (2 d_v d_k bytes each).  fp32 or per-channel decay (the token-level
+ * kernels): state checkpoints (d_v x d_k fp32 per 8 tokens of every head) and
+ * one partial of the row sums per 32-row value slice.  0 for rejected
+ * arguments.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
                                      gdn_dtype dtype, gdn_decay mode);
@@ -309,7 +314,10 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
  *   workspace gdn_chunk_bwd_workspace_bytes(...) bytes
  * No output may alias an input, another output or the workspace.  The
  * computation is deterministic (no atomics).  Gradients are accumulated in
- * fp32 and rounded once to `dtype`.  Errors as for gdn_chunk_fwd.
+ * fp32 and rounded once to `dtype`.  bf16 with no or scalar decay runs the
+ * reverse mode of the chunk form (MFMA products; X and dU as bf16 hi + lo
+ * pairs where dbeta needs them); the other cases run the token recurrence in
+ * reverse from state checkpoints.  Errors as for gdn_chunk_fwd.
  */
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha,
                          const float* beta, const float* S0, const void* dout,

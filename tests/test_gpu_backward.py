@@ -70,6 +70,26 @@ def test_backward_without_initial_state_or_final_gradient(gpu, mode):
     _check(_gpu(gpu, d, mode, with_dST=False), _ref(d, mode, with_dST=False), mode, 1e-4)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_backward_zero_beta_rows(gpu, mode):
+    """Every third token writes nothing (beta = 0): diag(beta) is singular, so
+    the chunk-level kernels must take M = (I + A)^-1 from the solve itself."""
+    d = _inputs(2, 130, 2, 128, 128, torch.bfloat16, mode, seed=125)
+    d["beta"][:, ::3] = 0.0
+    print("backward bf16 mode %d zero-beta rows" % mode, flush=True)
+    _check(_gpu(gpu, d, mode), _ref(d, mode), mode, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_backward_strong_decay(gpu, dtype):
+    """alpha in [0.05, 0.5]: the decay inside a chunk spans ~190 e-folds."""
+    d = _inputs(2, 150, 2, 128, 64, dtype, 1, seed=126)
+    g = torch.Generator().manual_seed(127)
+    d["alpha"] = 0.05 + 0.45 * torch.rand(d["alpha"].shape, generator=g)
+    print("backward %s strong decay" % dtype, flush=True)
+    _check(_gpu(gpu, d, 1), _ref(d, 1), 1, TOL[dtype])
+
+
 def test_backward_empty_sequence(gpu):
     """T = 0: dS0 = dS_final, nothing else."""
     d = _inputs(2, 0, 2, 64, 64, torch.float32, 1, seed=121)
