@@ -540,12 +540,13 @@ struct GradLds {
   static constexpr size_t dutlo = xtlo + (size_t)SL * LDT * 2;
   static constexpr size_t vb = dutlo + (size_t)SL * LDT * 2;     // V slice [C][LDO]
   static constexpr size_t slice_end = vb + (size_t)C * LDO * 2;
-  // C x C algebra: dT^T, (dP o E)^T, N1^T, W + W^T [C][LDT]
+  // C x C algebra: dT^T, (dP o E)^T, N1^T, W^T [C][LDT]
   static constexpr size_t dtt = un;
   static constexpr size_t dpe = dtt + (size_t)C * LDT * 2;
   static constexpr size_t n1t = dpe + (size_t)C * LDT * 2;
   static constexpr size_t ws = n1t + (size_t)C * LDT * 2;
-  static constexpr size_t alg_end = ws + (size_t)C * LDT * 2;
+  static constexpr size_t stg = ws + (size_t)C * LDT * 2;           // dq, then dk, [C][LDK] bf16
+  static constexpr size_t alg_end = stg + (size_t)C * LDK * 2;
   static constexpr size_t total = cmax(solve_end, cmax(slice_end, alg_end));
 };
 
@@ -589,6 +590,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
   bf* dPEt = reinterpret_cast<bf*>(smem + L::dpe);
   bf* N1t = reinterpret_cast<bf*>(smem + L::n1t);
   bf* Ws = reinterpret_cast<bf*>(smem + L::ws);
+  bf* Stg = reinterpret_cast<bf*>(smem + L::stg);
 
   // (the wave index in a scalar register: branches on it are uniform jumps)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -828,6 +830,14 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
     __syncthreads();
   }
 
+  // rows of the staging buffer -> [B, T, H, DK] in HBM, 16 bytes per thread and step
+  auto store_rows = [&](void* dst) __attribute__((always_inline)) {
+    bf* g = static_cast<bf*>(dst);
+    for (int q = tid; q < C * CPR; q += kGradThreads) {
+      const int r = q / CPR, cc = q % CPR;
+      if (r < cn) st16(g + tok(r) * DK + cc * 8, ld16(Stg + r * LDK + cc * 8));
+    }
+  };
   // ---- C x C algebra ----
   float* myG = dGp + wave * C;
   if (wave < 4) {   // dT -> dT^T
@@ -856,15 +866,14 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
         store4(dPEt + s * LDT + 32 * rr + 8 * g + 4 * hh, pe[4 * g], pe[4 * g + 1], pe[4 * g + 2], pe[4 * g + 3]);
     }
   }
-  if (wave < NT) {   // dG += rows(Q o diag(gamma) dO S)
-    f32x16 qv;
+  f32x16 qv = zero16();   // Q o diag(gamma) dO S: its row sums go into dG with those of the dK terms
+  if (wave < NT) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = 32 * rt + acc_row(v >> 2, v & 3, lane);
       dQi[v] *= eG[r];
       qv[v] = (float)Qb[r * LDK + 32 * jt + col] * dQi[v];
     }
-    tile_row_col_sums<false>(qv, myG, 32 * rt, nullptr, 0, lane);
   }
   __syncthreads();
   if (wave < 4) {   // N1 = M^T dT; dbeta += diag(N1); N1 -> N1^T
@@ -886,14 +895,15 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
 #pragma unroll
     for (int t = 0; t < C / 16; ++t)
       mma_bf16(dQi, frag_perm_tr(dPEt, LDT, 16 * t, 32 * rt, lane), frag_perm_tr(Kb, LDK, 16 * t, 32 * jt, lane));
-    bf* dq = static_cast<bf*>(a.dq);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = 32 * rt + acc_row(v >> 2, v & 3, lane);
-      if (r < cn) dq[tok(r) * DK + 32 * jt + col] = (bf)dQi[v];
-    }
+    for (int v = 0; v < 16; ++v) Stg[(32 * rt + acc_row(v >> 2, v & 3, lane)) * LDK + 32 * jt + col] = (bf)dQi[v];
   }
   __syncthreads();
+  store_rows(a.dq);
+  if (wave == 1) {   // W^T is zero where s >= 32 > r
+#pragma unroll
+    for (int g = 0; g < 4; ++g) store4(Ws + (32 + col) * LDT + 8 * g + 4 * hh, 0.f, 0.f, 0.f, 0.f);
+  }
   if (wave < 4 && rr >= sc) {   // dA = -tril_-1(N1 T^T); dbeta, Z, W
     f32x16 da = zero16();
 #pragma unroll
@@ -901,7 +911,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
       mma_bf16(da, frag_perm_tr(N1t, LDT, 16 * t, 32 * rr, lane), frag_perm(Tb + (32 * sc + col) * LDT, 16 * t, hh));
     const int s = 32 * sc + col;
     const float gs = Gs[s];
-    f32x16 bz, zz;
+    f32x16 bz, zz, wv;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = 32 * rr + acc_row(v >> 2, v & 3, lane);
@@ -909,16 +919,29 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
       const float ekk = (float)EK[r * LDT + s];
       bz[v] = d * ekk;
       zz[v] = bz[v] * Bt[r];
-      const float w = Bt[r] * d * __expf(Gs[r] - gs);
-      if (r > s) {
-        Ws[r * LDT + s] = (bf)w;
-        Ws[s * LDT + r] = (bf)w;
-      } else if (r == s) {
-        Ws[r * LDT + r] = (bf)0.f;
-      }
+      wv[v] = Bt[r] * d * __expf(Gs[r] - gs);
     }
-    tile_row_col_sums<false>(bz, dBp + wave * C, 32 * rr, nullptr, 0, lane);
-    tile_row_col_sums<true>(zz, myG, 32 * rr, myG, 32 * sc, lane);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)   // W^T[s][r], 8-byte stores
+      store4(Ws + s * LDT + 32 * rr + 8 * g + 4 * hh, wv[4 * g], wv[4 * g + 1], wv[4 * g + 2], wv[4 * g + 3]);
+    // Z = diag(beta) (dA o E o K K^T): its row sums are beta_r times those of bz
+    float sr[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sr[v] = half_sum(bz[v]);
+    const int j = lane & 31;
+    float mine = sr[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mine = j == v ? sr[v] : mine;
+    if (j < 16) {
+      const int r = 32 * rr + acc_row(j >> 2, j & 3, lane);
+      dBp[wave * C + r] += mine;
+      myG[r] += Bt[r] * mine;
+    }
+    float cz = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) cz += zz[v];
+    cz += __shfl_xor(cz, 32);
+    if (lane < 32) myG[32 * sc + lane] -= cz;
   }
   float gcp = 0.f;   // this wave's part of sum_r k_r . (exp(G_C - G_r) U dS)_r
   if (wave < NT) {   // dK so far: -diag(gamma) dX S + diag(exp(G_C - G)) U dS; dG terms of both
@@ -928,26 +951,25 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
       const int r = 32 * rt + acc_row(v >> 2, v & 3, lane);
       const float t1 = eG[r] * P1[v], t2 = eC[r] * P2[v];
       const float kr = (float)Kb[r * LDK + 32 * jt + col];
-      kv[v] = -kr * (t1 + t2);
+      kv[v] = qv[v] - kr * (t1 + t2);
       gcp += kr * t2;
       P1[v] = t2 - t1;
     }
     tile_row_col_sums<false>(kv, myG, 32 * rt, nullptr, 0, lane);
   }
   __syncthreads();
-  if (wave < NT) {   // dK += (W + W^T) K + (dP o E)^T Q
+  if (wave < NT) {   // dK += W K + W^T K + (dP o E)^T Q (W^T is stored)
 #pragma unroll
-    for (int t = 0; t < C / 16; ++t)
-      mma_bf16(P1, frag_perm(Ws + (32 * rt + col) * LDT, 16 * t, hh), frag_perm_tr(Kb, LDK, 16 * t, 32 * jt, lane));
+    for (int t = 0; t < C / 16; ++t) {
+      const bf16x8 kf = frag_perm_tr(Kb, LDK, 16 * t, 32 * jt, lane);
+      mma_bf16(P1, frag_perm_tr(Ws, LDT, 16 * t, 32 * rt, lane), kf);
+      mma_bf16(P1, frag_perm(Ws + (32 * rt + col) * LDT, 16 * t, hh), kf);
+    }
 #pragma unroll
     for (int t = 0; t < C / 16; ++t)
       mma_bf16(P1, frag_perm(dPEt + (32 * rt + col) * LDT, 16 * t, hh), frag_perm_tr(Qb, LDK, 16 * t, 32 * jt, lane));
-    bf* dk = static_cast<bf*>(a.dk);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = 32 * rt + acc_row(v >> 2, v & 3, lane);
-      if (r < cn) dk[tok(r) * DK + 32 * jt + col] = (bf)P1[v];
-    }
+    for (int v = 0; v < 16; ++v) Stg[(32 * rt + acc_row(v >> 2, v & 3, lane)) * LDK + 32 * jt + col] = (bf)P1[v];
   }
   {   // per-wave sums: <dS, S> and gcp
     float x = sd, y = gcp;
@@ -962,6 +984,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
     }
   }
   __syncthreads();
+  store_rows(a.dk);
   if (wave == 0) {   // dG -> dlog alpha (sum over the rows at or after each token), dbeta
     const int r = lane;
     float g = 0.f;
