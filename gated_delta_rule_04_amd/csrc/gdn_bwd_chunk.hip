@@ -221,9 +221,9 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_states(BackwardArgs a, co
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
       const int q = tid + kChainThreads * m, r = q / CPR, cc = q % CPR;
-      kreg[m] = r < cn ? ld16(kg + ((size_t)(b * T + t0 + r) * H + h) * DK + cc * 8) : zero_u4();
+      kreg[m] = r < cn ? ld16(kg + (((size_t)b * T + t0 + r) * H + h) * DK + cc * 8) : zero_u4();
     }
-    vreg = vrow < cn ? ld16(vg + ((size_t)(b * T + t0 + vrow) * H + h) * DV + i0 + vcc * 8) : zero_u4();
+    vreg = vrow < cn ? ld16(vg + (((size_t)b * T + t0 + vrow) * H + h) * DV + i0 + vcc * 8) : zero_u4();
     const bf* rec = recs + ((size_t)head * NC + n) * kRecElems;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_rev(BackwardArgs a, const
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
       const int q = tid + kChainThreads * m, r = q / CPR, cc = q % CPR;
-      const size_t off = ((size_t)(b * T + t0 + r) * H + h) * DK + cc * 8;
+      const size_t off = (((size_t)b * T + t0 + r) * H + h) * DK + cc * 8;
       kreg[m] = r < cn ? ld16(kg + off) : zero_u4();
       qreg[m] = r < cn ? ld16(qg + off) : zero_u4();
     }
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_rev(BackwardArgs a, const
     const float* rg = reinterpret_cast<const float*>(rec + kRecG);
     if (tid < 3 * C) greg = rg[tid];
     ograte = rg[C + orow];
-    oreg = orow < cn ? ld16(dout_g + ((size_t)(b * T + t0 + orow) * H + h) * DV + i0 + occ * 8) : zero_u4();
+    oreg = orow < cn ? ld16(dout_g + (((size_t)b * T + t0 + orow) * H + h) * DV + i0 + occ * 8) : zero_u4();
   };
   auto commit = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(kChainThreads, 2) void bc_rev(BackwardArgs a, const
     }
     __syncthreads();
     // dV rows -> HBM, one 16-byte piece per thread
-    if (orow < cn) st16(dvg + ((size_t)(b * T + t0 + orow) * H + h) * DV + i0 + occ * 8, ld16(dOb + orow * LDO + occ * 8));
+    if (orow < cn) st16(dvg + (((size_t)b * T + t0 + orow) * H + h) * DV + i0 + occ * 8, ld16(dOb + orow * LDO + occ * 8));
     if (wave < DK / 32) {   // dS^T <- gamma_C dS^T + Q^T diag(gamma) dO - K^T diag(gamma) dX
       const float gC = eG[C - 1];
 #pragma unroll
@@ -600,7 +600,7 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
   const int b = head / H, h = head % H, t0 = n * C, cn = min(C, T - t0);
   const bf* rec = recs + ((size_t)head * NC + n) * kRecElems;
   const float* rg = reinterpret_cast<const float*>(rec + kRecG);
-  auto tok = [&](int r) { return (size_t)(b * T + t0 + r) * H + h; };
+  auto tok = [&](int r) { return ((size_t)b * T + t0 + r) * H + h; };
 
   // The first chunk's entry state is S0 and the last chunk's end gradient is
   // dS_final, both fp32 inputs: those chunks take them whole (hi + lo parts)
