@@ -311,7 +311,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
 
   // K (and Q) rows, consecutive threads along a row (rows past the sequence
   // end repeat its last row: beta = 0 there, so they never reach A or T, and
-  // P's rows of them are never used)
+  // P's rows of them are never used).  K takes ordinary loads: the state
+  // kernel reads it again right after this kernel, and K plus the records fit
+  // the last-level cache at the batched workload's size (the non-temporal
+  // hint cost that second read 3-4 % of the call).
   {
     const E* kg = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
     const E* qg = static_cast<const E*>(a.q) + (tok0 * H + h) * DK;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     for (int m = 0; m < C * CPR / kThreads; ++m) {
       const int q = tid + kThreads * m, r = q / CPR, cc = q % CPR;
       const size_t off = (size_t)min(r, cn - 1) * ktok + cc * EPC;
-      *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = ld_once(kg + off);
+      *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = *reinterpret_cast<const u32x4*>(kg + off);
       if constexpr (WP) *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = ld_once(qg + off);
     }
   }
