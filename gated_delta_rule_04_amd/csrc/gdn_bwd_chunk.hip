@@ -596,7 +596,10 @@ __global__ __launch_bounds__(kGradThreads, 1) void bc_grad(BackwardArgs a, const
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
   const int T = a.T, H = a.H, NC = (T + C - 1) / C;
-  const int head = blockIdx.x / NC, n = blockIdx.x % NC;
+  // chunk index outermost, ascending: bc_rev visited the chunks in reverse,
+  // so the first chunks of every head are the ones still in the last-level cache
+  const int nheads = a.B * H;
+  const int head = blockIdx.x % nheads, n = blockIdx.x / nheads;
   const int b = head / H, h = head % H, t0 = n * C, cn = min(C, T - t0);
   const bf* rec = recs + ((size_t)head * NC + n) * kRecElems;
   const float* rg = reinterpret_cast<const float*>(rec + kRecG);
