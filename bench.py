@@ -169,8 +169,27 @@ def bench_step(w: W.Prefill, steps: int, warmup: int):
     b1.record()
     torch.cuda.synchronize()
     launch_ms = b0.elapsed_time(b1) / steps
+
+    # Cold last-level cache (256 MB on MI355X): before every launch a 512 MB
+    # write and a read of the same 512 MB (so none of the write's dirty lines
+    # drain during the launch), outside an event pair around the launch.  Its
+    # median compares with the warm launches' median under the same kind of
+    # event pair (step_events_us_median), which counts the marker packets too.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    reps = max(5, steps // 2)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        scratch.fill_(i & 255)
+        scratch.sum(dtype=torch.int32)
+        cev[i][0].record()
+        prefill()
+        cev[i][1].record()
+    torch.cuda.synchronize()
+    cold_ms = sorted(e0.elapsed_time(e1) for e0, e1 in cev)[reps // 2]
+    del scratch
     # outputs of the last launch, for the parity spot check against the oracle
-    return dict(wall_s=wall, kernel_ms=kern_ms, launch_ms=launch_ms, host=host, o=o, S=S)
+    return dict(wall_s=wall, kernel_ms=kern_ms, launch_ms=launch_ms, cold_ms=cold_ms, host=host, o=o,
+                S=S)
 
 
 def packed_bytes(w: W.Packed) -> int:
@@ -533,7 +552,10 @@ def main():
     log("prefill launch %.1f us (mean of %d back to back; %.1f us median with an event pair "
         "per step), step %.3f ms" % (kern_ms * 1e3, args.steps, ev_ms * 1e3, ms_step))
 
+    log("prefill launch with an event pair: %.1f us (median) warm, %.1f us on a cold last-level cache"
+        % (ev_ms * 1e3, r["cold_ms"] * 1e3))
     prefill = dict(launch_us=kern_ms * 1e3, step_events_us_median=ev_ms * 1e3,
+                   cold_cache_events_us_median=r["cold_ms"] * 1e3,
                    tokens_per_s_kernel=tokens / (kern_ms * 1e-3),
                    tflops_causal=f_c / (kern_ms * 1e-3) / 1e12,
                    mfma_frac_causal=f_c / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
