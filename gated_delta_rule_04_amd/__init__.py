@@ -130,25 +130,127 @@ def _require(t, name, dtype=None):
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
+
+def _expect(t, name, shape):
+    """Raise ValueError unless tensor ``t`` (if given) has exactly ``shape``."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check_prefill_shapes(q, k, v, alpha, beta, S0, o, S_final, mode, lead, nseq, extra_h=None):
+    """Shapes of a prefill call (batched: ``lead`` = (B, T, H); packed: (T, H)
+    or (1, T, H)) against q's; ``nseq`` states per head (B, or N for a packed
+    batch).  Every size the kernels derive from (B, T, H, dk, dv) must match,
+    since the C-ABI sees only pointers: a short tensor would be read or written
+    past its end."""
+    dk = q.shape[-1]
+    if v is None or v.dim() != q.dim():
+        raise ValueError("v must have as many axes as q")
+    dv = v.shape[-1]
+    H = lead[-1]
+    _expect(k, "k", tuple(lead) + (dk,))
+    _expect(v, "v", tuple(lead) + (dv,))
+    _expect(beta, "beta", tuple(lead))
+    if mode == DECAY_SCALAR:
+        _expect(alpha, "alpha", tuple(lead))
+    elif mode == DECAY_CHANNEL:
+        _expect(alpha, "alpha", tuple(lead) + (dk,))
+    _expect(S0, "S0", (nseq, H, dv, dk))
+    _expect(o, "o", tuple(lead) + (dv,))
+    _expect(S_final, "S_final", (nseq, H, dv, dk))
+    for t, n, last in (extra_h or ()):
+        _expect(t, n, tuple(lead) + (last,))
+    if mode not in (DECAY_NONE, DECAY_SCALAR, DECAY_CHANNEL):
+        raise ValueError("mode must be DECAY_NONE, DECAY_SCALAR or DECAY_CHANNEL")
+    if mode != DECAY_NONE and alpha is None:
+        raise ValueError("alpha is required for a decay mode")
+    return dk, dv
+
+
+def _check_decode_shapes(q, k, v, alpha, beta, S, o, mode, extra=None):
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, dk]")
+    B, H, dk = q.shape
+    if v is None or v.dim() != 3:
+        raise ValueError("v must be [B, H, dv]")
+    dv = v.shape[-1]
+    _expect(k, "k", (B, H, dk))
+    _expect(v, "v", (B, H, dv))
+    _expect(beta, "beta", (B, H))
+    if mode == DECAY_SCALAR:
+        _expect(alpha, "alpha", (B, H))
+    elif mode == DECAY_CHANNEL:
+        _expect(alpha, "alpha", (B, H, dk))
+    if mode != DECAY_NONE and alpha is None:
+        raise ValueError("alpha is required for a decay mode")
+    if S is None:
+        raise ValueError("S is required")
+    _expect(S, "S", (B, H, dv, dk))
+    _expect(o, "o", (B, H, dv))
+    for t, n, last in (extra or ()):
+        _expect(t, n, (B, H, last))
+    return B, H, dk, dv
+
+
+def _lead_of(q, cu_seqlens):
+    """(B, T, H, dk) of a batched call, or (N, T, H, dk) of a packed one."""
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, H, dk]")
+        B, T, H, dk = q.shape
+        return B, T, H, dk
+    if q.dim() not in (3, 4) or (q.dim() == 4 and q.shape[0] != 1):
+        raise ValueError("a packed q must be [T, H, dk] or [1, T, H, dk]")
+    if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor of N + 1 offsets")
+    T, H, dk = q.shape[-3:]
+    return cu_seqlens.shape[0] - 1, T, H, dk
+
+
+def _check_workspace(ws, nbytes):
+    if ws is None:
+        return None
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    if ws.numel() < nbytes:
+        raise ValueError("workspace holds %d bytes, the call needs %d" % (ws.numel(), nbytes))
+    return ws
+
+
+def _check_prologue_shapes(mode, H, dk, alpha_logits, A, dt_bias):
+    if A is not None:
+        _expect(A, "A", (H,))
+    if dt_bias is not None:
+        _expect(dt_bias, "dt_bias", (H,) if mode == DECAY_SCALAR else (H, dk))
+    if alpha_logits and mode != DECAY_NONE and A is None:
+        raise ValueError("alpha_logits needs the per-head rates A")
+
+
 def workspace_bytes(B, T, H, dk, dv, dtype=torch.bfloat16, mode=DECAY_SCALAR, chunk=64) -> int:
     return int(load().gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, _DTYPES[dtype], mode))
 
 
 def chunk_fwd(q, k, v, alpha, beta, S0=None, *, mode=None, chunk=64, o=None, S_final=None,
-              need_final=True, stream=None):
+              need_final=True, workspace=None, stream=None):
     """Chunked prefill through ``gdn_chunk_fwd``.
 
     q, k [B, T, H, dk]; v [B, T, H, dv] (fp32 or bf16, one dtype);
     alpha fp32 [B, T, H] (scalar decay), ``dtype`` [B, T, H, dk] (per-channel
     decay) or None (no decay); beta fp32 [B, T, H]; S0 fp32 [B, H, dv, dk] or None.
+    ``workspace``: a uint8 GPU tensor of at least :func:`workspace_bytes` bytes
+    (None: one is allocated per call).
     Returns (o, S_final); S_final is None when ``need_final`` is False."""
     lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    _, dv = _check_prefill_shapes(q, k, v, alpha, beta, S0, o, S_final, mode, (B, T, H), B)
     dtype = q.dtype
     if dtype not in _DTYPES:
         raise ValueError("q must be float32 or bfloat16")
-    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    ws_bytes = int(lib.gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, _DTYPES[dtype], mode))
+    ws = _check_workspace(workspace, ws_bytes)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, dtype)
     _require(beta, "beta", torch.float32)
@@ -163,8 +265,11 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, *, mode=None, chunk=64, o=None, S_f
         S_final = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
     _require(o, "o", dtype)
     _require(S_final, "S_final", torch.float32)
-    ws_bytes = int(lib.gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, _DTYPES[dtype], mode))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _require(ws, "workspace")
+    if ws is None and ws_bytes:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if ws is not None:
+        ws_bytes = ws.numel()
     st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None), _ptr(beta),
                            _ptr(S0), _ptr(o), _ptr(S_final), _ptr(ws), ws_bytes,
                            B, T, H, dk, dv, chunk, _DTYPES[dtype], mode, _stream(stream))
@@ -181,21 +286,23 @@ def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, S0=None, *, mode=None, ch
     cu_seqlens int32 GPU tensor [N + 1] (0, ..., T, non-decreasing); S0 fp32
     [N, H, dv, dk] or None.  Returns (o, S_final [N, H, dv, dk])."""
     lib = load()
+    if q.dim() not in (3, 4):
+        raise ValueError("q must be [T, H, dk] or [1, T, H, dk]")
     lead = q.dim() == 4
     T, H, dk = q.shape[-3:]
-    dv = v.shape[-1]
     if lead and q.shape[0] != 1:
         raise ValueError("a packed batch has a leading axis of 1, got %d" % q.shape[0])
-    dtype = q.dtype
-    if dtype not in _DTYPES:
-        raise ValueError("q must be float32 or bfloat16")
-    _require(cu_seqlens, "cu_seqlens", torch.int32)
-    if cu_seqlens is None or cu_seqlens.dim() != 1:
-        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor of N + 1 offsets")
     N = cu_seqlens.shape[0] - 1
     if mode is None:
         mode = DECAY_NONE if alpha is None else (
             DECAY_SCALAR if alpha.dim() == q.dim() - 1 else DECAY_CHANNEL)
+    _, dv = _check_prefill_shapes(q, k, v, alpha, beta, S0, o, S_final, mode, tuple(q.shape[:-1]), N)
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    _require(cu_seqlens, "cu_seqlens", torch.int32)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, dtype)
     _require(beta, "beta", torch.float32)
@@ -227,12 +334,11 @@ def decode_step(q, k, v, alpha, beta, S, *, mode=None, o=None, stream=None):
     q, k [B, H, dk]; v [B, H, dv]; alpha fp32 [B, H], ``dtype`` [B, H, dk] or
     None; beta fp32 [B, H]; S fp32 [B, H, dv, dk].  Returns o [B, H, dv]."""
     lib = load()
-    B, H, dk = q.shape
-    dv = v.shape[-1]
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    B, H, dk, dv = _check_decode_shapes(q, k, v, alpha, beta, S, o, mode)
     dtype = q.dtype
     if dtype not in _DTYPES:
         raise ValueError("q must be float32 or bfloat16")
-    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, dtype)
     _require(beta, "beta", torch.float32)
@@ -270,21 +376,17 @@ def chunk_fwd_fused(q, k, v, alpha, beta, S0=None, *, cu_seqlens=None, l2norm_qk
     logits; ``l2norm_qk`` normalises q and k per (token, head) with ``eps``."""
     lib = load()
     packed = cu_seqlens is not None
-    T, H, dk = q.shape[-3:]
-    dv = v.shape[-1]
-    if packed:
-        _require(cu_seqlens, "cu_seqlens", torch.int32)
-        if q.dim() == 4 and q.shape[0] != 1:
-            raise ValueError("a packed batch has a leading axis of 1, got %d" % q.shape[0])
-        B = cu_seqlens.shape[0] - 1
-    else:
-        B = q.shape[0]
-    dtype = q.dtype
-    if dtype not in _DTYPES:
-        raise ValueError("q must be float32 or bfloat16")
+    B, T, H, dk = _lead_of(q, cu_seqlens)
     if mode is None:
         mode = DECAY_NONE if alpha is None else (
             DECAY_SCALAR if alpha.dim() == q.dim() - 1 else DECAY_CHANNEL)
+    _, dv = _check_prefill_shapes(q, k, v, alpha, beta, S0, o, S_final, mode, tuple(q.shape[:-1]), B)
+    _check_prologue_shapes(mode, H, dk, alpha_logits, A, dt_bias)
+    if packed:
+        _require(cu_seqlens, "cu_seqlens", torch.int32)
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, dtype)
     _require(beta, "beta", torch.float32)
@@ -316,12 +418,12 @@ def decode_step_fused(q, k, v, alpha, beta, S, *, l2norm_qk=False, eps=1e-6, bet
     """One decode step with the prologue in the kernel (``gdn_decode_step_fused``);
     tensors as in :func:`decode_step`, prologue as in :func:`chunk_fwd_fused`."""
     lib = load()
-    B, H, dk = q.shape
-    dv = v.shape[-1]
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    B, H, dk, dv = _check_decode_shapes(q, k, v, alpha, beta, S, o, mode)
+    _check_prologue_shapes(mode, H, dk, alpha_logits, A, dt_bias)
     dtype = q.dtype
     if dtype not in _DTYPES:
         raise ValueError("q must be float32 or bfloat16")
-    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, dtype)
     _require(beta, "beta", torch.float32)
@@ -348,15 +450,15 @@ def gdn2_chunk_fwd(q, k, v, alpha, erase, write, S0=None, *, cu_seqlens=None, ch
     batched ([B, T, H, d]) or packed (``cu_seqlens``, [1, T, H, d] or [T, H, d])."""
     lib = load()
     packed = cu_seqlens is not None
-    T, H, dk = q.shape[-3:]
+    B, T, H, dk = _lead_of(q, cu_seqlens)
     dv = v.shape[-1]
+    lead = tuple(q.shape[:-1])
+    if erase is None or write is None:
+        raise ValueError("erase and write gates are required")
+    _check_prefill_shapes(q, k, v, alpha, None, S0, o, S_final, DECAY_CHANNEL, lead, B,
+                          extra_h=((erase, "erase", dk), (write, "write", dv)))
     if packed:
         _require(cu_seqlens, "cu_seqlens", torch.int32)
-        if q.dim() == 4 and q.shape[0] != 1:
-            raise ValueError("a packed batch has a leading axis of 1, got %d" % q.shape[0])
-        B = cu_seqlens.shape[0] - 1
-    else:
-        B = q.shape[0]
     dtype = q.dtype
     if dtype not in _DTYPES:
         raise ValueError("q must be float32 or bfloat16")
@@ -384,8 +486,13 @@ def gdn2_decode_step(q, k, v, alpha, erase, write, S, *, o=None, stream=None):
     """One Gated DeltaNet-2 decode step (``gdn2_decode_step``); S updated in place.
     q, k, alpha, erase [B, H, dk]; v, write [B, H, dv]; S fp32 [B, H, dv, dk]."""
     lib = load()
-    B, H, dk = q.shape
-    dv = v.shape[-1]
+    if erase is None or write is None:
+        raise ValueError("erase and write gates are required")
+    if q.dim() != 3 or v is None or v.dim() != 3:
+        raise ValueError("q must be [B, H, dk] and v [B, H, dv]")
+    dk, dv = q.shape[-1], v.shape[-1]
+    B, H, dk, dv = _check_decode_shapes(q, k, v, alpha, None, S, o, DECAY_CHANNEL,
+                                        extra=((erase, "erase", dk), (write, "write", dv)))
     dtype = q.dtype
     if dtype not in _DTYPES:
         raise ValueError("q must be float32 or bfloat16")
@@ -411,12 +518,16 @@ def chunk_bwd(q, k, v, alpha, beta, S0, dout, dS_final=None, *, mode=None, chunk
     alpha's shape; None without decay), dbeta (fp32), dS0 (fp32, or None when
     ``need_dS0`` is False)."""
     lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
     B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    _, dv = _check_prefill_shapes(q, k, v, alpha, beta, S0, dout, dS_final, mode, (B, T, H), B)
+    if beta is None or dout is None:
+        raise ValueError("beta and dout are required")
     dtype = q.dtype
     if dtype not in _DTYPES:
         raise ValueError("q must be float32 or bfloat16")
-    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _require(t, n, dtype)
     _require(beta, "beta", torch.float32)

@@ -37,7 +37,9 @@
  *  - Supported sizes: d_k in {64, 128}, d_v in {64, 128}, chunk = 64.
  *    Other sizes return GDN_ERR_UNSUPPORTED.
  *  - Decay numerics: log alpha is floored at -100 (alpha below e^-100 acts as
- *    e^-100, which is 0 in every fp32 product).  Per-channel decay: inside a
+ *    e^-100, about 3.7e-44: an fp32 subnormal, so a state or key term scaled by
+ *    it is some 1e-43 of the unit-size terms it is summed with, below fp32
+ *    resolution; exact zeros are accepted).  Per-channel decay: inside a
  *    chunk the kernels split decay ratios at anchor tokens at most 16 tokens
  *    away; a channel whose decay over such a span exceeds e^64 is handled by
  *    an exact element-wise path instead (slower, same results), so any alpha
