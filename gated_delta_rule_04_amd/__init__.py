@@ -21,14 +21,14 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_fused", "decode_step", "decode_step_fused",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_varlen", "chunk_fwd_fused", "decode_step", "decode_step_fused",
            "gdn2_chunk_fwd", "gdn2_decode_step", "chunk_bwd", "load", "lib_path", "GDNError",
            "DECAY_NONE", "DECAY_SCALAR", "DECAY_CHANNEL", "EXPORTED_SYMBOLS"]
 
 DECAY_NONE, DECAY_SCALAR, DECAY_CHANNEL = 0, 1, 2
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
-EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd",
+EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc",
                     "gdn_chunk_fwd_varlen_workspace_bytes", "gdn_chunk_fwd_varlen",
                     "gdn_chunk_fwd_fused", "gdn_decode_step", "gdn_decode_step_fused",
                     "gdn2_chunk_fwd", "gdn2_decode_step", "gdn_chunk_bwd_workspace_bytes",
@@ -72,6 +72,8 @@ def load():
         lib.gdn_chunk_fwd_workspace_bytes.restype = sz
         lib.gdn_chunk_fwd.argtypes = [vp] * 8 + [vp, sz] + [i] * 8 + [vp]
         lib.gdn_chunk_fwd.restype = i
+        lib.gdn_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 8 + [vp]
+        lib.gdn_chunk_fwd_noalloc.restype = i
         lib.gdn_chunk_fwd_varlen_workspace_bytes.argtypes = [i] * 8
         lib.gdn_chunk_fwd_varlen_workspace_bytes.restype = sz
         lib.gdn_chunk_fwd_varlen.argtypes = [vp] * 9 + [vp, sz] + [i] * 8 + [vp]
@@ -273,6 +275,42 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, *, mode=None, chunk=64, o=None, S_f
     st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None), _ptr(beta),
                            _ptr(S0), _ptr(o), _ptr(S_final), _ptr(ws), ws_bytes,
                            B, T, H, dk, dv, chunk, _DTYPES[dtype], mode, _stream(stream))
+    _check(st)
+    return o, S_final
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, beta, S0, o, S_final, *, mode=None, chunk=64, stream=None):
+    """Prefill through ``gdn_chunk_fwd_noalloc``: the library allocates nothing
+    (its chunk records live in a per-GPU scratch array of NOALLOC_SCRATCH_BYTES),
+    so the caller passes the outputs o [B, T, H, dv] and S_final [B, H, dv, dk]
+    (S_final may be None).  Calls that overlap on one GPU race; calls in order
+    on one stream do not."""
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, dk]")
+    if o is None:
+        raise ValueError("o is required: this entry point allocates nothing")
+    B, T, H, dk = q.shape
+    mode = _infer_mode(alpha, q.dim()) if mode is None else mode
+    _, dv = _check_prefill_shapes(q, k, v, alpha, beta, S0, o, S_final, mode, (B, T, H), B)
+    dtype = q.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("q must be float32 or bfloat16")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _require(t, n, dtype)
+    _require(beta, "beta", torch.float32)
+    _require(S0, "S0", torch.float32)
+    _require(S_final, "S_final", torch.float32)
+    if mode == DECAY_SCALAR:
+        _require(alpha, "alpha", torch.float32)
+    elif mode == DECAY_CHANNEL:
+        _require(alpha, "alpha", dtype)
+    st = lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha if mode else None),
+                                   _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final),
+                                   B, T, H, dk, dv, chunk, _DTYPES[dtype], mode, _stream(stream))
     _check(st)
     return o, S_final
 

@@ -9,6 +9,9 @@
 #include "gdn_backward.h"
 #include "gdn_internal.h"
 
+static_assert(gdn::kNoAllocScratchBytes == GDN_NOALLOC_SCRATCH_BYTES,
+              "the scratch size of the header and of the kernels agree");
+
 namespace {
 
 constexpr int kChunk = 64;
@@ -128,7 +131,8 @@ gdn_status prefill(const void* q, const void* k, const void* v, const void* alph
                    const int* cu_seqlens, bool packed, const gdn_prologue* pro, void* workspace,
                    size_t workspace_bytes, int B, int T, int H, int dk, int dv, int chunk,
                    gdn_dtype dtype, gdn_decay mode, hipStream_t stream,
-                   const void* erase = nullptr, const void* write = nullptr, bool gdn2 = false) {
+                   const void* erase = nullptr, const void* write = nullptr, bool gdn2 = false,
+                   bool noalloc = false) {
   gdn_status st = check_common(B, H, dk, dv, dtype, mode);
   if (st != GDN_OK) return st;
   if (T < 0) return GDN_ERR_SHAPE;
@@ -146,7 +150,8 @@ gdn_status prefill(const void* q, const void* k, const void* v, const void* alph
   const size_t ws_need = packed
                              ? gdn_chunk_fwd_varlen_workspace_bytes(B, T, H, dk, dv, chunk, dtype, mode)
                              : gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dtype, mode);
-  if (workspace_bytes < ws_need) return GDN_ERR_WORKSPACE;
+  if (noalloc ? ws_need > gdn::kNoAllocScratchBytes : workspace_bytes < ws_need)
+    return GDN_ERR_WORKSPACE;
   const bool has_tokens = T > 0;
   gdn::Prologue pa;
   Range rA, rbias;
@@ -154,7 +159,7 @@ gdn_status prefill(const void* q, const void* k, const void* v, const void* alph
   if (st != GDN_OK) return st;
   if (B == 0 || H == 0) return GDN_OK;
   if (packed && !cu_seqlens) return GDN_ERR_NULL;
-  if (ws_need > 0 && !workspace) return GDN_ERR_NULL;
+  if (ws_need > 0 && !workspace && !noalloc) return GDN_ERR_NULL;
   if (has_tokens) {
     if (!q || !k || !v || !o) return GDN_ERR_NULL;
     if (gdn2 ? (!erase || !write) : !beta) return GDN_ERR_NULL;
@@ -182,9 +187,12 @@ gdn_status prefill(const void* q, const void* k, const void* v, const void* alph
   for (Range in : {rq, rk, rv, ra, rb, re, rwg, ro, rcu, rA, rbias})
     if (overlaps(rsf, in)) return GDN_ERR_ALIAS;
   if (overlaps(rsf, rs0) && (const void*)S_final != (const void*)S0) return GDN_ERR_ALIAS;
-  Range rw = range_of(ws_need > 0 ? workspace : nullptr, ws_need);
+  // (the library's own scratch array cannot alias a caller's buffer)
+  Range rw = range_of(ws_need > 0 && !noalloc ? workspace : nullptr, ws_need);
   for (Range in : {rq, rk, rv, ra, rb, re, rwg, rs0, rcu, ro, rsf, rA, rbias})
     if (overlaps(rw, in)) return GDN_ERR_ALIAS;
+  if (noalloc && ws_need > 0 && gdn::noalloc_scratch(&workspace) != hipSuccess)
+    return GDN_ERR_LAUNCH;
 
   gdn::PrefillArgs a{q, k, v, alpha, gdn2 ? nullptr : beta, S0, o, S_final, B, T, H, dk, dv,
                      (int)dtype, gdn2 ? 3 : (int)mode};
@@ -252,6 +260,14 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void
                          hipStream_t stream) {
   return prefill(q, k, v, alpha, beta, S0, o, S_final, nullptr, false, nullptr, workspace,
                  workspace_bytes, B, T, H, dk, dv, chunk, dtype, mode, stream);
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                                 const float* beta, const float* S0, void* o, float* S_final,
+                                 int B, int T, int H, int dk, int dv, int chunk, gdn_dtype dtype,
+                                 gdn_decay mode, hipStream_t stream) {
+  return prefill(q, k, v, alpha, beta, S0, o, S_final, nullptr, false, nullptr, nullptr, 0, B, T,
+                 H, dk, dv, chunk, dtype, mode, stream, nullptr, nullptr, false, true);
 }
 
 gdn_status gdn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* alpha,

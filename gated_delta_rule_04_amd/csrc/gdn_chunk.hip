@@ -44,6 +44,7 @@
 //   workgroup owns one (b, h, d_v slice).
 // chunk_state_kernel (fp32; the same phases with four waves that also move
 //   the data themselves)
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_internal.h"
@@ -2010,6 +2011,31 @@ size_t prefill_varlen_workspace_bytes(int N, int T, int H, int dk, int dtype, in
 }
 
 size_t prefill_record_bytes(int dk, int dtype, int mode) { return record_bytes(dk, dtype, mode); }
+
+// Chunk records of the prefill entry point that allocates nothing: one copy
+// of this array per device, alive until the process ends.  In host code its
+// name is only a stand-in; kernels get the device address looked up below.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_prefill_prep(const PrefillArgs& a, void* workspace, hipStream_t stream) {
   if (a.dtype == 1)

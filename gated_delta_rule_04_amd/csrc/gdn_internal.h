@@ -90,6 +90,12 @@ hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t str
 size_t prefill_record_bytes(int dk, int dtype, int mode);
 // Enqueue only the first prefill kernel, which writes the chunk records.
 hipError_t launch_prefill_prep(const PrefillArgs& a, void* workspace, hipStream_t stream);
+// Bytes of the per-device scratch array of the prefill entry point that
+// allocates nothing (the same value as GDN_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// Device address of that array on the current device (looked up once per
+// device, then cached).
+hipError_t noalloc_scratch(void** ptr);
 // Enqueue one decode step; returns the launch status.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -152,6 +152,36 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
 
 /*
+ * gdn_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The chunk records live in a scratch array
+ * inside the library's device code, GDN_NOALLOC_SCRATCH_BYTES bytes per GPU,
+ * held by every GPU the library runs on until the process ends.  This call
+ * allocates nothing (no hipMalloc, no allocating library routine); the caller
+ * still passes every input and output, with the layouts, semantics and
+ * errors of gdn_chunk_fwd.
+ *
+ *   - A call whose gdn_chunk_fwd_workspace_bytes(...) exceeds
+ *     GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_WORKSPACE before anything is
+ *     enqueued (for bf16 scalar decay at d_k = 128: up to 7084 chunk-heads,
+ *     B * H * ceil(T / 64); per-channel decay: 1016).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on
+ *     one GPU (concurrent streams, or host threads sharing a device) race
+ *     and give unspecified results.  Calls in order on one stream are safe.
+ *     The array keeps the last call's contents; nothing in it needs to start
+ *     at zero.
+ *   - The current device must be the device of `stream` (the array of the
+ *     current device is used).  The first call on a device looks the array's
+ *     address up once (GDN_ERR_LAUNCH if the runtime refuses).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const void* alpha, const float* beta, const float* S0,
+                                 void* o, float* S_final,
+                                 int B, int T, int H, int dk, int dv, int chunk,
+                                 gdn_dtype dtype, gdn_decay mode, hipStream_t stream);
+
+/*
  * Bytes of device workspace gdn_chunk_fwd_varlen needs for N sequences with T
  * tokens in all (0 means the workspace pointer may be NULL).  It depends only
  * on N and T, not on how the tokens are split.  Returns 0 for arguments

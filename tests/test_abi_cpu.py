@@ -342,3 +342,32 @@ def test_backward_validation(lib):
     assert lib.gdn_chunk_bwd_workspace_bytes(2, 100, 3, 128, 128, 64, 1, 0) == need
     assert bwd(ws_bytes=need - 1) == E_WS
     assert bwd(B=0) == OK
+
+
+def test_noalloc_validation(lib):
+    """gdn_chunk_fwd_noalloc validates exactly as gdn_chunk_fwd and rejects a
+    call whose records exceed the scratch array before touching the device."""
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f = lib.gdn_chunk_fwd_noalloc
+    f.argtypes = [vp] * 8 + [i] * 8 + [vp]
+    f.restype = i
+    q, k, v, a, b, s0, o, sf = _bufs()
+
+    def call(B=2, T=100, H=3, dk=128, dv=128, chunk=64, dtype=1, mode=1, ptrs=None):
+        p = ptrs if ptrs is not None else (q, k, v, a, b, s0, o, sf)
+        return f(*p, B, T, H, dk, dv, chunk, dtype, mode, None)
+
+    scratch = 64 << 20
+    per = _ws_bytes(1, 64, 1, 2)                           # one bf16 scalar-decay record
+    assert scratch // per == 7084
+    assert call(B=1, T=64 * 7085, H=1) == E_WS             # one record too many
+    assert call(B=8, T=4096, H=16) == E_WS                 # 8192 records
+    assert call(B=1, T=64 * 1017, H=1, mode=2) == E_WS     # per-channel records are larger
+    assert call(dk=96) == E_UNSUP
+    assert call(chunk=32) == E_UNSUP
+    assert call(T=-1) == E_SHAPE
+    assert call(dtype=5) == E_DTYPE
+    assert call(ptrs=(0, k, v, a, b, s0, o, sf)) == E_NULL
+    assert call(ptrs=(q, k, v, a, b, s0, q + 64, sf)) == E_ALIAS
+    assert call(B=0) == OK and call(H=0) == OK
+    assert call(T=0, ptrs=(0, 0, 0, 0, 0, 0, 0, 0)) == OK  # nothing to write
