@@ -1404,7 +1404,8 @@ constexpr int kP1Ahead = 2;   // phase-1 fragments loaded this many k steps ahea
 constexpr int kFormPAhead = 2;   // fragments of P's product loaded this many k steps ahead
 
 template <typename E, int DK, int DVS, int MODE, bool NORM>
-__global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws) {
+__global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws, int npart,
+                                                             float lead_r) {
   static_assert(sizeof(E) == 2, "the eight-wave kernel is bf16");
   constexpr bool KDA = MODE >= 2;
   constexpr bool G2 = MODE == 3;   // Gated DeltaNet-2: V is scaled by the write gate
@@ -1452,22 +1453,41 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   const int H = a.H, dv = a.dv;
   const int nsl = dv / DVS;
   const int nheads = a.B * H;
-  // Workgroups are dispatched round-robin over the eight XCDs: give the slices
-  // of one head the same XCD (same L2) when the head count allows it.
-  int head, sl;
+  // Workgroups are dispatched round-robin over the eight XCDs: give the
+  // workgroups of one head the same XCD (same L2) when the head count allows it.
+  const int per_head = nsl * npart;
+  int head, rw;
   if ((nheads & 7) == 0) {
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    head = xcd + 8 * (j / nsl);
-    sl = j % nsl;
+    head = xcd + 8 * (j / per_head);
+    rw = j % per_head;
   } else {
-    head = blockIdx.x / nsl;
-    sl = blockIdx.x % nsl;
+    head = blockIdx.x / per_head;
+    rw = blockIdx.x % per_head;
   }
+  const int sl = rw % nsl, part = rw / nsl;
   const int h = head % H, b = head / H;
   const int i0 = sl * DVS;
   const Span sp = seq_span(a, b, h);
   const int T = sp.len;   // tokens of this sequence
   const int nchunks = (T + C - 1) / C;
+  // Parts of a value slice (used when the slices alone leave compute units
+  // idle): part p writes the outputs of chunks [m_p, m_p+1) and reaches its
+  // starting state by running the state recurrence alone over chunks
+  // [0, m_p) (no Q, P or O), with the same products in the same order as the
+  // full pass, so it starts from the very state the full pass holds there.
+  // With a lead-in chunk costing lead_r of a full one, the split
+  // m_p = N (1 - (1 - r)^p) / (1 - (1 - r)^npart) gives every part the same time.
+  auto split = [&](int p) {
+    if (p <= 0) return 0;
+    if (p >= npart) return nchunks;
+    const float q = 1.f - lead_r;
+    const float f = (1.f - __powf(q, (float)p)) / (1.f - __powf(q, (float)npart));
+    return min(nchunks, max(0, (int)((float)nchunks * f + 0.5f)));
+  };
+  const int n_so = split(part), n_end = split(part + 1);   // lead-in [0, n_so), outputs [n_so, n_end)
+  using Full = std::false_type;
+  using Lead = std::true_type;
   const size_t v_tok = (size_t)H * dv;
   const size_t sbase = ((size_t)b * H + h) * dv + i0;
 
@@ -1511,13 +1531,14 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       }
       pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(ptid, NG4 - 1));
     };
-    auto load_qv = [&](int n) __attribute__((always_inline)) {
+    // (so: the lead-in, which needs no Q and no P)
+    auto load_qv = [&](int n, auto so) __attribute__((always_inline)) {
       const int t0 = n * C;
       const int rmax = min(C, T - t0) - 1;
       const E* rq = recs + (size_t)n * R::elems;
       const E* qq = qg + (size_t)t0 * qk_tok;
 #pragma unroll
-      for (int m = 0; m < KPT; ++m) {
+      for (int m = 0; m < (decltype(so)::value ? 0 : KPT); ++m) {
         const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
         if constexpr (KDA)
           pq[m] = *reinterpret_cast<const u32x4*>(rq + R::qg + (uint32_t)r * DK + cc * EPC);
@@ -1533,17 +1554,17 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
           pw[m] = ld_once(wg + (size_t)t0 * v_tok + (uint32_t)min(r, rmax) * (uint32_t)v_tok + cc * EPC);
       }
     };
-    auto load_tp = [&](int n) __attribute__((always_inline)) {
+    auto load_tp = [&](int n, auto so) __attribute__((always_inline)) {
       const E* rq = recs + (size_t)n * R::elems;
 #pragma unroll
       for (int m = 0; m < TBT; ++m) {
         pt[m] = *reinterpret_cast<const u32x4*>(rq + R::t + (ptid + PT * m) * EPC);
-        if constexpr (KDA) pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (ptid + PT * m) * EPC);
+        if constexpr (KDA && !decltype(so)::value) pp[m] = *reinterpret_cast<const u32x4*>(rq + R::p + (ptid + PT * m) * EPC);
       }
     };
     // Rows of a chunk into buffer gb: Q, the state update's K operand (K, or
     // Kc), the per-channel phase-1 K operand, V, and the gates.
-    auto commit_rows = [&](int gb) __attribute__((always_inline)) {
+    auto commit_rows = [&](int gb, auto so) __attribute__((always_inline)) {
       E* Qr = Qrb + gb * C * LDK;
       E* Ks = Ksb + gb * C * LDKS;
       E* Kr = Krb + gb * C * LDK;
@@ -1552,7 +1573,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       for (int m = 0; m < KPT; ++m) {
         const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
         const int o = r * LDK + cc * EPC;
-        *reinterpret_cast<u32x4*>(Qr + o) = pq[m];
+        if constexpr (!decltype(so)::value) *reinterpret_cast<u32x4*>(Qr + o) = pq[m];
         *reinterpret_cast<u32x4*>(Ks + r * LDKS + swz_col(r, cc * EPC)) = KDA ? pkc[m] : pk[m];
         if constexpr (KDA) *reinterpret_cast<u32x4*>(Kr + o) = pk[m];
       }
@@ -1564,12 +1585,12 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * GS + 4 * ptid) = pg;
     };
     // T (and the per-channel P) of a chunk.
-    auto commit_tp = [&]() __attribute__((always_inline)) {
+    auto commit_tp = [&](auto so) __attribute__((always_inline)) {
 #pragma unroll
       for (int m = 0; m < TBT; ++m) {
         const int q = ptid + PT * m, r = q / CPT, cc = q % CPT;
         *reinterpret_cast<u32x4*>(Tm + r * LDT + cc * EPC) = pt[m];
-        if constexpr (KDA) {
+        if constexpr (KDA && !decltype(so)::value) {
           uint2* d = reinterpret_cast<uint2*>(Pmb + r * LDP + cc * EPC);
           d[0] = make_uint2(pp[m][0], pp[m][1]);
           d[1] = make_uint2(pp[m][2], pp[m][3]);
@@ -1645,42 +1666,51 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         st_once(oq + (uint32_t)r * (uint32_t)v_tok + cc * EPC, os_piece(r, cc));
       }
     };
-    // One chunk step.  The LDS writes of interval A use data loaded at least
-    // one interval earlier; the first step (nothing to flush) is peeled so that
-    // no global access in the loop is conditional.
-    auto step = [&](int n, auto first) __attribute__((always_inline)) {
+    // One chunk step of a pass whose last chunk is nlast.  The LDS writes of
+    // interval A use data loaded at least one interval earlier; the first step
+    // (nothing to flush) is peeled so that no global access in the loop is
+    // conditional.
+    auto step = [&](int n, int nlast, auto first, auto so) __attribute__((always_inline)) {
+      constexpr bool SO = decltype(so)::value;
       // interval A: the chain runs phase 1 of chunk n
-      if (n + 1 < nchunks) commit_rows((n + 1) & 1);
-      commit_tp();                   // T (and P) of chunk n
-      if constexpr (!decltype(first)::value) flush_o((n - 1) * C);
-      load_k(min(n + 2, nchunks - 1));
+      if (n + 1 <= nlast) commit_rows((n + 1) & 1, so);
+      commit_tp(so);                 // T (and P) of chunk n
+      if constexpr (!SO && !decltype(first)::value) flush_o((n - 1) * C);
+      load_k(min(n + 2, nlast));
       __syncthreads();
       // interval B: the chain runs U, O and S of chunk n
-      load_tp(min(n + 1, nchunks - 1));
-      load_qv(min(n + 2, nchunks - 1));
-      if constexpr (!KDA) {
-        if (n + 1 < nchunks) form_p((n + 1) & 1);
+      load_tp(min(n + 1, nlast), so);
+      load_qv(min(n + 2, nlast), so);
+      if constexpr (!KDA && !SO) {
+        if (n + 1 <= nlast) form_p((n + 1) & 1);
       }
       __syncthreads();
     };
+    auto prologue = [&](int n0, int nlast, auto so) __attribute__((always_inline)) {
+      load_k(n0);
+      load_qv(n0, so);
+      commit_rows(n0 & 1, so);
+      load_k(min(n0 + 1, nlast));
+      load_qv(min(n0 + 1, nlast), so);
+      load_tp(n0, so);
+    };
 
-    if (nchunks > 0) {
-      load_k(0);
-      load_qv(0);
-      commit_rows(0);
-      load_k(min(1, nchunks - 1));
-      load_qv(min(1, nchunks - 1));
-      load_tp(0);
+    if (n_so > 0) {   // lead-in: the state alone over chunks [0, n_so)
+      prologue(0, n_so - 1, Lead{});
+      __syncthreads();
+      __syncthreads();
+      for (int n = 0; n < n_so; ++n) step(n, n_so - 1, std::true_type{}, Lead{});
     }
+    if (n_end > n_so) prologue(n_so, n_end - 1, Full{});
     __syncthreads();
     if constexpr (!KDA) {
-      if (nchunks > 0) form_p(0);
+      if (n_end > n_so) form_p(n_so & 1);
     }
     __syncthreads();
-    if (nchunks > 0) step(0, std::true_type{});
-    for (int n = 1; n < nchunks; ++n) step(n, std::false_type{});
-    if (nchunks > 0) {   // the last chunk's rows
-      const int t0f = (nchunks - 1) * C, cnf = T - t0f;
+    if (n_end > n_so) step(n_so, n_end - 1, std::true_type{}, Full{});
+    for (int n = n_so + 1; n < n_end; ++n) step(n, n_end - 1, std::false_type{}, Full{});
+    if (n_end > n_so) {   // the last chunk's rows
+      const int t0f = (n_end - 1) * C, cnf = min(C, T - t0f);
       E* oq = og + (size_t)t0f * v_tok;
       for (int q = ptid; q < C * CPO; q += PT) {
         const int r = q / CPO, cc = q % CPO;
@@ -1723,10 +1753,9 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       }
     }
   }
-  __syncthreads();
-  __syncthreads();   // the data waves form P of the first chunk
-
-  for (int n = 0; n < nchunks; ++n) {
+  // One chunk of the chain (so: a lead-in chunk, X, U and S only).
+  auto chunk = [&](int n, auto so) __attribute__((always_inline)) {
+    constexpr bool SO = decltype(so)::value;
     const int nb = n & 1;
     const float* G = Gbuf + nb * GS;
     const float* Eg = G + C;       // exp(G_r) nk_r
@@ -1753,9 +1782,13 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       // O^T columns are the chunk rows r: exp(G_r) (normalised q: exp(G_r) and,
       // after the intra-chunk part, nq_r)
       const float egr = KDA ? 1.f : (NORM ? G[3 * C + own_rb * 32 + col] : Eg[own_rb * 32 + col]);
-      tile_nt2_shared_b<DK / 16, E, true, kP1Ahead, !KDA>(xacc, oacc, K1 + own_rb * 32 * (KDA ? LDK : LDKS),
-                                                           Qr + own_rb * 32 * LDK, KDA ? LDK : LDKS, LDK,
-                                          Sb + own_ib * 32 * LDSB, LDSB, lane);
+      if constexpr (SO)
+        tile_nt_k<DK / 16, E, !KDA, kP1Ahead>(xacc, K1 + own_rb * 32 * (KDA ? LDK : LDKS), KDA ? LDK : LDKS,
+                                             Sb + own_ib * 32 * LDSB, LDSB, lane);
+      else
+        tile_nt2_shared_b<DK / 16, E, true, kP1Ahead, !KDA>(xacc, oacc, K1 + own_rb * 32 * (KDA ? LDK : LDKS),
+                                                             Qr + own_rb * 32 * LDK, KDA ? LDK : LDKS, LDK,
+                                                             Sb + own_ib * 32 * LDSB, LDSB, lane);
       const int i = own_ib * 32 + col;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -1765,7 +1798,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
         store4(Xt + i * LDT + r0, v4.x - eg[g].x * xacc[4 * g + 0], v4.y - eg[g].y * xacc[4 * g + 1],
                v4.z - eg[g].z * xacc[4 * g + 2], v4.w - eg[g].w * xacc[4 * g + 3]);
       }
-      if constexpr (!KDA) {
+      if constexpr (!KDA && !SO) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[v] *= egr;
       }
@@ -1784,7 +1817,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       }
     }
     bf16x8 pa[2][2], ka[NST][2][2];  // P rows of the wave's O tile; K^T of its state tiles
-    if (own_rb >= 0) {
+    if (own_rb >= 0 && !SO) {
       const E* prow = Pm + (own_rb * 32 + col) * LDP;
 #pragma unroll
       for (int rj = 0; rj < 2; ++rj)
@@ -1835,7 +1868,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     }
 
     // ---- O^T = O_inter^T + U^T P^T for the wave's tile, staged for the data waves ----
-    if (own_rb >= 0) {
+    if (own_rb >= 0 && !SO) {
 #pragma unroll
       for (int rj = 0; rj < 2; ++rj) {
         if (rj > own_rb) break;
@@ -1887,9 +1920,18 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       }
     }
     __syncthreads();
-  }
+  };
 
-  if (a.S_final) {
+  if (n_so > 0) {   // lead-in
+    __syncthreads();
+    __syncthreads();
+    for (int n = 0; n < n_so; ++n) chunk(n, Lead{});
+  }
+  __syncthreads();
+  __syncthreads();   // the data waves form P of the first chunk
+  for (int n = n_so; n < n_end; ++n) chunk(n, Full{});
+
+  if (a.S_final && part == npart - 1) {
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       const int t = wave + 4 * st;
@@ -1906,27 +1948,48 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   }
 }
 
+// Lead-in chunk cost relative to a full chunk of the eight-wave kernel
+// (measured on the long-context workload): sets where the parts of a value
+// slice split the sequence.
+constexpr float kLeadCost = 0.65f;
+
+// Parts per value slice: while the slices fill at most half of the compute
+// units, each slice is split in two parts more.
+inline int state_parts(size_t slices) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 1;
+  int np = 1;
+  while (np < 4 && slices * (size_t)(2 * np) <= (size_t)cus) np *= 2;
+  return np;
+}
+
 template <typename E, int DK, int DVS>
 hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) {
-  dim3 grid((unsigned)((size_t)a.B * a.H * (a.dv / DVS))), block(kThreads);
+  const size_t slices = (size_t)a.B * a.H * (a.dv / DVS);
+  dim3 grid((unsigned)slices), block(kThreads);
   if constexpr (sizeof(E) == 2) {
+    const int np = state_parts(slices);
+    grid = dim3((unsigned)(slices * np));
+    const float r = kLeadCost;
     dim3 wblock(kWsThreads);
     // (normalised q and k: the per-channel records carry normalised operands, so
     // only the scalar / no-decay state kernel has a variant of its own)
     const bool nrm = a.pro.qk_norm != 0;
     if (a.mode == 0 && !nrm)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, false>), grid, wblock, 0, stream, a, tws);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, false>), grid, wblock, 0, stream, a, tws, np, r);
     else if (a.mode == 0)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, true>), grid, wblock, 0, stream, a, tws);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, true>), grid, wblock, 0, stream, a, tws, np, r);
     else if (a.mode == 1 && !nrm)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws, np, r);
     else if (a.mode == 1)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws, np, r);
     else if constexpr (DVS == 32) {   // the per-channel buffers leave room for 32-row slices only
       if (a.mode == 2)
-        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws);
+        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws, np, r);
       else
-        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws);
+        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws, np, r);
     } else {
       return hipErrorInvalidConfiguration;
     }

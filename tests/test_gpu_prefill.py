@@ -79,9 +79,9 @@ def test_prefill_channel_gates_at_boundary_values(gpu, dtype, dk):
 
 def test_prefill_kda_workload_sampled(gpu):
     """B=4, H=16, T=8192, d=128, bf16, per-channel decay: all heads on the GPU,
-    four checked."""
+    eight checked (outputs and final states)."""
     w = W.KDA_BF16_PREFILL
-    heads = [(0, 0), (1, 9), (2, 4), (3, 15)]
+    heads = [(0, 0), (0, 11), (1, 2), (1, 9), (2, 4), (2, 13), (3, 6), (3, 15)]
     eo, eS = check_prefill(gpu, W.make_prefill(w), w.mode, w.dtype, heads=heads)
     print("kda bf16 b4 h16 t8192: rel err o %.2e, S %.2e" % (eo, eS))
 
@@ -102,13 +102,16 @@ def test_prefill_gdn_bf16_workload_sampled(gpu):
 
 
 def test_prefill_long_context_and_decode_handoff(gpu):
-    """B=1, H=32, T=65536, d=128, bf16: two heads checked, then one decode step
-    from the GPU's final state against the oracle's decode from its own."""
+    """B=1, H=32, T=65536, d=128, bf16: eight heads checked (outputs and the
+    final state itself), then one decode step from the GPU's final state against
+    the oracle's decode from its own."""
     w = W.GDN_BF16_LONG
     inp = W.make_prefill(w)
-    heads = [(0, 3), (0, 30)]
+    heads = [(0, h) for h in (0, 3, 7, 12, 17, 22, 27, 30)]
     dev = to_dev(inp)
     o, S = gpu.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["S0"])
+    torch.cuda.synchronize()
+    S_fin = S[0].cpu().numpy()   # the decode step below updates S in place
     tok = W.make_decode(W.Decode("next", 1, 32, 128, 128, 1, torch.bfloat16, "range095", 0.0, 55))
     o1 = gpu.decode_step(tok["q"][0].cuda(), tok["k"][0].cuda(), tok["v"][0].cuda(),
                          tok["alpha"][0].cuda(), tok["beta"][0].cuda(), S)
@@ -118,15 +121,18 @@ def test_prefill_long_context_and_decode_handoff(gpu):
     o_s = np.stack([o[0, :, h].float().cpu().numpy() for _, h in heads])[:, :, None]
     eo = rel_o(o_s, ro)
     hs = [h for _, h in heads]
-    ro1, rS1 = oracle.gdn_decode(tok["q"][0][:, hs].reshape(2, 1, 128), tok["k"][0][:, hs].reshape(2, 1, 128),
-                                 tok["v"][0][:, hs].reshape(2, 1, 128), tok["alpha"][0][:, hs].reshape(2, 1),
-                                 tok["beta"][0][:, hs].reshape(2, 1), rS, mode=1)
+    nh = len(hs)
+    eSf = rel_S(S_fin[hs][:, None], rS)
+    ro1, rS1 = oracle.gdn_decode(tok["q"][0][:, hs].reshape(nh, 1, 128), tok["k"][0][:, hs].reshape(nh, 1, 128),
+                                 tok["v"][0][:, hs].reshape(nh, 1, 128), tok["alpha"][0][:, hs].reshape(nh, 1),
+                                 tok["beta"][0][:, hs].reshape(nh, 1), rS, mode=1)
     S_s = S[0, hs].cpu().numpy()[:, None]
     eS = rel_S(S_s, rS1)
     e1 = W.per_head_rel_err(o1[0, hs].float().cpu().numpy()[:, None], ro1, (0, 1))
-    print("gdn bf16 b1 h32 t65536: rel err o %.2e, S after decode %.2e, decode o %.2e" % (eo, eS, e1))
+    print("gdn bf16 b1 h32 t65536: rel err o %.2e, S_final %.2e, S after decode %.2e, decode o %.2e"
+          % (eo, eSf, eS, e1))
     tol = TOL[torch.bfloat16]
-    assert eo <= tol and eS <= tol and e1 <= tol
+    assert eo <= tol and eSf <= tol and eS <= tol and e1 <= tol
 
 
 def test_prefill_empty_sequence_copies_state(gpu):
