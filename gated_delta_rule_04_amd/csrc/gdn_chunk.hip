@@ -157,7 +157,7 @@ __device__ inline void st_once(void* p, const u32x4& v) {
 //     1  exp(G_r) nk_r          X = V - diag(row 1) K S^T
 //     2  exp(G_C - G_r) nk_r    S_{n+1} = gamma_C S_n + U^T diag(row 2) K
 //     3  exp(G_r) nq_r          O_inter = diag(row 3) Q S^T
-//     4  nk_r                   P[r][j] = exp(G_r - G_j) nq_r nk_j (q_r . k_j)
+//     4  G_r - ln nk_r          P[r][j] = exp(G_r - row 4_j) nq_r (q_r . k_j)
 //   nk_r and nq_r are 1 / sqrt(|k_r|^2 + eps) and 1 / sqrt(|q_r|^2 + eps) when
 //   the kernels normalise q and k, else 1.  The bf16 records hold nq = 1: that
 //   state kernel forms P itself and applies nq to its output rows.
@@ -206,17 +206,6 @@ __device__ inline float sumsq16(const u32x4& u) {
     }
   }
   return s;
-}
-
-// 1 / sqrt(|x|^2 + eps) of a row of N elements of the operand dtype in LDS,
-// 16 bytes at a time (one lane per row).
-template <typename E, int N>
-__device__ inline float inv_norm_row(const E* row, float eps) {
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < N * (int)sizeof(E) / 16; ++i)
-    ss += sumsq16<E>(*reinterpret_cast<const u32x4*>(row + i * (16 / (int)sizeof(E))));
-  return __builtin_amdgcn_rsqf(ss + eps);
 }
 
 // log alpha of one gate value of head h (channel c for a per-channel gate): the
@@ -281,7 +270,7 @@ struct PrepPlan {
 };
 
 template <typename E, int DK, int MODE, bool NORM>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* __restrict__ tws,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void chunk_prep_kernel(PrefillArgs a, E* __restrict__ tws,
                                                               int nchunks) {
   using L = PrepPlan<E, DK, NORM>;
   using R = GateRec<E>;
@@ -315,7 +304,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
   // P's rows of them are never used).  K takes ordinary loads: the state
   // kernel reads it again right after this kernel, and K plus the records fit
   // the last-level cache at the batched workload's size (the non-temporal
-  // hint cost that second read 3-4 % of the call).
+  // hint cost that second read 3-4 % of the call).  Normalised q and k: the
+  // inverse norms come from the loaded registers, summed over the CPR lanes
+  // that hold a row.
   {
     const E* kg = static_cast<const E*>(a.k) + (tok0 * H + h) * DK;
     const E* qg = static_cast<const E*>(a.q) + (tok0 * H + h) * DK;
@@ -326,8 +317,21 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
     for (int m = 0; m < C * CPR / kThreads; ++m) {
       const int q = tid + kThreads * m, r = q / CPR, cc = q % CPR;
       const size_t off = (size_t)min(r, cn - 1) * ktok + cc * EPC;
-      *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = *reinterpret_cast<const u32x4*>(kg + off);
-      if constexpr (WP) *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = ld_once(qg + off);
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kg + off);
+      *reinterpret_cast<u32x4*>(Kr + r * LDK + cc * EPC) = kv;
+      u32x4 qv = kv;
+      if constexpr (WP) {
+        qv = ld_once(qg + off);
+        *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = qv;
+      }
+      if constexpr (NORM) {
+        const float nk = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(kv)) + a.pro.norm_eps);
+        if (cc == 0) Nk[r] = nk;
+        if constexpr (WP) {
+          const float nq = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(qv)) + a.pro.norm_eps);
+          if (cc == 0) Nq[r] = nq;
+        }
+      }
     }
   }
   if (wave == 0) {
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
       gw[C + lane] = eg;
       gw[2 * C + lane] = __expf(gC - g);
       gw[3 * C + lane] = eg;
-      gw[4 * C + lane] = 1.f;
+      gw[4 * C + lane] = g;
     }
   }
   __syncthreads();
@@ -363,13 +367,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
                               Qr + rb * 32 * LDK, LDK, lane);
     else
       tile_nt_k<DK / 16>(acca, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
-  }
-  if constexpr (NORM) {
-    // wave 3, idle during the tile products: inverse norms, lane r takes row r
-    if (wave == 3) {
-      Nk[lane] = inv_norm_row<E, DK>(Kr + lane * LDK, a.pro.norm_eps);
-      if constexpr (WP) Nq[lane] = inv_norm_row<E, DK>(Qr + lane * LDK, a.pro.norm_eps);
-    }
   }
   __syncthreads();   // K and Q are dead: A takes their bytes
   // A[r][j] = beta_r exp(G_r - G_j) k_r.k_j (j < r); P[r][j] = exp(G_r - G_j) q_r.k_j
@@ -427,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrefillArgs a, E* 
       gw[C + lane] = eg * nk;
       gw[2 * C + lane] = __expf(G[C - 1] - g) * nk;
       gw[3 * C + lane] = WP ? eg * Nq[lane] : eg;
-      gw[4 * C + lane] = nk;
+      gw[4 * C + lane] = g - __logf(nk);
     }
   }
   __syncthreads();
@@ -1606,9 +1603,16 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       const int d = wave - 4;
       if (d >= 3) {
         // normalised q: the fourth data wave takes the inverse norms of the
-        // chunk's Q rows meanwhile (lane r reads row r), for the chain's output
-        if constexpr (NORM)
-          Gbuf[gb * GS + 5 * C + lane] = inv_norm_row<E, DK>(Qrb + gb * C * LDK + lane * LDK, a.pro.norm_eps);
+        // chunk's Q rows meanwhile, for the chain's output rows: lane r sums
+        // row r, all lanes reading the same 16-byte piece index at a time (the
+        // row stride puts 16 consecutive rows in distinct banks).
+        if constexpr (NORM) {
+          const E* row = Qrb + gb * C * LDK + lane * LDK;
+          float ss = 0.f;
+#pragma unroll
+          for (int p = 0; p < CPR; ++p) ss += sumsq16<E>(*reinterpret_cast<const u32x4*>(row + p * EPC));
+          Gbuf[gb * GS + 5 * C + lane] = __builtin_amdgcn_rsqf(ss + a.pro.norm_eps);
+        }
         return;
       }
       const int jb = d == 2 ? 1 : 0, rb = d == 0 ? 0 : 1;
@@ -1621,23 +1625,19 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       const float Gr = Gl[r];
       // Every weight is formed (clamped to at most 1) before the mask selects:
       // left conditional, the gate loads sink into per-element branches.
-      // Normalised q and k: the column factor nk_j joins the weight (nq_r is
-      // applied to the output rows).
+      // Normalised q and k: the column factor nk_j joins the exponent (the
+      // record's row 4 holds G_j - ln nk_j; the clamp then only keeps masked
+      // weights finite) and nq_r is applied to the output rows.
+      constexpr int GJ = NORM ? 4 * C : 0;
+      constexpr float WMAX = NORM ? 88.f : 0.f;
       float w[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 gj = *reinterpret_cast<const float4*>(Gl + jb * 32 + acc_row(g, 0, lane));
-        w[4 * g + 0] = __expf(fminf(Gr - gj.x, 0.f));
-        w[4 * g + 1] = __expf(fminf(Gr - gj.y, 0.f));
-        w[4 * g + 2] = __expf(fminf(Gr - gj.z, 0.f));
-        w[4 * g + 3] = __expf(fminf(Gr - gj.w, 0.f));
-        if constexpr (NORM) {
-          const float4 nj = *reinterpret_cast<const float4*>(Gl + 4 * C + jb * 32 + acc_row(g, 0, lane));
-          w[4 * g + 0] *= nj.x;
-          w[4 * g + 1] *= nj.y;
-          w[4 * g + 2] *= nj.z;
-          w[4 * g + 3] *= nj.w;
-        }
+        const float4 gj = *reinterpret_cast<const float4*>(Gl + GJ + jb * 32 + acc_row(g, 0, lane));
+        w[4 * g + 0] = __expf(fminf(Gr - gj.x, WMAX));
+        w[4 * g + 1] = __expf(fminf(Gr - gj.y, WMAX));
+        w[4 * g + 2] = __expf(fminf(Gr - gj.z, WMAX));
+        w[4 * g + 3] = __expf(fminf(Gr - gj.w, WMAX));
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) asm volatile("" ::"v"(w[v]));
