@@ -1722,14 +1722,20 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   }
 
   // ======================= chain waves =======================
-  // X and O tiles of row block own_rb and value block own_ib belong to one
-  // wave; its state tiles t = wave + 4 st all lie in value block ub.
-  int own_rb = -1, own_ib = 0;
+  // Phase-1 tiles of value block own_ib: the X tile of row block x_rb and the
+  // O tile of row block o_rb.  Two value blocks: wave (rb, ib) takes both
+  // tiles of (rb, ib), the two products sharing their S fragments.  One value
+  // block: waves 0 and 1 take the X tiles, waves 2 and 3 the O tiles, one
+  // product each (half the MFMA chain per wave; S is read twice).  The wave's
+  // state tiles t = wave + 4 st all lie in value block ub.
+  int x_rb = -1, o_rb = -1, own_ib = 0;
   if (NI == 2) {
-    own_rb = wave >> 1;
+    x_rb = o_rb = wave >> 1;
     own_ib = wave & 1;
   } else if (wave < 2) {
-    own_rb = wave;
+    x_rb = wave;
+  } else {
+    o_rb = wave - 2;
   }
   const int ub = NI == 2 ? (wave & 1) : 0;
 
@@ -1768,35 +1774,45 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
 
     // ---- interval A, phase 1: X = V - diag(gamma) K S^T, O_inter^T = S (diag(gamma) Q)^T ----
     f32x16 xacc = zero16(), oacc = zero16();
-    if (own_rb >= 0) {
+    const bool do_x = x_rb >= 0, do_o = o_rb >= 0 && !SO;
+    if (do_x || do_o) {
       // the V columns and gate rows of the epilogue are read before the product
       const int vc = own_ib * 32 + 16 * ((lane >> 4) & 1);
       uint2 vw[4];
       float4 eg[4];
+      if (do_x) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = own_rb * 32 + acc_row(g, 0, lane);
-        vw[g] = tr_read4(Vr, LDV, r0, vc, lane);   // V[r0 .. r0 + 3][i]
-        eg[g] = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = x_rb * 32 + acc_row(g, 0, lane);
+          vw[g] = tr_read4(Vr, LDV, r0, vc, lane);   // V[r0 .. r0 + 3][i]
+          eg[g] = KDA ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(Eg + r0);
+        }
       }
       // O^T columns are the chunk rows r: exp(G_r) (normalised q: exp(G_r) and,
       // after the intra-chunk part, nq_r)
-      const float egr = KDA ? 1.f : (NORM ? G[3 * C + own_rb * 32 + col] : Eg[own_rb * 32 + col]);
-      if constexpr (SO)
-        tile_nt_k<DK / 16, E, !KDA, kP1Ahead>(xacc, K1 + own_rb * 32 * (KDA ? LDK : LDKS), KDA ? LDK : LDKS,
-                                             Sb + own_ib * 32 * LDSB, LDSB, lane);
-      else
-        tile_nt2_shared_b<DK / 16, E, true, kP1Ahead, !KDA>(xacc, oacc, K1 + own_rb * 32 * (KDA ? LDK : LDKS),
-                                                             Qr + own_rb * 32 * LDK, KDA ? LDK : LDKS, LDK,
-                                                             Sb + own_ib * 32 * LDSB, LDSB, lane);
-      const int i = own_ib * 32 + col;
+      const float egr = KDA || !do_o ? 1.f : (NORM ? G[3 * C + o_rb * 32 + col] : Eg[o_rb * 32 + col]);
+      const E* Sf = Sb + own_ib * 32 * LDSB;
+      if (NI == 1 || SO) {
+        if (do_x)
+          tile_nt_k<DK / 16, E, !KDA, kP1Ahead>(xacc, K1 + x_rb * 32 * (KDA ? LDK : LDKS), KDA ? LDK : LDKS, Sf,
+                                               LDSB, lane);
+        else   // (the operand order of the shared-fragment product's second tile)
+          tile_nt_k<DK / 16, E, false, kP1Ahead>(oacc, Sf, LDSB, Qr + o_rb * 32 * LDK, LDK, lane);
+      } else {
+        tile_nt2_shared_b<DK / 16, E, true, kP1Ahead, !KDA>(xacc, oacc, K1 + x_rb * 32 * (KDA ? LDK : LDKS),
+                                                             Qr + o_rb * 32 * LDK, KDA ? LDK : LDKS, LDK, Sf,
+                                                             LDSB, lane);
+      }
+      if (do_x) {
+        const int i = own_ib * 32 + col;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = own_rb * 32 + acc_row(g, 0, lane);
-        const float4 v4 = make_float4(__uint_as_float(vw[g].x << 16), __uint_as_float(vw[g].x & 0xffff0000u),
-                                      __uint_as_float(vw[g].y << 16), __uint_as_float(vw[g].y & 0xffff0000u));
-        store4(Xt + i * LDT + r0, v4.x - eg[g].x * xacc[4 * g + 0], v4.y - eg[g].y * xacc[4 * g + 1],
-               v4.z - eg[g].z * xacc[4 * g + 2], v4.w - eg[g].w * xacc[4 * g + 3]);
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = x_rb * 32 + acc_row(g, 0, lane);
+          const float4 v4 = make_float4(__uint_as_float(vw[g].x << 16), __uint_as_float(vw[g].x & 0xffff0000u),
+                                        __uint_as_float(vw[g].y << 16), __uint_as_float(vw[g].y & 0xffff0000u));
+          store4(Xt + i * LDT + r0, v4.x - eg[g].x * xacc[4 * g + 0], v4.y - eg[g].y * xacc[4 * g + 1],
+                 v4.z - eg[g].z * xacc[4 * g + 2], v4.w - eg[g].w * xacc[4 * g + 3]);
+        }
       }
       if constexpr (!KDA && !SO) {
 #pragma unroll
@@ -1817,8 +1833,8 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       }
     }
     bf16x8 pa[2][2], ka[NST][2][2];  // P rows of the wave's O tile; K^T of its state tiles
-    if (own_rb >= 0 && !SO) {
-      const E* prow = Pm + (own_rb * 32 + col) * LDP;
+    if (o_rb >= 0 && !SO) {
+      const E* prow = Pm + (o_rb * 32 + col) * LDP;
 #pragma unroll
       for (int rj = 0; rj < 2; ++rj)
 #pragma unroll
@@ -1868,14 +1884,14 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     }
 
     // ---- O^T = O_inter^T + U^T P^T for the wave's tile, staged for the data waves ----
-    if (own_rb >= 0 && !SO) {
+    if (o_rb >= 0 && !SO) {
 #pragma unroll
       for (int rj = 0; rj < 2; ++rj) {
-        if (rj > own_rb) break;
+        if (rj > o_rb) break;
 #pragma unroll
         for (int s = 0; s < 2; ++s) mma_bf16(oacc, uf[rj][s], pa[rj][s]);
       }
-      const int r = own_rb * 32 + col;
+      const int r = o_rb * 32 + col;
       if constexpr (NORM) {
         const float nq = G[5 * C + r];
 #pragma unroll
