@@ -526,7 +526,7 @@ def short_kernel_name(name: str) -> str:
     import re
     m = re.match(r"_ZN3gdn12_GLOBAL__N_1(\d+)(.*)", name)
     if not m:
-        return name.split("(")[0].replace("void ", "").replace("(anonymous namespace)::", "").strip()
+        return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
     n = int(m.group(1))
     base, rest = m.group(2)[:n], m.group(2)[n:]
     args = []
@@ -740,8 +740,9 @@ def main():
             fused["launch_us"], fused["plain_launch_us_same_period"]))
         gdn2 = bench_gdn2(W.KDA_BF16_PREFILL, args.steps)
         log("gated deltanet-2: %.1f us per launch" % gdn2["launch_us"])
-        bwd = bench_backward(W.GDN_BF16_PREFILL, max(2, args.steps // 4))
-        log("backward: %.1f us per launch" % bwd["launch_us"])
+        bwd = [bench_backward(w, max(2, args.steps // 4)) for w in (W.GDN_BF16_PREFILL, W.KDA_BF16_PREFILL)]
+        for x in bwd:
+            log("backward %s: %.1f us per launch" % (x["workload"], x["launch_us"]))
     torch.cuda.empty_cache()
 
     sec, host, outs = head

@@ -35,10 +35,10 @@ struct BackwardArgs {
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, int mode);
 hipError_t launch_backward(const BackwardArgs& a, void* workspace, hipStream_t stream);
 
-// The chunk-level backward (gdn_bwd_chunk.hip): bf16, no or scalar decay,
-// T > 0.  The token-level kernels take every other case.
+// The chunk-level backward (gdn_bwd_chunk.hip): bf16, no, scalar or
+// per-channel decay, T > 0.  The token-level kernels take every other case.
 bool chunk_backward_applies(int T, int dk, int dv, int dtype, int mode);
-size_t chunk_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+size_t chunk_backward_workspace_bytes(int B, int T, int H, int dk, int dv, int mode);
 hipError_t launch_chunk_backward(const BackwardArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace gdn

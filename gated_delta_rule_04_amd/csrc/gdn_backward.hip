@@ -469,7 +469,7 @@ hipError_t launch_dk(const BackwardArgs& a, void* ws, hipStream_t stream) {
 }  // namespace
 
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, int mode) {
-  if (chunk_backward_applies(T, dk, dv, dtype, mode)) return chunk_backward_workspace_bytes(B, T, H, dk, dv);
+  if (chunk_backward_applies(T, dk, dv, dtype, mode)) return chunk_backward_workspace_bytes(B, T, H, dk, dv, mode);
   return bwd_ws(B, T, H, dk, dv, mode).total;
 }
 

@@ -841,9 +841,25 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
           const float v = acc[4 * g + e];
           x[e] = isP ? (j0 + e <= r ? v : 0.f) : (j0 + e < r ? br * v : 0.f);
         }
-        if (isP) store4(Pm + r * LDT + j0, x[0], x[1], x[2], x[3]);
-        else store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
+        if (isP) {
+          store4(Pm + r * LDT + j0, x[0], x[1], x[2], x[3]);
+        } else {
+          store4(Am + r * LDA + j0, x[0], x[1], x[2], x[3]);
+          if (a.a_tilde) {   // (the backward) At itself, without beta
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = j0 + e < r ? acc[4 * g + e] : 0.f;
+            *reinterpret_cast<float4*>(a.a_tilde + (at.sp.rec0 + n) * (size_t)(C * C) + r * C + j0) =
+                make_float4(y[0], y[1], y[2], y[3]);
+          }
+        }
       }
+    }
+    if (a.a_tilde && wave == 2) {   // At rows 0..31, columns 32..63 are zero
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(a.a_tilde + (at.sp.rec0 + n) * (size_t)(C * C) + col * C + 32 +
+                                   acc_row(g, 0, lane)) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (wave >= 2) {   // P rows 0..31, columns 32..63 are zero
       const int q = tid - 128, r = q >> 2, j0 = 32 + 8 * (q & 3);

@@ -48,6 +48,10 @@ struct PrefillArgs {
   const int* cu_seqlens = nullptr;
   int nslots = 0;    // packed batch: chunk records per head, T / 64 + B
   Prologue pro;
+  // Per-channel decay, backward only: the per-channel prep kernel also writes
+  // each chunk's At[r][s] = sum_c k_r[c] k_s[c] exp(G_r[c] - G_s[c]) (s < r,
+  // else 0), fp32 [C][C] per record slot.  Null in the forward.
+  float* a_tilde = nullptr;
 };
 
 // Arguments of one decode launch: q, k [B, H, dk]; v, o [B, H, dv];

@@ -70,7 +70,7 @@ def test_backward_without_initial_state_or_final_gradient(gpu, mode):
     _check(_gpu(gpu, d, mode, with_dST=False), _ref(d, mode, with_dST=False), mode, 1e-4)
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 def test_backward_zero_beta_rows(gpu, mode):
     """Every third token writes nothing (beta = 0): diag(beta) is singular, so
     the chunk-level kernels must take M = (I + A)^-1 from the solve itself."""
@@ -90,6 +90,21 @@ def test_backward_strong_decay(gpu, dtype):
     _check(_gpu(gpu, d, 1), _ref(d, 1), 1, TOL[dtype])
 
 
+@pytest.mark.parametrize("gate", ["kda_literal", "kda_clamped"])
+def test_backward_per_channel_gates(gpu, gate):
+    """bf16 per-channel decay (the chunk-level path): the literal gate (median
+    alpha about 0.05, single channels decaying by hundreds of e-folds inside a
+    chunk) and the clamped one; 200 tokens over four chunks."""
+    w = W.Prefill("bwd", 2, 2, 200, 128, 128, torch.bfloat16, gate, 0.2, seed=131)
+    d = W.make_prefill(w)
+    g = torch.Generator().manual_seed(132)
+    d["do"] = torch.randn(2, 200, 2, 128, generator=g).to(torch.bfloat16)
+    d["dST"] = 0.5 * torch.randn(2, 2, 128, 128, generator=g)
+    print("backward bf16 per-channel gate %s" % gate, flush=True)
+    errs = _check(_gpu(gpu, d, 2), _ref(d, 2), 2, TOL[torch.bfloat16])
+    print({k: "%.2e" % v for k, v in errs.items()}, flush=True)
+
+
 def test_backward_empty_sequence(gpu):
     """T = 0: dS0 = dS_final, nothing else."""
     d = _inputs(2, 0, 2, 64, 64, torch.float32, 1, seed=121)
@@ -97,7 +112,7 @@ def test_backward_empty_sequence(gpu):
     assert np.array_equal(g["dS0"], d["dST"].numpy())
 
 
-@pytest.mark.parametrize("mode", [1, 2], ids=["chunk_level", "token_level"])
+@pytest.mark.parametrize("mode", [1, 2], ids=["scalar", "per_channel"])
 def test_backward_is_deterministic(gpu, mode):
     d = _inputs(2, 150, 2, 128, 128, torch.bfloat16, mode, seed=122)
     a, b = _gpu(gpu, d, mode), _gpu(gpu, d, mode)
@@ -105,7 +120,7 @@ def test_backward_is_deterministic(gpu, mode):
         assert a[k] is None or np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 def test_backward_eight_heads(gpu, mode):
     """B * H a multiple of 8 (the chains group a head's value slices by XCD):
     every head against the reference, several chunks and a ragged tail."""
@@ -139,3 +154,33 @@ def test_backward_workload_sampled(gpu):
             picked[key] = np.stack([x[b, :, h] for b, h in heads])[:, :, None]
     errs = _check(picked, ref, 1, 2e-2)
     print("backward gdn bf16 b8 h16 t4096: %s" % {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+
+
+def test_backward_per_channel_workload_sampled(gpu):
+    """B=4, H=16, T=8192, d=128, bf16, per-channel decay (the per-channel
+    prefill workload's inputs): two heads of every gradient against the
+    reference."""
+    w = W.KDA_BF16_PREFILL
+    d = W.make_prefill(w)
+    g = torch.Generator().manual_seed(133)
+    d["do"] = torch.randn(w.B, w.T, w.H, w.dv, generator=g).to(w.dtype)
+    d["dST"] = 0.5 * torch.randn(w.B, w.H, w.dv, w.dk, generator=g)
+    out = _gpu(gpu, d, 2)
+    heads = [(0, 3), (3, 14)]
+    sub = {}
+    for key, t in d.items():
+        if t is None:
+            sub[key] = None
+        elif key in ("S0", "dST"):
+            sub[key] = torch.stack([t[b, h] for b, h in heads])[:, None]
+        else:
+            sub[key] = torch.stack([t[b, :, h] for b, h in heads])[:, :, None]
+    ref = _ref(sub, 2)
+    picked = {}
+    for key, x in out.items():
+        if key == "dS0":
+            picked[key] = np.stack([x[b, h] for b, h in heads])[:, None]
+        else:
+            picked[key] = np.stack([x[b, :, h] for b, h in heads])[:, :, None]
+    errs = _check(picked, ref, 2, 2e-2)
+    print("backward kda bf16 b4 h16 t8192: %s" % {k: "%.2e" % v for k, v in errs.items()}, flush=True)
