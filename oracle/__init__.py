@@ -14,6 +14,8 @@ Contents
 ``prologue.py``      fp64 per-token prologue of the mixer layers (L2-normalised
                      q and k, beta from logits, alpha = exp(-a softplus(x + b)))
                      in front of the loop.
+``epilogue.py``      fp64 gated RMSNorm of the output rows (RMSNorm, gain,
+                     SiLU gate), the mixer's output epilogue.
 ``backward.py``      fp64 gradients of the loop (torch reverse mode on the same
                      recurrence), pinned to finite differences of the C loop.
 ``chunk_form.py``    fp64 NumPy chunkwise (UT/WY) rewrite of the same loop;
@@ -26,7 +28,7 @@ all oracle functions are pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (worked example, closed forms, exact rational
 evaluation of the product form, invariants).
 """
-from . import backward, prologue  # noqa: F401
+from . import backward, epilogue, prologue  # noqa: F401
 from .loop import (gdn_fwd, gdn_fwd_varlen, gdn_decode, build, num_threads, Oracle, compile_library,
                    SOURCE, MODE_NONE, MODE_SCALAR, MODE_CHANNEL, MODE_GDN2)
 
