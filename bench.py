@@ -464,6 +464,29 @@ def bench_backward(w: W.Prefill, reps: int):
                 hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, algorithmic_bytes=nbytes)
 
 
+def bench_epilogue(w: W.Prefill, reps: int):
+    """Mean duration of one ``gdn_gated_rmsnorm`` launch on an output of the
+    workload's shape [B, T, H, d_v] (bf16), median of 3 trials."""
+    log("output epilogue (%s shape)" % w.name)
+    g = torch.Generator().manual_seed(w.seed + 500)
+    shape = (w.B, w.T, w.H, w.dv)
+    o = torch.randn(*shape, generator=g).to(w.dtype).cuda()
+    gate = torch.randn(*shape, generator=g).to(w.dtype).cuda()
+    wt = (1.0 + 0.5 * torch.randn(w.dv, generator=g)).cuda()
+    out = torch.empty_like(o)
+
+    def launch():
+        gdn.gated_rmsnorm(o, gate, wt, eps=1e-6, out=out)
+
+    launch()
+    trials = [_mean_launch_us(launch, reps) for _ in range(3)]
+    us = statistics.median(trials)
+    nbytes = 3 * o.numel() * o.element_size() + w.dv * 4   # o, gate read; out written; the gain
+    return dict(workload=w.name + "_gated_rmsnorm", launch_us=us, trials_us=trials,
+                hbm_gbps=nbytes / (us * 1e-6) / 1e9, hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                algorithmic_bytes=nbytes)
+
+
 def device_copy_gbps(nbytes=1 << 30):
     """Plain device-to-device copy of 1 GiB (read + write), five launches: the
     achievable-bandwidth reference, and the known-size kernel that scales the
@@ -731,7 +754,7 @@ def main():
                 dw.name, lit["us_per_step"], lit["gbps"], rot["us_per_step"], rot["gbps"],
                 100 * rot["hbm_frac"]))
 
-    packed = fused = gdn2 = bwd = None
+    packed = fused = gdn2 = bwd = epi = None
     if not args.no_variants:
         packed = bench_packed(W.GDN_BF16_PACKED, args.steps)
         log("packed: %.1f us per launch" % packed["launch_us"])
@@ -740,6 +763,8 @@ def main():
             fused["launch_us"], fused["plain_launch_us_same_period"]))
         gdn2 = bench_gdn2(W.KDA_BF16_PREFILL, args.steps)
         log("gated deltanet-2: %.1f us per launch" % gdn2["launch_us"])
+        epi = bench_epilogue(W.GDN_BF16_PREFILL, args.steps)
+        log("output epilogue: %.1f us per launch (%.0f GB/s)" % (epi["launch_us"], epi["hbm_gbps"]))
         bwd = [bench_backward(w, max(2, args.steps // 4)) for w in (W.GDN_BF16_PREFILL, W.KDA_BF16_PREFILL)]
         for x in bwd:
             log("backward %s: %.1f us per launch" % (x["workload"], x["launch_us"]))
@@ -772,7 +797,7 @@ def main():
                            step="chunked prefill + first decode token",
                            state="fp32", parallelism="single GPU"),
                roofline=roofline, cpu_baseline=base, prefill=prefill, decode=decode, packed=packed,
-               fused_prologue=fused, gdn2=gdn2, backward=bwd, device_copy_gbps=copy_gbps,
+               fused_prologue=fused, gdn2=gdn2, output_epilogue=epi, backward=bwd, device_copy_gbps=copy_gbps,
                host=host_info(), peaks=dict(hbm_gbps=HBM_PEAK_GBPS, bf16_tflops=BF16_PEAK_TFLOPS))
     print(json.dumps(out), flush=True)
 

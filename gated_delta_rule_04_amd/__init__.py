@@ -22,6 +22,7 @@ import threading
 import torch
 
 __all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_varlen", "chunk_fwd_fused", "decode_step", "decode_step_fused",
+           "gated_rmsnorm",
            "gdn2_chunk_fwd", "gdn2_decode_step", "chunk_bwd", "load", "lib_path", "GDNError",
            "DECAY_NONE", "DECAY_SCALAR", "DECAY_CHANNEL", "EXPORTED_SYMBOLS"]
 
@@ -32,7 +33,7 @@ EXPORTED_SYMBOLS = ("gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk
                     "gdn_chunk_fwd_varlen_workspace_bytes", "gdn_chunk_fwd_varlen",
                     "gdn_chunk_fwd_fused", "gdn_decode_step", "gdn_decode_step_fused",
                     "gdn2_chunk_fwd", "gdn2_decode_step", "gdn_chunk_bwd_workspace_bytes",
-                    "gdn_chunk_bwd", "gdn_status_string", "gdn_version")
+                    "gdn_chunk_bwd", "gdn_gated_rmsnorm", "gdn_status_string", "gdn_version")
 
 
 class Prologue(ctypes.Structure):
@@ -92,6 +93,8 @@ def load():
         lib.gdn_chunk_bwd.restype = i
         lib.gdn_decode_step.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.gdn_decode_step.restype = i
+        lib.gdn_gated_rmsnorm.argtypes = [vp] * 4 + [ctypes.c_longlong, i, ctypes.c_float, i, vp]
+        lib.gdn_gated_rmsnorm.restype = i
         lib.gdn_status_string.argtypes = [i]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_version.argtypes = []
@@ -392,6 +395,39 @@ def decode_step(q, k, v, alpha, beta, S, *, mode=None, o=None, stream=None):
                              _ptr(S), _ptr(o), B, H, dk, dv, _DTYPES[dtype], mode, _stream(stream))
     _check(st)
     return o
+
+
+def gated_rmsnorm(o, gate, weight, *, eps=1e-6, out=None, stream=None):
+    """Output epilogue through ``gdn_gated_rmsnorm``: out = o / sqrt(mean(o^2)
+    + eps) * weight * silu(gate) over the last axis of o (d_v values per row).
+
+    o, gate: the same shape [..., dv] (a prefill's [B, T, H, dv] or a decode
+    step's [B, H, dv]), float32 or bfloat16; weight fp32 [dv]; ``out`` may be
+    o itself (in place).  Returns out."""
+    lib = load()
+    if o.dim() < 1:
+        raise ValueError("o must have a value axis")
+    dv = o.shape[-1]
+    if tuple(gate.shape) != tuple(o.shape):
+        raise ValueError("gate shape %s must equal o's %s" % (tuple(gate.shape), tuple(o.shape)))
+    if tuple(weight.shape) != (dv,):
+        raise ValueError("weight shape %s must be (%d,)" % (tuple(weight.shape), dv))
+    dtype = o.dtype
+    if dtype not in _DTYPES:
+        raise ValueError("o must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty_like(o)
+    elif tuple(out.shape) != tuple(o.shape):
+        raise ValueError("out shape %s must equal o's %s" % (tuple(out.shape), tuple(o.shape)))
+    _require(o, "o", dtype)
+    _require(gate, "gate", dtype)
+    _require(weight, "weight", torch.float32)
+    _require(out, "out", dtype)
+    rows = o.numel() // dv if dv else 0
+    st = lib.gdn_gated_rmsnorm(_ptr(o), _ptr(gate), _ptr(weight), _ptr(out), rows, dv, float(eps),
+                               _DTYPES[dtype], _stream(stream))
+    _check(st)
+    return out
 
 
 def _prologue(l2norm_qk, eps, beta_logits, alpha_logits, A, dt_bias):

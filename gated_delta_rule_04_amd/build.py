@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk.hip", "gdn_backward.hip", "gdn_bwd_chunk.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk.hip", "gdn_backward.hip", "gdn_bwd_chunk.hip",
+           "gdn_epilogue.hip"]
 ARCH = "gfx950"
 
 

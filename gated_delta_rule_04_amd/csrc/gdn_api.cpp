@@ -7,6 +7,7 @@
 #include <cmath>
 
 #include "gdn_backward.h"
+#include "gdn_epilogue.h"
 #include "gdn_internal.h"
 
 static_assert(gdn::kNoAllocScratchBytes == GDN_NOALLOC_SCRATCH_BYTES,
@@ -317,6 +318,26 @@ gdn_status gdn2_decode_step(const void* q, const void* k, const void* v, const v
                             int H, int dk, int dv, gdn_dtype dtype, hipStream_t stream) {
   return decode(q, k, v, alpha, nullptr, S, o, nullptr, B, H, dk, dv, dtype, GDN_DECAY_CHANNEL,
                 stream, erase, write, true);
+}
+
+gdn_status gdn_gated_rmsnorm(const void* o, const void* gate, const float* weight, void* out, long long rows,
+                             int dv, float eps, gdn_dtype dtype, hipStream_t stream) {
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_DTYPE;
+  if (rows < 0 || dv <= 0) return GDN_ERR_SHAPE;
+  if (!supported_dim(dv)) return GDN_ERR_UNSUPPORTED;
+  long long n;
+  if (!count4(rows, dv, 1, 1, &n)) return GDN_ERR_SHAPE;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return GDN_ERR_VALUE;
+  if (rows == 0) return GDN_OK;
+  if (!o || !gate || !weight || !out) return GDN_ERR_NULL;
+  const size_t bytes = (size_t)n * elem_size(dtype);
+  const Range ro = range_of(out, bytes);
+  if (overlaps(ro, range_of(gate, bytes)) || overlaps(ro, range_of(weight, (size_t)dv * 4)))
+    return GDN_ERR_ALIAS;
+  if (out != o && overlaps(ro, range_of(o, bytes))) return GDN_ERR_ALIAS;
+  return gdn::launch_gated_rmsnorm(o, gate, weight, out, rows, dv, eps, (int)dtype, stream) == hipSuccess
+             ? GDN_OK
+             : GDN_ERR_LAUNCH;
 }
 
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,

@@ -316,13 +316,14 @@ gdn_status gdn2_decode_step(const void* q, const void* k, const void* v, const v
 
 /*
  * Bytes of device workspace gdn_chunk_bwd needs (0: the pointer may be NULL).
- * bf16 with no or scalar decay (the chunk-level kernels): per chunk of 64
- * tokens of every head, the forward's chunk record (T and five gate rows,
- * 9,472 bytes), the bf16 entry state and the bf16 end-of-chunk state
- * gradient (2 d_v d_k bytes each).  fp32 or per-channel decay (the token-level
- * kernels): state checkpoints (d_v x d_k fp32 per 8 tokens of every head) and
- * one partial of the row sums per 32-row value slice.  0 for rejected
- * arguments.
+ * bf16 (the chunk-level kernels): per chunk of 64 tokens of every head, the
+ * forward's chunk record (no or scalar decay: T and five gate rows, 9,472
+ * bytes; per-channel: the per-channel record), the bf16 entry state and the
+ * bf16 end-of-chunk state gradient (2 d_v d_k bytes each); per-channel decay
+ * also At (16 KB) and the intermediate products of the gradient kernels
+ * (fp32: 2 C^2 + 3 C d_k + d_k values).  fp32 (the token-level kernels): state
+ * checkpoints (d_v x d_k fp32 per 8 tokens of every head) and one partial of
+ * the row sums per 32-row value slice.  0 for rejected arguments.
  */
 size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
                                      gdn_dtype dtype, gdn_decay mode);
@@ -346,10 +347,11 @@ size_t gdn_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
  *   workspace gdn_chunk_bwd_workspace_bytes(...) bytes
  * No output may alias an input, another output or the workspace.  The
  * computation is deterministic (no atomics).  Gradients are accumulated in
- * fp32 and rounded once to `dtype`.  bf16 with no or scalar decay runs the
- * reverse mode of the chunk form (MFMA products; X and dU as bf16 hi + lo
- * pairs where dbeta needs them); the other cases run the token recurrence in
- * reverse from state checkpoints.  Errors as for gdn_chunk_fwd.
+ * fp32 and rounded once to `dtype`.  bf16 runs the reverse mode of the chunk
+ * form (MFMA products; X and dU as bf16 hi + lo pairs where dbeta needs them;
+ * with per-channel decay the channel-weighted C x C contractions run on the
+ * vector ALUs, every weight exp(G_r - G_s) at most 1); fp32 runs the token
+ * recurrence in reverse from state checkpoints.  Errors as for gdn_chunk_fwd.
  */
 gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void* alpha,
                          const float* beta, const float* S0, const void* dout,
@@ -357,6 +359,27 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void
                          float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
                          int B, int T, int H, int dk_, int dv_, int chunk, gdn_dtype dtype,
                          gdn_decay mode, hipStream_t stream);
+
+/*
+ * Output epilogue of the Gated DeltaNet mixer (NextTransformer "method
+ * sources" page, baseline section, Gated DeltaNet entry: the output passes an
+ * RMSNorm, a gain and a SiLU gate; backend section: the output-gated
+ * RMSNorm).  For each of `rows` rows of d_v values:
+ *
+ *     out = o / sqrt(mean(o^2) + eps) * weight * silu(gate),   silu(g) = g / (1 + e^-g)
+ *
+ *   o, gate   [rows, dv] `dtype` (rows = B * T * H for a prefill's output
+ *             [B, T, H, dv], B * H for a decode step's [B, H, dv])
+ *   weight    fp32 [dv], the gain, shared by all rows
+ *   out       [rows, dv] `dtype`, written; may be o itself (in place), must
+ *             not otherwise overlap o, gate or weight (GDN_ERR_ALIAS)
+ *   eps       >= 0 and finite (GDN_ERR_VALUE); the pages leave it open
+ * Arithmetic in fp32, one rounding to `dtype`.  dv in {64, 128}.  rows = 0
+ * does nothing.  The state kernels split d_v over workgroups, so this runs as
+ * its own pass over the finished output.
+ */
+gdn_status gdn_gated_rmsnorm(const void* o, const void* gate, const float* weight, void* out, long long rows,
+                             int dv, float eps, gdn_dtype dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(gdn_status s);

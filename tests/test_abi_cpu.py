@@ -53,6 +53,8 @@ def lib():
     lib.gdn_chunk_bwd.restype = i
     lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i] * 8
     lib.gdn_chunk_bwd_workspace_bytes.restype = sz
+    lib.gdn_gated_rmsnorm.argtypes = [vp] * 4 + [ctypes.c_longlong, i, ctypes.c_float, i, vp]
+    lib.gdn_gated_rmsnorm.restype = i
     return lib
 
 
@@ -371,3 +373,22 @@ def test_noalloc_validation(lib):
     assert call(ptrs=(q, k, v, a, b, s0, q + 64, sf)) == E_ALIAS
     assert call(B=0) == OK and call(H=0) == OK
     assert call(T=0, ptrs=(0, 0, 0, 0, 0, 0, 0, 0)) == OK  # nothing to write
+
+
+def test_gated_rmsnorm_validation(lib):
+    o, g, w, y = _bufs()[:4]
+    call = lambda o=o, g=g, w=w, y=y, rows=100, dv=128, eps=1e-6, dt=1: lib.gdn_gated_rmsnorm(
+        o, g, w, y, rows, dv, eps, dt, None)
+    assert call(dv=96) == E_UNSUP
+    assert call(rows=-1) == E_SHAPE
+    assert call(dv=0) == E_SHAPE
+    assert call(dt=5) == E_DTYPE
+    assert call(eps=-1.0) == E_VALUE
+    assert call(eps=float("inf")) == E_VALUE
+    assert call(eps=float("nan")) == E_VALUE
+    assert call(o=0) == E_NULL and call(g=0) == E_NULL and call(w=0) == E_NULL and call(y=0) == E_NULL
+    assert call(y=g) == E_ALIAS                  # out over the gate
+    assert call(y=o + 64) == E_ALIAS             # out partly over o
+    assert call(y=w - 16) == E_ALIAS             # out over the gain
+    assert call(rows=0, o=0, g=0, w=0, y=0) == OK   # nothing to do
+    assert call(rows=1 << 62) == E_SHAPE         # element count overflow
