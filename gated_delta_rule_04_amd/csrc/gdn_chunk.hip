@@ -266,7 +266,9 @@ struct PrepPlan {
   static constexpr size_t g = inplace ? r1 : mt + (size_t)32 * LDM * 4;
   // inverse norms (K, then Q in fp32)
   static constexpr size_t nk = g + 2 * C * 4;
-  static constexpr size_t total = g + (NORM ? (inplace ? 3 : 4) : 2) * C * 4;
+  // squared K row norms (the transition bound of scalar decay)
+  static constexpr size_t ksq = g + (NORM ? (inplace ? 3 : 4) : 2) * C * 4;
+  static constexpr size_t total = ksq + C * 4;
 };
 
 template <typename E, int DK, int MODE, bool NORM>
@@ -289,6 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   float* Bt = G + C;
   float* Nk = reinterpret_cast<float*>(smem + L::nk);   // NORM only
   float* Nq = Nk + C;                                   // NORM, fp32 only
+  float* Ksq = reinterpret_cast<float*>(smem + L::ksq);  // scalar decay with a bound array only
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
   PrepAt at;
@@ -324,12 +327,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         qv = ld_once(qg + off);
         *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = qv;
       }
-      if constexpr (NORM) {
-        const float nk = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(kv)) + a.pro.norm_eps);
-        if (cc == 0) Nk[r] = nk;
-        if constexpr (WP) {
-          const float nq = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(qv)) + a.pro.norm_eps);
-          if (cc == 0) Nq[r] = nq;
+      if (NORM || (MODE == 1 && a.horizon)) {
+        const float ks = lane_group_sum<CPR>(sumsq16<E>(kv));
+        if (MODE == 1 && cc == 0) Ksq[r] = ks;
+        if constexpr (NORM) {
+          const float nk = __builtin_amdgcn_rsqf(ks + a.pro.norm_eps);
+          if (cc == 0) Nk[r] = nk;
+          if constexpr (WP) {
+            const float nq = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(qv)) + a.pro.norm_eps);
+            if (cc == 0) Nq[r] = nq;
+          }
         }
       }
     }
@@ -425,6 +432,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       gw[2 * C + lane] = __expf(G[C - 1] - g) * nk;
       gw[3 * C + lane] = WP ? eg * Nq[lane] : eg;
       gw[4 * C + lane] = g - __logf(nk);
+    }
+    // The chunk's state transition S -> S prod_t alpha_t (I - beta_t k_t k_t^T)
+    // has spectral norm at most prod_t alpha_t max(1, |1 - beta_t |k_t|^2|)
+    // (each factor is symmetric with eigenvalues 1 and 1 - beta_t |k_t|^2); its
+    // log goes to the bound array.  (Tokens past the sequence end: beta = 0.)
+    if (MODE == 1 && a.horizon) {
+      float ks = Ksq[lane];
+      if constexpr (NORM) ks *= Nk[lane] * Nk[lane];
+      float grow = __logf(fmaxf(1.f, fabsf(1.f - Bt[lane] * ks)));
+      grow = lane_group_sum<32>(grow);
+      grow += __shfl_xor(grow, 32);
+      if (lane == 0) a.horizon[at.sp.rec0 + n] = G[C - 1] + grow;
     }
   }
   __syncthreads();
@@ -1416,9 +1435,15 @@ constexpr int kWsThreads = 512;
 constexpr int kP1Ahead = 2;   // phase-1 fragments loaded this many k steps ahead
 constexpr int kFormPAhead = 2;   // fragments of P's product loaded this many k steps ahead
 
+// One workgroup's share of a value slice: a lead-in over chunks [lead0, n_so)
+// that runs the state recurrence alone (no Q, P or O), with the same products
+// in the same order as the full pass, then the full pass over [n_so, n_end).
+// The lead-in starts from S0 when lead0 = 0, else from a zero state; the last
+// part of the slice writes S_final.  smem holds WsPlan::total bytes.
 template <typename E, int DK, int DVS, int MODE, bool NORM>
-__global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws, int npart,
-                                                             float lead_r) {
+__device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __restrict__ tws,
+                                              unsigned char* __restrict__ smem, int head, int sl, const Span& sp,
+                                              bool last, int lead0, int n_so, int n_end) {
   static_assert(sizeof(E) == 2, "the eight-wave kernel is bf16");
   constexpr bool KDA = MODE >= 2;
   constexpr bool G2 = MODE == 3;   // Gated DeltaNet-2: V is scaled by the write gate
@@ -1447,7 +1472,6 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   constexpr int TBT = C * CPT / PT;
   constexpr int NG4 = (KDA ? DK : (NORM ? 5 : 3) * C) / 4;   // 16-byte chunks of the fp32 rows
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::total];
   // Buffer pairs are C * LDK (rows; C * LDKS for Ks), C * LDV (V), C * LDP (P) elements and
   // GS floats apart.
   E* Qrb = reinterpret_cast<E*>(smem + L::qr);
@@ -1464,41 +1488,9 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
   const int H = a.H, dv = a.dv;
-  const int nsl = dv / DVS;
-  const int nheads = a.B * H;
-  // Workgroups are dispatched round-robin over the eight XCDs: give the
-  // workgroups of one head the same XCD (same L2) when the head count allows it.
-  const int per_head = nsl * npart;
-  int head, rw;
-  if ((nheads & 7) == 0) {
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    head = xcd + 8 * (j / per_head);
-    rw = j % per_head;
-  } else {
-    head = blockIdx.x / per_head;
-    rw = blockIdx.x % per_head;
-  }
-  const int sl = rw % nsl, part = rw / nsl;
   const int h = head % H, b = head / H;
   const int i0 = sl * DVS;
-  const Span sp = seq_span(a, b, h);
   const int T = sp.len;   // tokens of this sequence
-  const int nchunks = (T + C - 1) / C;
-  // Parts of a value slice (used when the slices alone leave compute units
-  // idle): part p writes the outputs of chunks [m_p, m_p+1) and reaches its
-  // starting state by running the state recurrence alone over chunks
-  // [0, m_p) (no Q, P or O), with the same products in the same order as the
-  // full pass, so it starts from the very state the full pass holds there.
-  // With a lead-in chunk costing lead_r of a full one, the split
-  // m_p = N (1 - (1 - r)^p) / (1 - (1 - r)^npart) gives every part the same time.
-  auto split = [&](int p) {
-    if (p <= 0) return 0;
-    if (p >= npart) return nchunks;
-    const float q = 1.f - lead_r;
-    const float f = (1.f - __powf(q, (float)p)) / (1.f - __powf(q, (float)npart));
-    return min(nchunks, max(0, (int)((float)nchunks * f + 0.5f)));
-  };
-  const int n_so = split(part), n_end = split(part + 1);   // lead-in [0, n_so), outputs [n_so, n_end)
   using Full = std::false_type;
   using Lead = std::true_type;
   const size_t v_tok = (size_t)H * dv;
@@ -1711,11 +1703,11 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       load_tp(n0, so);
     };
 
-    if (n_so > 0) {   // lead-in: the state alone over chunks [0, n_so)
-      prologue(0, n_so - 1, Lead{});
+    if (n_so > lead0) {   // lead-in: the state alone over chunks [lead0, n_so)
+      prologue(lead0, n_so - 1, Lead{});
       __syncthreads();
       __syncthreads();
-      for (int n = 0; n < n_so; ++n) step(n, n_so - 1, std::true_type{}, Lead{});
+      for (int n = lead0; n < n_so; ++n) step(n, n_so - 1, std::true_type{}, Lead{});
     }
     if (n_end > n_so) prologue(n_so, n_end - 1, Full{});
     __syncthreads();
@@ -1766,7 +1758,7 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
       for (int g = 0; g < 4; ++g) {
         const int c0 = cb * 32 + acc_row(g, 0, lane);
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (a.S0) x = *reinterpret_cast<const float4*>(a.S0 + (sbase + i) * DK + c0);
+        if (a.S0 && lead0 == 0) x = *reinterpret_cast<const float4*>(a.S0 + (sbase + i) * DK + c0);
         Sacc[st][4 * g + 0] = x.x;
         Sacc[st][4 * g + 1] = x.y;
         Sacc[st][4 * g + 2] = x.z;
@@ -1954,16 +1946,16 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
     __syncthreads();
   };
 
-  if (n_so > 0) {   // lead-in
+  if (n_so > lead0) {   // lead-in
     __syncthreads();
     __syncthreads();
-    for (int n = 0; n < n_so; ++n) chunk(n, Lead{});
+    for (int n = lead0; n < n_so; ++n) chunk(n, Lead{});
   }
   __syncthreads();
   __syncthreads();   // the data waves form P of the first chunk
   for (int n = n_so; n < n_end; ++n) chunk(n, Full{});
 
-  if (a.S_final && part == npart - 1) {
+  if (a.S_final && last) {
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       const int t = wave + 4 * st;
@@ -1980,10 +1972,134 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, cons
   }
 }
 
+// Workgroups are dispatched round-robin over the eight XCDs: give the
+// workgroups of one head the same XCD (same L2) when the head count allows it.
+__device__ inline void ws_head(const PrefillArgs& a, int per_head, int& head, int& rw) {
+  if (((a.B * a.H) & 7) == 0) {
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    head = xcd + 8 * (j / per_head);
+    rw = j % per_head;
+  } else {
+    head = blockIdx.x / per_head;
+    rw = blockIdx.x % per_head;
+  }
+}
+
+// Parts of a value slice with lead-ins from chunk 0: part p writes the outputs
+// of chunks [m_p, m_p+1) and reaches its starting state by the state
+// recurrence alone over [0, m_p), the very state the unsplit pass holds there.
+// With a lead-in chunk costing r of a full one, m_p = N (1 - (1 - r)^p) /
+// (1 - (1 - r)^npart) gives every part the same time.
+__device__ inline int geometric_split(int nchunks, int p, int npart, float r) {
+  if (p <= 0) return 0;
+  if (p >= npart) return nchunks;
+  const float q = 1.f - r;
+  const float f = (1.f - __powf(q, (float)p)) / (1.f - __powf(q, (float)npart));
+  return min(nchunks, max(0, (int)((float)nchunks * f + 0.5f)));
+}
+
+template <typename E, int DK, int DVS, int MODE, bool NORM>
+__global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws, int npart,
+                                                             float lead_r) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[WsPlan<E, DK, DVS, (MODE >= 2), NORM>::total];
+  const int nsl = a.dv / DVS;
+  int head, rw;
+  ws_head(a, nsl * npart, head, rw);
+  const int sl = rw % nsl, part = rw / nsl;
+  const Span sp = seq_span(a, head / a.H, head % a.H);
+  const int nchunks = (sp.len + C - 1) / C;
+  state_ws_body<E, DK, DVS, MODE, NORM>(a, tws, smem, head, sl, sp, part == npart - 1, 0,
+                                        geometric_split(nchunks, part, npart, lead_r),
+                                        geometric_split(nchunks, part + 1, npart, lead_r));
+}
+
+// The history horizon of a split slice (scalar decay).  With every chunk's
+// transition bounded in norm by e^{c_n} (the prep kernel's bound array), the
+// state at chunk m is S_s Phi(s, m) + (the recurrence over [s, m) from a zero
+// state), with |S_s Phi(s, m)| <= e^{c_s + ... + c_{m-1}} |S_s|.  A lead-in from
+// the last s at which that sum is at most -kHorizon, started from zero, thus
+// reaches the state at m up to a part below e^-100 of |S_s|: the same scale the
+// gate floor (kLogFloor) already neglects.  Strongly decaying gates forget the
+// far past within a few chunks, so the parts of a slice no longer need lead-ins
+// from chunk 0.
+constexpr float kHorizon = 100.f;
+
+// Lead-in length (chunks) for a part whose outputs start at chunk m: the
+// smallest L with c_{m-L} + ... + c_{m-1} <= -kHorizon, or m (a lead-in from
+// chunk 0 and S0, exact) when no L <= min(m, cap) qualifies.  One wave; every
+// lane returns the same value.  hz: the sequence's bound array.
+__device__ inline int horizon_lead(const float* __restrict__ hz, int m, int cap) {
+  const int lane = threadIdx.x & 63;
+  const int lim = min(m, cap);
+  float carry = 0.f;
+  for (int base = 0; base < lim; base += 256) {
+    float c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {   // four blocks of 64 chunks in flight, latest chunks first
+      const int off = base + 64 * u + lane;
+      c[u] = off < lim ? hz[m - 1 - off] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float sfx = chunk_prefix(c[u]) + carry;   // c_{m-1-off} + ... + c_{m-1}
+      const unsigned long long hit = __ballot(base + 64 * u + lane < lim && sfx <= -kHorizon);
+      if (hit) return base + 64 * u + __ffsll((long long)hit);
+      carry = __shfl(sfx, 63);
+    }
+  }
+  return m;
+}
+
 // Lead-in chunk cost relative to a full chunk of the eight-wave kernel
 // (measured on the long-context workload): sets where the parts of a value
 // slice split the sequence.
 constexpr float kLeadCost = 0.65f;
+// Per-chunk cost of a 64-row value slice relative to a 32-row one.
+constexpr float kSlice64Cost = 1.35f;
+
+// Scalar decay with split slices: per head, either 32-row slices in npart32
+// parts with lead-ins from chunk 0 (as chunk_state_ws), or 64-row slices in
+// twice as many parts of equal length with lead-ins from the history horizon,
+// whichever the cost model gives less time.  Same workgroup count per head;
+// every workgroup of a head reads the same bounds and takes the same choice.
+template <typename E, int DK, bool NORM>
+__global__ __launch_bounds__(kWsThreads) void chunk_state_ws_horizon(PrefillArgs a, const E* __restrict__ tws,
+                                                                     int npart32, float lead_r) {
+  using L32 = WsPlan<E, DK, 32, false, NORM>;
+  using L64 = WsPlan<E, DK, 64, false, NORM>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[cmax(L32::total, L64::total)];
+  const int nsl32 = a.dv / 32, nsl64 = a.dv / 64;
+  const int per_head = nsl32 * npart32, npart64 = per_head / nsl64;
+  int head, rw;
+  ws_head(a, per_head, head, rw);
+  const Span sp = seq_span(a, head / a.H, head % a.H);
+  const int nchunks = (sp.len + C - 1) / C;
+  // time of the 32-row plan (its first part has no lead-in); past the lead-in
+  // length at which the 64-row plan cannot win, the scan stops
+  const float t32 = (float)geometric_split(nchunks, 1, npart32, lead_r);
+  const float span64 = (float)nchunks / (float)npart64;
+  const int cap = max(0, (int)((t32 / kSlice64Cost - span64) / lead_r) + 1);
+  const float* hz = a.horizon + sp.rec0;
+  const int part64 = rw / nsl64;
+  int lmax = 0, lead = 0;
+  for (int q = 1; q < npart64; ++q) {
+    const int m = (int)((long long)q * nchunks / npart64);
+    const int l = horizon_lead(hz, m, cap);
+    lmax = max(lmax, l);
+    if (q == part64) lead = l;
+  }
+  if (kSlice64Cost * (span64 + lead_r * (float)lmax) < t32) {
+    const int so = (int)((long long)part64 * nchunks / npart64);
+    const int end = (int)((long long)(part64 + 1) * nchunks / npart64);
+    state_ws_body<E, DK, 64, 1, NORM>(a, tws, smem, head, rw % nsl64, sp, part64 == npart64 - 1, so - lead, so,
+                                      end);
+  } else {
+    const int part = rw / nsl32;
+    state_ws_body<E, DK, 32, 1, NORM>(a, tws, smem, head, rw % nsl32, sp, part == npart32 - 1, 0,
+                                      geometric_split(nchunks, part, npart32, lead_r),
+                                      geometric_split(nchunks, part + 1, npart32, lead_r));
+  }
+}
 
 // Parts per value slice: while the slices fill at most half of the compute
 // units, each slice is split in two parts more.
@@ -2009,7 +2125,12 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
     // (normalised q and k: the per-channel records carry normalised operands, so
     // only the scalar / no-decay state kernel has a variant of its own)
     const bool nrm = a.pro.qk_norm != 0;
-    if (a.mode == 0 && !nrm)
+    if (DVS == 32 && a.mode == 1 && np > 1 && a.horizon && np <= 4) {
+      if (nrm)
+        hipLaunchKernelGGL((chunk_state_ws_horizon<E, DK, true>), grid, wblock, 0, stream, a, tws, np, r);
+      else
+        hipLaunchKernelGGL((chunk_state_ws_horizon<E, DK, false>), grid, wblock, 0, stream, a, tws, np, r);
+    } else if (a.mode == 0 && !nrm)
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, false>), grid, wblock, 0, stream, a, tws, np, r);
     else if (a.mode == 0)
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, true>), grid, wblock, 0, stream, a, tws, np, r);
@@ -2072,15 +2193,23 @@ hipError_t launch_prep(const PrefillArgs& a, E* tws, hipStream_t stream) {
 }
 
 template <typename E, int DK>
-hipError_t launch_dk(const PrefillArgs& a, void* workspace, hipStream_t stream) {
+hipError_t launch_dk(const PrefillArgs& a0, void* workspace, hipStream_t stream) {
   E* tws = static_cast<E*>(workspace);
+  PrefillArgs a = a0;
+  const long long wg64 = (long long)a.B * a.H * (a.dv / 64);
+  const bool dvs64 = sizeof(E) == 2 && wg64 >= 256 && a.mode < 2;
+  // Scalar decay in bf16 with split 32-row slices: the prep kernel also writes
+  // the transition bounds, after the records.
+  if (sizeof(E) == 2 && a.mode == 1 && !dvs64 && state_parts((size_t)a.B * a.H * (a.dv / 32)) > 1) {
+    const size_t nrec = a.cu_seqlens ? (size_t)a.H * a.nslots : (size_t)a.B * a.H * ((a.T + C - 1) / C);
+    a.horizon = reinterpret_cast<float*>(tws + nrec * GateRec<E>::elems);
+  }
   const hipError_t e = launch_prep<E, DK>(a, tws, stream);
   if (e != hipSuccess) return e;
   if constexpr (sizeof(E) == 4) {
     return launch_state<E, DK, 32>(a, tws, stream);
   } else {
-    const long long wg64 = (long long)a.B * a.H * (a.dv / 64);
-    if (wg64 >= 256 && a.mode < 2) return launch_state<E, DK, 64>(a, tws, stream);
+    if (dvs64) return launch_state<E, DK, 64>(a, tws, stream);
     return launch_state<E, DK, 32>(a, tws, stream);
   }
 }
@@ -2094,15 +2223,23 @@ static size_t record_bytes(int dk, int dtype, int mode) {
   return (es == 4 ? 2 : 1) * (size_t)C * C * es + kGateFloats * 4;   // bf16: no P
 }
 
+// The transition bounds of scalar decay in bf16 (one fp32 per record) follow
+// the records, 256-byte aligned.
+static size_t horizon_bytes(size_t nrec, int dtype, int mode) {
+  return dtype == 1 && mode == 1 ? (nrec * 4 + 255) & ~(size_t)255 : 0;
+}
+
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dtype, int mode) {
-  return (size_t)B * H * (((size_t)T + C - 1) / C) * record_bytes(dk, dtype, mode);
+  const size_t nrec = (size_t)B * H * (((size_t)T + C - 1) / C);
+  return nrec * record_bytes(dk, dtype, mode) + horizon_bytes(nrec, dtype, mode);
 }
 
 int varlen_slots(int N, int T) { return T / C + N; }
 
 size_t prefill_varlen_workspace_bytes(int N, int T, int H, int dk, int dtype, int mode) {
   if (T == 0) return 0;
-  return (size_t)H * varlen_slots(N, T) * record_bytes(dk, dtype, mode);
+  const size_t nrec = (size_t)H * varlen_slots(N, T);
+  return nrec * record_bytes(dk, dtype, mode) + horizon_bytes(nrec, dtype, mode);
 }
 
 size_t prefill_record_bytes(int dk, int dtype, int mode) { return record_bytes(dk, dtype, mode); }

@@ -52,6 +52,11 @@ struct PrefillArgs {
   // each chunk's At[r][s] = sum_c k_r[c] k_s[c] exp(G_r[c] - G_s[c]) (s < r,
   // else 0), fp32 [C][C] per record slot.  Null in the forward.
   float* a_tilde = nullptr;
+  // Scalar decay, bf16: one fp32 per chunk record (same index), the log of a
+  // bound on the norm of the chunk's state transition (written by the prep
+  // kernel, read by the state kernel to place the lead-ins of split slices).
+  // Null: not written, and every lead-in starts at chunk 0.
+  float* horizon = nullptr;
 };
 
 // Arguments of one decode launch: q, k [B, H, dk]; v, o [B, H, dv];

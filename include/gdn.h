@@ -163,7 +163,7 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
  *
  *   - A call whose gdn_chunk_fwd_workspace_bytes(...) exceeds
  *     GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_WORKSPACE before anything is
- *     enqueued (for bf16 scalar decay at d_k = 128: up to 7084 chunk-heads,
+ *     enqueued (for bf16 scalar decay at d_k = 128: up to 7081 chunk-heads,
  *     B * H * ceil(T / 64); per-channel decay: 1016).
  *   - Every call on one GPU uses that GPU's one array: calls that overlap on
  *     one GPU (concurrent streams, or host threads sharing a device) race

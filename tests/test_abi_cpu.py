@@ -125,14 +125,19 @@ def _ws_bytes(B, T, H, es, dk=128, mode=1):
     chunks = B * H * ((T + 63) // 64)
     if mode == 2:   # T, P, three scaled copies of K / Q, per-channel decay
         return chunks * ((2 * 64 * 64 + 3 * 64 * dk) * es + 4 * dk)
-    # T per chunk (and P in fp32: the bf16 state kernel forms P itself) + five fp32 gate rows
-    return chunks * ((2 if es == 4 else 1) * 64 * 64 * es + 5 * 64 * 4)
+    # T per chunk (and P in fp32: the bf16 state kernel forms P itself) + five fp32 gate rows;
+    # scalar decay in bf16: one fp32 transition bound per chunk after the records, 256-byte aligned
+    return chunks * ((2 if es == 4 else 1) * 64 * 64 * es + 5 * 64 * 4) + _bound_bytes(chunks, es, mode)
+
+
+def _bound_bytes(chunks, es, mode):
+    return (chunks * 4 + 255) // 256 * 256 if (es == 2 and mode == 1) else 0
 
 
 def test_workspace_query(lib):
     assert lib.gdn_chunk_fwd_workspace_bytes(8, 4096, 16, 128, 128, 64, 1, 1) == _ws_bytes(8, 4096, 16, 2)
     assert lib.gdn_chunk_fwd_workspace_bytes(1, 256, 2, 64, 64, 64, 0, 1) == _ws_bytes(1, 256, 2, 4)
-    assert lib.gdn_chunk_fwd_workspace_bytes(2, 65, 3, 128, 64, 64, 1, 0) == _ws_bytes(2, 65, 3, 2)
+    assert lib.gdn_chunk_fwd_workspace_bytes(2, 65, 3, 128, 64, 64, 1, 0) == _ws_bytes(2, 65, 3, 2, mode=0)
     assert lib.gdn_chunk_fwd_workspace_bytes(4, 8192, 16, 128, 128, 64, 1, 2) == _ws_bytes(4, 8192, 16, 2, 128, 2)
     assert lib.gdn_chunk_fwd_workspace_bytes(1, 100, 2, 64, 128, 64, 0, 2) == _ws_bytes(1, 100, 2, 4, 64, 2)
     assert lib.gdn_chunk_fwd_workspace_bytes(2, 0, 3, 128, 64, 64, 1, 1) == 0
@@ -157,7 +162,7 @@ def _varlen_ws_bytes(N, T, H, es, dk=128, mode=1):
     slots = H * (T // 64 + N)
     if mode == 2:
         return slots * ((2 * 64 * 64 + 3 * 64 * dk) * es + 4 * dk)
-    return slots * ((2 if es == 4 else 1) * 64 * 64 * es + 5 * 64 * 4)
+    return slots * ((2 if es == 4 else 1) * 64 * 64 * es + 5 * 64 * 4) + _bound_bytes(slots, es, mode)
 
 
 def test_varlen_workspace_bounds_every_split():
@@ -360,9 +365,10 @@ def test_noalloc_validation(lib):
         return f(*p, B, T, H, dk, dv, chunk, dtype, mode, None)
 
     scratch = 64 << 20
-    per = _ws_bytes(1, 64, 1, 2)                           # one bf16 scalar-decay record
-    assert scratch // per == 7084
-    assert call(B=1, T=64 * 7085, H=1) == E_WS             # one record too many
+    # bf16 scalar decay: the most chunk records (with their bounds) that fit the array
+    nmax = max(n for n in range(7000, 7200) if _ws_bytes(1, 64 * n, 1, 2) <= scratch)
+    assert nmax == 7081
+    assert call(B=1, T=64 * (nmax + 1), H=1) == E_WS      # one record too many
     assert call(B=8, T=4096, H=16) == E_WS                 # 8192 records
     assert call(B=1, T=64 * 1017, H=1, mode=2) == E_WS     # per-channel records are larger
     assert call(dk=96) == E_UNSUP

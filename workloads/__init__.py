@@ -47,6 +47,10 @@ def _gate_exp01(z):        # alpha = exp(-0.1 softplus(z))
     return torch.exp(-0.1 * torch.nn.functional.softplus(z))
 
 
+def _gate_exp1(z):         # alpha = exp(-softplus(z)): strong decay, median about 0.50
+    return torch.exp(-torch.nn.functional.softplus(z))
+
+
 def _gate_range(lo):       # alpha = lo + (1 - lo) sigmoid(z), inside (lo, 1)
     return lambda z: lo + (1.0 - lo) * torch.sigmoid(z)
 
@@ -62,6 +66,7 @@ def _gate_kda_literal(z):  # alpha = exp(-softplus(z + 3)): strong decay, median
 GATES = {
     "none": (MODE_NONE, None),
     "exp01": (MODE_SCALAR, _gate_exp01),
+    "exp1": (MODE_SCALAR, _gate_exp1),
     "range090": (MODE_SCALAR, _gate_range(0.90)),
     "range095": (MODE_SCALAR, _gate_range(0.95)),
     "exp01_channel": (MODE_CHANNEL, _gate_exp01),
