@@ -327,16 +327,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         qv = ld_once(qg + off);
         *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = qv;
       }
-      if (NORM || (MODE == 1 && a.horizon)) {
+      if constexpr (NORM) {
         const float ks = lane_group_sum<CPR>(sumsq16<E>(kv));
-        if (MODE == 1 && cc == 0) Ksq[r] = ks;
-        if constexpr (NORM) {
-          const float nk = __builtin_amdgcn_rsqf(ks + a.pro.norm_eps);
-          if (cc == 0) Nk[r] = nk;
-          if constexpr (WP) {
-            const float nq = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(qv)) + a.pro.norm_eps);
-            if (cc == 0) Nq[r] = nq;
-          }
+        const float nk = __builtin_amdgcn_rsqf(ks + a.pro.norm_eps);
+        if (cc == 0) {
+          Nk[r] = nk;
+          if (MODE == 1) Ksq[r] = ks * nk * nk;   // |k|^2 of the normalised key
+        }
+        if constexpr (WP) {
+          const float nq = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(qv)) + a.pro.norm_eps);
+          if (cc == 0) Nq[r] = nq;
         }
       }
     }
@@ -407,6 +407,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) asm volatile("" ::"v"(w[v]));
+    // unnormalised keys: |k_r|^2 is the Gram tile's diagonal entry, held by
+    // one lane of the diagonal tiles (waves 0 and 2)
+    if (!NORM && MODE == 1 && a.horizon && jb == rb) {
+      float dg = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dg = jb * 32 + acc_row(g, e, lane) == r ? acca[4 * g + e] : dg;
+      if (((col >> 2) & 1) == (lane >> 5)) Ksq[r] = dg;
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int j0 = jb * 32 + acc_row(g, 0, lane);
@@ -433,23 +443,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       gw[3 * C + lane] = WP ? eg * Nq[lane] : eg;
       gw[4 * C + lane] = g - __logf(nk);
     }
-    // The chunk's state transition S -> S prod_t alpha_t (I - beta_t k_t k_t^T)
-    // has spectral norm at most prod_t alpha_t max(1, |1 - beta_t |k_t|^2|)
-    // (each factor is symmetric with eigenvalues 1 and 1 - beta_t |k_t|^2); its
-    // log goes to the bound array.  (Tokens past the sequence end: beta = 0.)
-    if (MODE == 1 && a.horizon) {
-      float ks = Ksq[lane];
-      if constexpr (NORM) ks *= Nk[lane] * Nk[lane];
-      float grow = __logf(fmaxf(1.f, fabsf(1.f - Bt[lane] * ks)));
-      grow = lane_group_sum<32>(grow);
-      grow += __shfl_xor(grow, 32);
-      if (lane == 0) a.horizon[at.sp.rec0 + n] = G[C - 1] + grow;
-    }
   }
   __syncthreads();
 
   if constexpr (L::inplace) {
     tri_solve<E, L::ldm, true>(Am, Li, Mt, Bt, rec + R::t, tid);   // T straight to the record
+    // The chunk's state transition S -> S prod_t alpha_t (I - beta_t k_t k_t^T)
+    // has spectral norm at most prod_t alpha_t max(1, |1 - beta_t |k_t|^2|)
+    // (each factor is symmetric with eigenvalues 1 and 1 - beta_t |k_t|^2); its
+    // log goes to the bound array.  (Tokens past the sequence end: beta = 0.)
+    // G, beta and |k|^2 outlive the solve, which writes neither.
+    if (MODE == 1 && a.horizon && wave == 3) {
+      float grow = __logf(fmaxf(1.f, fabsf(1.f - Bt[lane] * Ksq[lane])));
+      grow = lane_group_sum<32>(grow);
+      grow += __shfl_xor(grow, 32);
+      if (lane == 0) a.horizon[at.sp.rec0 + n] = G[C - 1] + grow;
+    }
   } else {
     tri_solve<E, L::ldm>(Am, Li, Mt, Bt, Tm, tid);
     // T -> the record, 64 x 64 contiguous, 16-byte stores
@@ -2080,17 +2089,23 @@ __global__ __launch_bounds__(kWsThreads) void chunk_state_ws_horizon(PrefillArgs
   const float span64 = (float)nchunks / (float)npart64;
   const int cap = max(0, (int)((t32 / kSlice64Cost - span64) / lead_r) + 1);
   const float* hz = a.horizon + sp.rec0;
-  const int part64 = rw / nsl64;
-  int lmax = 0, lead = 0;
-  for (int q = 1; q < npart64; ++q) {
-    const int m = (int)((long long)q * nchunks / npart64);
-    const int l = horizon_lead(hz, m, cap);
-    lmax = max(lmax, l);
-    if (q == part64) lead = l;
-  }
+  int lmax = 0;   // longest lead-in of an equal split
+  for (int q = 1; q < npart64; ++q)
+    lmax = max(lmax, horizon_lead(hz, (int)((long long)q * nchunks / npart64), cap));
   if (kSlice64Cost * (span64 + lead_r * (float)lmax) < t32) {
-    const int so = (int)((long long)part64 * nchunks / npart64);
-    const int end = (int)((long long)(part64 + 1) * nchunks / npart64);
+    // Part 0 has no lead-in: it takes the outputs the others' lead-ins cost,
+    // m_q = q tau - (q - 1) r L with tau = (N + (P - 1) r L) / P; the lead-ins
+    // are then taken at these boundaries (scanned a little further than L).
+    const float sh = lead_r * (float)lmax;
+    const float tau = ((float)nchunks + (float)(npart64 - 1) * sh) / (float)npart64;
+    auto bound = [&](int q) {
+      if (q <= 0) return 0;
+      if (q >= npart64) return nchunks;
+      return min(nchunks, max(0, (int)((float)q * tau - (float)(q - 1) * sh + 0.5f)));
+    };
+    const int part64 = rw / nsl64;
+    const int so = bound(part64), end = max(so, bound(part64 + 1));
+    const int lead = horizon_lead(hz, so, 2 * lmax + 64);
     state_ws_body<E, DK, 64, 1, NORM>(a, tws, smem, head, rw % nsl64, sp, part64 == npart64 - 1, so - lead, so,
                                       end);
   } else {
