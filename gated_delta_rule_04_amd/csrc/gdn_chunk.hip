@@ -188,15 +188,21 @@ __device__ inline float lane_group_sum(float x) {
   return x;
 }
 
-// Sum of squares of a 16-byte piece of the operand dtype.
+// Sum of squares of a 16-byte piece of the operand dtype, accumulated onto s0
+// (bf16: two products per dot instruction, summed in fp32; its clamp flag
+// stays off, which would saturate the sum to [0, 1]).
 template <typename E>
-__device__ inline float sumsq16(const u32x4& u) {
-  float s = 0.f;
+__device__ inline float sumsq16(const u32x4& u, float s0 = 0.f) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  float s = s0;
   if constexpr (sizeof(E) == 2) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float lo = __uint_as_float(u[w] << 16), hi = __uint_as_float(u[w] & 0xffff0000u);
-      s += lo * lo + hi * hi;
+      // (the word goes through a local first: a bit cast applied straight
+      // to u[w] in this unrolled loop compiles to u[0] every time)
+      const uint32_t uw = u[w];
+      const bf16x2_t x = __builtin_bit_cast(bf16x2_t, uw);
+      s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
     }
   } else {
 #pragma unroll
@@ -1625,10 +1631,10 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
         // row stride puts 16 consecutive rows in distinct banks).
         if constexpr (NORM) {
           const E* row = Qrb + gb * C * LDK + lane * LDK;
-          float ss = 0.f;
+          float ss[4] = {0.f, 0.f, 0.f, 0.f};   // (four independent sums)
 #pragma unroll
-          for (int p = 0; p < CPR; ++p) ss += sumsq16<E>(*reinterpret_cast<const u32x4*>(row + p * EPC));
-          Gbuf[gb * GS + 5 * C + lane] = __builtin_amdgcn_rsqf(ss + a.pro.norm_eps);
+          for (int p = 0; p < CPR; ++p) ss[p & 3] = sumsq16<E>(*reinterpret_cast<const u32x4*>(row + p * EPC), ss[p & 3]);
+          Gbuf[gb * GS + 5 * C + lane] = __builtin_amdgcn_rsqf((ss[0] + ss[1]) + (ss[2] + ss[3]) + a.pro.norm_eps);
         }
         return;
       }
