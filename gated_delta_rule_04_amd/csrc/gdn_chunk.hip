@@ -333,16 +333,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         qv = ld_once(qg + off);
         *reinterpret_cast<u32x4*>(Qr + r * LDK + cc * EPC) = qv;
       }
-      if constexpr (NORM) {
+      if constexpr (NORM && WP) {   // (bf16: the K norms come from the Gram tiles below)
         const float ks = lane_group_sum<CPR>(sumsq16<E>(kv));
         const float nk = __builtin_amdgcn_rsqf(ks + a.pro.norm_eps);
+        const float nq = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(qv)) + a.pro.norm_eps);
         if (cc == 0) {
           Nk[r] = nk;
-          if (MODE == 1) Ksq[r] = ks * nk * nk;   // |k|^2 of the normalised key
-        }
-        if constexpr (WP) {
-          const float nq = __builtin_amdgcn_rsqf(lane_group_sum<CPR>(sumsq16<E>(qv)) + a.pro.norm_eps);
-          if (cc == 0) Nq[r] = nq;
+          Nq[r] = nq;
         }
       }
     }
@@ -380,6 +377,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
                               Qr + rb * 32 * LDK, LDK, lane);
     else
       tile_nt_k<DK / 16>(acca, Kr + jb * 32 * LDK, LDK, Kr + rb * 32 * LDK, LDK, lane);
+    // bf16: |k_r|^2 is the diagonal entry of a diagonal Gram tile (waves 0 and
+    // 2), held by one lane: the inverse norms of normalised keys, or the
+    // squared norms for the transition bound of scalar decay
+    if (!WP && jb == rb && (NORM || (MODE == 1 && a.horizon))) {
+      const int r = rb * 32 + col;
+      float dg = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dg = jb * 32 + acc_row(g, e, lane) == r ? acca[4 * g + e] : dg;
+      if (((col >> 2) & 1) == (lane >> 5)) {
+        if constexpr (NORM) {
+          const float nk = __builtin_amdgcn_rsqf(dg + a.pro.norm_eps);
+          Nk[r] = nk;
+          Ksq[r] = dg * nk * nk;   // |k|^2 of the normalised key
+        } else {
+          Ksq[r] = dg;
+        }
+      }
+    }
   }
   __syncthreads();   // K and Q are dead: A takes their bytes
   // A[r][j] = beta_r exp(G_r - G_j) k_r.k_j (j < r); P[r][j] = exp(G_r - G_j) q_r.k_j
@@ -413,16 +430,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) asm volatile("" ::"v"(w[v]));
-    // unnormalised keys: |k_r|^2 is the Gram tile's diagonal entry, held by
-    // one lane of the diagonal tiles (waves 0 and 2)
-    if (!NORM && MODE == 1 && a.horizon && jb == rb) {
-      float dg = 0.f;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dg = jb * 32 + acc_row(g, e, lane) == r ? acca[4 * g + e] : dg;
-      if (((col >> 2) & 1) == (lane >> 5)) Ksq[r] = dg;
-    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int j0 = jb * 32 + acc_row(g, 0, lane);
