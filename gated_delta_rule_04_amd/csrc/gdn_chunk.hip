@@ -107,24 +107,51 @@ __device__ inline int seq_of_slot(const PrefillArgs& a, int slot) {
 }
 
 // The chunk one prep workgroup handles: sequence b, head h, chunk n of the
-// sequence.  B rows of T tokens: workgroup (b H + h) N_chunks + n.  Packed
-// batch: workgroup h nslots + slot; false when no chunk falls on the slot.
+// sequence (B rows of T tokens), or record slot n of head h (packed batch).
+//   BY_CHUNK (scalar gates): the H heads of one chunk (slot) run back to back
+//     on one XCD.  Workgroups are dispatched round-robin over the eight XCDs,
+//     so workgroup i = 8 j + x takes head j % H of chunk (slot) 8 c + x of row
+//     b, where j / H = b C8 + c (C8 = ceil(N / 8)).  The gates are [.., T, H]
+//     fp32: the heads of a token share their cache lines, which then come
+//     from HBM once per chunk rather than once per head.
+//   otherwise (per-channel gates, contiguous per head and token): workgroup
+//     (b H + h) N + n (slot: h nslots + slot), so that consecutive workgroups
+//     write consecutive records.
+// False for a workgroup past the last chunk (slot), or a packed slot that no
+// chunk falls on.
 struct PrepAt {
   int b, h, n;
   Span sp;
 };
 
+template <bool BY_CHUNK>
+__host__ __device__ inline size_t prep_grid(int rows, int H, int nunits) {
+  return BY_CHUNK ? (size_t)8 * rows * H * ((nunits + 7) / 8) : (size_t)rows * H * nunits;
+}
+
+template <bool BY_CHUNK>
 __device__ inline bool prep_at(const PrefillArgs& a, int nchunks, PrepAt& p) {
-  if (!a.cu_seqlens) {
+  int unit, g;
+  if (BY_CHUNK) {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int c8 = (nchunks + 7) / 8;
+    p.h = j % a.H;
+    unit = 8 * ((j / a.H) % c8) + x;
+    g = j / a.H / c8;   // row
+  } else {
     const int bh = blockIdx.x / nchunks;
-    p.n = blockIdx.x % nchunks;
+    unit = blockIdx.x % nchunks;
     p.h = bh % a.H;
-    p.b = bh / a.H;
+    g = bh / a.H;
+  }
+  if (unit >= nchunks) return false;
+  if (!a.cu_seqlens) {
+    p.b = g;
+    p.n = unit;
     p.sp = seq_span(a, p.b, p.h);
     return true;
   }
-  p.h = blockIdx.x / a.nslots;
-  const int slot = blockIdx.x % a.nslots;
+  const int slot = unit;
   p.b = seq_of_slot(a, slot);
   p.sp = seq_span(a, p.b, p.h);
   p.n = slot - (int)(p.sp.rec0 - (size_t)p.h * a.nslots);
@@ -301,7 +328,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
   PrepAt at;
-  if (!prep_at(a, nchunks, at)) return;
+  if (!prep_at<true>(a, nchunks, at)) return;
   const int H = a.H, h = at.h, n = at.n;
   const int t0 = n * C, cn = min(C, at.sp.len - t0);
   const size_t tok0 = at.sp.tok0 + t0;   // first token of the chunk on the token axis
@@ -651,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
   PrepAt at;
-  if (!prep_at(a, nchunks, at)) return;
+  if (!prep_at<false>(a, nchunks, at)) return;
   const int H = a.H, h = at.h, n = at.n;
   const int t0 = n * C, cn = min(C, at.sp.len - t0);
   const size_t tok0 = at.sp.tok0 + t0;
@@ -2195,7 +2222,10 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
 template <typename E, int DK>
 hipError_t launch_prep(const PrefillArgs& a, E* tws, hipStream_t stream) {
   const int nchunks = a.cu_seqlens ? a.nslots : (a.T + C - 1) / C;
-  const size_t nprep = a.cu_seqlens ? (a.T > 0 ? (size_t)a.H * a.nslots : 0) : (size_t)a.B * a.H * nchunks;
+  const bool by_chunk = a.mode < 2;   // (the prep kernel of none or scalar decay)
+  const int rows = a.cu_seqlens ? 1 : a.B;
+  const size_t nprep = a.cu_seqlens && a.T == 0 ? 0
+                       : (by_chunk ? prep_grid<true>(rows, a.H, nchunks) : prep_grid<false>(rows, a.H, nchunks));
   if (nprep > 0) {
     dim3 grid((unsigned)nprep), block(kThreads);
     if (a.pro.qk_norm) {
