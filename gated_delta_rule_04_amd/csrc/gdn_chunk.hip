@@ -2047,21 +2047,6 @@ __device__ inline int geometric_split(int nchunks, int p, int npart, float r) {
   return min(nchunks, max(0, (int)((float)nchunks * f + 0.5f)));
 }
 
-template <typename E, int DK, int DVS, int MODE, bool NORM>
-__global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws, int npart,
-                                                             float lead_r) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[WsPlan<E, DK, DVS, (MODE >= 2), NORM>::total];
-  const int nsl = a.dv / DVS;
-  int head, rw;
-  ws_head(a, nsl * npart, head, rw);
-  const int sl = rw % nsl, part = rw / nsl;
-  const Span sp = seq_span(a, head / a.H, head % a.H);
-  const int nchunks = (sp.len + C - 1) / C;
-  state_ws_body<E, DK, DVS, MODE, NORM>(a, tws, smem, head, sl, sp, part == npart - 1, 0,
-                                        geometric_split(nchunks, part, npart, lead_r),
-                                        geometric_split(nchunks, part + 1, npart, lead_r));
-}
-
 // The history horizon of a split slice (scalar decay).  With every chunk's
 // transition bounded in norm by e^{c_n} (the prep kernel's bound array), the
 // state at chunk m is S_s Phi(s, m) + (the recurrence over [s, m) from a zero
@@ -2097,6 +2082,46 @@ __device__ inline int horizon_lead(const float* __restrict__ hz, int m, int cap)
     }
   }
   return m;
+}
+
+// Packed batch of up to 64 sequences: the sequence of rank k when they are
+// ordered by length, longest first (ties by index).  One wave, every lane
+// returns the same value.
+__device__ inline int seq_by_length_rank(const PrefillArgs& a, int k) {
+  const int lane = threadIdx.x & 63, N = a.B;
+  int len = -1;
+  if (lane < N) {   // (as seq_span clamps the offsets)
+    const int s0 = min(max(a.cu_seqlens[lane], 0), a.T);
+    len = min(max(a.cu_seqlens[lane + 1], s0), a.T) - s0;
+  }
+  int rank = 0;
+  for (int j = 0; j < N; ++j) {
+    const int lj = __shfl(len, j);
+    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+  }
+  const unsigned long long hit = __ballot(lane < N && rank == k);
+  return hit ? __ffsll((long long)hit) - 1 : k;
+}
+
+// Value slices in npart parts each (geometric split, lead-ins from chunk 0).
+// Packed batch with by_length (more slices than compute units): the
+// workgroups take the sequences longest first (up to 64 sequences), so that
+// the longest slices start in the first round and the short ones fill in
+// behind them instead of the longest starting last.
+template <typename E, int DK, int DVS, int MODE, bool NORM>
+__global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws, int npart,
+                                                             float lead_r, int by_length) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[WsPlan<E, DK, DVS, (MODE >= 2), NORM>::total];
+  const int nsl = a.dv / DVS;
+  int head, rw;
+  ws_head(a, nsl * npart, head, rw);
+  const int sl = rw % nsl, part = rw / nsl;
+  if (by_length && a.B <= 64) head = seq_by_length_rank(a, head / a.H) * a.H + head % a.H;
+  const Span sp = seq_span(a, head / a.H, head % a.H);
+  const int nchunks = (sp.len + C - 1) / C;
+  state_ws_body<E, DK, DVS, MODE, NORM>(a, tws, smem, head, sl, sp, part == npart - 1, 0,
+                                        geometric_split(nchunks, part, npart, lead_r),
+                                        geometric_split(nchunks, part + 1, npart, lead_r));
 }
 
 // Lead-in chunk cost relative to a full chunk of the eight-wave kernel
@@ -2174,6 +2199,8 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
   dim3 grid((unsigned)slices), block(kThreads);
   if constexpr (sizeof(E) == 2) {
     const int np = state_parts(slices);
+    // packed batch of more slices than compute units: longest sequences first
+    const int by_length = a.cu_seqlens && np == 1 && a.B > 1 && a.B <= 64 ? 1 : 0;
     grid = dim3((unsigned)(slices * np));
     const float r = kLeadCost;
     dim3 wblock(kWsThreads);
@@ -2186,18 +2213,18 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
       else
         hipLaunchKernelGGL((chunk_state_ws_horizon<E, DK, false>), grid, wblock, 0, stream, a, tws, np, r);
     } else if (a.mode == 0 && !nrm)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, false>), grid, wblock, 0, stream, a, tws, np, r);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, false>), grid, wblock, 0, stream, a, tws, np, r, by_length);
     else if (a.mode == 0)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, true>), grid, wblock, 0, stream, a, tws, np, r);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, true>), grid, wblock, 0, stream, a, tws, np, r, by_length);
     else if (a.mode == 1 && !nrm)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws, np, r);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws, np, r, by_length);
     else if (a.mode == 1)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws, np, r);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws, np, r, by_length);
     else if constexpr (DVS == 32) {   // the per-channel buffers leave room for 32-row slices only
       if (a.mode == 2)
-        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws, np, r);
+        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws, np, r, by_length);
       else
-        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws, np, r);
+        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws, np, r, by_length);
     } else {
       return hipErrorInvalidConfiguration;
     }

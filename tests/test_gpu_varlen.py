@@ -131,3 +131,15 @@ def test_varlen_packed_workload_sampled(gpu):
     eo, eS = _rel_seq(o[:, :, heads], ro, S[:, heads], rS, inp["cu_seqlens"].tolist())
     print("packed workload: rel err o %.2e S %.2e" % (eo, eS), flush=True)
     assert eo <= TOL[w.dtype] and eS <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_varlen_many_rows_longest_first(gpu, mode):
+    """Twelve rows of very different lengths on 32 heads: more value slices than
+    compute units, so the state kernel takes the rows longest first.  Every
+    (row, head) against the oracle."""
+    lens = (1500, 64, 777, 1, 1203, 300, 65, 950, 0, 431, 1499, 130)
+    w = W.Packed("packed_longest_first", len(lens), sum(lens), 32, 128, 128, torch.bfloat16,
+                 GATE_OF_MODE[mode], 0.1, seed=49, lengths=lens)
+    eo, eS = _check(gpu, w)
+    print("  rel err o %.2e, S_final %.2e" % (eo, eS))
