@@ -617,12 +617,19 @@ __device__ inline u32x4 mul16(const u32x4& a, const u32x4& b) {
 constexpr float kSplitLimit = 64.f;
 
 // LDS: region 1 holds G (fp32 [C][LDG]) while the operands are built, then A
-// (fp32 [C][LDA], later T) and P [C][LDT]; region 2 holds three 32-row operand
-// tiles, then L^-1 and Mt of the solve; then the unscaled K and Q rows of the
-// current diagonal block, prefix segment totals, beta and the bit masks of
-// the channels left out of each diagonal block's MFMA.
+// (fp32 [C][LDA], later T) and P [C][LDT]; region 2 holds the 32-row operand
+// tiles; then prefix segment totals, beta and the bit masks of the channels
+// left out of each diagonal block's MFMA.
+//   bf16 (CMP, 52.5 KB: three workgroups per compute unit): two operand tiles,
+//     the r-side one taking the K operand for the A tile and then the Q
+//     operand for the P tile; the solve runs in place in A's bytes and writes
+//     T straight to the record; the exact path of strongly decayed channels
+//     reads the unscaled rows from global memory.
+//   fp32: three operand tiles, then L^-1 and Mt of the solve; the unscaled K
+//     and Q rows of the current diagonal block.
 template <typename E, int DK, bool NORM>
 struct KdaPrepPlan {
+  static constexpr bool CMP = sizeof(E) == 2;
   static constexpr int PAD = 16 / (int)sizeof(E);
   static constexpr int LDK = DK + PAD;
   static constexpr int LDG = DK + 4;
@@ -637,21 +644,25 @@ struct KdaPrepPlan {
   static constexpr size_t ops = r1;
   static constexpr size_t li = ops;
   static constexpr size_t mt = li + (size_t)C * LDA * 4;
-  static constexpr size_t r2 = cmax((size_t)3 * 32 * LDK * sizeof(E), (size_t)C * LDA * 4 + 32 * LDM * 4);
+  static constexpr size_t r2 = CMP ? (size_t)2 * 32 * LDK * sizeof(E)
+                                   : cmax((size_t)3 * 32 * LDK * sizeof(E), (size_t)C * LDA * 4 + 32 * LDM * 4);
   static constexpr size_t raw = ops + r2;
-  static constexpr size_t tot = raw + (size_t)2 * 32 * LDK * sizeof(E);
+  static constexpr size_t tot = raw + (CMP ? 0 : (size_t)2 * 32 * LDK * sizeof(E));
   static constexpr size_t bt = tot + (size_t)NSEG * DK * 4;
   static constexpr size_t msk = bt + C * 4;
   static constexpr size_t nrm = msk + (size_t)2 * (DK / 32) * 4;   // inverse norms of K, Q rows
-  static constexpr size_t total = nrm + (NORM ? 2 * C * 4 : 0);
+  // (CMP) one channel's 32 unscaled K values of a diagonal block, for its exact path
+  static constexpr size_t ksc = nrm + (NORM ? 2 * C * 4 : 0);
+  static constexpr size_t total = ksc + (CMP ? 32 * 4 : 0);
 };
 
 template <typename E, int DK, bool NORM, bool G2>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __restrict__ tws,
-                                                           int nchunks) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 3 : 1)))
+void chunk_prep_kda(PrefillArgs a, E* __restrict__ tws, int nchunks) {
   static_assert(!(NORM && G2), "the erase-gate variant takes no prologue");
   using L = KdaPrepPlan<E, DK, NORM>;
   using R = KdaRec<E, DK>;
+  constexpr bool CMP = L::CMP;
   constexpr int EPC = 16 / (int)sizeof(E);
   constexpr int CPR = DK / EPC;
   constexpr int LDK = L::LDK, LDG = L::LDG, LDA = L::LDA, LDT = L::LDT;
@@ -664,17 +675,18 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   E* Tm = reinterpret_cast<E*>(smem + L::am);
   E* Pm = reinterpret_cast<E*>(smem + L::pm);
   E* Rop = reinterpret_cast<E*>(smem + L::ops);   // r-side K operand
-  E* Qop = Rop + 32 * LDK;                         // r-side Q operand
-  E* Cop = Rop + 64 * LDK;                         // j-side K operand
+  E* Qop = CMP ? Rop : Rop + 32 * LDK;             // r-side Q operand (CMP: after the A tile)
+  E* Cop = Rop + (CMP ? 32 : 64) * LDK;            // j-side K operand
   float* Li = reinterpret_cast<float*>(smem + L::li);
   float* Mt = reinterpret_cast<float*>(smem + L::mt);
-  E* Kraw = reinterpret_cast<E*>(smem + L::raw);   // unscaled rows of the current block
+  E* Kraw = reinterpret_cast<E*>(smem + L::raw);   // unscaled rows of the current block (fp32)
   E* Qraw = Kraw + 32 * LDK;
   float* Tot = reinterpret_cast<float*>(smem + L::tot);
   float* Bt = reinterpret_cast<float*>(smem + L::bt);
   uint32_t* Msk = reinterpret_cast<uint32_t*>(smem + L::msk);   // [2][DK / 32]
   float* Nk = reinterpret_cast<float*>(smem + L::nrm);            // NORM only
   float* Nq = Nk + C;
+  float* Ksc = reinterpret_cast<float*>(smem + L::ksc);           // CMP only
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
   PrepAt at;
@@ -779,10 +791,45 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   //                                    wave 0: A(1,0)   wave 1: P(1,0)
   // (tile (R, J): rows r of block R, columns j of block J).  Passes 0 and 1 also
   // write Kg, Qg and Kc.  Accumulators stay in registers until G is dead.
+  // CMP: the A tile first; the Q operand waits in registers (yq) and then
+  // takes the K operand's tile for the P tile.
+  // Exact contributions of the channels left out of diagonal block D's MFMA
+  // (the P tile with its Q rows when isp, else the A tile), onto acc.
+  auto exact = [&](f32x16& acc, int D, bool isp) __attribute__((always_inline)) {
+    const int r = 32 * D + col;
+    const float xn = NORM ? (isp ? Nq[r] : Nk[r]) : 1.f;   // the rows are unscaled
+    const E* xg = (isp ? qgl : kgl) + (size_t)min(r, cn - 1) * qk_tok;
+#pragma unroll 1
+    for (int wd = 0; wd < DK / 32; ++wd) {
+      uint32_t bits = __builtin_amdgcn_readfirstlane(Msk[D * (DK / 32) + wd]);
+      while (bits) {
+        const int c = 32 * wd + __builtin_ctz(bits);
+        bits &= bits - 1;
+        const float gr = Gl[r * LDG + c];
+        if constexpr (CMP) {   // the channel's K values of the block, one wave at a time
+          if (lane < 32) Ksc[lane] = (float)kgl[(size_t)min(32 * D + lane, cn - 1) * qk_tok + c];
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's own row is written
+        }
+        float xv = (float)(CMP ? xg[c] : (isp ? Qraw : Kraw)[col * LDK + c]) * xn;
+        // G2, A tiles: the row side is the erase direction; its gate comes
+        // from HBM (a channel taking this path is rare)
+        if (G2 && !isp) xv *= (float)bgl[(size_t)min(r, cn - 1) * qk_tok + c];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int jl = acc_row(v >> 2, v & 3, lane), j = 32 * D + jl;
+          const float w = __expf(fminf(gr - Gl[j * LDG + c], 0.f)) * (NORM ? Nk[j] : 1.f);
+          const float kj = CMP ? Ksc[jl] : (float)Kraw[jl * LDK + c];
+          const float t = xv * kj * w;
+          acc[v] += j <= r ? t : 0.f;
+        }
+      }
+    }
+  };
   f32x16 acc0 = zero16(), acc1 = zero16();
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     if (pass > 0) __syncthreads();   // the previous pass's tiles are consumed
+    u32x4 yq[IPT];                   // (CMP) the r-side Q operand pieces of this pass
 #pragma unroll
     for (int m = (pass == 1 ? IPT : 0); m < (pass == 0 ? IPT : 2 * IPT); ++m) {
       const int it = tid + kThreads * m, r = it / CPR, c0 = (it % CPR) * EPC;
@@ -836,8 +883,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
       // diagonal blocks: channels outside the split take zero operands
       uint32_t keep = ~0u;
       if (pass < 2) {
-        *reinterpret_cast<u32x4*>(Kraw + lr * LDK + c0) = kraw;
-        *reinterpret_cast<u32x4*>(Qraw + lr * LDK + c0) = qraw;
+        if constexpr (!CMP) {
+          *reinterpret_cast<u32x4*>(Kraw + lr * LDK + c0) = kraw;
+          *reinterpret_cast<u32x4*>(Qraw + lr * LDK + c0) = qraw;
+        }
         keep = ~(Msk[pass * (DK / 32) + (c0 >> 5)] >> (c0 & 31));
       }
       if (pass < 2 || r >= 32) {   // r side: exp(G_r - G_m)
@@ -849,7 +898,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
           y[e] = k1 ? qf[e] * w : 0.f;
         }
         *reinterpret_cast<u32x4*>(Rop + lr * LDK + c0) = pack16<E>(x);
-        *reinterpret_cast<u32x4*>(Qop + lr * LDK + c0) = pack16<E>(y);
+        if constexpr (CMP) yq[m % IPT] = pack16<E>(y);
+        else *reinterpret_cast<u32x4*>(Qop + lr * LDK + c0) = pack16<E>(y);
       }
       if (pass < 2 || r < 32) {    // j side: exp(G_m - G_j)
 #pragma unroll
@@ -860,32 +910,26 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
     __syncthreads();
     // tile (R, J) accumulates rows j (Cop) x columns r (Rop or Qop)
     const bool mine = pass == 2 ? wave < 2 : (wave >> 1) == pass;
-    if (mine) tile_nt_k<DK / 16>(pass == 2 ? acc1 : acc0, Cop, LDK, (wave & 1) ? Qop : Rop, LDK, lane);
-    if (pass < 2 && mine) {
-      // exact contributions of the channels left out of this diagonal block
-      const int r = 32 * pass + col;
-      const E* xr = ((wave & 1) ? Qraw : Kraw) + col * LDK;
-      const float xn = NORM ? ((wave & 1) ? Nq[r] : Nk[r]) : 1.f;   // the rows are unscaled
-#pragma unroll 1
-      for (int wd = 0; wd < DK / 32; ++wd) {
-        uint32_t bits = __builtin_amdgcn_readfirstlane(Msk[pass * (DK / 32) + wd]);
-        while (bits) {
-          const int c = 32 * wd + __builtin_ctz(bits);
-          bits &= bits - 1;
-          const float gr = Gl[r * LDG + c];
-          float xv = (float)xr[c] * xn;
-          // G2, A tiles: the row side is the erase direction; its gate comes
-          // from HBM (a channel taking this path is rare)
-          if (G2 && !(wave & 1)) xv *= (float)bgl[(size_t)min(r, cn - 1) * qk_tok + c];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int jl = acc_row(v >> 2, v & 3, lane), j = 32 * pass + jl;
-            const float w = __expf(fminf(gr - Gl[j * LDG + c], 0.f)) * (NORM ? Nk[j] : 1.f);
-            const float t = xv * (float)Kraw[jl * LDK + c] * w;
-            acc0[v] += j <= r ? t : 0.f;
-          }
-        }
+    f32x16& acc = pass == 2 ? acc1 : acc0;
+    if constexpr (CMP) {
+      if (mine && !(wave & 1)) {
+        tile_nt_k<DK / 16>(acc, Cop, LDK, Rop, LDK, lane);
+        if (pass < 2) exact(acc, pass, false);
       }
+      __syncthreads();   // the K operand is consumed: the Q operand takes its tile
+#pragma unroll
+      for (int m = (pass == 1 ? IPT : 0); m < (pass == 0 ? IPT : 2 * IPT); ++m) {
+        const int it = tid + kThreads * m, r = it / CPR, c0 = (it % CPR) * EPC;
+        if (pass < 2 || r >= 32) *reinterpret_cast<u32x4*>(Rop + (r & 31) * LDK + c0) = yq[m % IPT];
+      }
+      __syncthreads();
+      if (mine && (wave & 1)) {
+        tile_nt_k<DK / 16>(acc, Cop, LDK, Rop, LDK, lane);
+        if (pass < 2) exact(acc, pass, true);
+      }
+    } else {
+      if (mine) tile_nt_k<DK / 16>(acc, Cop, LDK, (wave & 1) ? Qop : Rop, LDK, lane);
+      if (pass < 2 && mine) exact(acc, pass, wave & 1);
     }
   }
   __syncthreads();   // G is dead: A and P take region 1
@@ -937,13 +981,18 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kda(PrefillArgs a, E* __r
   }
   __syncthreads();
 
-  tri_solve<E>(Am, Li, Mt, Bt, Tm, tid);
-  // T and P -> the record, 64 x 64 contiguous each, 16-byte stores
+  // T (CMP: in place, straight to the record) and P -> the record, 64 x 64
+  // contiguous each, 16-byte stores
+  if constexpr (CMP)
+    tri_solve<E, LDA, true>(Am, Am, Am + 32, Bt, rec + R::t, tid);
+  else
+    tri_solve<E>(Am, Li, Mt, Bt, Tm, tid);
   {
     constexpr int CPT = C / EPC;
     for (int q = tid; q < C * CPT; q += kThreads) {
       const int r = q / CPT, cc = q % CPT;
-      st_once(rec + R::t + r * C + cc * EPC, *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC));
+      if constexpr (!CMP)
+        st_once(rec + R::t + r * C + cc * EPC, *reinterpret_cast<const u32x4*>(Tm + r * LDT + cc * EPC));
       st_once(rec + R::p + r * C + cc * EPC, *reinterpret_cast<const u32x4*>(Pm + r * LDT + cc * EPC));
     }
   }
