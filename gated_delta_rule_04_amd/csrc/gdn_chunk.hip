@@ -2153,24 +2153,79 @@ __device__ inline int seq_by_length_rank(const PrefillArgs& a, int k) {
 }
 
 // Value slices in npart parts each (geometric split, lead-ins from chunk 0).
-// Packed batch with by_length (more slices than compute units): the
-// workgroups take the sequences longest first (up to 64 sequences), so that
-// the longest slices start in the first round and the short ones fill in
-// behind them instead of the longest starting last.
+// Packed batch of up to 64 sequences with more slices than compute units
+// (split_above >= 0): the workgroups take the sequences longest first, so
+// that the longest slices start in the first round and the short ones fill in
+// behind them; the slices of a sequence of more than split_above chunks run
+// in two parts, the second reaching its start by a lead-in (from the history
+// horizon when the bound array is there); the grid has room for the parts of
+// split_max sequences.  Workgroup i takes head x + 8 k of
+// that order on XCD x = i % 8 (its slices and parts back to back in that
+// XCD's queue, which then shares their K, Q and records in its L2); the split
+// heads come first, and the workgroups past the last head, at the end of the
+// grid, return at once.
 template <typename E, int DK, int DVS, int MODE, bool NORM>
 __global__ __launch_bounds__(kWsThreads) void chunk_state_ws(PrefillArgs a, const E* __restrict__ tws, int npart,
-                                                             float lead_r, int by_length) {
+                                                             float lead_r, int split_above, int split_max) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[WsPlan<E, DK, DVS, (MODE >= 2), NORM>::total];
   const int nsl = a.dv / DVS;
-  int head, rw;
-  ws_head(a, nsl * npart, head, rw);
-  const int sl = rw % nsl, part = rw / nsl;
-  if (by_length && a.B <= 64) head = seq_by_length_rank(a, head / a.H) * a.H + head % a.H;
+  if (split_above < 0) {
+    int head, rw;
+    ws_head(a, nsl * npart, head, rw);
+    const int sl = rw % nsl, part = rw / nsl;
+    const Span sp = seq_span(a, head / a.H, head % a.H);
+    const int nchunks = (sp.len + C - 1) / C;
+    state_ws_body<E, DK, DVS, MODE, NORM>(a, tws, smem, head, sl, sp, part == npart - 1, 0,
+                                          geometric_split(nchunks, part, npart, lead_r),
+                                          geometric_split(nchunks, part + 1, npart, lead_r));
+    return;
+  }
+  // sequences (ranks 0 .. nsq - 1) whose slices are split
+  const int lane = threadIdx.x & 63;
+  int nsq = 0;
+  {
+    bool longer = false;
+    if (lane < a.B) {
+      const int s0 = min(max(a.cu_seqlens[lane], 0), a.T);
+      longer = (min(max(a.cu_seqlens[lane + 1], s0), a.T) - s0 + C - 1) / C > split_above;
+    }
+    nsq = min(__popcll(__ballot(longer)), split_max);   // (the grid's room)
+  }
+  const int nh = a.B * a.H, ks = nsq * a.H;   // heads; split heads (ranks 0 .. ks - 1)
+  const int x = blockIdx.x & 7, q = blockIdx.x >> 3, w2 = 2 * nsl;
+  const int sx = ks > x ? (ks - x + 7) / 8 : 0;   // split heads on this XCD
+  int k, within;
+  if (q < sx * w2) {
+    k = q / w2;
+    within = q % w2;
+  } else {
+    k = sx + (q - sx * w2) / nsl;
+    within = (q - sx * w2) % nsl;
+  }
+  const int hr = x + 8 * k;   // head rank
+  if (hr >= nh) return;
+  const int sl = within % nsl, part = within / nsl;
+  const int head = seq_by_length_rank(a, hr / a.H) * a.H + hr % a.H;
   const Span sp = seq_span(a, head / a.H, head % a.H);
   const int nchunks = (sp.len + C - 1) / C;
-  state_ws_body<E, DK, DVS, MODE, NORM>(a, tws, smem, head, sl, sp, part == npart - 1, 0,
-                                        geometric_split(nchunks, part, npart, lead_r),
-                                        geometric_split(nchunks, part + 1, npart, lead_r));
+  int lead0 = 0, n_so = 0, n_end = nchunks;
+  bool last = true;
+  if (hr < ks) {
+    // two parts: part 0 takes chunks [0, m), part 1 a lead-in of l chunks and
+    // [m, N), m balancing m against r l + N - m
+    int m = geometric_split(nchunks, 1, 2, lead_r), lead = m;
+    if (MODE == 1 && a.horizon) {
+      const float* hz = a.horizon + sp.rec0;
+      const int l0 = horizon_lead(hz, nchunks / 2, nchunks / 2);
+      m = min(nchunks - 1, (int)(0.5f * ((float)nchunks + lead_r * (float)l0) + 0.5f));
+      lead = horizon_lead(hz, m, m);
+    }
+    n_so = part == 0 ? 0 : m;
+    n_end = part == 0 ? m : nchunks;
+    lead0 = part == 0 ? 0 : m - lead;
+    last = part == 1;
+  }
+  state_ws_body<E, DK, DVS, MODE, NORM>(a, tws, smem, head, sl, sp, last, lead0, n_so, n_end);
 }
 
 // Lead-in chunk cost relative to a full chunk of the eight-wave kernel
@@ -2248,9 +2303,23 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
   dim3 grid((unsigned)slices), block(kThreads);
   if constexpr (sizeof(E) == 2) {
     const int np = state_parts(slices);
-    // packed batch of more slices than compute units: longest sequences first
-    const int by_length = a.cu_seqlens && np == 1 && a.B > 1 && a.B <= 64 ? 1 : 0;
+    // packed batch of more slices than compute units: longest sequences first,
+    // the slices longer than an even share of chunks per compute unit in two
+    // parts (Sum ceil(len_s / C) <= T / C + N bounds the chunks; at most
+    // (T / C + N) / (split + 1) sequences exceed split chunks)
+    int split = -1, nsq = 0;
     grid = dim3((unsigned)(slices * np));
+    if (a.cu_seqlens && np == 1 && a.B > 1 && a.B <= 64) {
+      int dev = 0, cus = 256;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+      const long long chunks = (long long)a.T / C + a.B, nsl = a.dv / DVS;
+      split = (int)(chunks * (long long)slices / ((long long)a.B * cus)) + 1;
+      nsq = (int)std::min<long long>(a.B, chunks / (split + 1));
+      const long long heads8 = ((long long)a.B * a.H + 7) / 8, split8 = (nsq * a.H + 7) / 8;
+      grid = dim3((unsigned)(8 * (heads8 * nsl + split8 * nsl)));
+    }
     const float r = kLeadCost;
     dim3 wblock(kWsThreads);
     // (normalised q and k: the per-channel records carry normalised operands, so
@@ -2262,18 +2331,18 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
       else
         hipLaunchKernelGGL((chunk_state_ws_horizon<E, DK, false>), grid, wblock, 0, stream, a, tws, np, r);
     } else if (a.mode == 0 && !nrm)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, false>), grid, wblock, 0, stream, a, tws, np, r, by_length);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
     else if (a.mode == 0)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, true>), grid, wblock, 0, stream, a, tws, np, r, by_length);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 0, true>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
     else if (a.mode == 1 && !nrm)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws, np, r, by_length);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
     else if (a.mode == 1)
-      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws, np, r, by_length);
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
     else if constexpr (DVS == 32) {   // the per-channel buffers leave room for 32-row slices only
       if (a.mode == 2)
-        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws, np, r, by_length);
+        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
       else
-        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws, np, r, by_length);
+        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
     } else {
       return hipErrorInvalidConfiguration;
     }
@@ -2332,9 +2401,11 @@ hipError_t launch_dk(const PrefillArgs& a0, void* workspace, hipStream_t stream)
   PrefillArgs a = a0;
   const long long wg64 = (long long)a.B * a.H * (a.dv / 64);
   const bool dvs64 = sizeof(E) == 2 && wg64 >= 256 && a.mode < 2;
-  // Scalar decay in bf16 with split 32-row slices: the prep kernel also writes
-  // the transition bounds, after the records.
-  if (sizeof(E) == 2 && a.mode == 1 && !dvs64 && state_parts((size_t)a.B * a.H * (a.dv / 32)) > 1) {
+  // Scalar decay in bf16 with split value slices (a head's, or a packed
+  // batch's longest rows'): the prep kernel also writes the transition
+  // bounds, after the records.
+  if (sizeof(E) == 2 && a.mode == 1 &&
+      (a.cu_seqlens || (!dvs64 && state_parts((size_t)a.B * a.H * (a.dv / 32)) > 1))) {
     const size_t nrec = a.cu_seqlens ? (size_t)a.H * a.nslots : (size_t)a.B * a.H * ((a.T + C - 1) / C);
     a.horizon = reinterpret_cast<float*>(tws + nrec * GateRec<E>::elems);
   }

@@ -143,3 +143,17 @@ def test_varlen_many_rows_longest_first(gpu, mode):
                  GATE_OF_MODE[mode], 0.1, seed=49, lengths=lens)
     eo, eS = _check(gpu, w)
     print("  rel err o %.2e, S_final %.2e" % (eo, eS))
+
+
+@pytest.mark.parametrize("mode,gate", [(0, "none"), (1, "exp01"), (1, "range090"), (2, "exp01_channel")])
+def test_varlen_long_rows_split(gpu, mode, gate):
+    """Eight rows on 16 heads, two of them (4000 and 2500 tokens) far longer than
+    an even share of chunks per compute unit: their value slices run in two
+    parts, the second reaching its start by a lead-in (from the history horizon
+    under scalar decay, else from chunk 0).  Every (row, head) against the
+    oracle, S0 drawn (std 0.1)."""
+    lens = (4000, 300, 200, 100, 64, 1, 2500, 0)
+    w = W.Packed("packed_long_rows", len(lens), sum(lens), 16, 128, 128, torch.bfloat16,
+                 gate, 0.1, seed=50, lengths=lens)
+    eo, eS = _check(gpu, w)
+    print("  rel err o %.2e, S_final %.2e" % (eo, eS))
