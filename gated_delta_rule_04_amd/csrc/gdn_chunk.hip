@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   __syncthreads();
 
   if constexpr (L::inplace) {
-    tri_solve<E, L::ldm, true>(Am, Li, Mt, Bt, rec + R::t, tid);   // T straight to the record
+    tri_solve<E, L::ldm, true, true>(Am, Li, Mt, Bt, rec + R::t, tid);   // T straight to the record
     // The chunk's state transition S -> S prod_t alpha_t (I - beta_t k_t k_t^T)
     // has spectral norm at most prod_t alpha_t max(1, |1 - beta_t |k_t|^2|)
     // (each factor is symmetric with eigenvalues 1 and 1 - beta_t |k_t|^2); its
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       if (lane == 0) a.horizon[at.sp.rec0 + n] = G[C - 1] + grow;
     }
   } else {
-    tri_solve<E, L::ldm>(Am, Li, Mt, Bt, Tm, tid);
+    tri_solve<E, L::ldm, false, true>(Am, Li, Mt, Bt, Tm, tid);
     // T -> the record, 64 x 64 contiguous, 16-byte stores
     constexpr int CPT = C / EPC;
     static_assert(C * CPT % kThreads == 0, "T must split evenly over the threads");
@@ -984,9 +984,9 @@ void chunk_prep_kda(PrefillArgs a, E* __restrict__ tws, int nchunks) {
   // T (CMP: in place, straight to the record) and P -> the record, 64 x 64
   // contiguous each, 16-byte stores
   if constexpr (CMP)
-    tri_solve<E, LDA, true>(Am, Am, Am + 32, Bt, rec + R::t, tid);
+    tri_solve<E, LDA, true, true>(Am, Am, Am + 32, Bt, rec + R::t, tid);
   else
-    tri_solve<E>(Am, Li, Mt, Bt, Tm, tid);
+    tri_solve<E, SolveLd<E>::LDM, false, true>(Am, Li, Mt, Bt, Tm, tid);
   {
     constexpr int CPT = C / EPC;
     for (int q = tid; q < C * CPT; q += kThreads) {

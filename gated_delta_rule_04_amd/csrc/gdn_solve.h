@@ -31,6 +31,9 @@ __device__ inline float quad_sum(float x) {
 //       share Am's bytes unless Li is Am), or (DIRECT) the chunk record in
 //       global memory, [C][C]
 // All threads of the workgroup take part; it ends with a barrier unless DIRECT.
+// COLUMNS: the diagonal blocks are inverted by wave 0 alone, one column per
+// lane (a quarter of the vector instructions, a longer dependent chain: for
+// kernels that run many workgroups per compute unit).
 template <typename E>
 struct SolveLd {
   static constexpr int LDA = C + 4;
@@ -38,15 +41,46 @@ struct SolveLd {
   static constexpr int LDM = 32 + 4;
 };
 
-template <typename E, int LDM = SolveLd<E>::LDM, bool DIRECT = false>
+template <typename E, int LDM = SolveLd<E>::LDM, bool DIRECT = false, bool COLUMNS = false>
 __device__ __attribute__((always_inline)) inline void tri_solve(const float* Am, float* Li, float* Mt,
                                                                 const float* Bt, E* Tm, int tid) {
   constexpr int LDA = SolveLd<E>::LDA, LDT = DIRECT ? C : SolveLd<E>::LDT;
   const int lane = tid & 63, wave = tid >> 6;
-  // (a) inverse of each unit-lower 16x16 diagonal block: wave w owns block w;
-  // lane 4c + p computes column c, rows 4p .. 4p + 3, summing its part of each
-  // row's dot product and finishing it across the quad.
-  {
+  if constexpr (COLUMNS) {
+    // (a) inverse of each unit-lower 16x16 diagonal block by forward
+    // substitution down one column: lane 16 I + c of wave 0 takes column c of
+    // block I, y_c = 1 and y_i = -sum_{j < i} A_ij y_j below it (y_j = 0 above
+    // c, so every lane runs the same rows; above the diagonal y_i is -0).
+    if (wave == 0) {
+      const int I = lane >> 4, c = lane & 15;
+      const float* ab = Am + (16 * I) * LDA + 16 * I;
+      float y[16];
+      y[0] = c == 0 ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        float s0 = 0.f, s1 = 0.f;   // (two partial sums: a shorter chain)
+#pragma unroll
+        for (int j4 = 0; j4 < i; j4 += 4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(ab + i * LDA + j4);
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (j4 + e >= i) break;
+            if ((j4 + e) & 1)
+              s1 += av[e] * y[j4 + e];
+            else
+              s0 += av[e] * y[j4 + e];
+          }
+        }
+        y[i] = i == c ? 1.f : -(s0 + s1);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Li[(16 * I + i) * LDA + 16 * I + c] = y[i];
+    }
+  } else {
+    // (a) inverse of each unit-lower 16x16 diagonal block: wave w owns block w;
+    // lane 4c + p computes column c, rows 4p .. 4p + 3, summing its part of each
+    // row's dot product and finishing it across the quad.
     const int I = wave, c = lane >> 2, p = lane & 3;
     const float* arow = Am + (16 * I) * LDA + 16 * I + 4 * p;
     float y[4] = {0.f, 0.f, 0.f, 0.f};
