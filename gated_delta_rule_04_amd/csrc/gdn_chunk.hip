@@ -301,7 +301,9 @@ struct PrepPlan {
   static constexpr size_t nk = g + 2 * C * 4;
   // squared K row norms (the transition bound of scalar decay)
   static constexpr size_t ksq = g + (NORM ? (inplace ? 3 : 4) : 2) * C * 4;
-  static constexpr size_t total = ksq + C * 4;
+  // bf16, normalised: G_j - ln nk_j (the column factor of A inside its weight)
+  static constexpr size_t gn = ksq + C * 4;
+  static constexpr size_t total = gn + (NORM && inplace ? C * 4 : 0);
 };
 
 template <typename E, int DK, int MODE, bool NORM>
@@ -325,6 +327,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   float* Nk = reinterpret_cast<float*>(smem + L::nk);   // NORM only
   float* Nq = Nk + C;                                   // NORM, fp32 only
   float* Ksq = reinterpret_cast<float*>(smem + L::ksq);  // scalar decay with a bound array only
+  float* Gn = reinterpret_cast<float*>(smem + L::gn);    // bf16, normalised only
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, col = lane & 31;
   PrepAt at;
@@ -418,6 +421,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         if constexpr (NORM) {
           const float nk = __builtin_amdgcn_rsqf(dg + a.pro.norm_eps);
           Nk[r] = nk;
+          Gn[r] = G[r] - __logf(nk);
           Ksq[r] = dg * nk * nk;   // |k|^2 of the normalised key
         } else {
           Ksq[r] = dg;
@@ -430,8 +434,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   // (j <= r).  Every weight is formed clamped to at most 1 before the masks
   // select (left conditional, its loads would sink into per-element branches).
   // Normalised q and k: A takes nk_r nk_j, P nq_r nk_j (the row factor joins
-  // beta_r, the column factor the weight).
+  // beta_r, the column factor the weight; in bf16 nk_j enters the exponent,
+  // and the clamp, at e^88, then only keeps the masked weights finite).
   if (wave < 3) {
+    constexpr bool GNJ = NORM && !WP;
+    constexpr float WMAX = GNJ ? 88.f : 0.f;
+    const float* Gj = GNJ ? Gn : G;
     const int r = rb * 32 + col;
     const float Gr = G[r];
     float br = Bt[r], pr = 1.f;
@@ -442,12 +450,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     float w[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float4 gj = *reinterpret_cast<const float4*>(G + jb * 32 + acc_row(g, 0, lane));
-      w[4 * g + 0] = __expf(fminf(Gr - gj.x, 0.f));
-      w[4 * g + 1] = __expf(fminf(Gr - gj.y, 0.f));
-      w[4 * g + 2] = __expf(fminf(Gr - gj.z, 0.f));
-      w[4 * g + 3] = __expf(fminf(Gr - gj.w, 0.f));
-      if constexpr (NORM) {
+      const float4 gj = *reinterpret_cast<const float4*>(Gj + jb * 32 + acc_row(g, 0, lane));
+      w[4 * g + 0] = __expf(fminf(Gr - gj.x, WMAX));
+      w[4 * g + 1] = __expf(fminf(Gr - gj.y, WMAX));
+      w[4 * g + 2] = __expf(fminf(Gr - gj.z, WMAX));
+      w[4 * g + 3] = __expf(fminf(Gr - gj.w, WMAX));
+      if constexpr (NORM && WP) {
         const float4 nj = *reinterpret_cast<const float4*>(Nk + jb * 32 + acc_row(g, 0, lane));
         w[4 * g + 0] *= nj.x;
         w[4 * g + 1] *= nj.y;
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
       gw[C + lane] = eg * nk;
       gw[2 * C + lane] = __expf(G[C - 1] - g) * nk;
       gw[3 * C + lane] = WP ? eg * Nq[lane] : eg;
-      gw[4 * C + lane] = g - __logf(nk);
+      gw[4 * C + lane] = WP ? g - __logf(nk) : Gn[lane];
     }
   }
   __syncthreads();
@@ -1707,20 +1715,7 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
     // the weight of a masked entry may overflow).
     auto form_p = [&](int gb) __attribute__((always_inline)) {
       const int d = wave - 4;
-      if (d >= 3) {
-        // normalised q: the fourth data wave takes the inverse norms of the
-        // chunk's Q rows meanwhile, for the chain's output rows: lane r sums
-        // row r, all lanes reading the same 16-byte piece index at a time (the
-        // row stride puts 16 consecutive rows in distinct banks).
-        if constexpr (NORM) {
-          const E* row = Qrb + gb * C * LDK + lane * LDK;
-          float ss[4] = {0.f, 0.f, 0.f, 0.f};   // (four independent sums)
-#pragma unroll
-          for (int p = 0; p < CPR; ++p) ss[p & 3] = sumsq16<E>(*reinterpret_cast<const u32x4*>(row + p * EPC), ss[p & 3]);
-          Gbuf[gb * GS + 5 * C + lane] = __builtin_amdgcn_rsqf((ss[0] + ss[1]) + (ss[2] + ss[3]) + a.pro.norm_eps);
-        }
-        return;
-      }
+      if (d >= 3) return;
       const int jb = d == 2 ? 1 : 0, rb = d == 0 ? 0 : 1;
       f32x16 acc = zero16();
       tile_nt_k<DK / 16, E, true, kFormPAhead>(acc, Ksb + gb * C * LDKS + jb * 32 * LDKS, LDKS,
@@ -1925,6 +1920,20 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
         for (int v = 0; v < 16; ++v) oacc[v] *= egr;
       }
     }
+    // Normalised q: the inverse norms of the chunk's Q rows, for its output
+    // rows in interval B (the chain waits for the data waves here anyway):
+    // wave w takes rows 16 w .. 16 w + 15, four lanes per row, a quarter of
+    // the row's 16-byte pieces each (at d_k = 128, 16 rows x 4 pieces in
+    // distinct banks per read).
+    if constexpr (NORM && !SO) {
+      const int r = 16 * wave + (lane >> 2), p = lane & 3;
+      const E* row = Qr + r * LDK + p * (CPR / 4) * EPC;
+      float ss[2] = {0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < CPR / 4; ++i) ss[i & 1] = sumsq16<E>(*reinterpret_cast<const u32x4*>(row + i * EPC), ss[i & 1]);
+      const float nq = __builtin_amdgcn_rsqf(quad_sum(ss[0] + ss[1]) + a.pro.norm_eps);
+      if (p == 0) Gbuf[nb * GS + 5 * C + r] = nq;
+    }
     __syncthreads();
 
     // ---- interval B: every LDS fragment of the interval first ----
@@ -2025,7 +2034,7 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
           Sacc[st][4 * g + 3] *= d.w;
         }
       } else {
-        const float gC = NORM ? __expf(G[C - 1]) : Eg[C - 1];
+        const float gC = NORM ? G[3 * C + C - 1] : Eg[C - 1];   // (exp(G_r) is row 3 when normalised)
 #pragma unroll
         for (int v = 0; v < 16; ++v) Sacc[st][v] *= gC;
       }
