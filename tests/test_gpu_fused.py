@@ -105,6 +105,27 @@ def test_fused_packed_rows(gpu, mode):
     assert eo <= 2e-2 and eS <= 2e-2, (eo, eS)
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+def test_fused_packed_long_rows_split(gpu, mode):
+    """The prologue on six packed rows over 16 heads, two of them (3000 and
+    1800 tokens) longer than an even share of chunks per compute unit: their
+    value slices run in two parts with a lead-in (from the history horizon
+    under scalar decay).  Every (row, head) against the oracle."""
+    lens = (3000, 100, 50, 1800, 0, 7)
+    T, H, N = sum(lens), 16, len(lens)
+    d = _inputs(1, T, H, 128, 128, torch.bfloat16, mode, 74, "norm+gates")
+    d["S0"] = 0.1 * torch.randn(N, H, 128, 128, generator=torch.Generator().manual_seed(75))
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    print("fused packed long rows mode %d" % mode, flush=True)
+    o, S = _gpu_fwd(gpu, d, mode, "norm+gates", cu=cu)
+    ro, rS = _oracle_fwd(d, mode, "norm+gates", cu=cu)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    eo = max(W.per_head_rel_err(o[:, a:b], ro[:, a:b], (0, 2))
+             for a, b in zip(cu[:-1].tolist(), cu[1:].tolist()) if b > a)
+    eS = W.per_head_rel_err(S, rS, (0, 1))
+    assert eo <= 2e-2 and eS <= 2e-2, (eo, eS)
+
+
 def test_fused_prefill_workload_sampled(gpu):
     """B=8, H=16, T=4096, d=128, bf16 with raw q, k and logit gates: two heads
     checked against the oracle."""
