@@ -1520,10 +1520,14 @@ struct WsPlan {
   // Q rows, the state update's K rows and (per-channel) the phase-1 K rows, V
   // rows, the gates: two buffers each (n and n + 1).  P: two buffers when the
   // data waves form it during the chain's use of the previous one.
+  // Per-channel decay with 64-row slices: one buffer each for Q and the
+  // phase-1 K rows, which only phase 1 reads (the data waves write those of
+  // n + 1 while the chain runs interval B of n).
+  static constexpr bool single = KDA && DVS == 64;
   static constexpr size_t qr = 0;
-  static constexpr size_t ks = qr + 2 * rows;
+  static constexpr size_t ks = qr + (single ? 1 : 2) * rows;
   static constexpr size_t kr = ks + 2 * srows;
-  static constexpr size_t sb = kr + (KDA ? 2 * rows : 0);
+  static constexpr size_t sb = kr + (KDA ? (single ? 1 : 2) * rows : 0);
   static constexpr size_t vr = sb + (size_t)DVS * LDSB * es;
   static constexpr size_t xt = vr + 2 * vrows;
   static constexpr size_t os = xt + (size_t)DVS * LDT * es;
@@ -1624,7 +1628,13 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
     // same loads (surplus threads repeat a valid block), so the wait counts
     // the compiler derives are exact; rows past the sequence end re-read its
     // last row, whose T rows and columns are zero.
-    auto load_k = [&](int n) __attribute__((always_inline)) {
+    // Row groups (parts): 1 the state update's K rows (K, or Kc), V and the
+    // gates; 2 Q and the per-channel phase-1 K rows; 3 both.
+    using AllRows = std::integral_constant<int, 3>;
+    using RowsA = std::integral_constant<int, 1>;
+    using RowsB = std::integral_constant<int, 2>;
+    auto load_k = [&](int n, auto parts) __attribute__((always_inline)) {
+      constexpr int PARTS = decltype(parts)::value;
       const int t0 = n * C;
       const int rmax = min(C, T - t0) - 1;
       const E* rq = recs + (size_t)n * R::elems;
@@ -1634,13 +1644,14 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
         const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
         if constexpr (KDA) {
           const uint32_t off = (uint32_t)r * DK + cc * EPC;
-          pk[m] = *reinterpret_cast<const u32x4*>(rq + R::kg + off);
-          pkc[m] = *reinterpret_cast<const u32x4*>(rq + R::kc + off);
-        } else {
+          if constexpr ((PARTS & 2) != 0) pk[m] = *reinterpret_cast<const u32x4*>(rq + R::kg + off);
+          if constexpr ((PARTS & 1) != 0) pkc[m] = *reinterpret_cast<const u32x4*>(rq + R::kc + off);
+        } else if constexpr ((PARTS & 1) != 0) {
           pk[m] = *reinterpret_cast<const u32x4*>(kq + (uint32_t)min(r, rmax) * (uint32_t)qk_tok + cc * EPC);
         }
       }
-      pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(ptid, NG4 - 1));
+      if constexpr ((PARTS & 1) != 0)
+        pg = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(rq + R::g) + 4 * min(ptid, NG4 - 1));
     };
     // (so: the lead-in, which needs no Q and no P)
     auto load_qv = [&](int n, auto so) __attribute__((always_inline)) {
@@ -1674,26 +1685,32 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
       }
     };
     // Rows of a chunk into buffer gb: Q, the state update's K operand (K, or
-    // Kc), the per-channel phase-1 K operand, V, and the gates.
-    auto commit_rows = [&](int gb, auto so) __attribute__((always_inline)) {
-      E* Qr = Qrb + gb * C * LDK;
+    // Kc), the per-channel phase-1 K operand, V, and the gates (the row groups
+    // of load_k; single Q and phase-1 K buffers take buffer 0).
+    auto commit_rows = [&](int gb, auto so, auto parts) __attribute__((always_inline)) {
+      constexpr int PARTS = decltype(parts)::value;
+      const int gq = L::single ? 0 : gb;
+      E* Qr = Qrb + gq * C * LDK;
       E* Ks = Ksb + gb * C * LDKS;
-      E* Kr = Krb + gb * C * LDK;
+      E* Kr = Krb + gq * C * LDK;
       E* Vr = Vrb + gb * C * LDV;
 #pragma unroll
       for (int m = 0; m < KPT; ++m) {
         const int q = ptid + PT * m, r = q / CPR, cc = q % CPR;
         const int o = r * LDK + cc * EPC;
-        if constexpr (!decltype(so)::value) *reinterpret_cast<u32x4*>(Qr + o) = pq[m];
-        *reinterpret_cast<u32x4*>(Ks + r * LDKS + swz_col(r, cc * EPC)) = KDA ? pkc[m] : pk[m];
-        if constexpr (KDA) *reinterpret_cast<u32x4*>(Kr + o) = pk[m];
+        if constexpr ((PARTS & 2) != 0 && !decltype(so)::value) *reinterpret_cast<u32x4*>(Qr + o) = pq[m];
+        if constexpr ((PARTS & 1) != 0)
+          *reinterpret_cast<u32x4*>(Ks + r * LDKS + swz_col(r, cc * EPC)) = KDA ? pkc[m] : pk[m];
+        if constexpr (KDA && (PARTS & 2) != 0) *reinterpret_cast<u32x4*>(Kr + o) = pk[m];
       }
+      if constexpr ((PARTS & 1) != 0) {
 #pragma unroll
-      for (int m = 0; m < VPT; ++m) {
-        const int q = ptid + PT * m, r = q / CPV, cc = q % CPV;
-        *reinterpret_cast<u32x4*>(Vr + r * LDV + cc * EPC) = G2 ? mul16<E>(pv[m], pw[m]) : pv[m];
+        for (int m = 0; m < VPT; ++m) {
+          const int q = ptid + PT * m, r = q / CPV, cc = q % CPV;
+          *reinterpret_cast<u32x4*>(Vr + r * LDV + cc * EPC) = G2 ? mul16<E>(pv[m], pw[m]) : pv[m];
+        }
+        if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * GS + 4 * ptid) = pg;
       }
-      if (ptid < NG4) *reinterpret_cast<u32x4*>(Gbuf + gb * GS + 4 * ptid) = pg;
     };
     // T (and the per-channel P) of a chunk.
     auto commit_tp = [&](auto so) __attribute__((always_inline)) {
@@ -1771,27 +1788,45 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
     // interval A use data loaded at least one interval earlier; the first step
     // (nothing to flush) is peeled so that no global access in the loop is
     // conditional.
+    // With single Q and phase-1 K buffers, Q and the phase-1 K rows of n + 1
+    // go in during interval B (phase 1 of n, their only reader, is over), and
+    // the phase-1 K rows of n + 2 are loaded there once those of n + 1 are in.
     auto step = [&](int n, int nlast, auto first, auto so) __attribute__((always_inline)) {
       constexpr bool SO = decltype(so)::value;
-      // interval A: the chain runs phase 1 of chunk n
-      if (n + 1 <= nlast) commit_rows((n + 1) & 1, so);
-      commit_tp(so);                 // T (and P) of chunk n
-      if constexpr (!SO && !decltype(first)::value) flush_o((n - 1) * C);
-      load_k(min(n + 2, nlast));
-      __syncthreads();
-      // interval B: the chain runs U, O and S of chunk n
-      load_tp(min(n + 1, nlast), so);
-      load_qv(min(n + 2, nlast), so);
-      if constexpr (!KDA && !SO) {
-        if (n + 1 <= nlast) form_p((n + 1) & 1);
+      if constexpr (L::single) {
+        // interval A: the chain runs phase 1 of chunk n
+        if (n + 1 <= nlast) commit_rows((n + 1) & 1, so, RowsA{});
+        commit_tp(so);                 // T (and P) of chunk n
+        if constexpr (!SO && !decltype(first)::value) flush_o((n - 1) * C);
+        load_k(min(n + 2, nlast), RowsA{});
+        __syncthreads();
+        // interval B: the chain runs U, O and S of chunk n
+        if (n + 1 <= nlast) commit_rows((n + 1) & 1, so, RowsB{});
+        load_tp(min(n + 1, nlast), so);
+        load_qv(min(n + 2, nlast), so);
+        load_k(min(n + 2, nlast), RowsB{});
+        __syncthreads();
+      } else {
+        // interval A: the chain runs phase 1 of chunk n
+        if (n + 1 <= nlast) commit_rows((n + 1) & 1, so, AllRows{});
+        commit_tp(so);                 // T (and P) of chunk n
+        if constexpr (!SO && !decltype(first)::value) flush_o((n - 1) * C);
+        load_k(min(n + 2, nlast), AllRows{});
+        __syncthreads();
+        // interval B: the chain runs U, O and S of chunk n
+        load_tp(min(n + 1, nlast), so);
+        load_qv(min(n + 2, nlast), so);
+        if constexpr (!KDA && !SO) {
+          if (n + 1 <= nlast) form_p((n + 1) & 1);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     };
     auto prologue = [&](int n0, int nlast, auto so) __attribute__((always_inline)) {
-      load_k(n0);
+      load_k(n0, AllRows{});
       load_qv(n0, so);
-      commit_rows(n0 & 1, so);
-      load_k(min(n0 + 1, nlast));
+      commit_rows(n0 & 1, so, AllRows{});
+      load_k(min(n0 + 1, nlast), AllRows{});
       load_qv(min(n0 + 1, nlast), so);
       load_tp(n0, so);
     };
@@ -1868,8 +1903,8 @@ __device__ __forceinline__ void state_ws_body(const PrefillArgs& a, const E* __r
     const float* Eg = G + C;       // exp(G_r) nk_r
     const float* Ec = G + 2 * C;   // exp(G_C - G_r) nk_r
     const E* Ks = Ksb + nb * C * LDKS;
-    const E* K1 = KDA ? Krb + nb * C * LDK : Ks;   // K operand of phase 1 (scalar: swizzled)
-    const E* Qr = Qrb + nb * C * LDK;
+    const E* K1 = KDA ? Krb + (L::single ? 0 : nb) * C * LDK : Ks;   // K operand of phase 1 (scalar: swizzled)
+    const E* Qr = Qrb + (L::single ? 0 : nb) * C * LDK;
     const E* Vr = Vrb + nb * C * LDV;
     const E* Pm = Pmb + (KDA ? 0 : nb) * C * LDP;
 
@@ -2347,14 +2382,10 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
     else if (a.mode == 1)
       hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 1, true>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
-    else if constexpr (DVS == 32) {   // the per-channel buffers leave room for 32-row slices only
-      if (a.mode == 2)
-        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
-      else
-        hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
-    } else {
-      return hipErrorInvalidConfiguration;
-    }
+    else if (a.mode == 2)
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 2, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
+    else
+      hipLaunchKernelGGL((chunk_state_ws<E, DK, DVS, 3, false>), grid, wblock, 0, stream, a, tws, np, r, split, nsq);
   } else {
     if (a.mode == 0)
       hipLaunchKernelGGL((chunk_state_kernel<E, DK, DVS, 0>), grid, block, 0, stream, a, tws);
@@ -2369,8 +2400,8 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
 }
 
 // Slice width: 64 value rows per workgroup (bf16) when that still gives at least
-// one workgroup per compute unit (256), else 32.  fp32 tiles take twice the LDS,
-// so fp32 always uses 32-row slices.
+// one workgroup per compute unit (256; per-channel decay: 128, in two parts),
+// else 32.  fp32 tiles take twice the LDS, so fp32 always uses 32-row slices.
 // One prep workgroup per chunk of every head; a packed batch takes one per
 // record slot (slots that no chunk falls on return at once).
 template <typename E, int DK>
@@ -2409,7 +2440,13 @@ hipError_t launch_dk(const PrefillArgs& a0, void* workspace, hipStream_t stream)
   E* tws = static_cast<E*>(workspace);
   PrefillArgs a = a0;
   const long long wg64 = (long long)a.B * a.H * (a.dv / 64);
-  const bool dvs64 = sizeof(E) == 2 && wg64 >= 256 && a.mode < 2;
+  // 64-row value slices (bf16): none or scalar decay, and Gated DeltaNet-2,
+  // when they give every compute unit a workgroup; per-channel decay already
+  // when two parts per slice do (its 32-row slices load the whole chunk record
+  // for half the rows: B=4 H=16 T=8192 458.8 -> 440.7 us with two parts,
+  // packed 16 rows 478 -> 420 us, Gated DeltaNet-2 at B=8 H=16 T=4096 503 ->
+  // 436 us; Gated DeltaNet-2 with two parts 498 -> 504 us).
+  const bool dvs64 = sizeof(E) == 2 && (wg64 >= 256 || (a.mode == 2 && wg64 >= 128));
   // Scalar decay in bf16 with split value slices (a head's, or a packed
   // batch's longest rows'): the prep kernel also writes the transition
   // bounds, after the records.
