@@ -2145,11 +2145,13 @@ __device__ inline int geometric_split(int nchunks, int p, int npart, float r) {
 // state at chunk m is S_s Phi(s, m) + (the recurrence over [s, m) from a zero
 // state), with |S_s Phi(s, m)| <= e^{c_s + ... + c_{m-1}} |S_s|.  A lead-in from
 // the last s at which that sum is at most -kHorizon, started from zero, thus
-// reaches the state at m up to a part below e^-100 of |S_s|: the same scale the
-// gate floor (kLogFloor) already neglects.  Strongly decaying gates forget the
-// far past within a few chunks, so the parts of a slice no longer need lead-ins
-// from chunk 0.
-constexpr float kHorizon = 100.f;
+// reaches the state at m up to a part below e^-40 (4e-18) of |S_s|: ten orders
+// of magnitude below the resolution of the fp32 state itself (e^-100, the gate
+// floor kLogFloor, took 2.5 times the lead-in chunks for nothing: the long-
+// context call ran 4 % slower).  Strongly decaying gates forget the far past
+// within a few chunks, so the parts of a slice no longer need lead-ins from
+// chunk 0.
+constexpr float kHorizon = 40.f;
 
 // Lead-in length (chunks) for a part whose outputs start at chunk m: the
 // smallest L with c_{m-L} + ... + c_{m-1} <= -kHorizon, or m (a lead-in from
