@@ -2146,9 +2146,9 @@ __device__ inline int geometric_split(int nchunks, int p, int npart, float r) {
 // state), with |S_s Phi(s, m)| <= e^{c_s + ... + c_{m-1}} |S_s|.  A lead-in from
 // the last s at which that sum is at most -kHorizon, started from zero, thus
 // reaches the state at m up to a part below e^-40 (4e-18) of |S_s|: ten orders
-// of magnitude below the resolution of the fp32 state itself (e^-100, the gate
-// floor kLogFloor, took 2.5 times the lead-in chunks for nothing: the long-
-// context call ran 4 % slower).  Strongly decaying gates forget the far past
+// of magnitude below the resolution of the fp32 state itself (a threshold at
+// the gate floor's e^-100 takes 2.5 times the lead-in chunks: 4 % more time on
+// the long-context workload).  Strongly decaying gates forget the far past
 // within a few chunks, so the parts of a slice no longer need lead-ins from
 // chunk 0.
 constexpr float kHorizon = 40.f;
@@ -2199,8 +2199,8 @@ __device__ inline int seq_by_length_rank(const PrefillArgs& a, int k) {
 }
 
 // Value slices in npart parts each (geometric split, lead-ins from chunk 0).
-// Packed batch of up to 64 sequences with more slices than compute units
-// (split_above >= 0): the workgroups take the sequences longest first, so
+// Packed batch of up to 64 sequences with at least half as many slices as
+// compute units (split_above >= 0): the workgroups take the sequences longest first, so
 // that the longest slices start in the first round and the short ones fill in
 // behind them; the slices of a sequence of more than split_above chunks run
 // in two parts, the second reaching its start by a lead-in (from the history
@@ -2349,7 +2349,8 @@ hipError_t launch_state(const PrefillArgs& a, const E* tws, hipStream_t stream) 
   dim3 grid((unsigned)slices), block(kThreads);
   if constexpr (sizeof(E) == 2) {
     const int np = state_parts(slices);
-    // packed batch of more slices than compute units: longest sequences first,
+    // packed batch of at least half as many slices as compute units (one
+    // part each otherwise): longest sequences first,
     // the slices longer than an even share of chunks per compute unit in two
     // parts (Sum ceil(len_s / C) <= T / C + N bounds the chunks; at most
     // (T / C + N) / (split + 1) sequences exceed split chunks)
