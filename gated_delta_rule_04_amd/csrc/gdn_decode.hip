@@ -72,11 +72,19 @@ __device__ inline float load1(const __bf16* p) {
 __device__ inline void store1(float* p, float x) { *p = x; }
 __device__ inline void store1(__bf16* p, float x) { *p = (__bf16)x; }
 
-// Sum over the LPR lanes that share a row (an aligned group of LPR lanes).
+// Sum over the LPR lanes that share a row (an aligned group of LPR lanes), by
+// DPP moves inside a row of 16 lanes: the two quad steps, then the half-row
+// and row mirrors (lane i of 8 takes lane 7 - i, lane i of 16 lane 15 - i);
+// every lane of the group ends with the sum.  (Cross-lane moves through LDS
+// would put an LDS round trip on each step of the reduction.)
 template <int LPR>
 __device__ inline float group_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off);
+  static_assert(LPR == 8 || LPR == 16, "groups of 8 or 16 lanes");
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  if constexpr (LPR == 16)
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));  // row_mirror
   return x;
 }
 
