@@ -13,11 +13,11 @@
 // Layout of the work: LPR lanes share a state row (8 at d_k = 128, 16 at
 // d_k = 64) and lane l owns its float4 columns {4l + 4 LPR j}, so each load
 // instruction of a wave covers whole rows as contiguous segments (coalesced
-// 128-bit accesses).  A thread holds one row at d_k = 128 (four float4) and two
-// rows at d_k = 64 (one float4 each); one 256-thread workgroup takes 32 rows
-// of a (b, h) head.  The fp32 rows are held in registers between the read and
-// the write, and the two row dot products are finished with xor-shuffles over
-// the row's lanes.
+// 128-bit accesses).  A thread holds one row at d_k = 128 (four float4; one
+// 256-thread workgroup takes 32 rows of a (b, h) head) and d_v / 16 rows at
+// d_k = 64 (one float4 each; one workgroup per head).  The fp32 rows are held
+// in registers between the read and the write, and the two row dot products
+// are finished with xor-shuffles over the row's lanes.
 // Gated DeltaNet-2 (MODE 3; "Linear Attention Architectures" notes, section
 // 2.6): the prediction reads the erase direction e = b * k, the target is
 // w_i v_i and there is no beta: s_k = S_i D e, u_i = w_i v_i - s_k; the write
@@ -38,10 +38,35 @@ namespace {
 constexpr int kThreads = 256;
 // Lanes that share a state row and 16-byte state pieces per thread: d_k = 128
 // takes 8 lanes per 512-byte row, one row per thread; d_k = 64 takes 16 lanes
-// per 256-byte row, two rows per thread (measured: 12.04 against 12.22 us per
-// step with 8 lanes, batch 64, 16 heads, d_v = 128).
+// per 256-byte row (measured: 12.04 against 12.22 us per step with 8 lanes,
+// batch 64, 16 heads, d_v = 128) and a whole head per workgroup, d_v / 16 rows
+// per thread: with the vector gate loads below, 12.5 -> 12.1 us per step with
+// HBM-resident states and a fresh token per step (each alone: about 12.55 and
+// 12.4 us; d_k = 128 keeps 32 rows per workgroup, 2 or 4 rows per thread
+// measured 23.8 and 24.8 against 22.5 us).
 template <int DK> constexpr int lanes_per_row() { return DK == 64 ? 16 : 8; }
-template <int DK> constexpr int f4_per_thread() { return DK == 64 ? 2 : 4; }
+template <int DK, int DV> constexpr int f4_per_thread() { return DK == 64 ? DV / 16 : 4; }
+
+// A zero the compiler cannot prove uniform: indexing the per-head gates with it
+// turns their loads into vector loads.  A uniform index makes them scalar
+// loads, whose round trip to memory is longer than the state rows' (measured:
+// about 0.15 us per step of 12.5 with fresh tokens from HBM) and which every
+// row's update waits for.
+// Wait until every vector memory load this wave has issued is back
+// (s_waitcnt vmcnt(0); the other counters at their maximum: expcnt 7,
+// lgkmcnt 15 in gfx9's encoding); the scheduling barriers keep the compiler
+// from moving loads across it.
+__device__ inline void wait_for_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ inline int lane_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -92,11 +117,22 @@ template <typename E, int DK, int DV, int MODE, bool PRO>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int LPR = lanes_per_row<DK>();               // lanes per row
   constexpr int NQ = DK / (4 * LPR);                     // float4 per lane per row
-  constexpr int NR = f4_per_thread<DK>() / NQ;           // rows per thread
+  constexpr int NR = f4_per_thread<DK, DV>() / NQ;       // rows per thread
   constexpr int RPW = kThreads / LPR;                    // rows per pass of the workgroup
   constexpr int RPG = RPW * NR;                          // rows per workgroup
   constexpr int GPH = DV / RPG;                          // workgroups per head
   static_assert(NQ >= 1 && NR >= 1 && GPH >= 1 && DV % RPG == 0, "unsupported head size");
+  // Rows of a lane group: g + RPW m, so that every load instruction of a wave
+  // covers whole rows that are consecutive in memory.  (Consecutive rows per
+  // group, g NR + m, would make a group's v and o entries one 16-byte run, but
+  // the waves' state accesses then become 256-byte pieces 2 KB apart: 12.29
+  // against 12.08 us per step at d_k = 64 with HBM-resident states.)
+  auto row = [](int g, int m) { return g + RPW * m; };
+  // The token's and the gates' loads are issued only once the state rows are
+  // in (an explicit wait): issued beside the state rows, these small loads
+  // from the token arrays slowed the step by about 0.9 us of 12.7 at d_k = 64
+  // (HBM-resident states, a fresh token per step from HBM).
+  constexpr bool STAGE = DK == 64;
 
   const size_t bh = blockIdx.x / GPH;
   const int r0 = (blockIdx.x % GPH) * RPG;               // first state row of this workgroup
@@ -114,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int m = 0; m < NR; ++m)
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) s[m][j] = load_state(S + (size_t)(g + RPW * m) * DK + 4 * l8 + 4 * LPR * j);
+    for (int j = 0; j < NQ; ++j) s[m][j] = load_state(S + (size_t)row(g, m) * DK + 4 * l8 + 4 * LPR * j);
+  if constexpr (STAGE) wait_for_loads();
 
   float4 kf[NQ], qf[NQ], af[NQ], bf[NQ];
 #pragma unroll
@@ -124,9 +161,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (MODE >= 2) af[j] = load4(static_cast<const E*>(a.alpha) + bh * DK + 4 * l8 + 4 * LPR * j);
     if (MODE == 3) bf[j] = load4(static_cast<const E*>(a.erase) + bh * DK + 4 * l8 + 4 * LPR * j);
   }
-  float beta = MODE == 3 ? 1.f : a.beta[bh];
+  const int z = DK == 64 ? lane_zero() : 0;   // (d_k = 128: scalar loads measured 0.2 us faster)
+  float beta = MODE == 3 ? 1.f : a.beta[bh + z];
   float alpha = 1.f;
-  if (MODE == 1) alpha = static_cast<const float*>(a.alpha)[bh];
+  if (MODE == 1) alpha = static_cast<const float*>(a.alpha)[bh + z];
   if constexpr (PRO) {
     const Prologue& p = a.pro;
     const int h = (int)(bh % a.H);
@@ -167,11 +205,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   float vr[NR];
 #pragma unroll
-  for (int m = 0; m < NR; ++m) vr[m] = load1(v + g + RPW * m);
+  for (int m = 0; m < NR; ++m) vr[m] = load1(v + row(g, m));
   if constexpr (MODE == 3) {   // target w_i v_i
     const E* wr = static_cast<const E*>(a.write) + bh * DV + r0;
 #pragma unroll
-    for (int m = 0; m < NR; ++m) vr[m] *= load1(wr + g + RPW * m);
+    for (int m = 0; m < NR; ++m) vr[m] *= load1(wr + row(g, m));
   }
 
   // k . q over the head (every group computes it; it is tiny)
@@ -214,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
     const float u = beta * (vr[m] - pk);
     const float out = pq + u * kq;
-    if (l8 == 0) store1(o + g + RPW * m, out);
+    if (l8 == 0) store1(o + row(g, m), out);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       float4 d = MODE >= 2 ? af[j] : make_float4(alpha, alpha, alpha, alpha);
@@ -223,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       r.y = s[m][j].y * d.y + u * kf[j].y;
       r.z = s[m][j].z * d.z + u * kf[j].z;
       r.w = s[m][j].w * d.w + u * kf[j].w;
-      store_state(S + (size_t)(g + RPW * m) * DK + 4 * l8 + 4 * LPR * j, r);
+      store_state(S + (size_t)row(g, m) * DK + 4 * l8 + 4 * LPR * j, r);
     }
   }
 }
@@ -231,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 template <typename E, int DK, int DV>
 hipError_t launch_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int LPR = lanes_per_row<DK>();
-  constexpr int RPG = kThreads / LPR * (f4_per_thread<DK>() / (DK / (4 * LPR)));
+  constexpr int RPG = kThreads / LPR * (f4_per_thread<DK, DV>() / (DK / (4 * LPR)));
   dim3 grid((unsigned)(a.B * a.H * (DV / RPG))), block(kThreads);
   const bool pro = a.pro.qk_norm || a.pro.beta_logits || a.pro.alpha_logits;
   switch (a.mode * 2 + (pro ? 1 : 0)) {
