@@ -62,9 +62,12 @@ NUM_SIMDS = 1024          # 256 compute units x 4 SIMDs
 NUM_XCDS = 8
 CHUNK = 64
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc", f)
-                  for f in ("gdn_chunk.hip", "gdn_mfma.h", "gdn_internal.h", "gdn_solve.h",
-                            "gdn_decode.hip")]
+_CSRC = os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc")
+# The sources the kernels of a workload are compiled from: a workload's counters
+# are valid while these files are unchanged.
+PREFILL_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_chunk.hip", "gdn_mfma.h", "gdn_internal.h",
+                                                     "gdn_solve.h")]
+DECODE_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_decode.hip", "gdn_internal.h")]
 HEADLINE = W.GDN_BF16_LONG
 PROTOCOL = dict(trials=3, warmup=10, reps=100)
 
@@ -113,9 +116,10 @@ def decode_bytes(w: W.Decode) -> int:
     return b
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(name: str) -> str:
+    """SHA-256 of the kernel sources workload ``name`` runs (decode or prefill)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (DECODE_SOURCES if name.startswith("decode") else PREFILL_SOURCES):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -129,7 +133,7 @@ def committed_counters(name):
             rec = json.load(f).get(name)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash(name):
         return None
     return rec
 
@@ -591,7 +595,7 @@ def summarize_pmc(dirs, name, out_json=COUNTER_FILE):
         if vals:
             scale[ctr] = copy_kib / (sum(vals) / len(vals))
     kernels = sorted({k for (k, c) in per if "gdn" in k})
-    rec = dict(kernel_source_sha256=kernel_source_hash(), workload=name, counter_scale=scale,
+    rec = dict(kernel_source_sha256=kernel_source_hash(name), workload=name, counter_scale=scale,
                note="per dispatch averages; HBM bytes = FETCH_SIZE / WRITE_SIZE KiB scaled so the "
                     "1 GiB device copy reads and writes 1 GiB; mfma_util = SQ_VALU_MFMA_BUSY_CYCLES "
                     "/ (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); clock = GRBM_GUI_ACTIVE / 8 / duration "
