@@ -42,8 +42,9 @@ constexpr int kThreads = 256;
 // batch 64, 16 heads, d_v = 128) and a whole head per workgroup, d_v / 16 rows
 // per thread: with the vector gate loads below, 12.5 -> 12.1 us per step with
 // HBM-resident states and a fresh token per step (each alone: about 12.55 and
-// 12.4 us; d_k = 128 keeps 32 rows per workgroup, 2 or 4 rows per thread
-// measured 23.8 and 24.8 against 22.5 us).
+// 12.4 us).  d_k = 128 keeps 32 rows per workgroup and issues all its loads at
+// once: 2 or 4 rows per thread measured 23.8 and 24.8 us against 22.5, and
+// with the staged loads below 24.2 and 24.5 (one row per thread: 24.3).
 template <int DK> constexpr int lanes_per_row() { return DK == 64 ? 16 : 8; }
 template <int DK, int DV> constexpr int f4_per_thread() { return DK == 64 ? DV / 16 : 4; }
 
@@ -79,19 +80,33 @@ __device__ inline void store_state(float* p, float4 v) {
   __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(p));
 }
 
-__device__ inline float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-
 __device__ inline float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-__device__ inline float4 load4(const __bf16* p) {
-  uint2 raw = *reinterpret_cast<const uint2*>(p);
-  return make_float4(bf16_to_f32(raw.x & 0xffff), bf16_to_f32(raw.x >> 16),
-                     bf16_to_f32(raw.y & 0xffff), bf16_to_f32(raw.y >> 16));
+// Token values as loaded: four elements (fp32: a float4; bf16: two words) or
+// one, converted to fp32 separately.
+template <typename E> struct Raw;
+template <> struct Raw<float> {
+  using four = float4;
+  using one = float;
+};
+template <> struct Raw<__bf16> {
+  using four = uint2;
+  using one = uint16_t;
+};
+__device__ inline float4 load_raw4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ inline uint2 load_raw4(const __bf16* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ inline float load_raw1(const float* p) { return *p; }
+__device__ inline uint16_t load_raw1(const __bf16* p) { return *reinterpret_cast<const uint16_t*>(p); }
+__device__ inline float4 to_f32x4(float4 x) { return x; }
+__device__ inline float4 to_f32x4(uint2 w) {
+  return make_float4(bf16_to_f32(w.x & 0xffff), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xffff),
+                     bf16_to_f32(w.y >> 16));
 }
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(uint16_t x) { return bf16_to_f32(x); }
 
-__device__ inline float load1(const float* p) { return *p; }
-__device__ inline float load1(const __bf16* p) {
-  return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+__device__ inline float dot4(const float4& a, const float4& b) {
+  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
 __device__ inline void store1(float* p, float x) { *p = x; }
@@ -153,18 +168,46 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int j = 0; j < NQ; ++j) s[m][j] = load_state(S + (size_t)row(g, m) * DK + 4 * l8 + 4 * LPR * j);
   if constexpr (STAGE) wait_for_loads();
 
-  float4 kf[NQ], qf[NQ], af[NQ], bf[NQ];
+  // The token's values and gates: every load is issued, as loaded words,
+  // before the first conversion (a conversion placed between the loads waits
+  // for its own load while the later ones are not yet issued; 0.2 us per step
+  // at d_k = 64 with a fresh token from HBM).
+  using R4 = typename Raw<E>::four;
+  using R1 = typename Raw<E>::one;
+  R4 kw[NQ], qw[NQ], aw[NQ], bw[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    kf[j] = load4(k + 4 * l8 + 4 * LPR * j);
-    qf[j] = load4(q + 4 * l8 + 4 * LPR * j);
-    if (MODE >= 2) af[j] = load4(static_cast<const E*>(a.alpha) + bh * DK + 4 * l8 + 4 * LPR * j);
-    if (MODE == 3) bf[j] = load4(static_cast<const E*>(a.erase) + bh * DK + 4 * l8 + 4 * LPR * j);
+    kw[j] = load_raw4(k + 4 * l8 + 4 * LPR * j);
+    qw[j] = load_raw4(q + 4 * l8 + 4 * LPR * j);
+    if (MODE >= 2) aw[j] = load_raw4(static_cast<const E*>(a.alpha) + bh * DK + 4 * l8 + 4 * LPR * j);
+    if (MODE == 3) bw[j] = load_raw4(static_cast<const E*>(a.erase) + bh * DK + 4 * l8 + 4 * LPR * j);
   }
   const int z = DK == 64 ? lane_zero() : 0;   // (d_k = 128: scalar loads measured 0.2 us faster)
   float beta = MODE == 3 ? 1.f : a.beta[bh + z];
   float alpha = 1.f;
   if (MODE == 1) alpha = static_cast<const float*>(a.alpha)[bh + z];
+  R1 vw[NR], ww[NR];
+  auto load_v = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      vw[m] = load_raw1(v + row(g, m));
+      if (MODE == 3) ww[m] = load_raw1(static_cast<const E*>(a.write) + bh * DV + r0 + row(g, m));   // target w_i v_i
+    }
+  };
+  // (d_k = 128: the v loads after the gates' arithmetic and no barrier; with
+  // the d_k = 64 order 0.1 - 0.4 us slower)
+  if constexpr (STAGE) {
+    load_v();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float4 kf[NQ], qf[NQ], af[NQ], bf[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    kf[j] = to_f32x4(kw[j]);
+    qf[j] = to_f32x4(qw[j]);
+    if (MODE >= 2) af[j] = to_f32x4(aw[j]);
+    if (MODE == 3) bf[j] = to_f32x4(bw[j]);
+  }
   if constexpr (PRO) {
     const Prologue& p = a.pro;
     const int h = (int)(bh % a.H);
@@ -188,11 +231,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
     }
     if (p.qk_norm) {   // fp32, exact scaling of the loaded values
-      float sk = 0.f, sq = 0.f;
+      float sk = dot4(kf[0], kf[0]), sq = dot4(qf[0], qf[0]);
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) {
-        sk += kf[j].x * kf[j].x + kf[j].y * kf[j].y + kf[j].z * kf[j].z + kf[j].w * kf[j].w;
-        sq += qf[j].x * qf[j].x + qf[j].y * qf[j].y + qf[j].z * qf[j].z + qf[j].w * qf[j].w;
+      for (int j = 1; j < NQ; ++j) {
+        sk += dot4(kf[j], kf[j]);
+        sq += dot4(qf[j], qf[j]);
       }
       const float nk = rsqrtf(group_sum<LPR>(sk) + p.norm_eps);
       const float nq = rsqrtf(group_sum<LPR>(sq) + p.norm_eps);
@@ -203,20 +246,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       }
     }
   }
-  float vr[NR];
-#pragma unroll
-  for (int m = 0; m < NR; ++m) vr[m] = load1(v + row(g, m));
-  if constexpr (MODE == 3) {   // target w_i v_i
-    const E* wr = static_cast<const E*>(a.write) + bh * DV + r0;
-#pragma unroll
-    for (int m = 0; m < NR; ++m) vr[m] *= load1(wr + row(g, m));
-  }
+
+  if constexpr (!STAGE) load_v();
 
   // k . q over the head (every group computes it; it is tiny)
-  float kq = 0.f;
+  float kq = dot4(kf[0], qf[0]);
 #pragma unroll
-  for (int j = 0; j < NQ; ++j)
-    kq += kf[j].x * qf[j].x + kf[j].y * qf[j].y + kf[j].z * qf[j].z + kf[j].w * qf[j].w;
+  for (int j = 1; j < NQ; ++j) kq += dot4(kf[j], qf[j]);
   kq = group_sum<LPR>(kq);
 
   // D k and D q for the per-channel decay (the scalar decay is applied to the sums)
@@ -238,11 +274,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
 #pragma unroll
   for (int m = 0; m < NR; ++m) {
-    float pk = 0.f, pq = 0.f;
+    // (sums start from their first term: an fp32 sum started at 0 keeps an
+    // add of +0 per sum, which the compiler may not drop)
+    float pk = dot4(s[m][0], kd[0]), pq = dot4(s[m][0], qd[0]);
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      pk += s[m][j].x * kd[j].x + s[m][j].y * kd[j].y + s[m][j].z * kd[j].z + s[m][j].w * kd[j].w;
-      pq += s[m][j].x * qd[j].x + s[m][j].y * qd[j].y + s[m][j].z * qd[j].z + s[m][j].w * qd[j].w;
+    for (int j = 1; j < NQ; ++j) {
+      pk += dot4(s[m][j], kd[j]);
+      pq += dot4(s[m][j], qd[j]);
     }
     pk = group_sum<LPR>(pk);
     pq = group_sum<LPR>(pq);
@@ -250,7 +288,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       pk *= alpha;
       pq *= alpha;
     }
-    const float u = beta * (vr[m] - pk);
+    // (v converted here, row by row: each row waits only for its own v)
+    const float vm = MODE == 3 ? to_f32(vw[m]) * to_f32(ww[m]) : to_f32(vw[m]);
+    const float u = beta * (vm - pk);
     const float out = pq + u * kq;
     if (l8 == 0) store1(o + row(g, m), out);
 #pragma unroll
