@@ -40,19 +40,14 @@ constexpr int kThreads = 256;
 // takes 8 lanes per 512-byte row, one row per thread; d_k = 64 takes 16 lanes
 // per 256-byte row (measured: 12.04 against 12.22 us per step with 8 lanes,
 // batch 64, 16 heads, d_v = 128) and a whole head per workgroup, d_v / 16 rows
-// per thread: with the vector gate loads below, 12.5 -> 12.1 us per step with
-// HBM-resident states and a fresh token per step (each alone: about 12.55 and
-// 12.4 us).  d_k = 128 keeps 32 rows per workgroup and issues all its loads at
+// per thread: with the vector gate loads and the staged token loads below,
+// 12.5 -> 11.9 us per step with HBM-resident states and a fresh token per step
+// (the layout alone about 12.55 us, the gate loads alone 12.4).  d_k = 128 keeps 32 rows per workgroup and issues all its loads at
 // once: 2 or 4 rows per thread measured 23.8 and 24.8 us against 22.5, and
 // with the staged loads below 24.2 and 24.5 (one row per thread: 24.3).
 template <int DK> constexpr int lanes_per_row() { return DK == 64 ? 16 : 8; }
 template <int DK, int DV> constexpr int f4_per_thread() { return DK == 64 ? DV / 16 : 4; }
 
-// A zero the compiler cannot prove uniform: indexing the per-head gates with it
-// turns their loads into vector loads.  A uniform index makes them scalar
-// loads, whose round trip to memory is longer than the state rows' (measured:
-// about 0.15 us per step of 12.5 with fresh tokens from HBM) and which every
-// row's update waits for.
 // Wait until every vector memory load this wave has issued is back
 // (s_waitcnt vmcnt(0); the other counters at their maximum: expcnt 7,
 // lgkmcnt 15 in gfx9's encoding); the scheduling barriers keep the compiler
@@ -63,6 +58,11 @@ __device__ inline void wait_for_loads() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// A zero the compiler cannot prove uniform: indexing the per-head gates with it
+// turns their loads into vector loads.  A uniform index makes them scalar
+// loads, whose round trip to memory is longer than the state rows' (measured:
+// about 0.15 us per step of 12.5 with fresh tokens from HBM) and which every
+// row's update waits for.
 __device__ inline int lane_zero() {
   int z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
