@@ -68,6 +68,9 @@ _CSRC = os.path.join(ROOT, "gated_delta_rule_04_amd", "csrc")
 PREFILL_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_chunk.hip", "gdn_mfma.h", "gdn_internal.h",
                                                      "gdn_solve.h")]
 DECODE_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_decode.hip", "gdn_internal.h")]
+# the backward also runs the prefill's prep kernel
+BACKWARD_SOURCES = PREFILL_SOURCES + [os.path.join(_CSRC, f) for f in ("gdn_bwd_chunk.hip", "gdn_backward.h")]
+EPILOGUE_SOURCES = [os.path.join(_CSRC, f) for f in ("gdn_epilogue.hip", "gdn_internal.h")]
 HEADLINE = W.GDN_BF16_LONG
 PROTOCOL = dict(trials=3, warmup=10, reps=100)
 
@@ -117,9 +120,12 @@ def decode_bytes(w: W.Decode) -> int:
 
 
 def kernel_source_hash(name: str) -> str:
-    """SHA-256 of the kernel sources workload ``name`` runs (decode or prefill)."""
+    """SHA-256 of the kernel sources workload ``name`` runs (decode, prefill,
+    backward or the output epilogue)."""
     h = hashlib.sha256()
-    for p in (DECODE_SOURCES if name.startswith("decode") else PREFILL_SOURCES):
+    srcs = (DECODE_SOURCES if name.startswith("decode") else BACKWARD_SOURCES if name.endswith("_backward")
+            else EPILOGUE_SOURCES if name.endswith("_gated_rmsnorm") else PREFILL_SOURCES)
+    for p in srcs:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -678,6 +684,24 @@ def profile_run(name, reps):
         run = PrefillRun(pw[name], W.make_prefill(pw[name]))
         for _ in range(reps):
             run()
+    elif name.endswith("_backward") and name[:-len("_backward")] in pw:
+        w = pw[name[:-len("_backward")]]
+        d = {k: (None if v is None else v.cuda()) for k, v in W.make_prefill(w).items()}
+        g = torch.Generator().manual_seed(w.seed + 400)
+        do = torch.randn(w.B, w.T, w.H, w.dv, generator=g).to(w.dtype).cuda()
+        dST = torch.randn(w.B, w.H, w.dv, w.dk, generator=g).cuda()
+        for _ in range(reps):
+            gdn.chunk_bwd(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], do, dST, mode=w.mode)
+    elif name.endswith("_gated_rmsnorm") and name[:-len("_gated_rmsnorm")] in pw:
+        w = pw[name[:-len("_gated_rmsnorm")]]
+        g = torch.Generator().manual_seed(w.seed + 500)
+        shape = (w.B, w.T, w.H, w.dv)
+        o = torch.randn(*shape, generator=g).to(w.dtype).cuda()
+        gate = torch.randn(*shape, generator=g).to(w.dtype).cuda()
+        wt = (1.0 + 0.5 * torch.randn(w.dv, generator=g)).cuda()
+        out = torch.empty_like(o)
+        for _ in range(reps):
+            gdn.gated_rmsnorm(o, gate, wt, eps=1e-6, out=out)
     elif name in dw:
         w = dw[name].with_(steps=min(dw[name].steps, reps))
         bench_decode(w, reps=1, rotate=16)
