@@ -382,7 +382,7 @@ def bench_packed(w: W.Packed, reps: int):
     return dict(workload=w.name, N=w.N, T=w.T, H=w.H, lengths_min=min(lens), lengths_max=max(lens),
                 launch_us=us, trials_us=trials, tokens_per_s=w.T / (us * 1e-6),
                 hbm_gbps=nbytes / (us * 1e-6) / 1e9, hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                algorithmic_bytes=nbytes)
+                algorithmic_bytes=nbytes, counters=committed_counters(w.name + "_gated_rmsnorm"))
 
 
 def bench_fused(w: W.Prefill, reps: int):
@@ -447,7 +447,7 @@ def bench_gdn2(w: W.Prefill, reps: int):
     return dict(workload="gdn2_" + w.name, launch_us=us, trials_us=trials,
                 tokens_per_s=w.B * w.T / (us * 1e-6),
                 hbm_gbps=nbytes / (us * 1e-6) / 1e9, hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                algorithmic_bytes=nbytes)
+                algorithmic_bytes=nbytes, counters=committed_counters(w.name + "_gated_rmsnorm"))
 
 
 def bench_backward(w: W.Prefill, reps: int):
@@ -471,7 +471,8 @@ def bench_backward(w: W.Prefill, reps: int):
     nbytes = 2 * prefill_bytes(w) + tok * w.dv * es + state   # inputs + dout, dS_final; the same again out
     return dict(workload=w.name + "_backward", launch_us=us, trials_us=trials,
                 tokens_per_s=w.B * w.T / (us * 1e-6), hbm_gbps=nbytes / (us * 1e-6) / 1e9,
-                hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, algorithmic_bytes=nbytes)
+                hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, algorithmic_bytes=nbytes,
+                counters=committed_counters(w.name + "_backward"))
 
 
 def bench_epilogue(w: W.Prefill, reps: int):
@@ -494,7 +495,7 @@ def bench_epilogue(w: W.Prefill, reps: int):
     nbytes = 3 * o.numel() * o.element_size() + w.dv * 4   # o, gate read; out written; the gain
     return dict(workload=w.name + "_gated_rmsnorm", launch_us=us, trials_us=trials,
                 hbm_gbps=nbytes / (us * 1e-6) / 1e9, hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                algorithmic_bytes=nbytes)
+                algorithmic_bytes=nbytes, counters=committed_counters(w.name + "_gated_rmsnorm"))
 
 
 def device_copy_gbps(nbytes=1 << 30):
